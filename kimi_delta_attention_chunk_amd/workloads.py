@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the KDA chunked forward.
+
+This module only draws random tensors with the shapes and value distributions of the
+workloads below; it holds none of the method's arithmetic.  The same host tensors feed the GPU
+library and the fp64 oracle.
+
+Conventions shared with the library (FlashKDA README, sections 参数说明 and 约束说明):
+q/k/v/beta are bf16, g and the states are fp32, cu_seqlens is an int32 prefix sum.
+By default q and k are raw N(0,1) rows and beta holds N(0,1) logits; the library is then
+called with its fused row L2-normalise and beta-sigmoid options switched on, which yields the
+"row L2-normalised q/k" and "beta = sigmoid(N(0,1))" distributions of the workloads.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+D = 128
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    layout: str                 # "BNSD" | "BSND" | "TND"
+    batch: int                  # B, or the number of packed sequences for TND
+    seq_len: int                # stored length S (TND: ignored, lengths are drawn)
+    n_qk: int
+    n_v: int
+    g_kind: str                 # "small" | "strong" | "unit" | "mixed"
+    init: bool                  # draw an fp32 N(0, 0.1^2) initial state
+    seed: int
+    tnd_max_len: int = 0        # TND: lengths uniform in [1, tnd_max_len]
+    note: str = ""
+
+
+WORKLOADS = [
+    Workload("tiny_s256", "BNSD", 1, 256, 1, 1, "small", False, 1000,
+             note="B=1, Nqk=Nv=1, S=256 (4 chunks); g = -0.05*U(0,1); zero state"),
+    Workload("prefill_s8k_n3", "BNSD", 1, 8192, 3, 3, "strong", True, 1001,
+             note="B=1, Nqk=Nv=3, S=8192, BNSD; g = -5*sigmoid(N(0,1)); state N(0,0.1^2)"),
+    Workload("gqa_tail_s4100", "BSND", 4, 4100, 4, 16, "unit", False, 1002,
+             note="B=4, Nqk=4, Nv=16, S=4100 (tail of 4), BSND; g = -sigmoid(N(0,1))"),
+    Workload("varlen_tnd_32seq", "TND", 32, 0, 32, 32, "strong", True, 1003, tnd_max_len=4096,
+             note="32 packed sequences, lengths U{1..4096}; Nqk=Nv=32; per-sequence states"),
+    Workload("long_s128k_n32", "BNSD", 1, 131072, 32, 32, "mixed", False, 1004,
+             note="B=1, Nqk=Nv=32, S=131072 (2048 chunks/head); mixed per-channel decay"),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+@dataclass
+class Inputs:
+    layout: str
+    batch: int
+    seq_len: int                # S for BNSD/BSND, T for TND
+    n_qk: int
+    n_v: int
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    initial_state: Optional[torch.Tensor]
+    cu_seqlens: Optional[torch.Tensor]
+    scale: float = 1.0 / math.sqrt(D)
+    qk_l2norm: bool = True
+    beta_sigmoid: bool = True
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def lengths(self) -> list:
+        if self.cu_seqlens is None:
+            return [self.seq_len] * self.batch
+        c = self.cu_seqlens.tolist()
+        return [c[i + 1] - c[i] for i in range(len(c) - 1)]
+
+    @property
+    def tokens(self) -> int:
+        return int(sum(self.lengths))
+
+    def to(self, device) -> "Inputs":
+        def mv(t):
+            return None if t is None else t.to(device)
+        return Inputs(self.layout, self.batch, self.seq_len, self.n_qk, self.n_v,
+                      mv(self.q), mv(self.k), mv(self.v), mv(self.g), mv(self.beta),
+                      mv(self.initial_state), mv(self.cu_seqlens), self.scale,
+                      self.qk_l2norm, self.beta_sigmoid, dict(self.meta))
+
+
+def _gate(kind: str, shape, gen: torch.Generator) -> torch.Tensor:
+    """Natural-log decay g <= 0 drawn per token and channel (last axis = channel)."""
+    if kind == "small":
+        return -0.05 * torch.rand(shape, generator=gen)
+    if kind == "strong":
+        return -5.0 * torch.sigmoid(torch.randn(shape, generator=gen))
+    if kind == "unit":
+        return -1.0 * torch.sigmoid(torch.randn(shape, generator=gen))
+    if kind == "mixed":
+        half = shape[-1] // 2
+        a = -0.01 * torch.rand(tuple(shape[:-1]) + (half,), generator=gen)
+        b = -5.0 * torch.sigmoid(torch.randn(tuple(shape[:-1]) + (shape[-1] - half,),
+                                             generator=gen))
+        return torch.cat([a, b], dim=-1)
+    if kind == "zero":
+        return torch.zeros(shape)
+    if kind == "floor":
+        return torch.full(shape, -5.0)
+    raise ValueError(kind)
+
+
+def make_inputs(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, *,
+                g_kind: str = "strong", init: bool = False, seed: int = 0,
+                lengths: Optional[list] = None, valid_lengths: Optional[list] = None,
+                d: int = D) -> Inputs:
+    """Draw one seeded input set.
+
+    layout "TND" packs ``lengths`` (a list of sequence lengths) into T tokens; for BNSD/BSND
+    ``valid_lengths`` (optional) becomes a cu_seqlens prefix sum of per-row valid lengths.
+    """
+    gen = torch.Generator().manual_seed(int(seed))
+    if layout == "TND":
+        assert lengths is not None and len(lengths) == batch
+        T = int(sum(lengths))
+        qs, vs, bs = (T, n_qk, d), (T, n_v, d), (T, n_v)
+        cu = torch.tensor([0] + list(torch.tensor(lengths).cumsum(0).tolist()),
+                          dtype=torch.int32)
+        stored = T
+    else:
+        if layout == "BNSD":
+            qs, vs, bs = (batch, n_qk, seq_len, d), (batch, n_v, seq_len, d), (batch, n_v,
+                                                                               seq_len)
+        elif layout == "BSND":
+            qs, vs, bs = (batch, seq_len, n_qk, d), (batch, seq_len, n_v, d), (batch, seq_len,
+                                                                               n_v)
+        else:
+            raise ValueError(layout)
+        cu = None
+        if valid_lengths is not None:
+            cu = torch.tensor([0] + list(torch.tensor(valid_lengths).cumsum(0).tolist()),
+                              dtype=torch.int32)
+        stored = seq_len
+    q = torch.randn(qs, generator=gen).to(torch.bfloat16)
+    k = torch.randn(qs, generator=gen).to(torch.bfloat16)
+    v = torch.randn(vs, generator=gen).to(torch.bfloat16)
+    g = _gate(g_kind, vs, gen).to(torch.float32).contiguous()
+    beta = torch.randn(bs, generator=gen).to(torch.bfloat16)
+    st = None
+    if init:
+        st = (0.1 * torch.randn((batch, n_v, d, d), generator=gen)).to(torch.float32)
+    return Inputs(layout, batch, stored, n_qk, n_v, q, k, v, g, beta, st, cu)
+
+
+def workload_inputs(w, seed: Optional[int] = None) -> Inputs:
+    """Inputs of one named workload (seed defaults to the workload's own)."""
+    if isinstance(w, str):
+        w = BY_NAME[w]
+    s = w.seed if seed is None else seed
+    if w.layout == "TND":
+        gen = torch.Generator().manual_seed(s + 7919)
+        lengths = torch.randint(1, w.tnd_max_len + 1, (w.batch,), generator=gen).tolist()
+        inp = make_inputs("TND", w.batch, 0, w.n_qk, w.n_v, g_kind=w.g_kind, init=w.init,
+                          seed=s, lengths=lengths)
+    else:
+        inp = make_inputs(w.layout, w.batch, w.seq_len, w.n_qk, w.n_v, g_kind=w.g_kind,
+                          init=w.init, seed=s)
+    inp.meta["workload"] = w.name
+    return inp

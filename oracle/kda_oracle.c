@@ -1,0 +1,255 @@
+/*
+ * kda_oracle.c -- fp64 CPU oracle for the chunked forward of Kimi Delta Attention (KDA).
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  The GPU library never includes, links or
+ * calls anything from this directory, and this file shares no code with it.
+ *
+ * What it computes (the plain token recurrence the chunked method reaches exactly):
+ *   For every sequence b and value head h, with query/key head hq = h / (n_v / n_qk):
+ *     S  = initial_state[b, h]            (a d_v x d_k matrix; rows are value channels)
+ *     for each token t of the sequence:
+ *       S[:, j] *= exp(g[t, j])           per-channel decay of the key columns
+ *       r  = v_t - S k_t                  delta-rule residual
+ *       S += beta_t * r k_t^T             rank-1 write
+ *       o_t = scale * S q_t               read after the write
+ *     final_state[b, h] = S
+ *   Optionally q and k rows are L2-normalised first (x / sqrt(sum x^2 + 1e-6)) and beta is
+ *   the logistic sigmoid of the stored value.
+ *
+ * Sources (the pages this follows):
+ *   - vLLM PR #43195 summary "KDA chunk prefill decay uses exp2", section 功能与动机: the
+ *     recurrence decays the state with a natural-base exp(g) (state *= exp(g)).
+ *   - FlashKDA README (CANNBot-DSL sample, Ascend 950), section 功能说明: gamma_t is the exp of
+ *     the running sum of g, the chunk matrices use gamma*K for the written key and gamma^-1*K for
+ *     the read key, which fixes decay-then-write and read-after-write; q/k row L2 normalise and
+ *     beta sigmoid are fused options; section 参数说明: the state's last two axes are (Dv, Dk);
+ *     the three layouts BNSD / BSND / TND and the cu_seqlens prefix sum (sections 参数说明 and
+ *     约束说明).
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *   - L2-norm epsilon 1e-6 inside the square root.
+ *   - GQA: value head h reads query/key head h / (n_v / n_qk) (contiguous groups).
+ *   - BNSD/BSND with cu_seqlens: batch row b holds cu[b+1]-cu[b] valid tokens at its start;
+ *     out rows past that length are left untouched by this oracle.
+ *   - initial_state == NULL means a zero state; final_state == NULL means it is not returned.
+ *
+ * Parity pins for this function live in the CPU test suite: a hand-worked two-token example,
+ * an independent brute-force evaluation of the chunk equations, and closed-form invariants.
+ * Compile-time planted mistakes (KDA_ORACLE_MUTANT) let the tests show that every pin set
+ * catches a wrong oracle; the default build defines none.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#ifndef KDA_ORACLE_MUTANT
+#define KDA_ORACLE_MUTANT 0
+#endif
+
+enum { ORACLE_BNSD = 0, ORACLE_BSND = 1, ORACLE_TND = 2 };
+enum { ORACLE_QK_L2NORM = 1u, ORACLE_BETA_SIGMOID = 2u };
+
+static double bf16_bits_to_double(uint16_t bits) {
+    uint32_t u = ((uint32_t)bits) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Element offset of (sequence b, token t, head h, channel 0) for a [.., D] tensor. */
+static size_t row_offset(int layout, int b, int t, int h, int n_heads, int seq_len,
+                         const int32_t *cu, int d) {
+    switch (layout) {
+    case ORACLE_BNSD: return (((size_t)b * n_heads + h) * seq_len + t) * (size_t)d;
+    case ORACLE_BSND: return (((size_t)b * seq_len + t) * n_heads + h) * (size_t)d;
+    default:          return (((size_t)cu[b] + t) * n_heads + h) * (size_t)d;
+    }
+}
+
+/* Offset of beta(sequence b, token t, head h) for a [..] tensor with no channel axis. */
+static size_t beta_offset(int layout, int b, int t, int h, int n_heads, int seq_len,
+                          const int32_t *cu) {
+    switch (layout) {
+    case ORACLE_BNSD: return ((size_t)b * n_heads + h) * seq_len + t;
+    case ORACLE_BSND: return ((size_t)b * seq_len + t) * n_heads + h;
+    default:          return ((size_t)cu[b] + t) * n_heads + h;
+    }
+}
+
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+int oracle_mutant_id(void) { return KDA_ORACLE_MUTANT; }
+
+/*
+ * Returns 0 on success, a negative number on invalid arguments.
+ * out:          doubles in v's shape and layout; only value channels dv in [dv_lo, dv_hi) of
+ *               valid rows are written.
+ * final_state:  doubles [batch, n_v, d_v, d_k] (NULL: not written); only rows [dv_lo, dv_hi).
+ * initial_state: fp32 [batch, n_v, d_v, d_k] or NULL.
+ * cu_seqlens:   int32 [batch + 1]; required for TND, optional (valid lengths) otherwise.
+ * Work is split over (sequence, value head, block of 16 state rows), the independent chains
+ * of the recurrence: every state row evolves on its own given q, k, g and beta.
+ */
+int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_k, int d_v,
+                   double scale, unsigned flags,
+                   const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                   const uint16_t *beta, const float *initial_state, const int32_t *cu_seqlens,
+                   int dv_lo, int dv_hi, double *out, double *final_state) {
+    if (layout < ORACLE_BNSD || layout > ORACLE_TND) return -1;
+    if (batch < 1 || n_qk < 1 || n_v < n_qk || n_v % n_qk != 0 || d_k < 1 || d_v < 1) return -2;
+    if (layout == ORACLE_TND && cu_seqlens == NULL) return -3;
+    if (layout != ORACLE_TND && seq_len < 1) return -4;
+    if (dv_lo < 0 || dv_hi > d_v || dv_lo >= dv_hi) return -5;
+    if (!q || !k || !v || !g || !beta || !out) return -6;
+
+    const int group = n_v / n_qk;
+    (void)group;
+    (void)scale;
+    const int rows_per_chain = 16;
+    const int n_blocks = (dv_hi - dv_lo + rows_per_chain - 1) / rows_per_chain;
+    const long n_chains = (long)batch * n_v * n_blocks;
+
+    #pragma omp parallel
+    {
+        double *S  = (double *)malloc(sizeof(double) * (size_t)rows_per_chain * d_k);
+        double *qh = (double *)malloc(sizeof(double) * (size_t)d_k);
+        double *kh = (double *)malloc(sizeof(double) * (size_t)d_k);
+        double *dec = (double *)malloc(sizeof(double) * (size_t)d_k);
+
+        #pragma omp for schedule(dynamic, 1)
+        for (long chain = 0; chain < n_chains; ++chain) {
+            const int blk = (int)(chain % n_blocks);
+            const int h = (int)((chain / n_blocks) % n_v);
+            const int b = (int)(chain / ((long)n_blocks * n_v));
+#if KDA_ORACLE_MUTANT == 5
+            const int hq = h % n_qk;                    /* planted: wrong GQA head map */
+#else
+            const int hq = h / group;
+#endif
+            const int r0 = dv_lo + blk * rows_per_chain;
+            const int r1 = (r0 + rows_per_chain < dv_hi) ? r0 + rows_per_chain : dv_hi;
+            const int nr = r1 - r0;
+            int len;
+            if (layout == ORACLE_TND || cu_seqlens) len = cu_seqlens[b + 1] - cu_seqlens[b];
+            else len = seq_len;
+
+            /* S rows r0..r1-1 of the [d_v, d_k] state */
+            for (int i = 0; i < nr; ++i)
+                for (int j = 0; j < d_k; ++j) {
+                    double s0 = 0.0;
+                    if (initial_state) {
+                        const size_t base = ((size_t)b * n_v + h) * (size_t)d_v * d_k;
+#if KDA_ORACLE_MUTANT == 9
+                        /* planted: state read transposed, as [d_k, d_v] */
+                        s0 = (j < d_v && (r0 + i) < d_k)
+                                 ? initial_state[base + (size_t)j * d_v + (r0 + i)] : 0.0;
+#else
+                        s0 = initial_state[base + (size_t)(r0 + i) * d_k + j];
+#endif
+                    }
+                    S[(size_t)i * d_k + j] = s0;
+                }
+
+            for (int t = 0; t < len; ++t) {
+                const size_t oq = row_offset(layout, b, t, hq, n_qk, seq_len, cu_seqlens, d_k);
+                const size_t ov = row_offset(layout, b, t, h, n_v, seq_len, cu_seqlens, d_v);
+                const size_t og = row_offset(layout, b, t, h, n_v, seq_len, cu_seqlens, d_k);
+                const size_t ob = beta_offset(layout, b, t, h, n_v, seq_len, cu_seqlens);
+
+                for (int j = 0; j < d_k; ++j) {
+                    qh[j] = bf16_bits_to_double(q[oq + j]);
+                    kh[j] = bf16_bits_to_double(k[oq + j]);
+                }
+#if KDA_ORACLE_MUTANT != 8
+                if (flags & ORACLE_QK_L2NORM) {
+                    double sq = 0.0, sk = 0.0;
+                    for (int j = 0; j < d_k; ++j) { sq += qh[j] * qh[j]; sk += kh[j] * kh[j]; }
+                    const double iq = 1.0 / sqrt(sq + 1e-6), ik = 1.0 / sqrt(sk + 1e-6);
+                    for (int j = 0; j < d_k; ++j) { qh[j] *= iq; kh[j] *= ik; }
+                }
+#endif
+                double bt = bf16_bits_to_double(beta[ob]);
+#if KDA_ORACLE_MUTANT != 7
+                if (flags & ORACLE_BETA_SIGMOID) bt = 1.0 / (1.0 + exp(-bt));
+#endif
+                for (int j = 0; j < d_k; ++j) {
+#if KDA_ORACLE_MUTANT == 11
+                    /* planted: gate taken from the previous token */
+                    const size_t ogp = (t > 0) ? row_offset(layout, b, t - 1, h, n_v, seq_len,
+                                                            cu_seqlens, d_k) : og;
+                    dec[j] = (t > 0) ? exp((double)g[ogp + j]) : 1.0;
+#elif KDA_ORACLE_MUTANT == 12
+                    dec[j] = exp2((double)g[og + j]);  /* planted: wrong base */
+#else
+                    dec[j] = exp((double)g[og + j]);
+#endif
+                }
+
+                for (int i = 0; i < nr; ++i) {
+                    double *Si = S + (size_t)i * d_k;
+                    const int dv = r0 + i;
+#if KDA_ORACLE_MUTANT == 3
+                    /* planted: decay the value rows instead of the key columns */
+                    const double drow = (dv < d_k) ? exp((double)g[og + dv]) : 1.0;
+                    for (int j = 0; j < d_k; ++j) Si[j] *= drow;
+#elif KDA_ORACLE_MUTANT == 1
+                    /* planted: decay applied after the write (below) */
+#else
+                    for (int j = 0; j < d_k; ++j) Si[j] *= dec[j];
+#endif
+#if KDA_ORACLE_MUTANT == 2
+                    double o_before = 0.0;      /* planted: read before the write */
+                    for (int j = 0; j < d_k; ++j) o_before += Si[j] * qh[j];
+#endif
+                    double sk = 0.0;
+                    for (int j = 0; j < d_k; ++j) sk += Si[j] * kh[j];
+                    const double vi = bf16_bits_to_double(v[ov + dv]);
+#if KDA_ORACLE_MUTANT == 4
+                    const double coef = bt * (vi + sk);          /* planted: sign */
+#elif KDA_ORACLE_MUTANT == 10
+                    const double coef = bt * vi - sk;             /* planted: beta on v only */
+#else
+                    const double coef = bt * (vi - sk);
+#endif
+                    for (int j = 0; j < d_k; ++j) Si[j] += coef * kh[j];
+#if KDA_ORACLE_MUTANT == 1
+                    for (int j = 0; j < d_k; ++j) Si[j] *= dec[j];
+#endif
+                    double o = 0.0;
+                    for (int j = 0; j < d_k; ++j) o += Si[j] * qh[j];
+#if KDA_ORACLE_MUTANT == 2
+                    o = o_before;
+#endif
+#if KDA_ORACLE_MUTANT == 6
+                    out[ov + dv] = o;                             /* planted: no scale */
+#else
+                    out[ov + dv] = scale * o;
+#endif
+                }
+            }
+
+            if (final_state) {
+                const size_t base = ((size_t)b * n_v + h) * (size_t)d_v * d_k;
+                for (int i = 0; i < nr; ++i)
+                    memcpy(final_state + base + (size_t)(r0 + i) * d_k, S + (size_t)i * d_k,
+                           sizeof(double) * (size_t)d_k);
+            }
+        }
+        free(S);
+        free(qh);
+        free(kh);
+        free(dec);
+    }
+    return 0;
+}
