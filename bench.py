@@ -1,0 +1,170 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA chunked forward (prefill) on one MI355X.
+
+One step = one kda_chunk_fwd call (every kernel of the path) over one batch of seeded synthetic
+inputs already resident in HBM.  Default workload: B=1, Nqk=Nv=3, S=8192, D=128, BNSD, strong
+decay g = -5*sigmoid(N(0,1)), fp32 initial state N(0, 0.1^2) -- the 8K-token prefill the metric
+is quoted on.  Prints one JSON line.
+
+Timing: W untimed warm-up steps, then K steps bracketed by torch.cuda.synchronize(); the input
+set rotates over enough copies that the step's inputs exceed the 256 MB last-level cache, so
+the bytes really come from HBM.  Per-kernel durations come from HIP events recorded by the
+library on the launch stream around each kernel (kda_chunk_fwd_timed) inside the same timed
+loop.  The CPU baseline times the fp64 oracle on the host cores on the full workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+MALL_BYTES = 256 << 20     # last-level (Infinity) cache
+
+METRIC = "KDA prefill tokens/s (all heads) at D=128, T=8K; % of MFMA/HBM roofline"
+
+
+def path_bytes(inp) -> int:
+    """Algorithmic bytes of one call: q,k (bf16) per q/k head, v (bf16), g (fp32), beta (bf16),
+    out (bf16) per value head, plus one fp32 state read and one written per (sequence, head)."""
+    t = inp.tokens
+    b = t * inp.n_qk * 128 * 2 * 2 + t * inp.n_v * (128 * 2 + 128 * 4 + 2 + 128 * 2)
+    states = inp.batch * inp.n_v * 128 * 128 * 4
+    return b + states * ((inp.initial_state is not None) + 1)
+
+
+def scan_bytes(inp) -> int:
+    """Compulsory bytes of the scan kernel: per (64-token chunk, value head) it reads W (bf16
+    hi+lo), Q' (bf16), K_dec (bf16 hi+lo), U (fp32), O_intra (bf16), gamma (fp32 x128) and writes
+    out; plus the states."""
+    chunks = sum((L + 63) // 64 for L in inp.lengths)
+    per_chunk = 64 * 128 * (4 + 2 + 4 + 4 + 2) + 128 * 4
+    out = inp.tokens * inp.n_v * 128 * 2
+    states = inp.batch * inp.n_v * 128 * 128 * 4
+    return chunks * inp.n_v * per_chunk + out + states * ((inp.initial_state is not None) + 1)
+
+
+def intra_bytes(inp) -> int:
+    """Compulsory bytes of the intra kernel: q,k,v,g,beta in, the per-chunk record out."""
+    chunks = sum((L + 63) // 64 for L in inp.lengths)
+    t = inp.tokens
+    rd = t * inp.n_v * (128 * 2 * 3 + 128 * 4 + 2)   # q,k re-read per value head
+    wr = chunks * inp.n_v * (64 * 128 * (4 + 2 + 4 + 4 + 2) + 128 * 4)
+    return rd + wr
+
+
+def cpu_baseline(inp, min_seconds: float = 10.0) -> dict:
+    from oracle import kda_oracle, oracle_threads, QK_L2NORM, BETA_SIGMOID
+    flags = (QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 3 or time.perf_counter() - t_start < min_seconds:
+        t0 = time.perf_counter()
+        kda_oracle(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
+                   inp.cu_seqlens, inp.layout, flags)
+        times.append(time.perf_counter() - t0)
+        if len(times) >= 200:
+            break
+    times.sort()
+    med = times[len(times) // 2]
+    return {"value": inp.tokens / med, "unit": "tokens/s", "cores": oracle_threads(),
+            "kind": "oracle",
+            "sample": f"full workload ({inp.tokens} tokens x {inp.n_v} heads), fp64 token "
+                      f"recurrence, median of {len(times)} runs over "
+                      f"{time.perf_counter() - t_start:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill_s8k_n3")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by whole heads with no communication; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    from kimi_delta_attention_chunk_amd import (chunk_fwd, kda_chunk_fwd_workspace,
+                                                kda_num_stages, kda_stage_name, make_shape)
+    from kimi_delta_attention_chunk_amd.workloads import workload_inputs, BY_NAME
+
+    wl = BY_NAME[args.workload]
+    host = workload_inputs(wl)
+    in_bytes = (host.q.numel() * 4 + host.v.numel() * 2 + host.g.numel() * 4 +
+                host.beta.numel() * 2)
+    copies = args.copies or max(1, min(16, math.ceil(2 * MALL_BYTES / max(in_bytes, 1))))
+    dev = torch.device("cuda", 0)
+    sets = [host.to(dev) for _ in range(copies)]
+    out = torch.empty_like(sets[0].v)
+    fin = torch.empty((host.batch, host.n_v, 128, 128), dtype=torch.float32, device=dev)
+    shape = make_shape(host.layout, host.batch, host.seq_len, host.n_qk, host.n_v, host.scale,
+                       host.qk_l2norm, host.beta_sigmoid)
+    ws = torch.empty(kda_chunk_fwd_workspace(shape), dtype=torch.uint8, device=dev)
+    nst = kda_num_stages()
+
+    for i in range(args.warmup):
+        chunk_fwd(sets[i % copies], out=out, final_state=fin, workspace=ws)
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(nst + 1)]
+              for _ in range(args.steps)]
+    for evs in events:          # torch creates the HIP event on its first record
+        for e in evs:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        chunk_fwd(sets[i % copies], out=out, final_state=fin, workspace=ws,
+                  stage_events=[e.cuda_event for e in events[i]])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    stage_ms = [sum(events[i][s].elapsed_time(events[i][s + 1]) for i in range(args.steps))
+                / args.steps for s in range(nst)]
+    dom = max(range(nst), key=lambda s: stage_ms[s])
+    kbytes = [intra_bytes(host), scan_bytes(host)]
+    achieved = kbytes[dom] / (stage_ms[dom] * 1e-3)
+    pbytes = path_bytes(host)
+    value = host.tokens / (ms_step * 1e-3)
+
+    res = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded; shapes and distributions of the workload)",
+        "config": {"workload": wl.name, "layout": host.layout, "batch": host.batch,
+                   "seq_len": host.seq_len, "tokens": host.tokens, "n_qk": host.n_qk,
+                   "n_v": host.n_v, "head_dim": 128, "input_copies": copies,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": kda_stage_name(dom), "achieved": achieved / 1e9,
+                     "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                     "traffic": None, "bytes_per_launch": kbytes[dom],
+                     "avg_launch_ms": stage_ms[dom]},
+        "path_roofline": {"bound": "hbm", "algorithmic_bytes": pbytes,
+                          "achieved": pbytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
+                          "frac": pbytes / (ms_step * 1e-3) / HBM_PEAK},
+        "stages_ms": {kda_stage_name(s): stage_ms[s] for s in range(nst)},
+        "token_heads_per_s": host.tokens * host.n_v / (ms_step * 1e-3),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(host)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

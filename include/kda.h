@@ -1,0 +1,137 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) chunked forward of Kimi Delta Attention (KDA).
+ *
+ * What one call computes.  For every sequence b and value head h (query/key head
+ * hq = h / (n_v / n_qk)), starting from S = initial_state[b, h] (a d_v x d_k fp32 matrix whose
+ * rows are value channels), every token t of the sequence does
+ *     S <- S * Diag(exp(g_t))                 decay of the key columns
+ *     S <- S + beta_t * (v_t - S k_t) k_t^T    delta-rule write
+ *     o_t = scale * S q_t                      read after the write
+ * and final_state[b, h] = S at the end.  This is the recurrence that the FlashKDA README
+ * (section 功能说明) evaluates chunk by chunk; the state decay is the natural-base exp(g) of the
+ * vLLM PR #43195 summary (section 功能与动机).  The library evaluates it in 64-token chunks
+ * with 16-token sub-blocks, log2-space gates and bf16 MFMA, exactly up to rounding.
+ *
+ * Interface model: the FlashKDA README (sections 参数说明, 返回值说明, 约束说明) -- q, k, v,
+ * g, beta, scale, initial_state, layout, cu_seqlens in; out and a new final_state back.  The
+ * raw-gate activation (A_log, dt_bias, lower_bound) and the Ascend scheduling metadata of that
+ * interface are not part of this library: g is the already activated natural-log decay.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer on the current HIP device, 16-byte aligned and
+ *     contiguous in the stated layout.  The caller owns all buffers and the stream; the library
+ *     allocates no device memory and keeps no state between calls (it is reentrant; concurrent
+ *     calls need distinct workspaces).
+ *   - Work is enqueued on `stream`; the call returns right after enqueueing.  The host never
+ *     reads device data.
+ *   - Arguments are validated on the host, from shapes and pointers only, before any launch.
+ *     A failed check returns an error and launches nothing.
+ *   - Not checked (preconditions, as in the FlashKDA README, section 约束说明): cu_seqlens
+ *     starts at 0, is strictly increasing and ends at seq_len (TND); with BNSD/BSND each valid
+ *     length lies in [1, seq_len]; -5 <= g <= 0; all tensors live on one device.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Physical layouts (FlashKDA README, section 参数说明).  B = batch, N = heads, S = stored
+ * length, T = packed tokens, D = 128:
+ *   BNSD: q,k [B,n_qk,S,D]  v,g,out [B,n_v,S,D]  beta [B,n_v,S]
+ *   BSND: q,k [B,S,n_qk,D]  v,g,out [B,S,n_v,D]  beta [B,S,n_v]
+ *   TND:  q,k [T,n_qk,D]    v,g,out [T,n_v,D]    beta [T,n_v]   (packed; cu_seqlens required) */
+typedef enum {
+    KDA_LAYOUT_BNSD = 0,
+    KDA_LAYOUT_BSND = 1,
+    KDA_LAYOUT_TND = 2
+} kda_layout;
+
+/* Fused prologue options (FlashKDA README, section 功能说明: q/k row L2 normalise and the beta
+ * sigmoid are fused into the operator).  KDA_QK_L2NORM replaces each q and k row x by
+ * x / sqrt(sum(x^2) + 1e-6); KDA_BETA_SIGMOID reads beta as a logit and applies 1/(1+e^-x). */
+enum {
+    KDA_QK_L2NORM = 1u << 0,
+    KDA_BETA_SIGMOID = 1u << 1
+};
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,  /* a NULL or misaligned pointer, bad enum, negative size, alias */
+    KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (d_k != 128) */
+    KDA_ERR_WORKSPACE = 3,    /* workspace pointer NULL or workspace_bytes too small */
+    KDA_ERR_HIP = 4           /* a HIP launch or event call failed (hipGetLastError) */
+} kda_status;
+
+typedef struct {
+    int32_t layout;    /* a kda_layout value                                                 */
+    int32_t batch;     /* B for BNSD/BSND; number of packed sequences for TND                 */
+    int32_t seq_len;   /* S (stored length) for BNSD/BSND; T (total packed tokens) for TND    */
+    int32_t n_qk;      /* query/key heads, 1 <= n_qk <= n_v                                   */
+    int32_t n_v;       /* value heads, n_v % n_qk == 0 (GQA groups of n_v / n_qk)            */
+    int32_t d_k;       /* must be 128                                                         */
+    int32_t d_v;       /* must be 128                                                         */
+    float scale;       /* output scale, typically d_k ** -0.5; must be finite                 */
+    uint32_t flags;    /* KDA_QK_L2NORM | KDA_BETA_SIGMOID                                    */
+} kda_shape;
+
+/* Bytes of device workspace kda_chunk_fwd needs for `shape` (FlashKDA README, section 功能说明:
+ * the per-chunk intermediates of the chunk equations, W, U, the q-side operand, the decayed
+ * keys and the intra-chunk output, live here between the two kernels).  Depends only on the
+ * shape.  Returns KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED for shapes kda_chunk_fwd rejects. */
+kda_status kda_chunk_fwd_workspace(const kda_shape* shape, size_t* bytes);
+
+/* The chunked forward (prefill) of KDA.  Semantics: see the top of this file.
+ *   q, k           bf16 in `layout`; raw rows when KDA_QK_L2NORM is set
+ *   v              bf16 in `layout`
+ *   g              fp32, same shape as v: activated natural-log decay per token and key channel
+ *   beta           bf16 (logits when KDA_BETA_SIGMOID is set)
+ *   initial_state  fp32 [batch, n_v, d_v, d_k] or NULL (zero state); never written
+ *   cu_seqlens     int32 [batch + 1] prefix sum: required for TND; for BNSD/BSND optional, then
+ *                  batch row b holds cu_seqlens[b+1]-cu_seqlens[b] valid tokens at its start
+ *   out            bf16, same shape and layout as v.  Rows past a row's valid length are
+ *                  written with zeros (the FlashKDA README leaves them undefined)
+ *   final_state    fp32 [batch, n_v, d_v, d_k] or NULL (not produced); must not overlap
+ *                  initial_state
+ *   workspace      device buffer of at least kda_chunk_fwd_workspace() bytes, 256-byte aligned
+ * Returns KDA_OK once both kernels are enqueued on `stream`. */
+kda_status kda_chunk_fwd(const kda_shape* shape,
+                         const void* q, const void* k, const void* v,
+                         const float* g, const void* beta,
+                         const float* initial_state, const int32_t* cu_seqlens,
+                         void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Number of kernel launches one kda_chunk_fwd call enqueues, and the name of each stage. */
+int32_t kda_num_stages(void);
+const char* kda_stage_name(int32_t stage);
+
+/* Profiling variant of kda_chunk_fwd: identical work, plus hipEventRecord(stage_events[0])
+ * before the first kernel and hipEventRecord(stage_events[i]) right after kernel i, all on
+ * `stream`.  n_stage_events must be at least kda_num_stages() + 1; the events are created by
+ * the caller.  Used to time each kernel inside a benchmark's timed region. */
+kda_status kda_chunk_fwd_timed(const kda_shape* shape,
+                               const void* q, const void* k, const void* v,
+                               const float* g, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens,
+                               void* out, float* final_state,
+                               void* workspace, size_t workspace_bytes,
+                               hipStream_t stream,
+                               hipEvent_t* stage_events, int32_t n_stage_events);
+
+/* Static string naming a status code ("KDA_OK", ...); "unknown kda_status" otherwise. */
+const char* kda_status_str(kda_status status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,935 @@
+// kda_kernels.hip -- gfx950 (MI355X, CDNA4) kernels and C ABI of the KDA chunked forward.
+//
+// Method (FlashKDA README, section 功能说明, chunk equations): inside a chunk of n <= 64 tokens
+// with running gate sums G (restarted every chunk),
+//     Kt = exp(G)*K,  Kb = exp(-G)*K,  Qt = scale*exp(G)*Q,
+//     T = strictly-lower(diag(beta) Kt Kb^T),  Ainv = (I + T)^-1,
+//     U = Ainv diag(beta) V,  W = Ainv diag(beta) Kt,
+// and the state is carried from chunk to chunk.  The carry used here (the plain reading; the
+// vLLM #43195 summary, sections 实现拆解 and 关键源码片段, names the same per-chunk products
+// h and v_new and an output kernel o = q h + A v_new):
+//     V_new = U - W S^T,   O = Qt S^T + Aqk V_new,   Aqk = lower-with-diagonal(Qt Kb^T),
+//     S <- S diag(exp(G_last)) + V_new^T (K * exp(G_last - G)).
+// Two kernels:
+//   kda_intra_kernel  one workgroup per (64-token chunk, value head), fully parallel.  Computes
+//                     the log2-space running gate sum, the decayed operands, T and Aqk on bf16
+//                     MFMA, the fp32 blocked inverse, W and U, and folds the chunk-local terms:
+//                     Q' = Qt - Aqk W and O_intra = Aqk U, so that O = Q' S^T + O_intra.
+//                     Writes W, Q', K_dec, U, O_intra and gamma_last in MFMA fragment order.
+//   kda_scan_kernel   one workgroup per (sequence, value head, 16-row Dv tile) walks the chunks
+//                     in order with its state tile resident in registers:
+//                     V_new = U - W S^T, O = Q' S^T + O_intra, S <- gamma*S + K_dec^T V_new.
+//
+// Overflow safety (vLLM #43195 summary, 实现拆解 / 关键源码片段: gates kept in log2 space and
+// every decay an exp2 of a difference; flash-linear-attention PR #656: 16-token sub-blocks).
+// exp(-G) is never formed.  For sub-blocks I > J the decay between rows i (block I) and j
+// (block J) is split at the first row r_I of block I into two factors <= 1; inside a diagonal
+// block the read key carries 2^(G_r - G_j) <= 2^(15 * 5 * log2 e) < 2^109 for g >= -5, finite
+// in fp32/bf16, and masked entries are removed by select, never by multiplication.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "kda.h"
+#include "kda_plan.h"
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct Params {
+    const __bf16* q;
+    const __bf16* k;
+    const __bf16* v;
+    const float* g;
+    const __bf16* beta;
+    const float* init;
+    const int32_t* cu;
+    __bf16* out;
+    float* fin;
+    __bf16* Wf;   // [record][hi/lo][tt 4][kb 4][lane 64][8]  W[16tt+m][32kb+8q+j]
+    __bf16* Qf;   // [record][tt 4][kb 4][lane 64][8]         Q'[16tt+m][32kb+8q+j]
+    __bf16* Kf;   // [record][hi/lo][mt 8][s 2][lane 64][8]   K_dec[32s+8q+j][16mt+m]
+    float* Uf;    // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n]
+    __bf16* Of;   // [record][nt 8][tt 4][lane 64][4]         O_intra[16tt+n][16nt+4q+i]
+    float* Gf;    // [record][128]                            2^(G2_last)
+    int layout, batch, seq_len, n_qk, n_v, group, nc_max;
+    int scan_tiles;
+    float scale;
+    uint32_t flags;
+};
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): about 16 mantissa bits in two MFMA
+// operands; a product of two such pairs drops only the lo*lo term.
+__device__ __forceinline__ __bf16 bf16_lo(float x, __bf16 hi) { return (__bf16)(x - (float)hi); }
+#define SPLIT_BF16(x, hi, lo)          \
+    do {                               \
+        const float x_ = (x);          \
+        (hi) = (__bf16)x_;             \
+        (lo) = bf16_lo(x_, (hi));      \
+    } while (0)
+
+// 16-byte fragment read from an LDS row whose stride is only 8-byte aligned.
+__device__ __forceinline__ bf16x8 lds_read8_a8(const __bf16* p) {
+    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
+    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 4);
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        r[e] = a[e];
+        r[4 + e] = b[e];
+    }
+    return r;
+}
+
+// LDS-only barrier: waits for this wave's LDS traffic, then the workgroup barrier.  Outstanding
+// global loads (prefetches) stay in flight.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Sequence geometry: valid length and the chunk-slot base, identical in both kernels.
+__device__ __forceinline__ void seq_info(const Params& p, int b, int& c0, int& len,
+                                         int& slot0) {
+    if (p.layout == KDA_LAYOUT_TND) {
+        int a = p.cu[b], e = p.cu[b + 1];
+        a = a < 0 ? 0 : (a > p.seq_len ? p.seq_len : a);
+        e = e < a ? a : (e > p.seq_len ? p.seq_len : e);
+        c0 = a;
+        len = e - a;
+        slot0 = a / kChunk + b;
+    } else {
+        int l = p.seq_len;
+        if (p.cu) {
+            l = p.cu[b + 1] - p.cu[b];
+            l = l < 0 ? 0 : (l > p.seq_len ? p.seq_len : l);
+        }
+        c0 = 0;
+        len = l;
+        slot0 = b * p.nc_max;
+    }
+}
+
+// Element offset of token 0 and the token stride for (sequence b, head h) of a tensor with
+// `heads` heads and `e` elements per (token, head): BNSD [B,H,S,e], BSND [B,S,H,e], TND [T,H,e].
+__device__ __forceinline__ void row_geom(const Params& p, int b, int h, int heads, int e,
+                                         int c0, size_t& base, size_t& stride) {
+    if (p.layout == KDA_LAYOUT_BNSD) {
+        base = (size_t(b) * heads + h) * size_t(p.seq_len) * e;
+        stride = size_t(e);
+    } else if (p.layout == KDA_LAYOUT_BSND) {
+        base = (size_t(b) * p.seq_len * heads + h) * size_t(e);
+        stride = size_t(heads) * e;
+    } else {
+        base = (size_t(c0) * heads + h) * size_t(e);
+        stride = size_t(heads) * e;
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Intra-chunk kernel
+// ---------------------------------------------------------------------------------------------
+
+constexpr int G2_LD = 132;   // fp32 [64][132]
+constexpr int RAW_LD = 136;  // bf16 [64][136]
+constexpr int TR_LD = 72;    // bf16 [128][72]  feature-major, token-contiguous (16-byte rows)
+constexpr int TP_LD = 68;    // bf16 [128][68]  same, packed to fit hi+lo pairs (8-byte rows)
+constexpr int F_LD = 68;     // fp32 [64][68]
+constexpr int R_LD = 136;    // bf16 [16][136]
+
+constexpr int OFF_G2 = 0;                  // sG2 33792 | later sR 26112 | later sAi 17408
+constexpr int OFF_QK = 33792;              // raw q,k 34816 | later sKt hi,lo | later sKd hi,lo
+constexpr int OFF_VT = OFF_QK + 34816;     // sVt 18432
+constexpr int OFF_T = OFF_VT + 18432;      // sT 17408 | later sWt 18432
+constexpr int OFF_AQK = OFF_T + 18432;     // sAqk 17408
+constexpr int OFF_UT = OFF_AQK + 17408;    // sUt 18432
+constexpr int OFF_TMP = OFF_UT + 18432;    // inverse temp [16][48] fp32 3072
+constexpr int OFF_VEC = OFF_TMP + 3072;    // 15 x 128 fp32 = 7680
+constexpr int OFF_SMALL = OFF_VEC + 7680;  // beta[64], qn[64], kn[64], tot[128]
+constexpr int INTRA_LDS = OFF_SMALL + 1280;
+constexpr int TP_BYTES = 128 * TP_LD * 2;  // one packed feature-major tile, 17408
+static_assert(2 * TP_BYTES <= 34816, "hi/lo tiles fit the raw q/k region");
+static_assert(INTRA_LDS <= 160 * 1024, "intra kernel LDS budget");
+
+// vector rows inside OFF_VEC
+constexpr int VEC_BV = 0;    // 6 rows: 2^(G2[16I] - G2[16J]) for (I,J) = (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
+constexpr int VEC_A = 6;     // 4 rows: 2^(G2[16I])
+constexpr int VEC_C = 10;    // 4 rows: 2^(G2[63] - G2[16I])
+constexpr int VEC_GAM = 14;  // 1 row : 2^(G2[63])
+
+__device__ __forceinline__ int pair_index(int I, int J) {  // I > J
+    return (I * (I - 1)) / 2 + J;
+}
+
+__global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) unsigned char smem[INTRA_LDS];
+    float* sG2 = reinterpret_cast<float*>(smem + OFF_G2);
+    __bf16* sQraw = reinterpret_cast<__bf16*>(smem + OFF_QK);
+    __bf16* sKraw = reinterpret_cast<__bf16*>(smem + OFF_QK + 64 * RAW_LD * 2);
+    __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
+    float* sT = reinterpret_cast<float*>(smem + OFF_T);
+    float* sAqk = reinterpret_cast<float*>(smem + OFF_AQK);
+    __bf16* sUt = reinterpret_cast<__bf16*>(smem + OFF_UT);
+    float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
+    float* sVec = reinterpret_cast<float*>(smem + OFF_VEC);
+    float* sBeta = reinterpret_cast<float*>(smem + OFF_SMALL);
+    float* sQn = sBeta + 64;
+    float* sKn = sBeta + 128;
+    float* sTot = sBeta + 192;
+    __bf16* sR = reinterpret_cast<__bf16*>(smem + OFF_G2);               // phase 1b-2
+    float* sAi = reinterpret_cast<float*>(smem + OFF_G2);                // phase 3-5
+    __bf16* sKtH = reinterpret_cast<__bf16*>(smem + OFF_QK);             // phase 1b-4
+    __bf16* sKtL = reinterpret_cast<__bf16*>(smem + OFF_QK + TP_BYTES);
+    __bf16* sKdH = reinterpret_cast<__bf16*>(smem + OFF_QK);             // phase 5-6
+    __bf16* sKdL = reinterpret_cast<__bf16*>(smem + OFF_QK + TP_BYTES);
+    __bf16* sWt = reinterpret_cast<__bf16*>(smem + OFF_T);               // phase 4-5
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+
+    const int64_t rec = blockIdx.x;
+    const int slot = int(rec / p.n_v);
+    const int h = int(rec % p.n_v);
+    const int hq = h / p.group;
+
+    // chunk slot -> (sequence b, chunk j)
+    int b, j;
+    if (p.layout == KDA_LAYOUT_TND) {
+        int lo = 0, hi = p.batch - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            int cm = p.cu[mid];
+            cm = cm < 0 ? 0 : (cm > p.seq_len ? p.seq_len : cm);
+            if (cm / kChunk + mid <= slot) lo = mid; else hi = mid - 1;
+        }
+        b = lo;
+    } else {
+        b = slot / p.nc_max;
+    }
+    int c0, len, slot0;
+    seq_info(p, b, c0, len, slot0);
+    j = slot - slot0;
+    if (j < 0 || j * kChunk >= len) return;  // an unused slot: nothing reads it
+    const int t0 = j * kChunk;
+    const int n = (len - t0) < kChunk ? (len - t0) : kChunk;
+
+    size_t qb, qs, vb, vs, bb, bs;
+    row_geom(p, b, hq, p.n_qk, kHead, c0, qb, qs);
+    row_geom(p, b, h, p.n_v, kHead, c0, vb, vs);
+    row_geom(p, b, h, p.n_v, 1, c0, bb, bs);
+    qb += size_t(t0) * qs;
+    vb += size_t(t0) * vs;
+    bb += size_t(t0) * bs;
+
+    // ---- phase 0: running gate sums (log2 space), raw q/k, v^T, beta -----------------------
+    {
+        const int c = tid & 127, half = tid >> 7;
+        float run = 0.f;
+        float vals[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            const int t = half * 32 + i;
+            const float x = (t < n) ? p.g[vb + size_t(t) * vs + c] : 0.f;
+            run += x;
+            vals[i] = run;
+        }
+        if (half == 0) sTot[c] = run;
+        __syncthreads();
+        const float add = half ? sTot[c] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sG2[(half * 32 + i) * G2_LD + c] = (vals[i] + add) * kLog2e;
+    }
+    {
+        const int r = tid >> 2, part = tid & 3;
+        const bool valid = r < n;
+        float sq = 0.f, sk = 0.f;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int c = part * 32 + u * 8;
+            bf16x8 xq, xk, xv;
+            if (valid) {
+                xq = *reinterpret_cast<const bf16x8*>(p.q + qb + size_t(r) * qs + c);
+                xk = *reinterpret_cast<const bf16x8*>(p.k + qb + size_t(r) * qs + c);
+                xv = *reinterpret_cast<const bf16x8*>(p.v + vb + size_t(r) * vs + c);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    xq[e] = (__bf16)0.f;
+                    xk[e] = (__bf16)0.f;
+                    xv[e] = (__bf16)0.f;
+                }
+            }
+            *reinterpret_cast<bf16x8*>(sQraw + r * RAW_LD + c) = xq;
+            *reinterpret_cast<bf16x8*>(sKraw + r * RAW_LD + c) = xk;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float fq = (float)xq[e], fk = (float)xk[e];
+                sq += fq * fq;
+                sk += fk * fk;
+                sVt[(c + e) * TR_LD + r] = xv[e];
+            }
+        }
+        sq += __shfl_xor(sq, 1);
+        sq += __shfl_xor(sq, 2);
+        sk += __shfl_xor(sk, 1);
+        sk += __shfl_xor(sk, 2);
+        if (part == 0) {
+            const bool l2 = (p.flags & KDA_QK_L2NORM) != 0;
+            sQn[r] = l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+            sKn[r] = l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+        }
+    }
+    if (tid < 64) {
+        float x = 0.f;
+        if (tid < n) {
+            x = (float)p.beta[bb + size_t(tid) * bs];
+            if (p.flags & KDA_BETA_SIGMOID) x = 1.0f / (1.0f + expf(-x));
+        }
+        sBeta[tid] = x;
+    }
+    __syncthreads();
+
+    // ---- phase 0b: per-channel block factors ------------------------------------------------
+    {
+        const int c = tid & 127, half = tid >> 7;
+        if (half == 0) {
+            const int PI[6] = {1, 2, 2, 3, 3, 3};
+            const int PJ[6] = {0, 0, 1, 0, 1, 2};
+#pragma unroll
+            for (int u = 0; u < 6; ++u)
+                sVec[(VEC_BV + u) * 128 + c] =
+                    exp2_fast(sG2[16 * PI[u] * G2_LD + c] - sG2[16 * PJ[u] * G2_LD + c]);
+        } else {
+            const float gl = sG2[63 * G2_LD + c];
+#pragma unroll
+            for (int I = 0; I < 4; ++I) {
+                const float gr = sG2[16 * I * G2_LD + c];
+                sVec[(VEC_A + I) * 128 + c] = exp2_fast(gr);
+                sVec[(VEC_C + I) * 128 + c] = exp2_fast(gl - gr);
+            }
+            const float gam = exp2_fast(gl);
+            sVec[VEC_GAM * 128 + c] = gam;
+            p.Gf[size_t(rec) * kHead + c] = gam;
+        }
+    }
+
+    // ---- phase 1a: row block I = w in registers (A-fragment order) ---------------------------
+    // lane (q4, n16) owns token 16I + n16 and channels 32kb + 8q4 + e
+    const int I = w;
+    const int irow = 16 * I + n16;
+    float Lk[32], Lq[32], KF[32];
+    {
+        const float qn = sQn[irow], kn = sKn[irow];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int cb = 32 * kb + 8 * q4;
+            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(sKraw + irow * RAW_LD + cb);
+            const bf16x8 qr = *reinterpret_cast<const bf16x8*>(sQraw + irow * RAW_LD + cb);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // e = 2^(G2_i - G2_r) <= 1 and f = 2^(G2_r - G2_i) < 2^109 with r = 16I
+                const float d = sG2[irow * G2_LD + cb + e] - sG2[16 * I * G2_LD + cb + e];
+                const float ef = exp2_fast(d);
+                const float ff = exp2_fast(-d);
+                const float kv = (float)kr[e] * kn;
+                Lk[kb * 8 + e] = kv * ef;
+                Lq[kb * 8 + e] = (float)qr[e] * qn * ef;
+                KF[kb * 8 + e] = kv * ff;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 1b: operands for the other sub-blocks, (beta K~)^T, Q~^T, K_dec ---------------
+    bf16x8 Lkb[4], Lqb[4], KFb[4];
+    float Qt[32];
+    float Kd[32];
+    {
+        const float bi = sBeta[irow];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int cb = 32 * kb + 8 * q4;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = cb + e;
+                const float a = sVec[(VEC_A + I) * 128 + c];
+                Lkb[kb][e] = (__bf16)Lk[kb * 8 + e];
+                Lqb[kb][e] = (__bf16)Lq[kb * 8 + e];
+                KFb[kb][e] = (__bf16)KF[kb * 8 + e];
+                Qt[kb * 8 + e] = p.scale * Lq[kb * 8 + e] * a;
+                Kd[kb * 8 + e] = KF[kb * 8 + e] * sVec[(VEC_C + I) * 128 + c];
+                __bf16 hi, lo;
+                SPLIT_BF16(bi * Lk[kb * 8 + e] * a, hi, lo);
+                sKtH[c * TP_LD + irow] = hi;
+                sKtL[c * TP_LD + irow] = lo;
+            }
+        }
+        for (int I2 = I + 1; I2 < 4; ++I2) {
+            const int pi = pair_index(I2, I);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int cb = 32 * kb + 8 * q4;
+                bf16x8 r;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    r[e] = (__bf16)(KF[kb * 8 + e] * sVec[(VEC_BV + pi) * 128 + cb + e]);
+                *reinterpret_cast<bf16x8*>(sR + (pi * 16 + n16) * R_LD + cb) = r;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: T and Aqk sub-blocks (row block I) on MFMA ---------------------------------
+    for (int J = 0; J < 4; ++J) {
+        if (J > I) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                sT[(16 * I + 4 * q4 + r) * F_LD + 16 * J + n16] = 0.f;
+                sAqk[(16 * I + 4 * q4 + r) * F_LD + 16 * J + n16] = 0.f;
+            }
+            continue;
+        }
+        f32x4 aT = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 bfrag;
+            if (J == I) {
+                bfrag = KFb[kb];
+            } else {
+                bfrag = *reinterpret_cast<const bf16x8*>(
+                    sR + (pair_index(I, J) * 16 + n16) * R_LD + 32 * kb + 8 * q4);
+            }
+            aT = mfma(Lkb[kb], bfrag, aT);
+            aQ = mfma(Lqb[kb], bfrag, aQ);
+        }
+        // masked entries of a diagonal block may be huge: removed by select
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = 16 * I + 4 * q4 + r;
+            const int jj = 16 * J + n16;
+            sT[i * F_LD + jj] = (i > jj) ? sBeta[i] * aT[r] : 0.f;
+            sAqk[i * F_LD + jj] = (i >= jj) ? p.scale * aQ[r] : 0.f;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: Ainv = (I + T)^-1 in fp32 -------------------------------------------------
+    for (int e = tid; e < 64 * 64; e += kThreads) {
+        const int r = e >> 6, c = e & 63;
+        if ((c >> 4) > (r >> 4)) sAi[r * F_LD + c] = 0.f;
+    }
+    if (lane < 16) {  // diagonal block I by forward substitution, column `lane`
+        float x[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float s = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < i; ++m) s -= sT[(16 * I + i) * F_LD + 16 * I + m] * x[m];
+            x[i] = s;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sAi[(16 * I + i) * F_LD + 16 * I + lane] = x[i];
+    }
+    __syncthreads();
+    for (int I2 = 1; I2 < 4; ++I2) {
+        // P_J = sum_{K=J}^{I2-1} T[I2,K] Ainv[K,J]
+        for (int e = tid; e < I2 * 256; e += kThreads) {
+            const int J = e >> 8, r = (e >> 4) & 15, c = e & 15;
+            float s = 0.f;
+            for (int K = J; K < I2; ++K)
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    s += sT[(16 * I2 + r) * F_LD + 16 * K + u] * sAi[(16 * K + u) * F_LD + 16 * J + c];
+            sTmp[r * 48 + 16 * J + c] = s;
+        }
+        __syncthreads();
+        // Ainv[I2,J] = -Ainv[I2,I2] P_J
+        for (int e = tid; e < I2 * 256; e += kThreads) {
+            const int J = e >> 8, r = (e >> 4) & 15, c = e & 15;
+            float s = 0.f;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                s += sAi[(16 * I2 + r) * F_LD + 16 * I2 + u] * sTmp[u * 48 + 16 * J + c];
+            sAi[(16 * I2 + r) * F_LD + 16 * J + c] = -s;
+        }
+        __syncthreads();
+    }
+
+    // ---- phase 4: W^T and U for token block I, three-term hi/lo products --------------------
+    const int nks = (I >= 2) ? 2 : 1;  // 32-token K steps that reach the diagonal
+    {
+        f32x4 accW[8], accU[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            accW[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accU[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        for (int s = 0; s < nks; ++s) {
+            // Ainv[16I + n16][32s + 8q4 + e]: B fragment of W^T = (beta K~)^T Ainv^T and A
+            // fragment of U = Ainv (beta V)
+            bf16x8 ah, al;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) SPLIT_BF16(sAi[irow * F_LD + 32 * s + 8 * q4 + e], ah[e], al[e]);
+            float b8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) b8[e] = sBeta[32 * s + 8 * q4 + e];
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft) {
+                const int kb = ft >> 1, hf = ft & 1;
+                const int feat = 32 * kb + 8 * (n16 >> 2) + 4 * hf + (n16 & 3);
+                const bf16x8 xh = lds_read8_a8(sKtH + feat * TP_LD + 32 * s + 8 * q4);
+                const bf16x8 xl = lds_read8_a8(sKtL + feat * TP_LD + 32 * s + 8 * q4);
+                accW[ft] = mfma(xh, ah, accW[ft]);
+                accW[ft] = mfma(xl, ah, accW[ft]);
+                accW[ft] = mfma(xh, al, accW[ft]);
+            }
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const bf16x8 vv =
+                    *reinterpret_cast<const bf16x8*>(sVt + (16 * nt + n16) * TR_LD + 32 * s + 8 * q4);
+                bf16x8 vh, vl;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) SPLIT_BF16((float)vv[e] * b8[e], vh[e], vl[e]);
+                accU[nt] = mfma(ah, vh, accU[nt]);
+                accU[nt] = mfma(al, vh, accU[nt]);
+                accU[nt] = mfma(ah, vl, accU[nt]);
+            }
+        }
+        // W^T C layout: lane (q4, n16) holds W[token 16I + n16][32kb + 8q4 + 4hf + r]
+        __bf16* wdst = p.Wf + size_t(rec) * (kWBytes / 2);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 oh, ol;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                SPLIT_BF16(accW[2 * kb][r], oh[r], ol[r]);
+                SPLIT_BF16(accW[2 * kb + 1][r], oh[4 + r], ol[4 + r]);
+            }
+            *reinterpret_cast<bf16x8*>(wdst + ((I * 4 + kb) * 64 + lane) * 8) = oh;
+            *reinterpret_cast<bf16x8*>(wdst + 8192 + ((I * 4 + kb) * 64 + lane) * 8) = ol;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sWt[(32 * kb + 8 * q4 + e) * TR_LD + irow] = oh[e];
+        }
+        // U C layout: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
+        float* udst = p.Uf + size_t(rec) * (kUBytes / 4);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            *reinterpret_cast<f32x4*>(udst + ((nt * 4 + I) * 64 + lane) * 4) = accU[nt];
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (__bf16)accU[nt][r];
+            *reinterpret_cast<bf16x4*>(sUt + (16 * nt + n16) * TR_LD + 16 * I + 4 * q4) = o;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 5: O_intra^T = U^T Aqk^T and Q'^T = Q~^T - W^T Aqk^T (token block I) --------
+    {
+        f32x4 accO[8], accQ[8];
+#pragma unroll
+        for (int f = 0; f < 8; ++f) {
+            accO[f] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int kb = f >> 1, hf = f & 1;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accQ[f][r] = Qt[kb * 8 + 4 * hf + r];
+        }
+        for (int s = 0; s < nks; ++s) {
+            bf16x8 qh, ql;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) SPLIT_BF16(sAqk[irow * F_LD + 32 * s + 8 * q4 + e], qh[e], ql[e]);
+#pragma unroll
+            for (int nt = 0; nt < 8; ++nt) {
+                const bf16x8 a =
+                    *reinterpret_cast<const bf16x8*>(sUt + (16 * nt + n16) * TR_LD + 32 * s + 8 * q4);
+                accO[nt] = mfma(a, qh, accO[nt]);
+                accO[nt] = mfma(a, ql, accO[nt]);
+            }
+#pragma unroll
+            for (int ft = 0; ft < 8; ++ft) {
+                const int kb = ft >> 1, hf = ft & 1;
+                const int feat = 32 * kb + 8 * (n16 >> 2) + 4 * hf + (n16 & 3);
+                bf16x8 a = *reinterpret_cast<const bf16x8*>(sWt + feat * TR_LD + 32 * s + 8 * q4);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) a[e] = -a[e];
+                accQ[ft] = mfma(a, qh, accQ[ft]);
+                accQ[ft] = mfma(a, ql, accQ[ft]);
+            }
+        }
+        __bf16* odst = p.Of + size_t(rec) * (kOBytes / 2);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (__bf16)accO[nt][r];
+            *reinterpret_cast<bf16x4*>(odst + ((nt * 4 + I) * 64 + lane) * 4) = o;
+        }
+        __bf16* qdst = p.Qf + size_t(rec) * (kQBytes / 2);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            bf16x8 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                o[r] = (__bf16)accQ[2 * kb][r];
+                o[4 + r] = (__bf16)accQ[2 * kb + 1][r];
+            }
+            *reinterpret_cast<bf16x8*>(qdst + ((I * 4 + kb) * 64 + lane) * 8) = o;
+        }
+        // K_dec hi/lo into the feature-major staging tiles (the (beta K~)^T tiles are dead)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                __bf16 hi, lo;
+                SPLIT_BF16(Kd[kb * 8 + e], hi, lo);
+                sKdH[(32 * kb + 8 * q4 + e) * TP_LD + irow] = hi;
+                sKdL[(32 * kb + 8 * q4 + e) * TP_LD + irow] = lo;
+            }
+    }
+    __syncthreads();
+
+    // ---- phase 6: K_dec fragments (A operand of the state update), hi then lo ---------------
+    {
+        __bf16* kdst = p.Kf + size_t(rec) * (kKBytes / 2);
+        for (int f = tid; f < 2 * 16 * 64; f += kThreads) {
+            const int hl = f >> 10, frag = (f >> 6) & 15, ln = f & 63;
+            const int mt = frag >> 1, s = frag & 1;
+            const int qq = ln >> 4, m = ln & 15;
+            const __bf16* src = (hl ? sKdL : sKdH) + (16 * mt + m) * TP_LD + 32 * s + 8 * qq;
+            *reinterpret_cast<bf16x8*>(kdst + size_t(f) * 8) = lds_read8_a8(src);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------------------------
+// Inter-chunk scan kernel
+// ---------------------------------------------------------------------------------------------
+
+constexpr int S_LD = 136;   // bf16 [BV][136]  state tile (hi or lo), row = value channel
+constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = value channel
+
+struct ChunkFrags {
+    bf16x8 wh[4], wl[4];      // W hi/lo, token tile w, 32-channel block kb
+    bf16x8 qp[4];             // Q', token tile w
+    bf16x8 kh[2][2], kl[2][2];// K_dec^T hi/lo, Dk tile 2w+mt, token step s
+    f32x4 gm[2];              // gamma_last for the lane's Dk rows
+};
+
+template <int NT>
+struct ChunkTile {
+    f32x4 u[NT];              // U (fp32), token tile w, Dv tile
+    bf16x4 o[NT];             // O_intra (bf16), token tile w, Dv tile
+};
+
+template <int NT>
+__device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
+                                           int dv_tile0, ChunkFrags& f, ChunkTile<NT>& t) {
+    const __bf16* wsrc = p.Wf + size_t(rec) * (kWBytes / 2);
+    const __bf16* qsrc = p.Qf + size_t(rec) * (kQBytes / 2);
+    const __bf16* ksrc = p.Kf + size_t(rec) * (kKBytes / 2);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+        f.wh[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * 4 + kb) * 64 + lane) * 8);
+        f.wl[kb] = *reinterpret_cast<const bf16x8*>(wsrc + 8192 + ((w * 4 + kb) * 64 + lane) * 8);
+        f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * 4 + kb) * 64 + lane) * 8);
+    }
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int off = (((2 * w + mt) * 2 + s) * 64 + lane) * 8;
+            f.kh[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + off);
+            f.kl[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + 8192 + off);
+        }
+    const float* gsrc = p.Gf + size_t(rec) * kHead;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+        f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (2 * w + mt) + 4 * (lane >> 4));
+    const float* usrc = p.Uf + size_t(rec) * (kUBytes / 4);
+    const __bf16* osrc = p.Of + size_t(rec) * (kOBytes / 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int dt = dv_tile0 + nt;
+        t.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
+        t.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
+    }
+}
+
+// Writes one fp32 state fragment (4 consecutive Dk values of one Dv row) as hi/lo bf16.
+__device__ __forceinline__ void put_state(__bf16* sSh, __bf16* sSl, int row, int col,
+                                          f32x4 x) {
+    bf16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) SPLIT_BF16(x[i], h[i], l[i]);
+    *reinterpret_cast<bf16x4*>(sSh + row * S_LD + col) = h;
+    *reinterpret_cast<bf16x4*>(sSl + row * S_LD + col) = l;
+}
+
+template <int NT>
+__global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
+    constexpr int BV = 16 * NT;
+    __shared__ __attribute__((aligned(16))) __bf16 sSh[BV * S_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 sSl[BV * S_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 sVh[BV * VN_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 sVl[BV * VN_LD];
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+
+    // XCD-aware decode: the Dv tiles of one (sequence, head) share blockIdx.x mod 8, so they run
+    // on one XCD and share its L2 for the chunk operands they all read.
+    const int pid = blockIdx.x;
+    const int xcd = pid & 7, r8 = pid >> 3;
+    const int bh = (r8 / p.scan_tiles) * 8 + xcd;
+    const int tile = r8 % p.scan_tiles;
+    if (bh >= p.batch * p.n_v) return;
+    const int b = bh / p.n_v;
+    const int h = bh % p.n_v;
+    const int dv_tile0 = tile * NT;   // first 16-wide Dv tile of this workgroup
+
+    int c0, len, slot0;
+    seq_info(p, b, c0, len, slot0);
+    const int nchunks = (len + kChunk - 1) / kChunk;
+    size_t ob, os;
+    row_geom(p, b, h, p.n_v, kHead, c0, ob, os);
+
+    // state tile: S[mt][nt][i] = S[dv = 16(dv_tile0+nt) + n16][dk = 16(2w+mt) + 4q4 + i]
+    f32x4 S[2][NT];
+    const size_t st_base = (size_t(b) * p.n_v + h) * kHead * kHead;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int dv = 16 * (dv_tile0 + nt) + n16;
+            const int dk = 16 * (2 * w + mt) + 4 * q4;
+            if (p.init)
+                S[mt][nt] = *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * kHead + dk);
+            else
+                S[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            put_state(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
+        }
+    lds_barrier();
+
+    ChunkFrags cur, nxt;
+    ChunkTile<NT> curt, nxtt;
+    if (nchunks > 0)
+        load_chunk<NT>(p, int64_t(slot0) * p.n_v + h, w, lane, dv_tile0, cur, curt);
+
+    for (int jc = 0; jc < nchunks; ++jc) {
+        if (jc + 1 < nchunks)
+            load_chunk<NT>(p, int64_t(slot0 + jc + 1) * p.n_v + h, w, lane, dv_tile0, nxt, nxtt);
+
+        // X = W S^T (tokens of tile w x Dv), three-term hi/lo; Y^T = S Q'^T (Dv x tokens)
+        f32x4 accX[NT], accY[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accY[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
+                const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sSh + off);
+                const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSl + off);
+                accX[nt] = mfma(cur.wh[kb], sh, accX[nt]);
+                accX[nt] = mfma(cur.wl[kb], sh, accX[nt]);
+                accX[nt] = mfma(cur.wh[kb], sl, accX[nt]);
+                accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
+            }
+        }
+        const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            bf16x4 vh, vl;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) SPLIT_BF16(curt.u[nt][r] - accX[nt][r], vh[r], vl[r]);
+            const int off = (16 * nt + n16) * VN_LD + 16 * w + 4 * q4;
+            *reinterpret_cast<bf16x4*>(sVh + off) = vh;
+            *reinterpret_cast<bf16x4*>(sVl + off) = vl;
+            if (tok < len) {
+                bf16x4 o;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)curt.o[nt][r]);
+                *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * (dv_tile0 + nt) +
+                                           4 * q4) = o;
+            }
+        }
+        lds_barrier();
+
+        // S^T <- gamma * S^T + K_dec^T V_new  (Dk rows of this wave x Dv), three-term hi/lo
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            bf16x8 vh[2], vl[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int off = (16 * nt + n16) * VN_LD + 32 * s + 8 * q4;
+                vh[s] = *reinterpret_cast<const bf16x8*>(sVh + off);
+                vl[s] = *reinterpret_cast<const bf16x8*>(sVl + off);
+            }
+#pragma unroll
+            for (int mt = 0; mt < 2; ++mt) {
+                f32x4 acc = S[mt][nt] * cur.gm[mt];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    acc = mfma(cur.kh[mt][s], vh[s], acc);
+                    acc = mfma(cur.kl[mt][s], vh[s], acc);
+                    acc = mfma(cur.kh[mt][s], vl[s], acc);
+                }
+                S[mt][nt] = acc;
+                put_state(sSh, sSl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, acc);
+            }
+        }
+        lds_barrier();
+        cur = nxt;
+        curt = nxtt;
+    }
+
+    if (p.fin) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int dv = 16 * (dv_tile0 + nt) + n16;
+                const int dk = 16 * (2 * w + mt) + 4 * q4;
+                *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * kHead + dk) = S[mt][nt];
+            }
+    }
+    // rows past a batch row's valid length (BNSD/BSND with cu_seqlens) are written as zeros
+    if (p.layout != KDA_LAYOUT_TND && len < p.seq_len) {
+        const int rows = p.seq_len - len;
+        for (int e = tid; e < rows * NT * 4; e += kThreads) {
+            const int t = len + e / (NT * 4);
+            const int part = e % (NT * 4);
+            bf16x4 z;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = (__bf16)0.f;
+            *reinterpret_cast<bf16x4*>(p.out + ob + size_t(t) * os + 16 * dv_tile0 + 4 * part) = z;
+        }
+    }
+}
+
+constexpr int kScanNT = 1;
+
+kda_status launch(const kda_shape* shape, const void* q, const void* k, const void* v,
+                  const float* g, const void* beta, const float* initial_state,
+                  const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev, int n_ev) {
+    Plan plan;
+    kda_status st = make_plan(shape, kScanNT, &plan);
+    if (st != KDA_OK) return st;
+    st = check_call(shape, plan, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                    workspace, workspace_bytes);
+    if (st != KDA_OK) return st;
+    if (ev && n_ev < 3) return KDA_ERR_INVALID_ARG;
+
+    Params p;
+    p.q = static_cast<const __bf16*>(q);
+    p.k = static_cast<const __bf16*>(k);
+    p.v = static_cast<const __bf16*>(v);
+    p.g = g;
+    p.beta = static_cast<const __bf16*>(beta);
+    p.init = initial_state;
+    p.cu = cu_seqlens;
+    p.out = static_cast<__bf16*>(out);
+    p.fin = final_state;
+    unsigned char* ws = static_cast<unsigned char*>(workspace);
+    p.Wf = reinterpret_cast<__bf16*>(ws + plan.off_w);
+    p.Qf = reinterpret_cast<__bf16*>(ws + plan.off_q);
+    p.Kf = reinterpret_cast<__bf16*>(ws + plan.off_k);
+    p.Uf = reinterpret_cast<float*>(ws + plan.off_u);
+    p.Of = reinterpret_cast<__bf16*>(ws + plan.off_o);
+    p.Gf = reinterpret_cast<float*>(ws + plan.off_g);
+    p.layout = plan.layout;
+    p.batch = plan.batch;
+    p.seq_len = plan.seq_len;
+    p.n_qk = plan.n_qk;
+    p.n_v = plan.n_v;
+    p.group = plan.group;
+    p.nc_max = plan.nc_max;
+    p.scan_tiles = plan.scan_tiles;
+    p.scale = shape->scale;
+    p.flags = shape->flags;
+
+    (void)hipGetLastError();  // clear a stale error so the checks below see only ours
+    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return KDA_ERR_HIP;
+    hipLaunchKernelGGL(kda_intra_kernel, dim3(unsigned(plan.intra_blocks)), dim3(kThreads), 0,
+                       stream, p);
+    if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return KDA_ERR_HIP;
+    hipLaunchKernelGGL(kda_scan_kernel<kScanNT>, dim3(unsigned(plan.scan_blocks)), dim3(kThreads),
+                       0, stream, p);
+    if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return KDA_ERR_HIP;
+    return KDA_OK;
+}
+
+}  // namespace kda
+
+extern "C" {
+
+kda_status kda_chunk_fwd_workspace(const kda_shape* shape, size_t* bytes) {
+    if (!bytes) return KDA_ERR_INVALID_ARG;
+    kda::Plan plan;
+    const kda_status st = kda::make_plan(shape, kda::kScanNT, &plan);
+    if (st != KDA_OK) return st;
+    *bytes = plan.total;
+    return KDA_OK;
+}
+
+kda_status kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, const void* v,
+                         const float* g, const void* beta, const float* initial_state,
+                         const int32_t* cu_seqlens, void* out, float* final_state,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                       workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+kda_status kda_chunk_fwd_timed(const kda_shape* shape, const void* q, const void* k,
+                               const void* v, const float* g, const void* beta,
+                               const float* initial_state, const int32_t* cu_seqlens, void* out,
+                               float* final_state, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream, hipEvent_t* stage_events,
+                               int32_t n_stage_events) {
+    if (!stage_events || n_stage_events < 3) return KDA_ERR_INVALID_ARG;
+    return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+                       workspace, workspace_bytes, stream, stage_events, n_stage_events);
+}
+
+int32_t kda_num_stages(void) { return 2; }
+
+const char* kda_stage_name(int32_t stage) {
+    switch (stage) {
+    case 0: return "kda_intra_kernel";
+    case 1: return "kda_scan_kernel";
+    default: return "unknown stage";
+    }
+}
+
+const char* kda_status_str(kda_status status) {
+    switch (status) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_INVALID_ARG: return "KDA_ERR_INVALID_ARG";
+    case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    default: return "unknown kda_status";
+    }
+}
+
+int32_t kda_version(void) { return 100; }
+
+}  // extern "C"

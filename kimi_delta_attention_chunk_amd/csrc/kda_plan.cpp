@@ -1,0 +1,104 @@
+// kda_plan.cpp -- host-side validation and planning for the KDA chunked forward.
+//
+// The accepted argument space follows the FlashKDA README, section 约束说明: Dk = Dv = 128,
+// B >= 1, stored length > 0, layouts BNSD / BSND / TND, 1 <= Nqk <= Nv with Nv % Nqk == 0,
+// TND needs an int32 cu_seqlens of B+1 entries, and final_state is a new tensor (here: it must
+// not overlap initial_state).  Only shapes and pointers are inspected; device data is never read.
+#include "kda_plan.h"
+
+#include <cmath>
+#include <limits>
+
+namespace kda {
+
+namespace {
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+}  // namespace
+
+kda_status make_plan(const kda_shape* s, int scan_nt, Plan* plan) {
+    if (!s || !plan) return KDA_ERR_INVALID_ARG;
+    if (s->layout < KDA_LAYOUT_BNSD || s->layout > KDA_LAYOUT_TND) return KDA_ERR_INVALID_ARG;
+    if (s->batch < 1 || s->seq_len < 1) return KDA_ERR_INVALID_ARG;
+    if (s->n_qk < 1 || s->n_v < s->n_qk || s->n_v % s->n_qk != 0) return KDA_ERR_INVALID_ARG;
+    if (s->d_k < 1 || s->d_v < 1) return KDA_ERR_INVALID_ARG;
+    if (s->d_k != kHead || s->d_v != kHead) return KDA_ERR_UNSUPPORTED;
+    if (!std::isfinite(s->scale)) return KDA_ERR_INVALID_ARG;
+    if (s->flags & ~uint32_t(KDA_QK_L2NORM | KDA_BETA_SIGMOID)) return KDA_ERR_INVALID_ARG;
+    if (s->layout == KDA_LAYOUT_TND && s->seq_len < s->batch) return KDA_ERR_INVALID_ARG;
+    if (scan_nt != 1 && scan_nt != 2 && scan_nt != 4) return KDA_ERR_INVALID_ARG;
+
+    Plan p;
+    p.layout = s->layout;
+    p.batch = s->batch;
+    p.seq_len = s->seq_len;
+    p.n_qk = s->n_qk;
+    p.n_v = s->n_v;
+    p.group = s->n_v / s->n_qk;
+    if (s->layout == KDA_LAYOUT_TND) {
+        // chunk j of sequence b lives in slot floor(cu[b]/64) + b + j: distinct for distinct
+        // (b, j) and below floor(T/64) + N for every valid prefix sum
+        p.nc_max = 0;
+        p.n_slots = int64_t(s->seq_len) / kChunk + s->batch;
+    } else {
+        p.nc_max = (s->seq_len + kChunk - 1) / kChunk;
+        p.n_slots = int64_t(s->batch) * p.nc_max;
+    }
+    p.n_records = p.n_slots * s->n_v;
+    p.intra_blocks = p.n_records;
+    p.scan_tiles = kHead / (16 * scan_nt);
+    const int64_t bh = int64_t(s->batch) * s->n_v;
+    p.scan_blocks = ((bh + 7) / 8) * 8 * p.scan_tiles;
+    const int64_t max_grid = std::numeric_limits<int32_t>::max();
+    if (p.intra_blocks > max_grid || p.scan_blocks > max_grid) return KDA_ERR_UNSUPPORTED;
+
+    // element counts of the largest tensors must fit the 64-bit offsets used on the device
+    const double tokens = (s->layout == KDA_LAYOUT_TND) ? double(s->seq_len)
+                                                        : double(s->batch) * s->seq_len;
+    if (tokens * s->n_v * kHead > 9.0e18) return KDA_ERR_UNSUPPORTED;
+
+    const size_t n = size_t(p.n_records);
+    size_t off = 0;
+    p.off_w = off; off = align_up(off + n * kWBytes, 256);
+    p.off_q = off; off = align_up(off + n * kQBytes, 256);
+    p.off_k = off; off = align_up(off + n * kKBytes, 256);
+    p.off_u = off; off = align_up(off + n * kUBytes, 256);
+    p.off_o = off; off = align_up(off + n * kOBytes, 256);
+    p.off_g = off; off = align_up(off + n * kGBytes, 256);
+    p.total = off;
+    *plan = p;
+    return KDA_OK;
+}
+
+kda_status check_call(const kda_shape* s, const Plan& p, const void* q, const void* k,
+                      const void* v, const float* g, const void* beta,
+                      const float* initial_state, const int32_t* cu_seqlens, const void* out,
+                      const float* final_state, const void* workspace,
+                      size_t workspace_bytes) {
+    if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
+    if (s->layout == KDA_LAYOUT_TND && !cu_seqlens) return KDA_ERR_INVALID_ARG;
+    const void* ptrs16[] = {q, k, v, g, out};
+    for (const void* ptr : ptrs16)
+        if (!aligned(ptr, 16)) return KDA_ERR_INVALID_ARG;
+    if (!aligned(beta, 2)) return KDA_ERR_INVALID_ARG;
+    if (initial_state && !aligned(initial_state, 16)) return KDA_ERR_INVALID_ARG;
+    if (final_state && !aligned(final_state, 16)) return KDA_ERR_INVALID_ARG;
+    if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
+    const size_t state_bytes = size_t(p.batch) * p.n_v * kHead * kHead * sizeof(float);
+    if (initial_state && final_state &&
+        overlap(initial_state, state_bytes, final_state, state_bytes))
+        return KDA_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < p.total) return KDA_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return KDA_ERR_WORKSPACE;
+    return KDA_OK;
+}
+
+}  // namespace kda

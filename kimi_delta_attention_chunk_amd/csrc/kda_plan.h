@@ -1,0 +1,51 @@
+// kda_plan.h -- host-side argument validation, chunk-slot plan and workspace carve-up for the
+// KDA chunked forward.  Pure C++ (no HIP calls), so every error path is testable without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#include "kda.h"
+
+namespace kda {
+
+constexpr int kChunk = 64;   // tokens per chunk (FlashKDA README, section 功能说明: 64-token chunks)
+constexpr int kHead = 128;   // d_k = d_v = 128 (FlashKDA README, section 约束说明)
+constexpr int kThreads = 256;
+
+// Per (chunk slot, value head) workspace record, in bytes.  Layouts are the MFMA fragment
+// orders the scan kernel reads (see kda_kernels.hip).  W and K_dec are kept as bf16 hi/lo pairs
+// and U in fp32, so that the innovation V_new = U - W S^T, a small difference of large terms
+// once the state predicts v well, keeps about 16 mantissa bits.
+constexpr size_t kWBytes = size_t(kChunk) * kHead * 2 * 2;   // W       bf16 hi + lo
+constexpr size_t kQBytes = size_t(kChunk) * kHead * 2;       // Q'      bf16
+constexpr size_t kKBytes = size_t(kChunk) * kHead * 2 * 2;   // K_dec   bf16 hi + lo
+constexpr size_t kUBytes = size_t(kChunk) * kHead * 4;       // U       fp32
+constexpr size_t kOBytes = size_t(kChunk) * kHead * 2;       // O_intra bf16
+constexpr size_t kGBytes = size_t(kHead) * 4;                // gamma_last fp32
+constexpr size_t kRecordBytes = kWBytes + kQBytes + kKBytes + kUBytes + kOBytes + kGBytes;
+
+struct Plan {
+    int layout = 0;
+    int batch = 0, seq_len = 0, n_qk = 0, n_v = 0, group = 0;
+    int nc_max = 0;            // BNSD/BSND: chunk slots per batch row, ceil(S / 64)
+    int64_t n_slots = 0;       // chunk slots: B * nc_max, or floor(T / 64) + N for TND
+    int64_t n_records = 0;     // n_slots * n_v
+    int64_t intra_blocks = 0;  // one workgroup per record
+    int64_t scan_blocks = 0;   // one workgroup per (sequence, value head, Dv tile), XCD padded
+    int scan_tiles = 0;        // Dv tiles per head
+    // byte offsets of each workspace array (256-byte aligned)
+    size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0, total = 0;
+};
+
+// Validates the shape alone; fills `plan` when it is valid.
+kda_status make_plan(const kda_shape* shape, int scan_nt, Plan* plan);
+
+// Validates pointers and sizes of a call against a valid plan.
+kda_status check_call(const kda_shape* shape, const Plan& plan, const void* q, const void* k,
+                      const void* v, const float* g, const void* beta,
+                      const float* initial_state, const int32_t* cu_seqlens, const void* out,
+                      const float* final_state, const void* workspace,
+                      size_t workspace_bytes);
+
+}  // namespace kda

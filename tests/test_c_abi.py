@@ -1,0 +1,122 @@
+"""The C ABI on the CPU: the library loads, exports every declared symbol, and rejects bad
+arguments on the host before touching a device (no kernel is launched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kimi_delta_attention_chunk_amd import _lib
+from kimi_delta_attention_chunk_amd.ops import make_shape
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_lib.LIB_PATH):
+        from kimi_delta_attention_chunk_amd.build import build_library
+        build_library()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("kda_chunk_fwd", "kda_chunk_fwd_workspace", "kda_status_str"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), f"{name} declared in kda.h but not exported"
+    assert set(declared_functions()) == set(_lib.EXPORTED)
+
+
+def test_status_strings(lib):
+    assert lib.kda_status_str(0) == b"KDA_OK"
+    assert lib.kda_status_str(3) == b"KDA_ERR_WORKSPACE"
+    assert lib.kda_status_str(99) == b"unknown kda_status"
+    assert lib.kda_num_stages() == 2
+    assert lib.kda_stage_name(1) == b"kda_scan_kernel"
+    assert lib.kda_version() >= 100
+
+
+def ws(lib, shape):
+    n = ctypes.c_size_t(0)
+    st = lib.kda_chunk_fwd_workspace(ctypes.byref(shape), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_sizes(lib):
+    st, n1 = ws(lib, make_shape("BNSD", 1, 8192, 3, 3, 0.088))
+    assert st == 0
+    # 128 chunks x 3 heads x (W, K_dec hi+lo, U fp32, Q', O_intra bf16, gamma)
+    rec = 32768 + 16384 + 32768 + 32768 + 16384 + 512
+    assert rec == 131584
+    assert n1 >= 128 * 3 * rec
+    st, n2 = ws(lib, make_shape("TND", 32, 65536, 32, 32, 0.088))
+    assert st == 0 and n2 >= (65536 // 64 + 32) * 32 * 131584
+    # a ragged tail adds one chunk slot per batch row
+    st, n3 = ws(lib, make_shape("BSND", 4, 4100, 4, 16, 0.088))
+    assert st == 0 and n3 >= 4 * 65 * 16 * 131584
+
+
+@pytest.mark.parametrize("bad, code", [
+    (dict(layout=7), 1), (dict(batch=0), 1), (dict(seq_len=0), 1), (dict(n_qk=0), 1),
+    (dict(n_qk=4, n_v=2), 1), (dict(n_qk=3, n_v=4), 1), (dict(d_k=64), 2), (dict(d_v=256), 2),
+    (dict(scale=float("nan")), 1), (dict(flags=8), 1),
+])
+def test_shape_rejections(lib, bad, code):
+    kw = dict(layout="BNSD", batch=1, seq_len=100, n_qk=1, n_v=2, scale=0.1)
+    shape = make_shape(**kw)
+    for key, val in bad.items():
+        setattr(shape, key, val)
+    st, _ = ws(lib, shape)
+    assert st == code
+
+
+def call(lib, shape, **ptrs):
+    base = dict(q=0x10000, k=0x20000, v=0x30000, g=0x40000, beta=0x50000, init=None, cu=None,
+                out=0x60000, fin=0x70000, ws=0x100000, ws_bytes=1 << 40)
+    base.update(ptrs)
+    P = ctypes.c_void_p
+    return lib.kda_chunk_fwd(ctypes.byref(shape), P(base["q"]), P(base["k"]), P(base["v"]),
+                             P(base["g"]), P(base["beta"]), P(base["init"]), P(base["cu"]),
+                             P(base["out"]), P(base["fin"]), P(base["ws"]),
+                             ctypes.c_size_t(base["ws_bytes"]), P(None))
+
+
+@pytest.mark.parametrize("ptrs, code", [
+    (dict(q=None), 1), (dict(k=None), 1), (dict(v=None), 1), (dict(g=None), 1),
+    (dict(beta=None), 1), (dict(out=None), 1), (dict(q=0x10008), 1), (dict(g=0x40004), 1),
+    (dict(out=0x60002), 1), (dict(init=0x80000, fin=0x80000), 1),
+    (dict(init=0x80000, fin=0x80000 + 4096), 1), (dict(ws=None), 3), (dict(ws_bytes=1024), 3),
+    (dict(ws=0x100010), 3),
+])
+def test_call_rejections(lib, ptrs, code):
+    shape = make_shape("BNSD", 1, 100, 1, 2, 0.1)
+    assert call(lib, shape, **ptrs) == code
+
+
+def test_tnd_needs_cu_seqlens(lib):
+    shape = make_shape("TND", 2, 100, 1, 1, 0.1)
+    assert call(lib, shape, cu=None) == 1
+    shape = make_shape("TND", 5, 3, 1, 1, 0.1)   # fewer tokens than sequences
+    assert ws(lib, shape)[0] == 1
+
+
+def test_timed_needs_events(lib):
+    shape = make_shape("BNSD", 1, 100, 1, 1, 0.1)
+    P = ctypes.c_void_p
+    evs = (ctypes.c_void_p * 2)()
+    st = lib.kda_chunk_fwd_timed(ctypes.byref(shape), P(0x10000), P(0x20000), P(0x30000),
+                                 P(0x40000), P(0x50000), P(None), P(None), P(0x60000),
+                                 P(None), P(0x100000), ctypes.c_size_t(1 << 40), P(None), evs, 2)
+    assert st == 1

@@ -1,0 +1,241 @@
+"""GPU parity: the gfx950 library against the fp64 oracle, through the C ABI.
+
+Small cases (several chunks, ragged tails, every layout, GQA, both fused-option settings) are
+compared in full.  The five named workloads run at their full sizes in the launch configuration
+the benchmark times; the oracle checks every output of the tiny and 8K workloads and one full
+16-row Dv tile (all tokens, all heads) of the three large ones, since state rows evolve
+independently in the recurrence.  Further tests check invariants that hold at any size.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import kda_oracle, QK_L2NORM, BETA_SIGMOID
+from parity import assert_parity
+from kimi_delta_attention_chunk_amd import kda_chunk_fwd, chunk_fwd
+from kimi_delta_attention_chunk_amd.workloads import (Inputs, make_inputs, workload_inputs,
+                                                      WORKLOADS)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from kimi_delta_attention_chunk_amd import _lib
+    _lib.load()   # raises if libkda.so is missing: there is no fallback
+
+
+def oracle_of(inp: Inputs, dv_range=None):
+    flags = (QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+    return kda_oracle(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
+                      inp.cu_seqlens, inp.layout, flags, dv_range=dv_range)
+
+
+def run_gpu(inp: Inputs, **kw):
+    d = inp.to("cuda")
+    out, fin = chunk_fwd(d, **kw)
+    torch.cuda.synchronize()
+    return out, fin
+
+
+def compare(inp: Inputs, what: str, dv_range=None):
+    print(f"[case] {what}", flush=True)
+    out, fin = run_gpu(inp)
+    ro, rf = oracle_of(inp, dv_range)
+    assert_parity(out, ro, f"{what} out")
+    assert_parity(fin, rf, f"{what} final_state")
+    return out, fin
+
+
+def test_hand_example_zero_padded():
+    ex = json.load(open(os.path.join(GOLDEN, "hand_example_d4.json")))
+    D = 128
+    q = torch.zeros(1, 1, 2, D)
+    k = torch.zeros(1, 1, 2, D)
+    v = torch.zeros(1, 1, 2, D)
+    g = torch.zeros(1, 1, 2, D)
+    q[0, 0, :, :4] = torch.tensor(ex["q"], dtype=torch.float32)
+    k[0, 0, :, :4] = torch.tensor(ex["k"], dtype=torch.float32)
+    v[0, 0, :, :4] = torch.tensor(ex["v"], dtype=torch.float32)
+    g[0, 0, 1, 0] = math.log(0.5)
+    beta = torch.tensor(ex["beta"]).reshape(1, 1, 2)
+    inp = Inputs("BNSD", 1, 2, 1, 1, q.bfloat16(), k.bfloat16(), v.bfloat16(), g,
+                 beta.bfloat16(), None, None, scale=ex["scale"], qk_l2norm=False,
+                 beta_sigmoid=False)
+    out, fin = run_gpu(inp)
+    exp_out = np.zeros((2, D))
+    exp_out[:, :4] = ex["out"]
+    exp_fin = np.zeros((D, D))
+    exp_fin[:4, :4] = ex["final_state"]
+    assert_parity(out[0, 0], exp_out, "hand example out")
+    assert_parity(fin[0, 0], exp_fin, "hand example final_state")
+
+
+SMALL = [
+    ("bnsd_b2_n2_s200_strong_init", dict(layout="BNSD", batch=2, seq_len=200, n_qk=2, n_v=2,
+                                         g_kind="strong", init=True, seed=5)),
+    ("bsnd_gqa_b2_s150", dict(layout="BSND", batch=2, seq_len=150, n_qk=1, n_v=4,
+                              g_kind="unit", init=False, seed=6)),
+    ("tnd_ragged", dict(layout="TND", batch=6, seq_len=0, n_qk=2, n_v=2, g_kind="strong",
+                        init=True, seed=7, lengths=[1, 63, 64, 65, 130, 17])),
+    ("bnsd_valid_lengths", dict(layout="BNSD", batch=3, seq_len=140, n_qk=1, n_v=1,
+                                g_kind="small", init=True, seed=8, valid_lengths=[140, 65, 3])),
+    ("bnsd_floor_decay", dict(layout="BNSD", batch=1, seq_len=256, n_qk=1, n_v=2,
+                              g_kind="floor", init=True, seed=9)),
+    ("bnsd_no_decay", dict(layout="BNSD", batch=1, seq_len=192, n_qk=1, n_v=1,
+                           g_kind="zero", init=True, seed=10)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
+def test_small_cases(name, kw):
+    inp = make_inputs(**kw)
+    compare(inp, name)
+
+
+def test_flags_off_prenormalised_inputs():
+    inp = make_inputs("BNSD", 1, 160, 1, 2, g_kind="strong", init=True, seed=12)
+    q = inp.q.double()
+    k = inp.k.double()
+    inp.q = (q / q.norm(dim=-1, keepdim=True)).bfloat16()
+    inp.k = (k / k.norm(dim=-1, keepdim=True)).bfloat16()
+    inp.beta = torch.sigmoid(inp.beta.double()).bfloat16()
+    inp.qk_l2norm = False
+    inp.beta_sigmoid = False
+    compare(inp, "flags off")
+
+
+WL_ROWS = {"tiny_s256": None, "prefill_s8k_n3": None, "gqa_tail_s4100": (16, 32),
+           "varlen_tnd_32seq": (48, 64), "long_s128k_n32": (112, 128)}
+
+
+@pytest.mark.parametrize("name", [w.name for w in WORKLOADS])
+def test_workload(name):
+    inp = workload_inputs(name)
+    compare(inp, f"workload {name}", WL_ROWS[name])
+
+
+def test_layout_invariance_bitwise():
+    inp = make_inputs("BNSD", 2, 130, 2, 4, g_kind="strong", init=True, seed=21)
+    o1, f1 = run_gpu(inp)
+
+    def bsnd(x):
+        return x.permute(0, 2, 1, 3).contiguous() if x.dim() == 4 else \
+            x.permute(0, 2, 1).contiguous()
+    b = Inputs("BSND", 2, 130, 2, 4, bsnd(inp.q), bsnd(inp.k), bsnd(inp.v), bsnd(inp.g),
+               bsnd(inp.beta), inp.initial_state, None, inp.scale)
+    o2, f2 = run_gpu(b)
+    def tnd(x):
+        y = bsnd(x)
+        return y.reshape((-1,) + tuple(y.shape[2:]))
+    t = Inputs("TND", 2, 260, 2, 4, tnd(inp.q), tnd(inp.k), tnd(inp.v), tnd(inp.g),
+               tnd(inp.beta), inp.initial_state, torch.tensor([0, 130, 260], dtype=torch.int32),
+               inp.scale)
+    o3, f3 = run_gpu(t)
+    assert torch.equal(o2.permute(0, 2, 1, 3), o1)
+    assert torch.equal(f2, f1)
+    assert torch.equal(o3.reshape(2, 130, 4, 128).permute(0, 2, 1, 3), o1)
+    assert torch.equal(f3, f1)
+
+
+def test_packing_invariance_bitwise():
+    lengths = [5, 64, 129, 1, 70]
+    inp = make_inputs("TND", 5, 0, 1, 2, g_kind="strong", init=True, seed=22, lengths=lengths)
+    o, f = run_gpu(inp)
+    cu = inp.cu_seqlens.tolist()
+    for s, L in enumerate(lengths):
+        sl = slice(cu[s], cu[s + 1])
+        one = Inputs("TND", 1, L, 1, 2, inp.q[sl].contiguous(), inp.k[sl].contiguous(),
+                     inp.v[sl].contiguous(), inp.g[sl].contiguous(), inp.beta[sl].contiguous(),
+                     inp.initial_state[s:s + 1].contiguous(),
+                     torch.tensor([0, L], dtype=torch.int32), inp.scale)
+        o1, f1 = run_gpu(one)
+        assert torch.equal(o1, o[sl]), f"sequence {s} out"
+        assert torch.equal(f1[0], f[s]), f"sequence {s} final_state"
+
+
+def test_gqa_equals_repeated_heads_bitwise():
+    inp = make_inputs("BNSD", 1, 100, 2, 6, g_kind="unit", init=True, seed=23)
+    o, f = run_gpu(inp)
+    idx = [0, 0, 0, 1, 1, 1]
+    rep = Inputs("BNSD", 1, 100, 6, 6, inp.q[:, idx].contiguous(), inp.k[:, idx].contiguous(),
+                 inp.v, inp.g, inp.beta, inp.initial_state, None, inp.scale)
+    o2, f2 = run_gpu(rep)
+    assert torch.equal(o, o2) and torch.equal(f, f2)
+
+
+def test_run_to_run_determinism():
+    inp = make_inputs("BSND", 2, 300, 2, 4, g_kind="strong", init=True, seed=24)
+    o1, f1 = run_gpu(inp)
+    o2, f2 = run_gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+def test_resume_split():
+    full = make_inputs("BNSD", 1, 300, 1, 2, g_kind="strong", init=True, seed=25)
+    o, f = run_gpu(full)
+    for cut in (128, 100):
+        parts = []
+        for sl in (slice(0, cut), slice(cut, 300)):
+            x = make_inputs("BNSD", 1, 300, 1, 2, g_kind="strong", init=True, seed=25)
+            x.q, x.k, x.v = x.q[:, :, sl].contiguous(), x.k[:, :, sl].contiguous(), \
+                x.v[:, :, sl].contiguous()
+            x.g, x.beta = x.g[:, :, sl].contiguous(), x.beta[:, :, sl].contiguous()
+            x.seq_len = sl.stop - sl.start
+            parts.append(x)
+        oa, fa = run_gpu(parts[0])
+        parts[1].initial_state = fa.cpu()
+        ob, fb = run_gpu(parts[1])
+        oc = torch.cat([oa, ob], dim=2)
+        if cut % 64 == 0:   # same chunk boundaries: identical arithmetic
+            assert torch.equal(oc, o) and torch.equal(fb, f)
+        else:
+            ref_o, ref_f = oracle_of(full)
+            assert_parity(oc, ref_o, f"resume at {cut} out")
+            assert_parity(fb, ref_f, f"resume at {cut} final_state")
+
+
+def test_output_guard_bands_and_padding_rows():
+    """NaN-poisoned output with canary bands: every valid row is written, rows past a valid
+    length are zero, nothing outside the tensor is touched, and the state is finite."""
+    inp = make_inputs("BNSD", 2, 150, 1, 2, g_kind="floor", init=True, seed=26,
+                      valid_lengths=[150, 77])
+    d = inp.to("cuda")
+    n = d.v.numel()
+    guard = 4096
+    buf = torch.full((n + 2 * guard,), float("nan"), dtype=torch.bfloat16, device="cuda")
+    canary = torch.randn(guard, device="cuda").bfloat16()
+    buf[:guard] = canary
+    buf[-guard:] = canary
+    out = buf[guard:guard + n].view(d.v.shape)
+    fbuf = torch.full((d.initial_state.numel() + 2 * guard,), float("nan"), device="cuda")
+    fin = fbuf[guard:guard + d.initial_state.numel()].view(d.initial_state.shape)
+    chunk_fwd(d, out=out, final_state=fin)
+    torch.cuda.synchronize()
+    assert torch.equal(buf[:guard], canary) and torch.equal(buf[-guard:], canary)
+    assert torch.isnan(fbuf[:guard]).all() and torch.isnan(fbuf[-guard:]).all()
+    assert torch.isfinite(out[0]).all() and torch.isfinite(out[1, :, :77]).all()
+    assert (out[1, :, 77:] == 0).all()
+    assert torch.isfinite(fin).all()
+    ro, rf = oracle_of(inp)
+    assert_parity(out, ro, "guarded out")
+    assert_parity(fin, rf, "guarded final_state")
+
+
+def test_null_states():
+    inp = make_inputs("BNSD", 1, 100, 1, 1, g_kind="strong", init=False, seed=27)
+    d = inp.to("cuda")
+    out, fin = kda_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.scale, None, None, "BNSD",
+                             output_final_state=False)
+    torch.cuda.synchronize()
+    assert fin is None
+    ro, _ = oracle_of(inp)
+    assert_parity(out, ro, "no final_state out")
