@@ -40,11 +40,11 @@ def path_bytes(inp) -> int:
 
 
 def scan_bytes(inp) -> int:
-    """Compulsory bytes of the scan kernel: per (64-token chunk, value head) it reads W (bf16
-    hi+lo), Q' (bf16), K_dec (bf16 hi+lo), U (fp32), O_intra (bf16), gamma (fp32 x128) and writes
-    out; plus the states."""
+    """Compulsory bytes of the scan kernel: per (64-token chunk, value head) it reads W (bf16),
+    Q' (bf16), K_dec (bf16 hi+lo), U (fp32), O_intra (bf16), gamma (fp32 x128) and writes out;
+    plus the states."""
     chunks = sum((L + 63) // 64 for L in inp.lengths)
-    per_chunk = 64 * 128 * (4 + 2 + 4 + 4 + 2) + 128 * 4
+    per_chunk = 64 * 128 * (2 + 2 + 4 + 4 + 2) + 128 * 4
     out = inp.tokens * inp.n_v * 128 * 2
     states = inp.batch * inp.n_v * 128 * 128 * 4
     return chunks * inp.n_v * per_chunk + out + states * ((inp.initial_state is not None) + 1)
@@ -55,7 +55,7 @@ def intra_bytes(inp) -> int:
     chunks = sum((L + 63) // 64 for L in inp.lengths)
     t = inp.tokens
     rd = t * inp.n_v * (128 * 2 * 3 + 128 * 4 + 2)   # q,k re-read per value head
-    wr = chunks * inp.n_v * (64 * 128 * (4 + 2 + 4 + 4 + 2) + 128 * 4)
+    wr = chunks * inp.n_v * (64 * 128 * (2 + 2 + 4 + 4 + 2) + 128 * 4)
     return rd + wr
 
 

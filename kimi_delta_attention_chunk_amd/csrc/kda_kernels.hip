@@ -51,7 +51,7 @@ struct Params {
     const int32_t* cu;
     __bf16* out;
     float* fin;
-    __bf16* Wf;   // [record][hi/lo][tt 4][kb 4][lane 64][8]  W[16tt+m][32kb+8q+j]
+    __bf16* Wf;   // [record][tt 4][kb 4][lane 64][8]         W[16tt+m][32kb+8q+j]
     __bf16* Qf;   // [record][tt 4][kb 4][lane 64][8]         Q'[16tt+m][32kb+8q+j]
     __bf16* Kf;   // [record][hi/lo][mt 8][s 2][lane 64][8]   K_dec[32s+8q+j][16mt+m]
     float* Uf;    // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n]
@@ -153,8 +153,8 @@ constexpr int OFF_VT = OFF_QK + 34816;     // sVt 18432
 constexpr int OFF_T = OFF_VT + 18432;      // sT 17408 | later sWt 18432
 constexpr int OFF_AQK = OFF_T + 18432;     // sAqk 17408
 constexpr int OFF_UT = OFF_AQK + 17408;    // sUt 18432
-constexpr int OFF_TMP = OFF_UT + 18432;    // inverse temp [16][48] fp32 3072
-constexpr int OFF_VEC = OFF_TMP + 3072;    // 15 x 128 fp32 = 7680
+constexpr int OFF_TMP = OFF_UT + 18432;    // inverse temp: 4 waves x [16][16] fp32 4096
+constexpr int OFF_VEC = OFF_TMP + 4096;    // 15 x 128 fp32 = 7680
 constexpr int OFF_SMALL = OFF_VEC + 7680;  // beta[64], qn[64], kn[64], tot[128]
 constexpr int INTRA_LDS = OFF_SMALL + 1280;
 constexpr int TP_BYTES = 128 * TP_LD * 2;  // one packed feature-major tile, 17408
@@ -235,70 +235,84 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
     bb += size_t(t0) * bs;
 
     // ---- phase 0: running gate sums (log2 space), raw q/k, v^T, beta -----------------------
+    // Every global load of the workgroup is issued here, before the first use, with rows
+    // clamped into the sequence and zeroed afterwards, so the phase pays one memory latency.
+    const int c_g = tid & 127, half_g = tid >> 7;       // gate sums: channel, token half
+    const int r_x = tid >> 2, part_x = tid & 3;          // q/k/v: row, 32-channel quarter
+    const bool valid_x = r_x < n;
+    float gv[32];
+    bf16x8 xq[4], xk[4], xv[4];
+    float braw = 0.f;
     {
-        const int c = tid & 127, half = tid >> 7;
-        float run = 0.f;
-        float vals[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) {
-            const int t = half * 32 + i;
-            const float x = (t < n) ? p.g[vb + size_t(t) * vs + c] : 0.f;
-            run += x;
-            vals[i] = run;
+            const int t = half_g * 32 + i;
+            const int tc = t < n ? t : n - 1;
+            gv[i] = p.g[vb + size_t(tc) * vs + c_g];
         }
-        if (half == 0) sTot[c] = run;
-        __syncthreads();
-        const float add = half ? sTot[c] : 0.f;
+        const int rc = valid_x ? r_x : n - 1;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) sG2[(half * 32 + i) * G2_LD + c] = (vals[i] + add) * kLog2e;
+        for (int u = 0; u < 4; ++u) {
+            const int c = part_x * 32 + u * 8;
+            xq[u] = *reinterpret_cast<const bf16x8*>(p.q + qb + size_t(rc) * qs + c);
+            xk[u] = *reinterpret_cast<const bf16x8*>(p.k + qb + size_t(rc) * qs + c);
+            xv[u] = *reinterpret_cast<const bf16x8*>(p.v + vb + size_t(rc) * vs + c);
+        }
+        if (tid < 64) braw = (float)p.beta[bb + size_t(tid < n ? tid : n - 1) * bs];
     }
     {
-        const int r = tid >> 2, part = tid & 3;
-        const bool valid = r < n;
+        float run = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+            run += (half_g * 32 + i < n) ? gv[i] : 0.f;
+            gv[i] = run;
+        }
+        if (half_g == 0) sTot[c_g] = run;
+    }
+    {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int c = part * 32 + u * 8;
-            bf16x8 xq, xk, xv;
-            if (valid) {
-                xq = *reinterpret_cast<const bf16x8*>(p.q + qb + size_t(r) * qs + c);
-                xk = *reinterpret_cast<const bf16x8*>(p.k + qb + size_t(r) * qs + c);
-                xv = *reinterpret_cast<const bf16x8*>(p.v + vb + size_t(r) * vs + c);
-            } else {
+            const int c = part_x * 32 + u * 8;
+            if (!valid_x) {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    xq[e] = (__bf16)0.f;
-                    xk[e] = (__bf16)0.f;
-                    xv[e] = (__bf16)0.f;
+                    xq[u][e] = (__bf16)0.f;
+                    xk[u][e] = (__bf16)0.f;
+                    xv[u][e] = (__bf16)0.f;
                 }
             }
-            *reinterpret_cast<bf16x8*>(sQraw + r * RAW_LD + c) = xq;
-            *reinterpret_cast<bf16x8*>(sKraw + r * RAW_LD + c) = xk;
+            *reinterpret_cast<bf16x8*>(sQraw + r_x * RAW_LD + c) = xq[u];
+            *reinterpret_cast<bf16x8*>(sKraw + r_x * RAW_LD + c) = xk[u];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float fq = (float)xq[e], fk = (float)xk[e];
+                const float fq = (float)xq[u][e], fk = (float)xk[u][e];
                 sq += fq * fq;
                 sk += fk * fk;
-                sVt[(c + e) * TR_LD + r] = xv[e];
+                sVt[(c + e) * TR_LD + r_x] = xv[u][e];
             }
         }
         sq += __shfl_xor(sq, 1);
         sq += __shfl_xor(sq, 2);
         sk += __shfl_xor(sk, 1);
         sk += __shfl_xor(sk, 2);
-        if (part == 0) {
+        if (part_x == 0) {
             const bool l2 = (p.flags & KDA_QK_L2NORM) != 0;
-            sQn[r] = l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-            sKn[r] = l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+            sQn[r_x] = l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+            sKn[r_x] = l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+        }
+        if (tid < 64) {
+            float x = 0.f;
+            if (tid < n) x = (p.flags & KDA_BETA_SIGMOID) ? 1.0f / (1.0f + expf(-braw)) : braw;
+            sBeta[tid] = x;
         }
     }
-    if (tid < 64) {
-        float x = 0.f;
-        if (tid < n) {
-            x = (float)p.beta[bb + size_t(tid) * bs];
-            if (p.flags & KDA_BETA_SIGMOID) x = 1.0f / (1.0f + expf(-x));
-        }
-        sBeta[tid] = x;
+    __syncthreads();
+    {
+        const float add = half_g ? sTot[c_g] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i)
+            sG2[(half_g * 32 + i) * G2_LD + c_g] = (gv[i] + add) * kLog2e;
     }
     __syncthreads();
 
@@ -393,6 +407,7 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
     __syncthreads();
 
     // ---- phase 2: T and Aqk sub-blocks (row block I) on MFMA ---------------------------------
+#pragma unroll
     for (int J = 0; J < 4; ++J) {
         if (J > I) {
 #pragma unroll
@@ -444,29 +459,34 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
         for (int i = 0; i < 16; ++i) sAi[(16 * I + i) * F_LD + 16 * I + lane] = x[i];
     }
     __syncthreads();
-    for (int I2 = 1; I2 < 4; ++I2) {
-        // P_J = sum_{K=J}^{I2-1} T[I2,K] Ainv[K,J]
-        for (int e = tid; e < I2 * 256; e += kThreads) {
-            const int J = e >> 8, r = (e >> 4) & 15, c = e & 15;
-            float s = 0.f;
-            for (int K = J; K < I2; ++K)
+    // Below the diagonal, wave w fills block column w, top to bottom:
+    //     Ainv[I2][w] = -Ainv[I2][I2] * sum_{K=w}^{I2-1} T[I2][K] Ainv[K][w]
+    // (block forward substitution of (I + T) X = I).  Every block it reads in column w is its
+    // own earlier result, so no workgroup barrier is needed; products run on fp32 MFMA.
+    {
+        float* sP = sTmp + w * 256;   // wave-private 16x16 staging tile
+        const int lr = lane & 15, lk = lane >> 4;
+        for (int I2 = w + 1; I2 < 4; ++I2) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int K = w; K < I2; ++K)
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    s += sT[(16 * I2 + r) * F_LD + 16 * K + u] * sAi[(16 * K + u) * F_LD + 16 * J + c];
-            sTmp[r * 48 + 16 * J + c] = s;
-        }
-        __syncthreads();
-        // Ainv[I2,J] = -Ainv[I2,I2] P_J
-        for (int e = tid; e < I2 * 256; e += kThreads) {
-            const int J = e >> 8, r = (e >> 4) & 15, c = e & 15;
-            float s = 0.f;
+                for (int ks = 0; ks < 4; ++ks)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        sT[(16 * I2 + lr) * F_LD + 16 * K + 4 * ks + lk],
+                        sAi[(16 * K + 4 * ks + lk) * F_LD + 16 * w + lr], acc, 0, 0, 0);
 #pragma unroll
-            for (int u = 0; u < 16; ++u)
-                s += sAi[(16 * I2 + r) * F_LD + 16 * I2 + u] * sTmp[u * 48 + 16 * J + c];
-            sAi[(16 * I2 + r) * F_LD + 16 * J + c] = -s;
+            for (int i = 0; i < 4; ++i) sP[(4 * lk + i) * 16 + lr] = acc[i];
+            f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    sAi[(16 * I2 + lr) * F_LD + 16 * I2 + 4 * ks + lk],
+                    sP[(4 * ks + lk) * 16 + lr], acc2, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sAi[(16 * I2 + 4 * lk + i) * F_LD + 16 * w + lr] = -acc2[i];
         }
-        __syncthreads();
     }
+    __syncthreads();
 
     // ---- phase 4: W^T and U for token block I, three-term hi/lo products --------------------
     const int nks = (I >= 2) ? 2 : 1;  // 32-token K steps that reach the diagonal
@@ -512,14 +532,13 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
         __bf16* wdst = p.Wf + size_t(rec) * (kWBytes / 2);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            bf16x8 oh, ol;
+            bf16x8 oh;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                SPLIT_BF16(accW[2 * kb][r], oh[r], ol[r]);
-                SPLIT_BF16(accW[2 * kb + 1][r], oh[4 + r], ol[4 + r]);
+                oh[r] = (__bf16)accW[2 * kb][r];
+                oh[4 + r] = (__bf16)accW[2 * kb + 1][r];
             }
             *reinterpret_cast<bf16x8*>(wdst + ((I * 4 + kb) * 64 + lane) * 8) = oh;
-            *reinterpret_cast<bf16x8*>(wdst + 8192 + ((I * 4 + kb) * 64 + lane) * 8) = ol;
 #pragma unroll
             for (int e = 0; e < 8; ++e) sWt[(32 * kb + 8 * q4 + e) * TR_LD + irow] = oh[e];
         }
@@ -616,33 +635,35 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
 // ---------------------------------------------------------------------------------------------
 // Inter-chunk scan kernel
 // ---------------------------------------------------------------------------------------------
+//
+// One workgroup walks the chunks of one (sequence, value head) for NT 16-row Dv tiles.  Each
+// step needs the chunk's W, Q' and K_dec (all 64 tokens, all 128 key channels) and gamma,
+// which do not depend on the Dv tile, and the tile's U and O_intra fragments.  Each wave loads
+// the fragments it multiplies straight into registers, one chunk ahead (two register sets,
+// alternated by unrolling the chunk loop by two, so no register copy forces an early wait).
 
 constexpr int S_LD = 136;   // bf16 [BV][136]  state tile (hi or lo), row = value channel
 constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = value channel
 
+template <int NT>
 struct ChunkFrags {
-    bf16x8 wh[4], wl[4];      // W hi/lo, token tile w, 32-channel block kb
+    bf16x8 w[4];              // W, token tile w, 32-channel block kb
     bf16x8 qp[4];             // Q', token tile w
     bf16x8 kh[2][2], kl[2][2];// K_dec^T hi/lo, Dk tile 2w+mt, token step s
     f32x4 gm[2];              // gamma_last for the lane's Dk rows
-};
-
-template <int NT>
-struct ChunkTile {
     f32x4 u[NT];              // U (fp32), token tile w, Dv tile
     bf16x4 o[NT];             // O_intra (bf16), token tile w, Dv tile
 };
 
 template <int NT>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
-                                           int dv_tile0, ChunkFrags& f, ChunkTile<NT>& t) {
+                                           int dv_tile0, ChunkFrags<NT>& f) {
     const __bf16* wsrc = p.Wf + size_t(rec) * (kWBytes / 2);
     const __bf16* qsrc = p.Qf + size_t(rec) * (kQBytes / 2);
     const __bf16* ksrc = p.Kf + size_t(rec) * (kKBytes / 2);
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
-        f.wh[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * 4 + kb) * 64 + lane) * 8);
-        f.wl[kb] = *reinterpret_cast<const bf16x8*>(wsrc + 8192 + ((w * 4 + kb) * 64 + lane) * 8);
+        f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * 4 + kb) * 64 + lane) * 8);
         f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * 4 + kb) * 64 + lane) * 8);
     }
 #pragma unroll
@@ -662,8 +683,8 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int dt = dv_tile0 + nt;
-        t.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
-        t.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
+        f.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
+        f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
     }
 }
 
@@ -675,6 +696,81 @@ __device__ __forceinline__ void put_state(__bf16* sSh, __bf16* sSl, int row, int
     for (int i = 0; i < 4; ++i) SPLIT_BF16(x[i], h[i], l[i]);
     *reinterpret_cast<bf16x4*>(sSh + row * S_LD + col) = h;
     *reinterpret_cast<bf16x4*>(sSl + row * S_LD + col) = l;
+}
+
+// One chunk of the scan for this workgroup's Dv tile(s):
+//   X = W S^T and Y^T = S Q'^T for token tile w; V_new = U - X; out = Y + O_intra;
+//   S^T <- gamma * S^T + K_dec^T V_new for Dk rows 32w..32w+31.
+template <int NT>
+__device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>& cur,
+                                          f32x4 (&S)[2][NT], __bf16* sSh, __bf16* sSl,
+                                          __bf16* sVh, __bf16* sVl, int jc, int len, size_t ob,
+                                          size_t os, int dv_tile0) {
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+
+    // X = W (S_hi + S_lo)^T (tokens of tile w x Dv); Y^T = S_hi Q'^T (Dv x tokens)
+    f32x4 accX[NT], accY[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accY[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
+            const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sSh + off);
+            const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSl + off);
+            accX[nt] = mfma(cur.w[kb], sh, accX[nt]);
+            accX[nt] = mfma(cur.w[kb], sl, accX[nt]);
+            accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
+        }
+    }
+    const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        bf16x4 vh, vl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) SPLIT_BF16(cur.u[nt][r] - accX[nt][r], vh[r], vl[r]);
+        const int off = (16 * nt + n16) * VN_LD + 16 * w + 4 * q4;
+        *reinterpret_cast<bf16x4*>(sVh + off) = vh;
+        *reinterpret_cast<bf16x4*>(sVl + off) = vl;
+        if (tok < len) {
+            bf16x4 o;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)cur.o[nt][r]);
+            *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * (dv_tile0 + nt) +
+                                       4 * q4) = o;
+        }
+    }
+    lds_barrier();
+
+    // S^T <- gamma * S^T + K_dec^T V_new  (Dk rows of this wave x Dv), three-term hi/lo
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        bf16x8 vh[2], vl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int off = (16 * nt + n16) * VN_LD + 32 * s + 8 * q4;
+            vh[s] = *reinterpret_cast<const bf16x8*>(sVh + off);
+            vl[s] = *reinterpret_cast<const bf16x8*>(sVl + off);
+        }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            f32x4 acc = S[mt][nt] * cur.gm[mt];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                acc = mfma(cur.kh[mt][s], vh[s], acc);
+                acc = mfma(cur.kl[mt][s], vh[s], acc);
+                acc = mfma(cur.kh[mt][s], vl[s], acc);
+            }
+            S[mt][nt] = acc;
+            put_state(sSh, sSl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, acc);
+        }
+    }
+    lds_barrier();
 }
 
 template <int NT>
@@ -725,77 +821,15 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
         }
     lds_barrier();
 
-    ChunkFrags cur, nxt;
-    ChunkTile<NT> curt, nxtt;
-    if (nchunks > 0)
-        load_chunk<NT>(p, int64_t(slot0) * p.n_v + h, w, lane, dv_tile0, cur, curt);
-
-    for (int jc = 0; jc < nchunks; ++jc) {
-        if (jc + 1 < nchunks)
-            load_chunk<NT>(p, int64_t(slot0 + jc + 1) * p.n_v + h, w, lane, dv_tile0, nxt, nxtt);
-
-        // X = W S^T (tokens of tile w x Dv), three-term hi/lo; Y^T = S Q'^T (Dv x tokens)
-        f32x4 accX[NT], accY[NT];
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accY[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
-                const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sSh + off);
-                const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSl + off);
-                accX[nt] = mfma(cur.wh[kb], sh, accX[nt]);
-                accX[nt] = mfma(cur.wl[kb], sh, accX[nt]);
-                accX[nt] = mfma(cur.wh[kb], sl, accX[nt]);
-                accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
-            }
-        }
-        const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            bf16x4 vh, vl;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) SPLIT_BF16(curt.u[nt][r] - accX[nt][r], vh[r], vl[r]);
-            const int off = (16 * nt + n16) * VN_LD + 16 * w + 4 * q4;
-            *reinterpret_cast<bf16x4*>(sVh + off) = vh;
-            *reinterpret_cast<bf16x4*>(sVl + off) = vl;
-            if (tok < len) {
-                bf16x4 o;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)curt.o[nt][r]);
-                *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * (dv_tile0 + nt) +
-                                           4 * q4) = o;
-            }
-        }
-        lds_barrier();
-
-        // S^T <- gamma * S^T + K_dec^T V_new  (Dk rows of this wave x Dv), three-term hi/lo
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-            bf16x8 vh[2], vl[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int off = (16 * nt + n16) * VN_LD + 32 * s + 8 * q4;
-                vh[s] = *reinterpret_cast<const bf16x8*>(sVh + off);
-                vl[s] = *reinterpret_cast<const bf16x8*>(sVl + off);
-            }
-#pragma unroll
-            for (int mt = 0; mt < 2; ++mt) {
-                f32x4 acc = S[mt][nt] * cur.gm[mt];
-#pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    acc = mfma(cur.kh[mt][s], vh[s], acc);
-                    acc = mfma(cur.kl[mt][s], vh[s], acc);
-                    acc = mfma(cur.kh[mt][s], vl[s], acc);
-                }
-                S[mt][nt] = acc;
-                put_state(sSh, sSl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, acc);
-            }
-        }
-        lds_barrier();
-        cur = nxt;
-        curt = nxtt;
+    ChunkFrags<NT> fa, fb;
+    const int64_t rec0 = int64_t(slot0) * p.n_v + h;
+    if (nchunks > 0) load_chunk<NT>(p, rec0, w, lane, dv_tile0, fa);
+    for (int jc = 0; jc < nchunks; jc += 2) {
+        if (jc + 1 < nchunks) load_chunk<NT>(p, rec0 + int64_t(jc + 1) * p.n_v, w, lane, dv_tile0, fb);
+        scan_step<NT>(p, fa, S, sSh, sSl, sVh, sVl, jc, len, ob, os, dv_tile0);
+        if (jc + 1 >= nchunks) break;
+        if (jc + 2 < nchunks) load_chunk<NT>(p, rec0 + int64_t(jc + 2) * p.n_v, w, lane, dv_tile0, fa);
+        scan_step<NT>(p, fb, S, sSh, sSl, sVh, sVl, jc + 1, len, ob, os, dv_tile0);
     }
 
     if (p.fin) {
@@ -822,14 +856,12 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
     }
 }
 
-constexpr int kScanNT = 1;
-
 kda_status launch(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const float* g, const void* beta, const float* initial_state,
                   const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
                   size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev, int n_ev) {
     Plan plan;
-    kda_status st = make_plan(shape, kScanNT, &plan);
+    kda_status st = make_plan(shape, &plan);
     if (st != KDA_OK) return st;
     st = check_call(shape, plan, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                     workspace, workspace_bytes);
@@ -870,8 +902,13 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
                        stream, p);
     if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return KDA_ERR_HIP;
-    hipLaunchKernelGGL(kda_scan_kernel<kScanNT>, dim3(unsigned(plan.scan_blocks)), dim3(kThreads),
-                       0, stream, p);
+    const dim3 sgrid(unsigned(plan.scan_blocks));
+    if (plan.scan_nt == 4)
+        hipLaunchKernelGGL(kda_scan_kernel<4>, sgrid, dim3(kThreads), 0, stream, p);
+    else if (plan.scan_nt == 2)
+        hipLaunchKernelGGL(kda_scan_kernel<2>, sgrid, dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(kda_scan_kernel<1>, sgrid, dim3(kThreads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
     if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
@@ -884,7 +921,7 @@ extern "C" {
 kda_status kda_chunk_fwd_workspace(const kda_shape* shape, size_t* bytes) {
     if (!bytes) return KDA_ERR_INVALID_ARG;
     kda::Plan plan;
-    const kda_status st = kda::make_plan(shape, kda::kScanNT, &plan);
+    const kda_status st = kda::make_plan(shape, &plan);
     if (st != KDA_OK) return st;
     *bytes = plan.total;
     return KDA_OK;

@@ -24,7 +24,7 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 
 }  // namespace
 
-kda_status make_plan(const kda_shape* s, int scan_nt, Plan* plan) {
+kda_status make_plan(const kda_shape* s, Plan* plan) {
     if (!s || !plan) return KDA_ERR_INVALID_ARG;
     if (s->layout < KDA_LAYOUT_BNSD || s->layout > KDA_LAYOUT_TND) return KDA_ERR_INVALID_ARG;
     if (s->batch < 1 || s->seq_len < 1) return KDA_ERR_INVALID_ARG;
@@ -34,7 +34,6 @@ kda_status make_plan(const kda_shape* s, int scan_nt, Plan* plan) {
     if (!std::isfinite(s->scale)) return KDA_ERR_INVALID_ARG;
     if (s->flags & ~uint32_t(KDA_QK_L2NORM | KDA_BETA_SIGMOID)) return KDA_ERR_INVALID_ARG;
     if (s->layout == KDA_LAYOUT_TND && s->seq_len < s->batch) return KDA_ERR_INVALID_ARG;
-    if (scan_nt != 1 && scan_nt != 2 && scan_nt != 4) return KDA_ERR_INVALID_ARG;
 
     Plan p;
     p.layout = s->layout;
@@ -54,8 +53,14 @@ kda_status make_plan(const kda_shape* s, int scan_nt, Plan* plan) {
     }
     p.n_records = p.n_slots * s->n_v;
     p.intra_blocks = p.n_records;
-    p.scan_tiles = kHead / (16 * scan_nt);
+    // Each scan workgroup streams a whole chunk record per step whatever its Dv width, so a
+    // wider tile cuts the bytes streamed per unit of work; it is taken only while enough
+    // workgroups remain to occupy all 256 compute units of an MI355X.
     const int64_t bh = int64_t(s->batch) * s->n_v;
+    p.scan_nt = 1;
+    for (int nt = 4; nt >= 2; nt /= 2)
+        if (bh * (8 / nt) >= 256) { p.scan_nt = nt; break; }
+    p.scan_tiles = 8 / p.scan_nt;
     p.scan_blocks = ((bh + 7) / 8) * 8 * p.scan_tiles;
     const int64_t max_grid = std::numeric_limits<int32_t>::max();
     if (p.intra_blocks > max_grid || p.scan_blocks > max_grid) return KDA_ERR_UNSUPPORTED;

@@ -14,10 +14,10 @@ constexpr int kHead = 128;   // d_k = d_v = 128 (FlashKDA README, section 约束
 constexpr int kThreads = 256;
 
 // Per (chunk slot, value head) workspace record, in bytes.  Layouts are the MFMA fragment
-// orders the scan kernel reads (see kda_kernels.hip).  W and K_dec are kept as bf16 hi/lo pairs
-// and U in fp32, so that the innovation V_new = U - W S^T, a small difference of large terms
-// once the state predicts v well, keeps about 16 mantissa bits.
-constexpr size_t kWBytes = size_t(kChunk) * kHead * 2 * 2;   // W       bf16 hi + lo
+// orders the scan kernel reads (see kda_kernels.hip).  K_dec is kept as a bf16 hi/lo pair and
+// U in fp32, so that the innovation V_new = U - W S^T (a small difference of large terms once
+// the state predicts v well) and the state update keep about 16 mantissa bits.
+constexpr size_t kWBytes = size_t(kChunk) * kHead * 2;       // W       bf16
 constexpr size_t kQBytes = size_t(kChunk) * kHead * 2;       // Q'      bf16
 constexpr size_t kKBytes = size_t(kChunk) * kHead * 2 * 2;   // K_dec   bf16 hi + lo
 constexpr size_t kUBytes = size_t(kChunk) * kHead * 4;       // U       fp32
@@ -33,13 +33,14 @@ struct Plan {
     int64_t n_records = 0;     // n_slots * n_v
     int64_t intra_blocks = 0;  // one workgroup per record
     int64_t scan_blocks = 0;   // one workgroup per (sequence, value head, Dv tile), XCD padded
-    int scan_tiles = 0;        // Dv tiles per head
+    int scan_nt = 1;           // 16-row Dv tiles per scan workgroup (1, 2 or 4)
+    int scan_tiles = 0;        // scan workgroups per (sequence, head) = 8 / scan_nt
     // byte offsets of each workspace array (256-byte aligned)
     size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0, total = 0;
 };
 
 // Validates the shape alone; fills `plan` when it is valid.
-kda_status make_plan(const kda_shape* shape, int scan_nt, Plan* plan);
+kda_status make_plan(const kda_shape* shape, Plan* plan);
 
 // Validates pointers and sizes of a call against a valid plan.
 kda_status check_call(const kda_shape* shape, const Plan& plan, const void* q, const void* k,
