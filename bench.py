@@ -59,6 +59,32 @@ def intra_bytes(inp) -> int:
     return rd + wr
 
 
+def source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kda_kernels.hip", "kda_plan.cpp", "kda_plan.h"):
+        h.update(open(os.path.join(ROOT, "kimi_delta_attention_chunk_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel calibration), or None when
+    there is no summary or the kernel sources changed since the counters were taken."""
+    import re
+    path = os.path.join(ROOT, "profiles", f"kda_kernels_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)```", open(path).read(), re.S)
+    if not m:
+        return None
+    d = json.loads(m.group(1))
+    if d.get("source_hash") != source_hash() or kernel not in d.get("kernels", {}):
+        return None
+    k = d["kernels"][kernel]
+    return (k["fetch_kib"] * d["fetch_scale"] + k["write_kib"] * d["write_scale"]) * 1024
+
+
 def cpu_baseline(inp, min_seconds: float = 10.0) -> dict:
     from oracle import kda_oracle, oracle_threads, QK_L2NORM, BETA_SIGMOID
     flags = (QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
@@ -88,6 +114,9 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_s8k_n3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="input copies rotated (0 = auto)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (the reference "
+                         "kernel for scaling the FETCH_SIZE / WRITE_SIZE counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -97,6 +126,18 @@ def main() -> int:
         return 2
 
     import torch
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        print(json.dumps({"copy_bytes": n, "ms": dt * 1e3, "GB/s (read+write)": 2 * n / dt / 1e9}))
+        return 0
     from kimi_delta_attention_chunk_amd import (chunk_fwd, kda_chunk_fwd_workspace,
                                                 kda_num_stages, kda_stage_name, make_shape)
     from kimi_delta_attention_chunk_amd.workloads import workload_inputs, BY_NAME
@@ -152,7 +193,8 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kda_stage_name(dom), "achieved": achieved / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
-                     "traffic": None, "bytes_per_launch": kbytes[dom],
+                     "traffic": measured_traffic(wl.name, kda_stage_name(dom)),
+                     "bytes_per_launch": kbytes[dom],
                      "avg_launch_ms": stage_ms[dom]},
         "path_roofline": {"bound": "hbm", "algorithmic_bytes": pbytes,
                           "achieved": pbytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
