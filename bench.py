@@ -39,15 +39,28 @@ def path_bytes(inp) -> int:
     return b + states * ((inp.initial_state is not None) + 1)
 
 
+def seg_p_of(inp) -> int:
+    """Segments per sequence chosen by the library's plan (kda_plan.cpp) for this shape."""
+    bh = inp.batch * inp.n_v
+    if bh * 8 >= 256:
+        return 1
+    nc = -(-inp.seq_len // 64) if inp.layout != "TND" else -(-(inp.seq_len // inp.batch) // 64)
+    sp = min((256 // (bh * 8) + 3) // 2, nc // 8, 16)
+    return sp if sp >= 2 else 1
+
+
 def scan_bytes(inp) -> int:
     """Compulsory bytes of the scan kernel: per (64-token chunk, value head) it reads W (bf16),
     Q' (bf16), K_dec (bf16 hi+lo), U (fp32), O_intra (bf16), gamma (fp32 x128) and writes out;
-    plus the states."""
+    plus the states, and with a two-level scan the segment matrices it combines."""
     chunks = sum((L + 63) // 64 for L in inp.lengths)
     per_chunk = 64 * 128 * (2 + 2 + 4 + 4 + 2) + 128 * 4
     out = inp.tokens * inp.n_v * 128 * 2
     states = inp.batch * inp.n_v * 128 * 128 * 4
-    return chunks * inp.n_v * per_chunk + out + states * ((inp.initial_state is not None) + 1)
+    sp = seg_p_of(inp)
+    mats = inp.batch * inp.n_v * max(sp - 1, 0) * 2 * 128 * 128 * 4
+    return (chunks * inp.n_v * per_chunk + out + states * ((inp.initial_state is not None) + 1)
+            + mats)
 
 
 def intra_bytes(inp) -> int:
@@ -57,6 +70,22 @@ def intra_bytes(inp) -> int:
     rd = t * inp.n_v * (128 * 2 * 3 + 128 * 4 + 2)   # q,k re-read per value head
     wr = chunks * inp.n_v * (64 * 128 * (2 + 2 + 4 + 4 + 2) + 128 * 4)
     return rd + wr
+
+
+def seg_bytes(inp) -> int:
+    """Compulsory bytes of the segment pass of the two-level scan: W, K_dec (hi+lo), gamma and
+    U of every chunk outside the last segment, the initial states, and the N and P matrices."""
+    sp = seg_p_of(inp)
+    if sp == 1:
+        return 0
+    frac = 0
+    for L in inp.lengths:
+        nc = (L + 63) // 64
+        frac += min((sp - 1) * (-(-nc // sp)), nc)   # chunks outside the last segment
+    per_chunk = 64 * 128 * (2 + 4 + 4) + 128 * 4
+    states = inp.batch * inp.n_v * 128 * 128 * 4
+    mats = inp.batch * inp.n_v * (sp - 1) * 2 * 128 * 128 * 4
+    return frac * inp.n_v * per_chunk + states * (inp.initial_state is not None) + mats
 
 
 def source_hash() -> str:
@@ -177,7 +206,7 @@ def main() -> int:
     stage_ms = [sum(events[i][s].elapsed_time(events[i][s + 1]) for i in range(args.steps))
                 / args.steps for s in range(nst)]
     dom = max(range(nst), key=lambda s: stage_ms[s])
-    kbytes = [intra_bytes(host), scan_bytes(host)]
+    kbytes = [intra_bytes(host), seg_bytes(host), scan_bytes(host)]
     achieved = kbytes[dom] / (stage_ms[dom] * 1e-3)
     pbytes = path_bytes(host)
     value = host.tokens / (ms_step * 1e-3)

@@ -99,7 +99,7 @@ kda_status kda_chunk_fwd_workspace(const kda_shape* shape, size_t* bytes);
  *   final_state    fp32 [batch, n_v, d_v, d_k] or NULL (not produced); must not overlap
  *                  initial_state
  *   workspace      device buffer of at least kda_chunk_fwd_workspace() bytes, 256-byte aligned
- * Returns KDA_OK once both kernels are enqueued on `stream`. */
+ * Returns KDA_OK once the kernels are enqueued on `stream`. */
 kda_status kda_chunk_fwd(const kda_shape* shape,
                          const void* q, const void* k, const void* v,
                          const float* g, const void* beta,
@@ -108,7 +108,10 @@ kda_status kda_chunk_fwd(const kda_shape* shape,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
-/* Number of kernel launches one kda_chunk_fwd call enqueues, and the name of each stage. */
+/* Number of stages of one kda_chunk_fwd call and the name of each: the intra-chunk kernel, the
+ * segment pass of the two-level scan (enqueued only when few (sequence, head) chains would
+ * leave the GPU idle through a long sequential scan; otherwise the stage is empty), and the
+ * scan with outputs. */
 int32_t kda_num_stages(void);
 const char* kda_stage_name(int32_t stage);
 

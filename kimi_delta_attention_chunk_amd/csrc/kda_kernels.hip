@@ -57,8 +57,11 @@ struct Params {
     float* Uf;    // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n]
     __bf16* Of;   // [record][nt 8][tt 4][lane 64][4]         O_intra[16tt+n][16nt+4q+i]
     float* Gf;    // [record][128]                            2^(G2_last)
+    float* Pt;    // [seq*head][segment][128][128]  segment transfer matrix, transposed
+    float* Nst;   // [seq*head][segment][128][128]  segment end state from a zero start
     int layout, batch, seq_len, n_qk, n_v, group, nc_max;
     int scan_tiles;
+    int seg_p;     // segments per sequence of the two-level scan (1 = one level)
     float scale;
     uint32_t flags;
 };
@@ -633,14 +636,21 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Inter-chunk scan kernel
+// Inter-chunk scan kernels
 // ---------------------------------------------------------------------------------------------
 //
-// One workgroup walks the chunks of one (sequence, value head) for NT 16-row Dv tiles.  Each
+// A scan workgroup walks chunks of one (sequence, value head) for NT 16-row Dv tiles.  Each
 // step needs the chunk's W, Q' and K_dec (all 64 tokens, all 128 key channels) and gamma,
 // which do not depend on the Dv tile, and the tile's U and O_intra fragments.  Each wave loads
 // the fragments it multiplies straight into registers, one chunk ahead (two register sets,
 // alternated by unrolling the chunk loop by two, so no register copy forces an early wait).
+//
+// Two-level form for few (sequence, head) chains: a sequence of C chunks is cut into P
+// segments.  Chunk c maps the state affinely, S -> S M_c + N_c with M_c = Diag(gamma_c) -
+// W_c^T K_dec,c, so segment s has S_out = S_in P_s + N_s.  kda_seg_kernel runs each segment but
+// the last from S = 0 (giving N_s; segment 0 starts from the initial state instead) and from
+// the identity (giving P_s, 8 workgroups of 16 identity rows); kda_scan_kernel then forms
+// S_in(s) = S_in(s-1) P_{s-1} + N_{s-1} on MFMA and reruns segment s with outputs.
 
 constexpr int S_LD = 136;   // bf16 [BV][136]  state tile (hi or lo), row = value channel
 constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = value channel
@@ -655,7 +665,7 @@ struct ChunkFrags {
     bf16x4 o[NT];             // O_intra (bf16), token tile w, Dv tile
 };
 
-template <int NT>
+template <int NT, bool WITH_U, bool WITH_OUT>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
                                            int dv_tile0, ChunkFrags<NT>& f) {
     const __bf16* wsrc = p.Wf + size_t(rec) * (kWBytes / 2);
@@ -664,7 +674,8 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
         f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * 4 + kb) * 64 + lane) * 8);
-        f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * 4 + kb) * 64 + lane) * 8);
+        if constexpr (WITH_OUT)
+            f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * 4 + kb) * 64 + lane) * 8);
     }
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
@@ -683,8 +694,10 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int dt = dv_tile0 + nt;
-        f.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
-        f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
+        if constexpr (WITH_U)
+            f.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
+        if constexpr (WITH_OUT)
+            f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
     }
 }
 
@@ -698,14 +711,21 @@ __device__ __forceinline__ void put_state(__bf16* sSh, __bf16* sSl, int row, int
     *reinterpret_cast<bf16x4*>(sSl + row * S_LD + col) = l;
 }
 
+struct ScanLds {
+    __bf16* sh;
+    __bf16* sl;
+    __bf16* vh;
+    __bf16* vl;
+};
+
 // One chunk of the scan for this workgroup's Dv tile(s):
-//   X = W S^T and Y^T = S Q'^T for token tile w; V_new = U - X; out = Y + O_intra;
-//   S^T <- gamma * S^T + K_dec^T V_new for Dk rows 32w..32w+31.
-template <int NT>
+//   X = W S^T and (with outputs) Y^T = S Q'^T for token tile w; V_new = U - X (U = 0 for the
+//   transfer-matrix pass); out = Y + O_intra; S^T <- gamma * S^T + K_dec^T V_new for Dk rows
+//   32w..32w+31.
+template <int NT, bool WITH_U, bool WITH_OUT>
 __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>& cur,
-                                          f32x4 (&S)[2][NT], __bf16* sSh, __bf16* sSl,
-                                          __bf16* sVh, __bf16* sVl, int jc, int len, size_t ob,
-                                          size_t os, int dv_tile0) {
+                                          f32x4 (&S)[2][NT], const ScanLds& L, int jc, int len,
+                                          size_t ob, size_t os, int dv_tile0) {
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -721,11 +741,11 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
-            const bf16x8 sh = *reinterpret_cast<const bf16x8*>(sSh + off);
-            const bf16x8 sl = *reinterpret_cast<const bf16x8*>(sSl + off);
+            const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
+            const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
             accX[nt] = mfma(cur.w[kb], sh, accX[nt]);
             accX[nt] = mfma(cur.w[kb], sl, accX[nt]);
-            accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
+            if constexpr (WITH_OUT) accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
         }
     }
     const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
@@ -733,16 +753,21 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
     for (int nt = 0; nt < NT; ++nt) {
         bf16x4 vh, vl;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) SPLIT_BF16(cur.u[nt][r] - accX[nt][r], vh[r], vl[r]);
+        for (int r = 0; r < 4; ++r) {
+            const float u = WITH_U ? cur.u[nt][r] : 0.f;
+            SPLIT_BF16(u - accX[nt][r], vh[r], vl[r]);
+        }
         const int off = (16 * nt + n16) * VN_LD + 16 * w + 4 * q4;
-        *reinterpret_cast<bf16x4*>(sVh + off) = vh;
-        *reinterpret_cast<bf16x4*>(sVl + off) = vl;
-        if (tok < len) {
-            bf16x4 o;
+        *reinterpret_cast<bf16x4*>(L.vh + off) = vh;
+        *reinterpret_cast<bf16x4*>(L.vl + off) = vl;
+        if constexpr (WITH_OUT) {
+            if (tok < len) {
+                bf16x4 o;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)cur.o[nt][r]);
-            *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * (dv_tile0 + nt) +
-                                       4 * q4) = o;
+                for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)cur.o[nt][r]);
+                *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os +
+                                           16 * (dv_tile0 + nt) + 4 * q4) = o;
+            }
         }
     }
     lds_barrier();
@@ -754,8 +779,8 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int off = (16 * nt + n16) * VN_LD + 32 * s + 8 * q4;
-            vh[s] = *reinterpret_cast<const bf16x8*>(sVh + off);
-            vl[s] = *reinterpret_cast<const bf16x8*>(sVl + off);
+            vh[s] = *reinterpret_cast<const bf16x8*>(L.vh + off);
+            vl[s] = *reinterpret_cast<const bf16x8*>(L.vl + off);
         }
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
@@ -767,9 +792,92 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
                 acc = mfma(cur.kh[mt][s], vl[s], acc);
             }
             S[mt][nt] = acc;
-            put_state(sSh, sSl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, acc);
+            put_state(L.sh, L.sl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, acc);
         }
     }
+    lds_barrier();
+}
+
+// Chunks [cb, ce) of one sequence (records rec0 + c * n_v), state in S and in LDS on entry.
+template <int NT, bool WITH_U, bool WITH_OUT>
+__device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[2][NT], const ScanLds& L,
+                                           int64_t rec0, int cb, int ce, int len, size_t ob,
+                                           size_t os, int dv_tile0) {
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    ChunkFrags<NT> fa, fb;
+    if (cb < ce)
+        load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
+    for (int jc = cb; jc < ce; jc += 2) {
+        if (jc + 1 < ce)
+            load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(jc + 1) * p.n_v, w, lane,
+                                             dv_tile0, fb);
+        scan_step<NT, WITH_U, WITH_OUT>(p, fa, S, L, jc, len, ob, os, dv_tile0);
+        if (jc + 1 >= ce) break;
+        if (jc + 2 < ce)
+            load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(jc + 2) * p.n_v, w, lane,
+                                             dv_tile0, fa);
+        scan_step<NT, WITH_U, WITH_OUT>(p, fb, S, L, jc + 1, len, ob, os, dv_tile0);
+    }
+}
+
+// Chunk range [cb, ce) of segment `seg` of a sequence with `nchunks` chunks cut into seg_p
+// segments of ceil(nchunks / seg_p) chunks.
+__device__ __forceinline__ void segment_range(int nchunks, int seg_p, int seg, int& cb, int& ce) {
+    const int L = (nchunks + seg_p - 1) / seg_p;
+    cb = seg * L;
+    ce = cb + L < nchunks ? cb + L : nchunks;
+    if (cb > nchunks) cb = nchunks;
+}
+
+// S^T <- P_s^T S^T + N_s^T for this wave's Dk rows, i.e. S <- S P_s + N_s, with the state in S
+// (registers) and in LDS (B operand).  P_s is stored transposed: Pt[dk'][dk] = P_s[dk][dk'].
+template <int NT>
+__device__ __forceinline__ void combine_step(const float* Pt, const float* Nst,
+                                             f32x4 (&S)[2][NT], const ScanLds& L, int dv_tile0) {
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+    bf16x8 ph[2][4], pl[2][4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const float* src = Pt + size_t(16 * (2 * w + mt) + n16) * kHead + 32 * kb + 8 * q4;
+            const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                SPLIT_BF16(a[e], ph[mt][kb][e], pl[mt][kb][e]);
+                SPLIT_BF16(b[e], ph[mt][kb][4 + e], pl[mt][kb][4 + e]);
+            }
+        }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int dv = 16 * (dv_tile0 + nt) + n16;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+            f32x4 acc = *reinterpret_cast<const f32x4*>(Nst + size_t(dv) * kHead +
+                                                        16 * (2 * w + mt) + 4 * q4);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
+                const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
+                const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
+                acc = mfma(ph[mt][kb], sh, acc);
+                acc = mfma(pl[mt][kb], sh, acc);
+                acc = mfma(ph[mt][kb], sl, acc);
+            }
+            S[mt][nt] = acc;
+        }
+    }
+    lds_barrier();   // every wave has read the old state
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            put_state(L.sh, L.sl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, S[mt][nt]);
     lds_barrier();
 }
 
@@ -780,6 +888,7 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) __bf16 sSl[BV * S_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[BV * VN_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sVl[BV * VN_LD];
+    const ScanLds L{sSh, sSl, sVh, sVl};
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -787,13 +896,15 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
-    // XCD-aware decode: the Dv tiles of one (sequence, head) share blockIdx.x mod 8, so they run
-    // on one XCD and share its L2 for the chunk operands they all read.
+    // XCD-aware decode: the Dv tiles of one (sequence, head, segment) share blockIdx.x mod 8,
+    // so they run on one XCD and share its L2 for the chunk operands they all read.
     const int pid = blockIdx.x;
     const int xcd = pid & 7, r8 = pid >> 3;
-    const int bh = (r8 / p.scan_tiles) * 8 + xcd;
+    const int grp = (r8 / p.scan_tiles) * 8 + xcd;
     const int tile = r8 % p.scan_tiles;
-    if (bh >= p.batch * p.n_v) return;
+    if (grp >= p.batch * p.n_v * p.seg_p) return;
+    const int bh = grp / p.seg_p;
+    const int seg = grp % p.seg_p;
     const int b = bh / p.n_v;
     const int h = bh % p.n_v;
     const int dv_tile0 = tile * NT;   // first 16-wide Dv tile of this workgroup
@@ -801,38 +912,37 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
     int c0, len, slot0;
     seq_info(p, b, c0, len, slot0);
     const int nchunks = (len + kChunk - 1) / kChunk;
+    int cb, ce;
+    segment_range(nchunks, p.seg_p, seg, cb, ce);
     size_t ob, os;
     row_geom(p, b, h, p.n_v, kHead, c0, ob, os);
 
     // state tile: S[mt][nt][i] = S[dv = 16(dv_tile0+nt) + n16][dk = 16(2w+mt) + 4q4 + i]
     f32x4 S[2][NT];
     const size_t st_base = (size_t(b) * p.n_v + h) * kHead * kHead;
+    const float* s0 = p.init ? p.init + st_base : nullptr;
+    if (seg > 0) s0 = p.Nst + (size_t(bh) * p.seg_p + 0) * kHead * kHead;   // N_0
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int dv = 16 * (dv_tile0 + nt) + n16;
             const int dk = 16 * (2 * w + mt) + 4 * q4;
-            if (p.init)
-                S[mt][nt] = *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * kHead + dk);
-            else
-                S[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            S[mt][nt] = s0 ? *reinterpret_cast<const f32x4*>(s0 + size_t(dv) * kHead + dk)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
             put_state(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
         }
     lds_barrier();
-
-    ChunkFrags<NT> fa, fb;
-    const int64_t rec0 = int64_t(slot0) * p.n_v + h;
-    if (nchunks > 0) load_chunk<NT>(p, rec0, w, lane, dv_tile0, fa);
-    for (int jc = 0; jc < nchunks; jc += 2) {
-        if (jc + 1 < nchunks) load_chunk<NT>(p, rec0 + int64_t(jc + 1) * p.n_v, w, lane, dv_tile0, fb);
-        scan_step<NT>(p, fa, S, sSh, sSl, sVh, sVl, jc, len, ob, os, dv_tile0);
-        if (jc + 1 >= nchunks) break;
-        if (jc + 2 < nchunks) load_chunk<NT>(p, rec0 + int64_t(jc + 2) * p.n_v, w, lane, dv_tile0, fa);
-        scan_step<NT>(p, fb, S, sSh, sSl, sVh, sVl, jc + 1, len, ob, os, dv_tile0);
+    // S_in(seg) = (((N_0) P_1 + N_1) P_2 + ...) P_{seg-1} + N_{seg-1}
+    for (int sp = 1; sp < seg; ++sp) {
+        const size_t m = (size_t(bh) * p.seg_p + sp) * kHead * kHead;
+        combine_step<NT>(p.Pt + m, p.Nst + m, S, L, dv_tile0);
     }
 
-    if (p.fin) {
+    run_chunks<NT, true, true>(p, S, L, int64_t(slot0) * p.n_v + h, cb, ce, len, ob, os,
+                               dv_tile0);
+
+    if (p.fin && seg == p.seg_p - 1) {
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -843,7 +953,7 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
             }
     }
     // rows past a batch row's valid length (BNSD/BSND with cu_seqlens) are written as zeros
-    if (p.layout != KDA_LAYOUT_TND && len < p.seq_len) {
+    if (p.layout != KDA_LAYOUT_TND && len < p.seq_len && seg == p.seg_p - 1) {
         const int rows = p.seq_len - len;
         for (int e = tid; e < rows * NT * 4; e += kThreads) {
             const int t = len + e / (NT * 4);
@@ -853,6 +963,78 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
             for (int i = 0; i < 4; ++i) z[i] = (__bf16)0.f;
             *reinterpret_cast<bf16x4*>(p.out + ob + size_t(t) * os + 16 * dv_tile0 + 4 * part) = z;
         }
+    }
+}
+
+// Segment pass of the two-level scan: 16 workgroups per (sequence, head, segment s < seg_p-1).
+// Slots 0..7: N_s tiles (from S = 0, or from the initial state for s = 0, with U); slots 8..15:
+// P_s tiles (from 16 identity rows each, without U; not needed for s = 0).
+__global__ __launch_bounds__(kThreads) void kda_seg_kernel(Params p) {
+    __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * S_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * S_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 sVh[16 * VN_LD];
+    __shared__ __attribute__((aligned(16))) __bf16 sVl[16 * VN_LD];
+    const ScanLds L{sSh, sSl, sVh, sVl};
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+
+    const int pid = blockIdx.x;
+    const int xcd = pid & 7, r8 = pid >> 3;
+    const int grp = (r8 >> 4) * 8 + xcd;
+    const int slot = r8 & 15;
+    if (grp >= p.batch * p.n_v * (p.seg_p - 1)) return;
+    const int bh = grp / (p.seg_p - 1);
+    const int seg = grp % (p.seg_p - 1);
+    const bool is_p = slot >= 8;
+    const int tile = slot & 7;
+    if (is_p && seg == 0) return;
+    const int b = bh / p.n_v;
+    const int h = bh % p.n_v;
+
+    int c0, len, slot0;
+    seq_info(p, b, c0, len, slot0);
+    const int nchunks = (len + kChunk - 1) / kChunk;
+    int cb, ce;
+    segment_range(nchunks, p.seg_p, seg, cb, ce);
+
+    f32x4 S[2][1];
+    const size_t st_base = (size_t(b) * p.n_v + h) * kHead * kHead;
+    const int row = 16 * tile + n16;   // state row (value channel, or identity row)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+        const int dk = 16 * (2 * w + mt) + 4 * q4;
+        f32x4 x = {0.f, 0.f, 0.f, 0.f};
+        if (is_p) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[i] = (dk + i == row) ? 1.f : 0.f;
+        } else if (seg == 0 && p.init) {
+            x = *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(row) * kHead + dk);
+        }
+        S[mt][0] = x;
+        put_state(sSh, sSl, n16, dk, x);
+    }
+    lds_barrier();
+
+    const int64_t rec0 = int64_t(slot0) * p.n_v + h;
+    const size_t m = (size_t(bh) * p.seg_p + seg) * kHead * kHead;
+    if (is_p) {
+        run_chunks<1, false, false>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
+        // rows 16 tile .. of P_s, stored transposed: Pt[dk'][row]
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                p.Pt[m + size_t(16 * (2 * w + mt) + 4 * q4 + i) * kHead + row] = S[mt][0][i];
+    } else {
+        run_chunks<1, true, false>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            *reinterpret_cast<f32x4*>(p.Nst + m + size_t(row) * kHead + 16 * (2 * w + mt) +
+                                      4 * q4) = S[mt][0];
     }
 }
 
@@ -866,7 +1048,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     st = check_call(shape, plan, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                     workspace, workspace_bytes);
     if (st != KDA_OK) return st;
-    if (ev && n_ev < 3) return KDA_ERR_INVALID_ARG;
+    if (ev && n_ev < 4) return KDA_ERR_INVALID_ARG;
 
     Params p;
     p.q = static_cast<const __bf16*>(q);
@@ -893,6 +1075,9 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.group = plan.group;
     p.nc_max = plan.nc_max;
     p.scan_tiles = plan.scan_tiles;
+    p.seg_p = plan.seg_p;
+    p.Pt = plan.seg_p > 1 ? reinterpret_cast<float*>(ws + plan.off_pt) : nullptr;
+    p.Nst = plan.seg_p > 1 ? reinterpret_cast<float*>(ws + plan.off_n) : nullptr;
     p.scale = shape->scale;
     p.flags = shape->flags;
 
@@ -902,6 +1087,12 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
                        stream, p);
     if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
     if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return KDA_ERR_HIP;
+    if (plan.seg_p > 1) {
+        hipLaunchKernelGGL(kda_seg_kernel, dim3(unsigned(plan.seg_blocks)), dim3(kThreads), 0,
+                           stream, p);
+        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+    }
+    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return KDA_ERR_HIP;
     const dim3 sgrid(unsigned(plan.scan_blocks));
     if (plan.scan_nt == 4)
         hipLaunchKernelGGL(kda_scan_kernel<4>, sgrid, dim3(kThreads), 0, stream, p);
@@ -910,7 +1101,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     else
         hipLaunchKernelGGL(kda_scan_kernel<1>, sgrid, dim3(kThreads), 0, stream, p);
     if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
-    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return KDA_ERR_HIP;
+    if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return KDA_ERR_HIP;
     return KDA_OK;
 }
 
@@ -941,17 +1132,18 @@ kda_status kda_chunk_fwd_timed(const kda_shape* shape, const void* q, const void
                                float* final_state, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t* stage_events,
                                int32_t n_stage_events) {
-    if (!stage_events || n_stage_events < 3) return KDA_ERR_INVALID_ARG;
+    if (!stage_events || n_stage_events < 4) return KDA_ERR_INVALID_ARG;
     return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                        workspace, workspace_bytes, stream, stage_events, n_stage_events);
 }
 
-int32_t kda_num_stages(void) { return 2; }
+int32_t kda_num_stages(void) { return 3; }
 
 const char* kda_stage_name(int32_t stage) {
     switch (stage) {
     case 0: return "kda_intra_kernel";
-    case 1: return "kda_scan_kernel";
+    case 1: return "kda_seg_kernel";
+    case 2: return "kda_scan_kernel";
     default: return "unknown stage";
     }
 }

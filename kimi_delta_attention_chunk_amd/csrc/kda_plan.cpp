@@ -60,10 +60,30 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     p.scan_nt = 1;
     for (int nt = 4; nt >= 2; nt /= 2)
         if (bh * (8 / nt) >= 256) { p.scan_nt = nt; break; }
+    // Few (sequence, head) chains leave most compute units idle through a long sequential scan.
+    // Then each sequence is cut into seg_p segments: a segment pass runs every segment but the
+    // last from a zero state and from identity rows (8 + 8 workgroups per segment), giving its
+    // end state N_s and transfer matrix P_s, and the output pass starts segment s from
+    // S_in(s) = S_in(s-1) P_{s-1} + N_{s-1}.  seg_p is the largest count whose segment pass
+    // fits 256 workgroups, with at least 8 chunks per segment.
+    p.seg_p = 1;
+    if (bh * 8 < 256) {
+        const int64_t nc_est = (s->layout == KDA_LAYOUT_TND)
+                                   ? (int64_t(s->seq_len) / s->batch + kChunk - 1) / kChunk
+                                   : p.nc_max;
+        int64_t sp = (256 / (bh * 8) + 3) / 2;
+        if (sp > nc_est / 8) sp = nc_est / 8;
+        if (sp > 16) sp = 16;
+        if (sp >= 2) p.seg_p = int(sp);
+    }
+    if (p.seg_p > 1) p.scan_nt = 1;
     p.scan_tiles = 8 / p.scan_nt;
-    p.scan_blocks = ((bh + 7) / 8) * 8 * p.scan_tiles;
+    const int64_t out_groups = bh * p.seg_p;
+    p.scan_blocks = ((out_groups + 7) / 8) * 8 * p.scan_tiles;
+    p.seg_blocks = (p.seg_p > 1) ? ((bh * (p.seg_p - 1) + 7) / 8) * 8 * 16 : 0;
     const int64_t max_grid = std::numeric_limits<int32_t>::max();
-    if (p.intra_blocks > max_grid || p.scan_blocks > max_grid) return KDA_ERR_UNSUPPORTED;
+    if (p.intra_blocks > max_grid || p.scan_blocks > max_grid || p.seg_blocks > max_grid)
+        return KDA_ERR_UNSUPPORTED;
 
     // element counts of the largest tensors must fit the 64-bit offsets used on the device
     const double tokens = (s->layout == KDA_LAYOUT_TND) ? double(s->seq_len)
@@ -78,6 +98,11 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     p.off_u = off; off = align_up(off + n * kUBytes, 256);
     p.off_o = off; off = align_up(off + n * kOBytes, 256);
     p.off_g = off; off = align_up(off + n * kGBytes, 256);
+    if (p.seg_p > 1) {
+        const size_t mats = size_t(bh) * p.seg_p * kHead * kHead * sizeof(float);
+        p.off_pt = off; off = align_up(off + mats, 256);
+        p.off_n = off; off = align_up(off + mats, 256);
+    }
     p.total = off;
     *plan = p;
     return KDA_OK;

@@ -34,9 +34,13 @@ struct Plan {
     int64_t intra_blocks = 0;  // one workgroup per record
     int64_t scan_blocks = 0;   // one workgroup per (sequence, value head, Dv tile), XCD padded
     int scan_nt = 1;           // 16-row Dv tiles per scan workgroup (1, 2 or 4)
-    int scan_tiles = 0;        // scan workgroups per (sequence, head) = 8 / scan_nt
+    int scan_tiles = 0;        // scan workgroups per (sequence, head, segment) = 8 / scan_nt
+    int seg_p = 1;             // segments per sequence of the two-level scan (1 = one level)
+    int64_t seg_blocks = 0;    // workgroups of the segment pass (0 when seg_p == 1)
     // byte offsets of each workspace array (256-byte aligned)
-    size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0, total = 0;
+    size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0;
+    size_t off_pt = 0, off_n = 0;   // segment transfer matrices and zero-start end states
+    size_t total = 0;
 };
 
 // Validates the shape alone; fills `plan` when it is valid.

@@ -43,8 +43,9 @@ def test_status_strings(lib):
     assert lib.kda_status_str(0) == b"KDA_OK"
     assert lib.kda_status_str(3) == b"KDA_ERR_WORKSPACE"
     assert lib.kda_status_str(99) == b"unknown kda_status"
-    assert lib.kda_num_stages() == 2
-    assert lib.kda_stage_name(1) == b"kda_scan_kernel"
+    assert lib.kda_num_stages() == 3
+    assert lib.kda_stage_name(1) == b"kda_seg_kernel"
+    assert lib.kda_stage_name(2) == b"kda_scan_kernel"
     assert lib.kda_version() >= 100
 
 
@@ -57,10 +58,15 @@ def ws(lib, shape):
 def test_workspace_sizes(lib):
     st, n1 = ws(lib, make_shape("BNSD", 1, 8192, 3, 3, 0.088))
     assert st == 0
-    # 128 chunks x 3 heads x (W, K_dec hi+lo, U fp32, Q', O_intra bf16, gamma)
+    # 128 chunks x 3 heads x (W, K_dec hi+lo, U fp32, Q', O_intra bf16, gamma), plus the
+    # two-level scan's matrices: 3 heads x 6 segments x (P_s, N_s) fp32 128x128
     rec = 16384 + 16384 + 32768 + 32768 + 16384 + 512
     assert rec == 115200
-    assert n1 >= 128 * 3 * rec
+    assert n1 >= 128 * 3 * rec + 3 * 6 * 2 * 65536
+    assert n1 < 128 * 3 * rec + 3 * 6 * 2 * 65536 + 16 * 256
+    # many heads: one-level scan, no matrices
+    st, n4 = ws(lib, make_shape("BNSD", 1, 8192, 32, 32, 0.088))
+    assert st == 0 and n4 < 128 * 32 * rec + 16 * 256
     st, n2 = ws(lib, make_shape("TND", 32, 65536, 32, 32, 0.088))
     assert st == 0 and n2 >= (65536 // 64 + 32) * 32 * 115200
     # a ragged tail adds one chunk slot per batch row
@@ -115,8 +121,8 @@ def test_tnd_needs_cu_seqlens(lib):
 def test_timed_needs_events(lib):
     shape = make_shape("BNSD", 1, 100, 1, 1, 0.1)
     P = ctypes.c_void_p
-    evs = (ctypes.c_void_p * 2)()
+    evs = (ctypes.c_void_p * 3)()
     st = lib.kda_chunk_fwd_timed(ctypes.byref(shape), P(0x10000), P(0x20000), P(0x30000),
                                  P(0x40000), P(0x50000), P(None), P(None), P(0x60000),
-                                 P(None), P(0x100000), ctypes.c_size_t(1 << 40), P(None), evs, 2)
+                                 P(None), P(0x100000), ctypes.c_size_t(1 << 40), P(None), evs, 3)
     assert st == 1

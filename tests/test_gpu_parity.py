@@ -95,6 +95,26 @@ SMALL = [
 ]
 
 
+# Few (sequence, head) chains and long enough sequences: the library runs the two-level scan
+# (segments from zero and from the identity, then an affine combine); see kda_plan.cpp.
+TWO_LEVEL = [
+    ("bnsd_1head_41chunks_tail", dict(layout="BNSD", batch=1, seq_len=64 * 40 + 17, n_qk=1,
+                                      n_v=1, g_kind="strong", init=True, seed=31)),
+    ("bnsd_valid_lengths", dict(layout="BNSD", batch=2, seq_len=3000, n_qk=1, n_v=1,
+                                g_kind="unit", init=True, seed=32, valid_lengths=[3000, 1300])),
+    ("tnd_two_seqs", dict(layout="TND", batch=2, seq_len=0, n_qk=1, n_v=1, g_kind="small",
+                          init=True, seed=33, lengths=[2100, 700])),
+    ("bsnd_gqa", dict(layout="BSND", batch=1, seq_len=1600, n_qk=1, n_v=2, g_kind="mixed",
+                      init=False, seed=34)),
+]
+
+
+@pytest.mark.parametrize("name,kw", TWO_LEVEL, ids=[s[0] for s in TWO_LEVEL])
+def test_two_level_scan(name, kw):
+    inp = make_inputs(**kw)
+    compare(inp, name)
+
+
 @pytest.mark.parametrize("name,kw", SMALL, ids=[s[0] for s in SMALL])
 def test_small_cases(name, kw):
     inp = make_inputs(**kw)
