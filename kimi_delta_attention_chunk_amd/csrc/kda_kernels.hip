@@ -799,24 +799,26 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
 }
 
 // Chunks [cb, ce) of one sequence (records rec0 + c * n_v), state in S and in LDS on entry.
+// The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
+// record, never used): with the same number of loads in flight on every path, the compiler's
+// wait counts let each step wait only for its own operands, not for the next chunk's.
 template <int NT, bool WITH_U, bool WITH_OUT>
 __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[2][NT], const ScanLds& L,
                                            int64_t rec0, int cb, int ce, int len, size_t ob,
                                            size_t os, int dv_tile0) {
+    if (cb >= ce) return;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int last = ce - 1;
     ChunkFrags<NT> fa, fb;
-    if (cb < ce)
-        load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
+    load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
     for (int jc = cb; jc < ce; jc += 2) {
-        if (jc + 1 < ce)
-            load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(jc + 1) * p.n_v, w, lane,
-                                             dv_tile0, fb);
+        const int c1 = jc + 1 < last ? jc + 1 : last;
+        load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
         scan_step<NT, WITH_U, WITH_OUT>(p, fa, S, L, jc, len, ob, os, dv_tile0);
         if (jc + 1 >= ce) break;
-        if (jc + 2 < ce)
-            load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(jc + 2) * p.n_v, w, lane,
-                                             dv_tile0, fa);
+        const int c2 = jc + 2 < last ? jc + 2 : last;
+        load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
         scan_step<NT, WITH_U, WITH_OUT>(p, fb, S, L, jc + 1, len, ob, os, dv_tile0);
     }
 }
