@@ -82,19 +82,6 @@ __device__ __forceinline__ __bf16 bf16_lo(float x, __bf16 hi) { return (__bf16)(
         (lo) = bf16_lo(x_, (hi));      \
     } while (0)
 
-// 16-byte fragment read from an LDS row whose stride is only 8-byte aligned.
-__device__ __forceinline__ bf16x8 lds_read8_a8(const __bf16* p) {
-    const bf16x4 a = *reinterpret_cast<const bf16x4*>(p);
-    const bf16x4 b = *reinterpret_cast<const bf16x4*>(p + 4);
-    bf16x8 r;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        r[e] = a[e];
-        r[4 + e] = b[e];
-    }
-    return r;
-}
-
 // LDS-only barrier: waits for this wave's LDS traffic, then the workgroup barrier.  Outstanding
 // global loads (prefetches) stay in flight.
 __device__ __forceinline__ void lds_barrier() {
@@ -142,60 +129,153 @@ __device__ __forceinline__ void row_geom(const Params& p, int b, int h, int head
 // ---------------------------------------------------------------------------------------------
 // Intra-chunk kernel
 // ---------------------------------------------------------------------------------------------
+//
+// One workgroup of four waves per (64-token chunk, value head); wave w owns token block I = w
+// (tokens 16I .. 16I+15).  Lane (q4, n16) holds token 16I + n16 and channels 32kb + 8q4 + e
+// (kb, e = 0..3, 0..7) of q, k, v and g, loaded straight from HBM in this "row layout", which
+// is at once the A operand of an MFMA over channels and its B operand with tokens as columns.
+//
+// Products over tokens (W, U, O_intra, Q') need operands with eight consecutive tokens per
+// lane.  Those are made exactly on the MFMA unit: a row-layout fragment times a 0/1 selection
+// matrix returns, in the accumulator layout, four consecutive tokens of one channel per lane
+// (bf16 inputs, fp32 sums of one nonzero term: no rounding).  Lanes then store 8-byte pieces
+// into token-grouped LDS tiles that the consumers read back with 16-byte loads.
+//
+// The workgroup keeps its LDS under 80 KB and its registers under 256 per lane, so two
+// workgroups share a compute unit and one's memory phase overlaps the other's arithmetic.
 
-constexpr int G2_LD = 132;   // fp32 [64][132]
-constexpr int RAW_LD = 136;  // bf16 [64][136]
-constexpr int TR_LD = 72;    // bf16 [128][72]  feature-major, token-contiguous (16-byte rows)
-constexpr int TP_LD = 68;    // bf16 [128][68]  same, packed to fit hi+lo pairs (8-byte rows)
-constexpr int F_LD = 68;     // fp32 [64][68]
-constexpr int R_LD = 136;    // bf16 [16][136]
+constexpr int BLK_LD = 20;              // fp32 row stride of a stored 16 x 16 block
+constexpr int BLK_SZ = 16 * BLK_LD;     // floats per stored block
+constexpr int N_BLK = 10;               // lower-triangular 16 x 16 blocks of a 64 x 64 matrix
+constexpr int TILE_BYTES = 8 * 8 * 16 * 16;   // [tile 8][token group 8][n16][8] bf16 = 16 KB
 
-constexpr int OFF_G2 = 0;                  // sG2 33792 | later sR 26112 | later sAi 17408
-constexpr int OFF_QK = 33792;              // raw q,k 34816 | later sKt hi,lo | later sKd hi,lo
-constexpr int OFF_VT = OFF_QK + 34816;     // sVt 18432
-constexpr int OFF_T = OFF_VT + 18432;      // sT 17408 | later sWt 18432
-constexpr int OFF_AQK = OFF_T + 18432;     // sAqk 17408
-constexpr int OFF_UT = OFF_AQK + 17408;    // sUt 18432
-constexpr int OFF_TMP = OFF_UT + 18432;    // inverse temp: 4 waves x [16][16] fp32 4096
-constexpr int OFF_VEC = OFF_TMP + 4096;    // 15 x 128 fp32 = 7680
-constexpr int OFF_SMALL = OFF_VEC + 7680;  // beta[64], qn[64], kn[64], tot[128]
-constexpr int INTRA_LDS = OFF_SMALL + 1280;
-constexpr int TP_BYTES = 128 * TP_LD * 2;  // one packed feature-major tile, 17408
-static_assert(2 * TP_BYTES <= 34816, "hi/lo tiles fit the raw q/k region");
-static_assert(INTRA_LDS <= 160 * 1024, "intra kernel LDS budget");
+constexpr int OFF_AQK = 0;                                 // Aqk blocks          12800
+constexpr int OFF_AI = OFF_AQK + N_BLK * BLK_SZ * 4;       // Ainv blocks         12800
+constexpr int OFF_BETA = OFF_AI + N_BLK * BLK_SZ * 4;      // beta[64]              256
+constexpr int OFF_X = OFF_BETA + 256;                      // phase-shared region 49152
+// inside region X, by phase:
+//   gate sums      first[4][128], dlast[4][128] fp32                        at X + 0
+//   T/Aqk          sKF [wave 4][kb 4][lane 64] bf16x8 (16384)              at X + 0
+//                  sT blocks (12800)                                        at X + 16384
+//                  vec: BV[6][128], C[4][128] fp32 (5120)                   at X + 29184
+//                  vecA[4][128] fp32 (2048)                                 at X + 34304
+//   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                    at X + 29184
+//   W, U           sKt hi/lo tiles (32768)                                  at X + 0
+//                  sVt tile (16384)                                         at X + 32768
+//   O_intra, Q'    sW tile (16384)                                          at X + 0
+//                  sU tile (16384)                                          at X + 16384
+constexpr int X_KF = 0;
+constexpr int X_T = 16384;
+constexpr int X_VEC = 29184;
+constexpr int X_VECA = 34304;
+constexpr int X_TMP = 29184;
+constexpr int X_KT = 0;
+constexpr int X_VT = 32768;
+constexpr int X_W = 0;
+constexpr int X_U = 16384;
+constexpr int X_BYTES = 49152;
+constexpr int INTRA_LDS = OFF_X + X_BYTES;
+static_assert(X_VECA + 2048 <= X_VT + TILE_BYTES, "vector rows fit region X");
+static_assert(X_T + N_BLK * BLK_SZ * 4 <= X_VEC, "T blocks end before the vector rows");
+static_assert(X_TMP + 4 * BLK_SZ * 4 <= X_BYTES, "inverse staging fits region X");
+static_assert(2 * INTRA_LDS <= 160 * 1024, "two intra workgroups fit one compute unit");
 
-// vector rows inside OFF_VEC
-constexpr int VEC_BV = 0;    // 6 rows: 2^(G2[16I] - G2[16J]) for (I,J) = (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
-constexpr int VEC_A = 6;     // 4 rows: 2^(G2[16I])
-constexpr int VEC_C = 10;    // 4 rows: 2^(G2[63] - G2[16I])
-constexpr int VEC_GAM = 14;  // 1 row : 2^(G2[63])
+// vector rows inside vec (X + X_VEC), 128 floats each
+constexpr int VEC_BV = 0;   // 6 rows: exp(G[16I] - G[16J]) for (I,J) = (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
+constexpr int VEC_C = 6;    // 4 rows: exp(G_last - G[16I])
 
 __device__ __forceinline__ int pair_index(int I, int J) {  // I > J
     return (I * (I - 1)) / 2 + J;
 }
+__device__ __forceinline__ int blk(int I, int J) {         // I >= J
+    return (I * (I + 1)) / 2 + J;
+}
 
-__global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
+// Inclusive prefix sum over the 16 lanes of a DPP row (lanes 16r .. 16r+15).
+__device__ __forceinline__ float row_scan16(float x) {
+#define KDA_ROW_SHR(v, ctrl) \
+    __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xf, 0xf, true))
+    x += KDA_ROW_SHR(x, 0x111);
+    x += KDA_ROW_SHR(x, 0x112);
+    x += KDA_ROW_SHR(x, 0x114);
+    x += KDA_ROW_SHR(x, 0x118);
+#undef KDA_ROW_SHR
+    return x;
+}
+
+// 0/1 selection fragments (B operands).  With A a row-layout fragment of K-step kb,
+//   sel_nat(h): C[token][n] = X[token][32kb + 16h + n]                   (channel tile 2kb+h)
+//   sel_phi(h): C[token][n] = X[token][32kb + 8(n>>2) + 4h + (n&3)]       (tile 2kb+h, phi order)
+// The phi order makes the accumulator rows 4q4 + r of tile (kb, h) the lane's own channels
+// 32kb + 8q4 + 4h + r, so an accumulator initialised from row-layout registers lines up.
+__device__ __forceinline__ bf16x8 sel_nat(int h, int q4, int n16) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (8 * q4 + j == 16 * h + n16) ? (__bf16)1.f : (__bf16)0.f;
+    return r;
+}
+__device__ __forceinline__ bf16x8 sel_phi(int h, int q4, int n16) {
+    bf16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        r[j] = (q4 == (n16 >> 2) && j == 4 * h + (n16 & 3)) ? (__bf16)1.f : (__bf16)0.f;
+    return r;
+}
+
+__device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
+    bf16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (__bf16)x[i];
+    return r;
+}
+
+// Token-grouped tile [tile 8][group 8][n16 16][8] bf16: group g holds tokens 8g .. 8g+7.  The
+// accumulator lane (q4, n16) of token block I holds tokens 16I + 4q4 .. +3, i.e. half of group
+// 2I + (q4 >> 1).
+__device__ __forceinline__ void tile_put(__bf16* tile, int t, int I, int q4, int n16, bf16x4 v) {
+    *reinterpret_cast<bf16x4*>(tile + ((t * 8 + 2 * I + (q4 >> 1)) * 16 + n16) * 8 + 4 * (q4 & 1)) = v;
+}
+__device__ __forceinline__ bf16x8 tile_get(const __bf16* tile, int t, int g, int n16) {
+    return *reinterpret_cast<const bf16x8*>(tile + ((t * 8 + g) * 16 + n16) * 8);
+}
+
+// Eight consecutive fp32 entries of row n16 of a stored lower-triangular 64 x 64 matrix, row
+// block I, columns 32s + 8q4 .. +7 (zero above the block diagonal).
+__device__ __forceinline__ void blk_row8(const float* m, int I, int s, int q4, int n16, float (&x)[8]) {
+    const int J = 2 * s + (q4 >> 1);
+    if (J <= I) {
+        const float* src = m + blk(I, J) * BLK_SZ + n16 * BLK_LD + 8 * (q4 & 1);
+        const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            x[e] = a[e];
+            x[4 + e] = b[e];
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = 0.f;
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[INTRA_LDS];
-    float* sG2 = reinterpret_cast<float*>(smem + OFF_G2);
-    __bf16* sQraw = reinterpret_cast<__bf16*>(smem + OFF_QK);
-    __bf16* sKraw = reinterpret_cast<__bf16*>(smem + OFF_QK + 64 * RAW_LD * 2);
-    __bf16* sVt = reinterpret_cast<__bf16*>(smem + OFF_VT);
-    float* sT = reinterpret_cast<float*>(smem + OFF_T);
     float* sAqk = reinterpret_cast<float*>(smem + OFF_AQK);
-    __bf16* sUt = reinterpret_cast<__bf16*>(smem + OFF_UT);
-    float* sTmp = reinterpret_cast<float*>(smem + OFF_TMP);
-    float* sVec = reinterpret_cast<float*>(smem + OFF_VEC);
-    float* sBeta = reinterpret_cast<float*>(smem + OFF_SMALL);
-    float* sQn = sBeta + 64;
-    float* sKn = sBeta + 128;
-    float* sTot = sBeta + 192;
-    __bf16* sR = reinterpret_cast<__bf16*>(smem + OFF_G2);               // phase 1b-2
-    float* sAi = reinterpret_cast<float*>(smem + OFF_G2);                // phase 3-5
-    __bf16* sKtH = reinterpret_cast<__bf16*>(smem + OFF_QK);             // phase 1b-4
-    __bf16* sKtL = reinterpret_cast<__bf16*>(smem + OFF_QK + TP_BYTES);
-    __bf16* sKdH = reinterpret_cast<__bf16*>(smem + OFF_QK);             // phase 5-6
-    __bf16* sKdL = reinterpret_cast<__bf16*>(smem + OFF_QK + TP_BYTES);
-    __bf16* sWt = reinterpret_cast<__bf16*>(smem + OFF_T);               // phase 4-5
+    float* sAi = reinterpret_cast<float*>(smem + OFF_AI);
+    float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
+    unsigned char* X = smem + OFF_X;
+    float* sFirst = reinterpret_cast<float*>(X);               // [4][128]
+    float* sDlast = sFirst + 512;                              // [4][128]
+    bf16x8* sKF = reinterpret_cast<bf16x8*>(X + X_KF);         // [4][4][64]
+    float* sT = reinterpret_cast<float*>(X + X_T);
+    float* sVec = reinterpret_cast<float*>(X + X_VEC);
+    float* sVecA = reinterpret_cast<float*>(X + X_VECA);
+    float* sTmp = reinterpret_cast<float*>(X + X_TMP);
+    __bf16* sKtH = reinterpret_cast<__bf16*>(X + X_KT);
+    __bf16* sKtL = reinterpret_cast<__bf16*>(X + X_KT + TILE_BYTES);
+    __bf16* sVt = reinterpret_cast<__bf16*>(X + X_VT);
+    __bf16* sW = reinterpret_cast<__bf16*>(X + X_W);
+    __bf16* sU = reinterpret_cast<__bf16*>(X + X_U);
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -209,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
     const int hq = h / p.group;
 
     // chunk slot -> (sequence b, chunk j)
-    int b, j;
+    int b;
     if (p.layout == KDA_LAYOUT_TND) {
         int lo = 0, hi = p.batch - 1;
         while (lo < hi) {
@@ -224,7 +304,7 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
     }
     int c0, len, slot0;
     seq_info(p, b, c0, len, slot0);
-    j = slot - slot0;
+    const int j = slot - slot0;
     if (j < 0 || j * kChunk >= len) return;  // an unused slot: nothing reads it
     const int t0 = j * kChunk;
     const int n = (len - t0) < kChunk ? (len - t0) : kChunk;
@@ -237,262 +317,271 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
     vb += size_t(t0) * vs;
     bb += size_t(t0) * bs;
 
-    // ---- phase 0: running gate sums (log2 space), raw q/k, v^T, beta -----------------------
-    // Every global load of the workgroup is issued here, before the first use, with rows
-    // clamped into the sequence and zeroed afterwards, so the phase pays one memory latency.
-    const int c_g = tid & 127, half_g = tid >> 7;       // gate sums: channel, token half
-    const int r_x = tid >> 2, part_x = tid & 3;          // q/k/v: row, 32-channel quarter
-    const bool valid_x = r_x < n;
-    float gv[32];
+    const int I = w;
+    const int tok = 16 * I + n16;        // this lane's token inside the chunk
+    const bool tv = tok < n;
+    const int tc = tv ? tok : n - 1;     // rows past the tail are read clamped, then zeroed
+
+    // ---- phase 0: every global load of the workgroup, in row layout --------------------------
     bf16x8 xq[4], xk[4], xv[4];
-    float braw = 0.f;
+    f32x4 xg[8];
+    float braw;
     {
+        const __bf16* qr = p.q + qb + size_t(tc) * qs;
+        const __bf16* kr = p.k + qb + size_t(tc) * qs;
+        const __bf16* vr = p.v + vb + size_t(tc) * vs;
+        const float* gr = p.g + vb + size_t(tc) * vs;
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            const int t = half_g * 32 + i;
-            const int tc = t < n ? t : n - 1;
-            gv[i] = p.g[vb + size_t(tc) * vs + c_g];
+        for (int kb = 0; kb < 4; ++kb) {
+            const int c = 32 * kb + 8 * q4;
+            xq[kb] = *reinterpret_cast<const bf16x8*>(qr + c);
+            xk[kb] = *reinterpret_cast<const bf16x8*>(kr + c);
+            xv[kb] = *reinterpret_cast<const bf16x8*>(vr + c);
+            xg[2 * kb] = *reinterpret_cast<const f32x4*>(gr + c);
+            xg[2 * kb + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
         }
-        const int rc = valid_x ? r_x : n - 1;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = part_x * 32 + u * 8;
-            xq[u] = *reinterpret_cast<const bf16x8*>(p.q + qb + size_t(rc) * qs + c);
-            xk[u] = *reinterpret_cast<const bf16x8*>(p.k + qb + size_t(rc) * qs + c);
-            xv[u] = *reinterpret_cast<const bf16x8*>(p.v + vb + size_t(rc) * vs + c);
-        }
-        if (tid < 64) braw = (float)p.beta[bb + size_t(tid < n ? tid : n - 1) * bs];
+        braw = (float)p.beta[bb + size_t(tc) * bs];
     }
-    {
-        float run = 0.f;
+    if (!tv) {
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            run += (half_g * 32 + i < n) ? gv[i] : 0.f;
-            gv[i] = run;
-        }
-        if (half_g == 0) sTot[c_g] = run;
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                xq[kb][e] = (__bf16)0.f;
+                xk[kb][e] = (__bf16)0.f;
+                xv[kb][e] = (__bf16)0.f;
+            }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) xg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+
+    // ---- phase 0a: gate sums -------------------------------------------------------------------
+    // d = sum of g over tokens 16I+1 .. tok (the lane's decay relative to the block's first
+    // token, natural log), a prefix sum across the 16 lanes of a DPP row with the first token's
+    // term removed.  The block sums go through LDS to give, per channel, G at each block's
+    // first token (G[16I]) and G_last = G at the last valid token.
+    float d[32];
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+        const float gi = xg[i >> 2][i & 3];
+        d[i] = row_scan16(n16 == 0 ? 0.f : gi);
+        if (n16 == 0) sFirst[I * 128 + 32 * (i >> 3) + 8 * q4 + (i & 7)] = gi;
+        if (n16 == 15) sDlast[I * 128 + 32 * (i >> 3) + 8 * q4 + (i & 7)] = d[i];
+    }
+    __syncthreads();
+    if (tid < 128) {
+        const int c = tid;
+        float Gr[4];
+        float acc = 0.f;
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            Gr[J] = acc + sFirst[J * 128 + c];
+            acc = Gr[J] + sDlast[J * 128 + c];
+        }
+        const float Gl = acc;
+        const int PI[6] = {1, 2, 2, 3, 3, 3};
+        const int PJ[6] = {0, 0, 1, 0, 1, 2};
+#pragma unroll
+        for (int u = 0; u < 6; ++u)
+            sVec[(VEC_BV + u) * 128 + c] = exp2_fast((Gr[PI[u]] - Gr[PJ[u]]) * kLog2e);
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            sVec[(VEC_C + J) * 128 + c] = exp2_fast((Gl - Gr[J]) * kLog2e);
+            sVecA[J * 128 + c] = exp2_fast(Gr[J] * kLog2e);
+        }
+        p.Gf[size_t(rec) * kHead + c] = exp2_fast(Gl * kLog2e);
+    }
+
+    // ---- phase 1: normalised, decayed operands in registers; K_dec record ---------------------
+    float qn, kn, bt;
     {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int c = part_x * 32 + u * 8;
-            if (!valid_x) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    xq[u][e] = (__bf16)0.f;
-                    xk[u][e] = (__bf16)0.f;
-                    xv[u][e] = (__bf16)0.f;
-                }
-            }
-            *reinterpret_cast<bf16x8*>(sQraw + r_x * RAW_LD + c) = xq[u];
-            *reinterpret_cast<bf16x8*>(sKraw + r_x * RAW_LD + c) = xk[u];
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const float fq = (float)xq[u][e], fk = (float)xk[u][e];
+                const float fq = (float)xq[kb][e], fk = (float)xk[kb][e];
                 sq += fq * fq;
                 sk += fk * fk;
-                sVt[(c + e) * TR_LD + r_x] = xv[u][e];
             }
-        }
-        sq += __shfl_xor(sq, 1);
-        sq += __shfl_xor(sq, 2);
-        sk += __shfl_xor(sk, 1);
-        sk += __shfl_xor(sk, 2);
-        if (part_x == 0) {
-            const bool l2 = (p.flags & KDA_QK_L2NORM) != 0;
-            sQn[r_x] = l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-            sKn[r_x] = l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
-        }
-        if (tid < 64) {
-            float x = 0.f;
-            if (tid < n) x = (p.flags & KDA_BETA_SIGMOID) ? 1.0f / (1.0f + expf(-braw)) : braw;
-            sBeta[tid] = x;
-        }
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        sk += __shfl_xor(sk, 16);
+        sk += __shfl_xor(sk, 32);
+        const bool l2 = (p.flags & KDA_QK_L2NORM) != 0;
+        qn = l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
+        kn = l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+        bt = 0.f;
+        if (tv) bt = (p.flags & KDA_BETA_SIGMOID) ? 1.0f / (1.0f + expf(-braw)) : braw;
     }
-    __syncthreads();
-    {
-        const float add = half_g ? sTot[c_g] : 0.f;
-#pragma unroll
-        for (int i = 0; i < 32; ++i)
-            sG2[(half_g * 32 + i) * G2_LD + c_g] = (gv[i] + add) * kLog2e;
-    }
-    __syncthreads();
+    __syncthreads();   // vector rows ready; first/dlast dead
+    if (q4 == 0) sBeta[tok] = bt;
 
-    // ---- phase 0b: per-channel block factors ------------------------------------------------
+    float Lk[32], Lq[32];
+    bf16x8 KFb[4];
     {
-        const int c = tid & 127, half = tid >> 7;
-        if (half == 0) {
-            const int PI[6] = {1, 2, 2, 3, 3, 3};
-            const int PJ[6] = {0, 0, 1, 0, 1, 2};
-#pragma unroll
-            for (int u = 0; u < 6; ++u)
-                sVec[(VEC_BV + u) * 128 + c] =
-                    exp2_fast(sG2[16 * PI[u] * G2_LD + c] - sG2[16 * PJ[u] * G2_LD + c]);
-        } else {
-            const float gl = sG2[63 * G2_LD + c];
-#pragma unroll
-            for (int I = 0; I < 4; ++I) {
-                const float gr = sG2[16 * I * G2_LD + c];
-                sVec[(VEC_A + I) * 128 + c] = exp2_fast(gr);
-                sVec[(VEC_C + I) * 128 + c] = exp2_fast(gl - gr);
-            }
-            const float gam = exp2_fast(gl);
-            sVec[VEC_GAM * 128 + c] = gam;
-            p.Gf[size_t(rec) * kHead + c] = gam;
-        }
-    }
-
-    // ---- phase 1a: row block I = w in registers (A-fragment order) ---------------------------
-    // lane (q4, n16) owns token 16I + n16 and channels 32kb + 8q4 + e
-    const int I = w;
-    const int irow = 16 * I + n16;
-    float Lk[32], Lq[32], KF[32];
-    {
-        const float qn = sQn[irow], kn = sKn[irow];
+        __bf16* kdst = p.Kf + size_t(rec) * (kKBytes / 2);
+        const int s_k = I >> 1;
+        const int lane_k = (2 * (I & 1) + (q4 >> 1)) * 16 + n16;
+        const int j0 = 4 * (q4 & 1);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            const int cb = 32 * kb + 8 * q4;
-            const bf16x8 kr = *reinterpret_cast<const bf16x8*>(sKraw + irow * RAW_LD + cb);
-            const bf16x8 qr = *reinterpret_cast<const bf16x8*>(sQraw + irow * RAW_LD + cb);
+            bf16x8 kdh, kdl;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                // e = 2^(G2_i - G2_r) <= 1 and f = 2^(G2_r - G2_i) < 2^109 with r = 16I
-                const float d = sG2[irow * G2_LD + cb + e] - sG2[16 * I * G2_LD + cb + e];
-                const float ef = exp2_fast(d);
-                const float ff = exp2_fast(-d);
-                const float kv = (float)kr[e] * kn;
-                Lk[kb * 8 + e] = kv * ef;
-                Lq[kb * 8 + e] = (float)qr[e] * qn * ef;
-                KF[kb * 8 + e] = kv * ff;
+                const int i = 8 * kb + e;
+                const int c = 32 * kb + 8 * q4 + e;
+                // e^{d} <= 1 and e^{-d} < 2^109 (d over at most 15 tokens, g >= -5)
+                const float dd = d[i] * kLog2e;
+                const float ef = exp2_fast(dd);
+                const float ff = exp2_fast(-dd);
+                const float kv = (float)xk[kb][e] * kn;
+                Lk[i] = kv * ef;
+                Lq[i] = (float)xq[kb][e] * qn * ef;
+                const float kf = kv * ff;
+                KFb[kb][e] = (__bf16)kf;
+                SPLIT_BF16(kf * sVec[(VEC_C + I) * 128 + c], kdh[e], kdl[e]);   // K_dec <= 1
+            }
+            sKF[(I * 4 + kb) * 64 + lane] = KFb[kb];
+            // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [hi/lo][mt 8][s 2][lane 64][8]
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const bf16x8 sel = sel_nat(hh, q4, n16);
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const bf16x4 th = to_bf16x4(mfma(kdh, sel, zero));
+                const bf16x4 tl = to_bf16x4(mfma(kdl, sel, zero));
+                const int mt = 2 * kb + hh;
+                *reinterpret_cast<bf16x4*>(kdst + ((size_t(mt) * 2 + s_k) * 64 + lane_k) * 8 + j0) = th;
+                *reinterpret_cast<bf16x4*>(kdst + 8192 + ((size_t(mt) * 2 + s_k) * 64 + lane_k) * 8 + j0) = tl;
             }
         }
     }
-    __syncthreads();
+    __syncthreads();   // sKF, sBeta ready
 
-    // ---- phase 1b: operands for the other sub-blocks, (beta K~)^T, Q~^T, K_dec ---------------
-    bf16x8 Lkb[4], Lqb[4], KFb[4];
-    float Qt[32];
-    float Kd[32];
-    {
-        const float bi = sBeta[irow];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int cb = 32 * kb + 8 * q4;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int c = cb + e;
-                const float a = sVec[(VEC_A + I) * 128 + c];
-                Lkb[kb][e] = (__bf16)Lk[kb * 8 + e];
-                Lqb[kb][e] = (__bf16)Lq[kb * 8 + e];
-                KFb[kb][e] = (__bf16)KF[kb * 8 + e];
-                Qt[kb * 8 + e] = p.scale * Lq[kb * 8 + e] * a;
-                Kd[kb * 8 + e] = KF[kb * 8 + e] * sVec[(VEC_C + I) * 128 + c];
-                __bf16 hi, lo;
-                SPLIT_BF16(bi * Lk[kb * 8 + e] * a, hi, lo);
-                sKtH[c * TP_LD + irow] = hi;
-                sKtL[c * TP_LD + irow] = lo;
-            }
-        }
-        for (int I2 = I + 1; I2 < 4; ++I2) {
-            const int pi = pair_index(I2, I);
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int cb = 32 * kb + 8 * q4;
-                bf16x8 r;
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    r[e] = (__bf16)(KF[kb * 8 + e] * sVec[(VEC_BV + pi) * 128 + cb + e]);
-                *reinterpret_cast<bf16x8*>(sR + (pi * 16 + n16) * R_LD + cb) = r;
-            }
-        }
-    }
-    __syncthreads();
-
-    // ---- phase 2: T and Aqk sub-blocks (row block I) on MFMA ---------------------------------
+    // ---- phase 2: T and Aqk blocks of row block I on MFMA -------------------------------------
+    // Off-diagonal (I > J): key j relative to the first token of block J (KF of wave J, factor
+    // <= 2^109), query/key i scaled by exp(G_i - G[16J]) <= 1.  Diagonal: both relative to 16I.
+    // Masked entries of a diagonal block may be huge and are removed by select.
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-        if (J > I) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                sT[(16 * I + 4 * q4 + r) * F_LD + 16 * J + n16] = 0.f;
-                sAqk[(16 * I + 4 * q4 + r) * F_LD + 16 * J + n16] = 0.f;
-            }
-            continue;
-        }
+        if (J > I) continue;
         f32x4 aT = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            bf16x8 bfrag;
+            bf16x8 ak, aq, bf;
             if (J == I) {
-                bfrag = KFb[kb];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ak[e] = (__bf16)Lk[8 * kb + e];
+                    aq[e] = (__bf16)Lq[8 * kb + e];
+                }
+                bf = KFb[kb];
             } else {
-                bfrag = *reinterpret_cast<const bf16x8*>(
-                    sR + (pair_index(I, J) * 16 + n16) * R_LD + 32 * kb + 8 * q4);
+                const float* bv = sVec + (VEC_BV + pair_index(I, J)) * 128 + 32 * kb + 8 * q4;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    ak[e] = (__bf16)(Lk[8 * kb + e] * bv[e]);
+                    aq[e] = (__bf16)(Lq[8 * kb + e] * bv[e]);
+                }
+                bf = sKF[(J * 4 + kb) * 64 + lane];
             }
-            aT = mfma(Lkb[kb], bfrag, aT);
-            aQ = mfma(Lqb[kb], bfrag, aQ);
+            aT = mfma(ak, bf, aT);
+            aQ = mfma(aq, bf, aQ);
         }
-        // masked entries of a diagonal block may be huge: removed by select
+        float* tb = sT + blk(I, J) * BLK_SZ;
+        float* qb2 = sAqk + blk(I, J) * BLK_SZ;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = 16 * I + 4 * q4 + r;
             const int jj = 16 * J + n16;
-            sT[i * F_LD + jj] = (i > jj) ? sBeta[i] * aT[r] : 0.f;
-            sAqk[i * F_LD + jj] = (i >= jj) ? p.scale * aQ[r] : 0.f;
+            tb[(4 * q4 + r) * BLK_LD + n16] = (i > jj) ? sBeta[i] * aT[r] : 0.f;
+            qb2[(4 * q4 + r) * BLK_LD + n16] = (i >= jj) ? p.scale * aQ[r] : 0.f;
         }
     }
-    __syncthreads();
+    // operands kept for later phases: Q~ = scale * q * exp(G) and (beta K~) hi/lo
+    float Qt[32];
+    bf16x8 bkh[4], bkl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float a = sVecA[I * 128 + 32 * kb + 8 * q4 + e];
+            Qt[8 * kb + e] = p.scale * Lq[8 * kb + e] * a;
+            SPLIT_BF16(bt * Lk[8 * kb + e] * a, bkh[kb][e], bkl[kb][e]);
+        }
+    __syncthreads();   // T, Aqk ready
 
-    // ---- phase 3: Ainv = (I + T)^-1 in fp32 -------------------------------------------------
-    for (int e = tid; e < 64 * 64; e += kThreads) {
-        const int r = e >> 6, c = e & 63;
-        if ((c >> 4) > (r >> 4)) sAi[r * F_LD + c] = 0.f;
-    }
+    // ---- phase 3: Ainv = (I + T)^-1 in fp32 ---------------------------------------------------
     if (lane < 16) {  // diagonal block I by forward substitution, column `lane`
+        const float* tb = sT + blk(I, I) * BLK_SZ;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float s = (i == lane) ? 1.f : 0.f;
 #pragma unroll
-            for (int m = 0; m < i; ++m) s -= sT[(16 * I + i) * F_LD + 16 * I + m] * x[m];
+            for (int m = 0; m < i; ++m) s -= tb[i * BLK_LD + m] * x[m];
             x[i] = s;
         }
+        float* ab = sAi + blk(I, I) * BLK_SZ;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sAi[(16 * I + i) * F_LD + 16 * I + lane] = x[i];
+        for (int i = 0; i < 16; ++i) ab[i * BLK_LD + lane] = x[i];
     }
     __syncthreads();
     // Below the diagonal, wave w fills block column w, top to bottom:
     //     Ainv[I2][w] = -Ainv[I2][I2] * sum_{K=w}^{I2-1} T[I2][K] Ainv[K][w]
-    // (block forward substitution of (I + T) X = I).  Every block it reads in column w is its
-    // own earlier result, so no workgroup barrier is needed; products run on fp32 MFMA.
+    // (block forward substitution of (I + T) X = I); every block it reads in column w is its
+    // own earlier result.  Products on fp32 MFMA.
     {
-        float* sP = sTmp + w * 256;   // wave-private 16x16 staging tile
+        float* sP = sTmp + w * BLK_SZ;
         const int lr = lane & 15, lk = lane >> 4;
         for (int I2 = w + 1; I2 < 4; ++I2) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int K = w; K < I2; ++K)
+            for (int K = w; K < I2; ++K) {
+                const float* tb = sT + blk(I2, K) * BLK_SZ;
+                const float* ab = sAi + blk(K, w) * BLK_SZ;
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        sT[(16 * I2 + lr) * F_LD + 16 * K + 4 * ks + lk],
-                        sAi[(16 * K + 4 * ks + lk) * F_LD + 16 * w + lr], acc, 0, 0, 0);
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tb[lr * BLK_LD + 4 * ks + lk],
+                                                               ab[(4 * ks + lk) * BLK_LD + lr],
+                                                               acc, 0, 0, 0);
+            }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sP[(4 * lk + i) * 16 + lr] = acc[i];
+            for (int i = 0; i < 4; ++i) sP[(4 * lk + i) * BLK_LD + lr] = acc[i];
+            const float* dg = sAi + blk(I2, I2) * BLK_SZ;
             f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    sAi[(16 * I2 + lr) * F_LD + 16 * I2 + 4 * ks + lk],
-                    sP[(4 * ks + lk) * 16 + lr], acc2, 0, 0, 0);
+                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(dg[lr * BLK_LD + 4 * ks + lk],
+                                                            sP[(4 * ks + lk) * BLK_LD + lr],
+                                                            acc2, 0, 0, 0);
+            float* ob = sAi + blk(I2, w) * BLK_SZ;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) sAi[(16 * I2 + 4 * lk + i) * F_LD + 16 * w + lr] = -acc2[i];
+            for (int i = 0; i < 4; ++i) ob[(4 * lk + i) * BLK_LD + lr] = -acc2[i];
+        }
+    }
+    __syncthreads();   // Ainv ready; T and the staging tiles dead
+
+    // ---- phase 3b: token-major tiles of (beta K~) hi/lo (phi channel order) and V ----------------
+    {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const bf16x8 sp = sel_phi(hh, q4, n16);
+            const bf16x8 sn = sel_nat(hh, q4, n16);
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int t = 2 * kb + hh;
+                tile_put(sKtH, t, I, q4, n16, to_bf16x4(mfma(bkh[kb], sp, zero)));
+                tile_put(sKtL, t, I, q4, n16, to_bf16x4(mfma(bkl[kb], sp, zero)));
+                tile_put(sVt, t, I, q4, n16, to_bf16x4(mfma(xv[kb], sn, zero)));
+            }
         }
     }
     __syncthreads();
 
-    // ---- phase 4: W^T and U for token block I, three-term hi/lo products --------------------
+    // ---- phase 4: W^T (phi channel tiles) and U for token block I, three-term hi/lo ----------
     const int nks = (I >= 2) ? 2 : 1;  // 32-token K steps that reach the diagonal
+    bf16x4 wT[8], uT[8];
     {
         f32x4 accW[8], accU[8];
 #pragma unroll
@@ -503,26 +592,25 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
         for (int s = 0; s < nks; ++s) {
             // Ainv[16I + n16][32s + 8q4 + e]: B fragment of W^T = (beta K~)^T Ainv^T and A
             // fragment of U = Ainv (beta V)
+            float ai[8];
+            blk_row8(sAi, I, s, q4, n16, ai);
             bf16x8 ah, al;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) SPLIT_BF16(sAi[irow * F_LD + 32 * s + 8 * q4 + e], ah[e], al[e]);
+            for (int e = 0; e < 8; ++e) SPLIT_BF16(ai[e], ah[e], al[e]);
             float b8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) b8[e] = sBeta[32 * s + 8 * q4 + e];
 #pragma unroll
             for (int ft = 0; ft < 8; ++ft) {
-                const int kb = ft >> 1, hf = ft & 1;
-                const int feat = 32 * kb + 8 * (n16 >> 2) + 4 * hf + (n16 & 3);
-                const bf16x8 xh = lds_read8_a8(sKtH + feat * TP_LD + 32 * s + 8 * q4);
-                const bf16x8 xl = lds_read8_a8(sKtL + feat * TP_LD + 32 * s + 8 * q4);
+                const bf16x8 xh = tile_get(sKtH, ft, 4 * s + q4, n16);
+                const bf16x8 xl = tile_get(sKtL, ft, 4 * s + q4, n16);
                 accW[ft] = mfma(xh, ah, accW[ft]);
                 accW[ft] = mfma(xl, ah, accW[ft]);
                 accW[ft] = mfma(xh, al, accW[ft]);
             }
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 vv =
-                    *reinterpret_cast<const bf16x8*>(sVt + (16 * nt + n16) * TR_LD + 32 * s + 8 * q4);
+                const bf16x8 vv = tile_get(sVt, nt, 4 * s + q4, n16);
                 bf16x8 vh, vl;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) SPLIT_BF16((float)vv[e] * b8[e], vh[e], vl[e]);
@@ -531,8 +619,10 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
                 accU[nt] = mfma(ah, vl, accU[nt]);
             }
         }
-        // W^T C layout: lane (q4, n16) holds W[token 16I + n16][32kb + 8q4 + 4hf + r]
+        // W^T accumulator: lane (q4, n16) holds W[token 16I + n16][32kb + 8q4 + 4hf + r] for
+        // tile 2kb + hf, so the pair of tiles is the W fragment the scan multiplies.
         __bf16* wdst = p.Wf + size_t(rec) * (kWBytes / 2);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             bf16x8 oh;
@@ -542,19 +632,23 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
                 oh[4 + r] = (__bf16)accW[2 * kb + 1][r];
             }
             *reinterpret_cast<bf16x8*>(wdst + ((I * 4 + kb) * 64 + lane) * 8) = oh;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) sWt[(32 * kb + 8 * q4 + e) * TR_LD + irow] = oh[e];
+            // token-major W (phi channel order) for Q' = Q~ - Aqk W
+            wT[2 * kb] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16), zero));
+            wT[2 * kb + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16), zero));
         }
-        // U C layout: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
+        // U accumulator: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
         float* udst = p.Uf + size_t(rec) * (kUBytes / 4);
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) {
             *reinterpret_cast<f32x4*>(udst + ((nt * 4 + I) * 64 + lane) * 4) = accU[nt];
-            bf16x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = (__bf16)accU[nt][r];
-            *reinterpret_cast<bf16x4*>(sUt + (16 * nt + n16) * TR_LD + 16 * I + 4 * q4) = o;
+            uT[nt] = to_bf16x4(accU[nt]);
         }
+    }
+    __syncthreads();   // every wave is done with the (beta K~) and V tiles
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        tile_put(sW, t, I, q4, n16, wT[t]);
+        tile_put(sU, t, I, q4, n16, uT[t]);
     }
     __syncthreads();
 
@@ -569,21 +663,20 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
             for (int r = 0; r < 4; ++r) accQ[f][r] = Qt[kb * 8 + 4 * hf + r];
         }
         for (int s = 0; s < nks; ++s) {
+            float aq[8];
+            blk_row8(sAqk, I, s, q4, n16, aq);
             bf16x8 qh, ql;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) SPLIT_BF16(sAqk[irow * F_LD + 32 * s + 8 * q4 + e], qh[e], ql[e]);
+            for (int e = 0; e < 8; ++e) SPLIT_BF16(aq[e], qh[e], ql[e]);
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
-                const bf16x8 a =
-                    *reinterpret_cast<const bf16x8*>(sUt + (16 * nt + n16) * TR_LD + 32 * s + 8 * q4);
+                const bf16x8 a = tile_get(sU, nt, 4 * s + q4, n16);
                 accO[nt] = mfma(a, qh, accO[nt]);
                 accO[nt] = mfma(a, ql, accO[nt]);
             }
 #pragma unroll
             for (int ft = 0; ft < 8; ++ft) {
-                const int kb = ft >> 1, hf = ft & 1;
-                const int feat = 32 * kb + 8 * (n16 >> 2) + 4 * hf + (n16 & 3);
-                bf16x8 a = *reinterpret_cast<const bf16x8*>(sWt + feat * TR_LD + 32 * s + 8 * q4);
+                bf16x8 a = tile_get(sW, ft, 4 * s + q4, n16);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) a[e] = -a[e];
                 accQ[ft] = mfma(a, qh, accQ[ft]);
@@ -592,12 +685,8 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
         }
         __bf16* odst = p.Of + size_t(rec) * (kOBytes / 2);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
-            bf16x4 o;
-#pragma unroll
-            for (int r = 0; r < 4; ++r) o[r] = (__bf16)accO[nt][r];
-            *reinterpret_cast<bf16x4*>(odst + ((nt * 4 + I) * 64 + lane) * 4) = o;
-        }
+        for (int nt = 0; nt < 8; ++nt)
+            *reinterpret_cast<bf16x4*>(odst + ((nt * 4 + I) * 64 + lane) * 4) = to_bf16x4(accO[nt]);
         __bf16* qdst = p.Qf + size_t(rec) * (kQBytes / 2);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -608,29 +697,6 @@ __global__ __launch_bounds__(kThreads) void kda_intra_kernel(Params p) {
                 o[4 + r] = (__bf16)accQ[2 * kb + 1][r];
             }
             *reinterpret_cast<bf16x8*>(qdst + ((I * 4 + kb) * 64 + lane) * 8) = o;
-        }
-        // K_dec hi/lo into the feature-major staging tiles (the (beta K~)^T tiles are dead)
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                __bf16 hi, lo;
-                SPLIT_BF16(Kd[kb * 8 + e], hi, lo);
-                sKdH[(32 * kb + 8 * q4 + e) * TP_LD + irow] = hi;
-                sKdL[(32 * kb + 8 * q4 + e) * TP_LD + irow] = lo;
-            }
-    }
-    __syncthreads();
-
-    // ---- phase 6: K_dec fragments (A operand of the state update), hi then lo ---------------
-    {
-        __bf16* kdst = p.Kf + size_t(rec) * (kKBytes / 2);
-        for (int f = tid; f < 2 * 16 * 64; f += kThreads) {
-            const int hl = f >> 10, frag = (f >> 6) & 15, ln = f & 63;
-            const int mt = frag >> 1, s = frag & 1;
-            const int qq = ln >> 4, m = ln & 15;
-            const __bf16* src = (hl ? sKdL : sKdH) + (16 * mt + m) * TP_LD + 32 * s + 8 * qq;
-            *reinterpret_cast<bf16x8*>(kdst + size_t(f) * 8) = lds_read8_a8(src);
         }
     }
 }
