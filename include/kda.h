@@ -115,10 +115,12 @@ kda_status kda_chunk_fwd(const kda_shape* shape,
 int32_t kda_num_stages(void);
 const char* kda_stage_name(int32_t stage);
 
-/* Profiling variant of kda_chunk_fwd: identical work, plus hipEventRecord(stage_events[0])
- * before the first kernel and hipEventRecord(stage_events[i]) right after kernel i, all on
- * `stream`.  n_stage_events must be at least kda_num_stages() + 1; the events are created by
- * the caller.  Used to time each kernel inside a benchmark's timed region. */
+/* Profiling variant of kda_chunk_fwd: identical work.  For each stage s, the kernel's own
+ * dispatch records stage_events[2s] when the kernel starts and stage_events[2s+1] when it ends
+ * (hipExtLaunchKernel; no marker packet between the kernels), so hipEventElapsedTime of the pair
+ * is the kernel's duration.  A stage with no kernel records its two events back to back on
+ * `stream`.  n_stage_events must be at least 2 * kda_num_stages(); the caller creates the events.
+ * Returns KDA_ERR_INVALID_ARG for a NULL array or too few events, launching nothing. */
 kda_status kda_chunk_fwd_timed(const kda_shape* shape,
                                const void* q, const void* k, const void* v,
                                const float* g, const void* beta,

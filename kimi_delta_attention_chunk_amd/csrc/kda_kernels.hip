@@ -26,6 +26,7 @@
 // (block J) is split at the first row r_I of block I into two factors <= 1; inside a diagonal
 // block the read key carries 2^(G_r - G_j) <= 2^(15 * 5 * log2 e) < 2^109 for g >= -5, finite
 // in fp32/bf16, and masked entries are removed by select, never by multiplication.
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -1106,6 +1107,19 @@ __global__ __launch_bounds__(kThreads) void kda_seg_kernel(Params p) {
     }
 }
 
+constexpr int kStages = 3;   // intra, segment pass, scan
+
+// One kernel launch.  With events, the dispatch itself records e0 when the kernel starts and
+// e1 when it ends (hipExtLaunchKernel), so no marker packet sits between the kernels.
+kda_status launch_kernel(const void* kernel, unsigned grid, hipStream_t stream, hipEvent_t e0,
+                         hipEvent_t e1, Params& p) {
+    void* args[] = {&p};
+    if (hipExtLaunchKernel(kernel, dim3(grid), dim3(kThreads), args, 0, stream, e0, e1, 0) !=
+        hipSuccess)
+        return KDA_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
+}
+
 kda_status launch(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const float* g, const void* beta, const float* initial_state,
                   const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
@@ -1116,7 +1130,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     st = check_call(shape, plan, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                     workspace, workspace_bytes);
     if (st != KDA_OK) return st;
-    if (ev && n_ev < 4) return KDA_ERR_INVALID_ARG;
+    if (ev && n_ev < 2 * kStages) return KDA_ERR_INVALID_ARG;
 
     Params p;
     p.q = static_cast<const __bf16*>(q);
@@ -1150,26 +1164,24 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.flags = shape->flags;
 
     (void)hipGetLastError();  // clear a stale error so the checks below see only ours
-    if (ev && hipEventRecord(ev[0], stream) != hipSuccess) return KDA_ERR_HIP;
-    hipLaunchKernelGGL(kda_intra_kernel, dim3(unsigned(plan.intra_blocks)), dim3(kThreads), 0,
-                       stream, p);
-    if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
-    if (ev && hipEventRecord(ev[1], stream) != hipSuccess) return KDA_ERR_HIP;
+    auto e = [&](int i) { return ev ? ev[i] : hipEvent_t(nullptr); };
+    kda_status st2 = launch_kernel(reinterpret_cast<const void*>(&kda_intra_kernel),
+                                   unsigned(plan.intra_blocks), stream, e(0), e(1), p);
+    if (st2 != KDA_OK) return st2;
     if (plan.seg_p > 1) {
-        hipLaunchKernelGGL(kda_seg_kernel, dim3(unsigned(plan.seg_blocks)), dim3(kThreads), 0,
-                           stream, p);
-        if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
+        st2 = launch_kernel(reinterpret_cast<const void*>(&kda_seg_kernel),
+                            unsigned(plan.seg_blocks), stream, e(2), e(3), p);
+        if (st2 != KDA_OK) return st2;
+    } else if (ev) {   // no segment pass: an empty stage
+        if (hipEventRecord(ev[2], stream) != hipSuccess ||
+            hipEventRecord(ev[3], stream) != hipSuccess)
+            return KDA_ERR_HIP;
     }
-    if (ev && hipEventRecord(ev[2], stream) != hipSuccess) return KDA_ERR_HIP;
-    const dim3 sgrid(unsigned(plan.scan_blocks));
-    if (plan.scan_nt == 4)
-        hipLaunchKernelGGL(kda_scan_kernel<4>, sgrid, dim3(kThreads), 0, stream, p);
-    else if (plan.scan_nt == 2)
-        hipLaunchKernelGGL(kda_scan_kernel<2>, sgrid, dim3(kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL(kda_scan_kernel<1>, sgrid, dim3(kThreads), 0, stream, p);
-    if (hipGetLastError() != hipSuccess) return KDA_ERR_HIP;
-    if (ev && hipEventRecord(ev[3], stream) != hipSuccess) return KDA_ERR_HIP;
+    const void* scan = plan.scan_nt == 4   ? reinterpret_cast<const void*>(&kda_scan_kernel<4>)
+                       : plan.scan_nt == 2 ? reinterpret_cast<const void*>(&kda_scan_kernel<2>)
+                                           : reinterpret_cast<const void*>(&kda_scan_kernel<1>);
+    st2 = launch_kernel(scan, unsigned(plan.scan_blocks), stream, e(4), e(5), p);
+    if (st2 != KDA_OK) return st2;
     return KDA_OK;
 }
 
@@ -1200,12 +1212,12 @@ kda_status kda_chunk_fwd_timed(const kda_shape* shape, const void* q, const void
                                float* final_state, void* workspace, size_t workspace_bytes,
                                hipStream_t stream, hipEvent_t* stage_events,
                                int32_t n_stage_events) {
-    if (!stage_events || n_stage_events < 4) return KDA_ERR_INVALID_ARG;
+    if (!stage_events || n_stage_events < 2 * kda::kStages) return KDA_ERR_INVALID_ARG;
     return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                        workspace, workspace_bytes, stream, stage_events, n_stage_events);
 }
 
-int32_t kda_num_stages(void) { return 3; }
+int32_t kda_num_stages(void) { return kda::kStages; }
 
 const char* kda_stage_name(int32_t stage) {
     switch (stage) {

@@ -119,10 +119,16 @@ def test_tnd_needs_cu_seqlens(lib):
 
 
 def test_timed_needs_events(lib):
+    """Two events per stage; fewer is rejected before any launch (so fake pointers are safe)."""
     shape = make_shape("BNSD", 1, 100, 1, 1, 0.1)
     P = ctypes.c_void_p
-    evs = (ctypes.c_void_p * 3)()
+    n = 2 * lib.kda_num_stages() - 1
+    evs = (ctypes.c_void_p * n)()
     st = lib.kda_chunk_fwd_timed(ctypes.byref(shape), P(0x10000), P(0x20000), P(0x30000),
                                  P(0x40000), P(0x50000), P(None), P(None), P(0x60000),
-                                 P(None), P(0x100000), ctypes.c_size_t(1 << 40), P(None), evs, 3)
+                                 P(None), P(0x100000), ctypes.c_size_t(1 << 40), P(None), evs, n)
+    assert st == 1
+    st = lib.kda_chunk_fwd_timed(ctypes.byref(shape), P(0x10000), P(0x20000), P(0x30000),
+                                 P(0x40000), P(0x50000), P(None), P(None), P(0x60000),
+                                 P(None), P(0x100000), ctypes.c_size_t(1 << 40), P(None), None, 6)
     assert st == 1
