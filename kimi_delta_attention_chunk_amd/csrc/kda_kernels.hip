@@ -899,36 +899,61 @@ __device__ __forceinline__ void segment_range(int nchunks, int seg_p, int seg, i
     if (cb > nchunks) cb = nchunks;
 }
 
-// S^T <- P_s^T S^T + N_s^T for this wave's Dk rows, i.e. S <- S P_s + N_s, with the state in S
-// (registers) and in LDS (B operand).  P_s is stored transposed: Pt[dk'][dk] = P_s[dk][dk'].
+// Operands of one combine step S <- S P_s + N_s for this wave's Dk rows: rows 16(2w+mt)+n16 of
+// P_s^T (stored transposed: Pt[dk'][dk] = P_s[dk][dk']) and this workgroup's tiles of N_s.
 template <int NT>
-__device__ __forceinline__ void combine_step(const float* Pt, const float* Nst,
-                                             f32x4 (&S)[2][NT], const ScanLds& L, int dv_tile0) {
+struct CombFrags {
+    f32x4 pa[2][4], pb[2][4];   // Pt[16(2w+mt)+n16][32kb+8q4 .. +3] and [.. +4 .. +7]
+    f32x4 n[NT][2];             // N_s[16(dv_tile0+nt)+n16][16(2w+mt)+4q4 .. +3]
+};
+
+template <int NT>
+__device__ __forceinline__ void load_comb(const float* Pt, const float* Nst, int dv_tile0,
+                                          CombFrags<NT>& f) {
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const float* src = Pt + size_t(16 * (2 * w + mt) + n16) * kHead + 32 * kb + 8 * q4;
+            f.pa[mt][kb] = *reinterpret_cast<const f32x4*>(src);
+            f.pb[mt][kb] = *reinterpret_cast<const f32x4*>(src + 4);
+        }
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+            f.n[nt][mt] = *reinterpret_cast<const f32x4*>(
+                Nst + size_t(16 * (dv_tile0 + nt) + n16) * kHead + 16 * (2 * w + mt) + 4 * q4);
+}
+
+// S^T <- P_s^T S^T + N_s^T for this wave's Dk rows, i.e. S <- S P_s + N_s, with the state in S
+// (registers) and in LDS (B operand); three-term hi/lo products.
+template <int NT>
+__device__ __forceinline__ void combine_step(const CombFrags<NT>& f, f32x4 (&S)[2][NT],
+                                             const ScanLds& L) {
+    const int lane = threadIdx.x & 63;
+    const int w = threadIdx.x >> 6;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
     bf16x8 ph[2][4], pl[2][4];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const float* src = Pt + size_t(16 * (2 * w + mt) + n16) * kHead + 32 * kb + 8 * q4;
-            const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-            const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                SPLIT_BF16(a[e], ph[mt][kb][e], pl[mt][kb][e]);
-                SPLIT_BF16(b[e], ph[mt][kb][4 + e], pl[mt][kb][4 + e]);
+                SPLIT_BF16(f.pa[mt][kb][e], ph[mt][kb][e], pl[mt][kb][e]);
+                SPLIT_BF16(f.pb[mt][kb][e], ph[mt][kb][4 + e], pl[mt][kb][4 + e]);
             }
-        }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        const int dv = 16 * (dv_tile0 + nt) + n16;
 #pragma unroll
         for (int mt = 0; mt < 2; ++mt) {
-            f32x4 acc = *reinterpret_cast<const f32x4*>(Nst + size_t(dv) * kHead +
-                                                        16 * (2 * w + mt) + 4 * q4);
+            f32x4 acc = f.n[nt][mt];
 #pragma unroll
             for (int kb = 0; kb < 4; ++kb) {
                 const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
@@ -950,8 +975,32 @@ __device__ __forceinline__ void combine_step(const float* Pt, const float* Nst,
     lds_barrier();
 }
 
+// S_in(seg) = (((N_0) P_1 + N_1) P_2 + ...) P_{seg-1} + N_{seg-1}, with S = N_0 on entry.  The
+// next step's operands load while the current one multiplies (two register sets; the load is
+// issued on every step, past the end as a reload of the last matrices, never used).
 template <int NT>
-__global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
+__device__ __forceinline__ void combine_segments(const Params& p, int bh, int seg,
+                                                 f32x4 (&S)[2][NT], const ScanLds& L,
+                                                 int dv_tile0) {
+    if (seg < 2) return;
+    auto mat = [&](int sp) {
+        return (size_t(bh) * p.seg_p + (sp < seg - 1 ? sp : seg - 1)) * kHead * kHead;
+    };
+    CombFrags<NT> ca, cb;
+    load_comb<NT>(p.Pt + mat(1), p.Nst + mat(1), dv_tile0, ca);
+    int sp = 1;
+    for (; sp + 2 <= seg; sp += 2) {
+        load_comb<NT>(p.Pt + mat(sp + 1), p.Nst + mat(sp + 1), dv_tile0, cb);
+        combine_step<NT>(ca, S, L);
+        load_comb<NT>(p.Pt + mat(sp + 2), p.Nst + mat(sp + 2), dv_tile0, ca);
+        combine_step<NT>(cb, S, L);
+    }
+    if (sp < seg) combine_step<NT>(ca, S, L);
+}
+
+// The one-tile form keeps under 256 registers so that two workgroups share a compute unit.
+template <int NT>
+__global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Params p) {
     constexpr int BV = 16 * NT;
     __shared__ __attribute__((aligned(16))) __bf16 sSh[BV * S_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sSl[BV * S_LD];
@@ -1002,11 +1051,7 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
             put_state(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
         }
     lds_barrier();
-    // S_in(seg) = (((N_0) P_1 + N_1) P_2 + ...) P_{seg-1} + N_{seg-1}
-    for (int sp = 1; sp < seg; ++sp) {
-        const size_t m = (size_t(bh) * p.seg_p + sp) * kHead * kHead;
-        combine_step<NT>(p.Pt + m, p.Nst + m, S, L, dv_tile0);
-    }
+    combine_segments<NT>(p, bh, seg, S, L, dv_tile0);
 
     run_chunks<NT, true, true>(p, S, L, int64_t(slot0) * p.n_v + h, cb, ce, len, ob, os,
                                dv_tile0);
@@ -1038,7 +1083,7 @@ __global__ __launch_bounds__(kThreads) void kda_scan_kernel(Params p) {
 // Segment pass of the two-level scan: 16 workgroups per (sequence, head, segment s < seg_p-1).
 // Slots 0..7: N_s tiles (from S = 0, or from the initial state for s = 0, with U); slots 8..15:
 // P_s tiles (from 16 identity rows each, without U; not needed for s = 0).
-__global__ __launch_bounds__(kThreads) void kda_seg_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * S_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * S_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[16 * VN_LD];
