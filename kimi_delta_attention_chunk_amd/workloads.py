@@ -34,6 +34,7 @@ class Workload:
     seed: int
     tnd_max_len: int = 0        # TND: lengths uniform in [1, tnd_max_len]
     note: str = ""
+    scalar_gate: bool = False   # one gate per (token, value head), shaped like beta
 
 
 WORKLOADS = [
@@ -47,6 +48,9 @@ WORKLOADS = [
              note="32 packed sequences, lengths U{1..4096}; Nqk=Nv=32; per-sequence states"),
     Workload("long_s128k_n32", "BNSD", 1, 131072, 32, 32, "mixed", False, 1004,
              note="B=1, Nqk=Nv=32, S=131072 (2048 chunks/head); mixed per-channel decay"),
+    Workload("gdn_prefill_s8k_n3", "BNSD", 1, 8192, 3, 3, "strong", True, 1005,
+             note="the 8K prefill with one gate per (token, head) (the GDN form); "
+                  "g = -5*sigmoid(N(0,1))", scalar_gate=True),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -71,6 +75,11 @@ class Inputs:
     meta: dict = field(default_factory=dict)
 
     @property
+    def scalar_gate(self) -> bool:
+        """g holds one value per (token, value head) (beta's shape) instead of one per channel."""
+        return tuple(self.g.shape) == tuple(self.beta.shape)
+
+    @property
     def lengths(self) -> list:
         if self.cu_seqlens is None:
             return [self.seq_len] * self.batch
@@ -91,7 +100,7 @@ class Inputs:
 
 
 def _gate(kind: str, shape, gen: torch.Generator) -> torch.Tensor:
-    """Natural-log decay g <= 0 drawn per token and channel (last axis = channel)."""
+    """Natural-log decay g <= 0, one draw per element of `shape` ("mixed" splits the last axis)."""
     if kind == "small":
         return -0.05 * torch.rand(shape, generator=gen)
     if kind == "strong":
@@ -114,11 +123,12 @@ def _gate(kind: str, shape, gen: torch.Generator) -> torch.Tensor:
 def make_inputs(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, *,
                 g_kind: str = "strong", init: bool = False, seed: int = 0,
                 lengths: Optional[list] = None, valid_lengths: Optional[list] = None,
-                d: int = D) -> Inputs:
+                d: int = D, scalar_gate: bool = False) -> Inputs:
     """Draw one seeded input set.
 
     layout "TND" packs ``lengths`` (a list of sequence lengths) into T tokens; for BNSD/BSND
     ``valid_lengths`` (optional) becomes a cu_seqlens prefix sum of per-row valid lengths.
+    ``scalar_gate`` draws g with beta's shape (one gate per token and value head).
     """
     gen = torch.Generator().manual_seed(int(seed))
     if layout == "TND":
@@ -145,7 +155,7 @@ def make_inputs(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, *,
     q = torch.randn(qs, generator=gen).to(torch.bfloat16)
     k = torch.randn(qs, generator=gen).to(torch.bfloat16)
     v = torch.randn(vs, generator=gen).to(torch.bfloat16)
-    g = _gate(g_kind, vs, gen).to(torch.float32).contiguous()
+    g = _gate(g_kind, bs if scalar_gate else vs, gen).to(torch.float32).contiguous()
     beta = torch.randn(bs, generator=gen).to(torch.bfloat16)
     st = None
     if init:
@@ -162,9 +172,9 @@ def workload_inputs(w, seed: Optional[int] = None) -> Inputs:
         gen = torch.Generator().manual_seed(s + 7919)
         lengths = torch.randint(1, w.tnd_max_len + 1, (w.batch,), generator=gen).tolist()
         inp = make_inputs("TND", w.batch, 0, w.n_qk, w.n_v, g_kind=w.g_kind, init=w.init,
-                          seed=s, lengths=lengths)
+                          seed=s, lengths=lengths, scalar_gate=w.scalar_gate)
     else:
         inp = make_inputs(w.layout, w.batch, w.seq_len, w.n_qk, w.n_v, g_kind=w.g_kind,
-                          init=w.init, seed=s)
+                          init=w.init, seed=s, scalar_gate=w.scalar_gate)
     inp.meta["workload"] = w.name
     return inp

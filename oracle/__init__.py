@@ -10,6 +10,7 @@ from .oracle import (  # noqa: F401
     LAYOUTS,
     QK_L2NORM,
     BETA_SIGMOID,
+    SCALAR_GATE,
     build_oracle,
     load_oracle,
     kda_oracle,

@@ -16,6 +16,8 @@
  *     final_state[b, h] = S
  *   Optionally q and k rows are L2-normalised first (x / sqrt(sum x^2 + 1e-6)) and beta is
  *   the logistic sigmoid of the stored value.
+ *   With ORACLE_SCALAR_GATE, g holds one value per (token, value head), laid out like beta,
+ *   and exp(g_t) decays every key column alike: the scalar-gate (GDN) form of the same rule.
  *
  * Sources (the pages this follows):
  *   - vLLM PR #43195 summary "KDA chunk prefill decay uses exp2", section 功能与动机: the
@@ -26,6 +28,10 @@
  *     beta sigmoid are fused options; section 参数说明: the state's last two axes are (Dv, Dk);
  *     the three layouts BNSD / BSND / TND and the cu_seqlens prefix sum (sections 参数说明 and
  *     约束说明).
+ *   - vLLM PR #42076 summary (GDN KKT kernel precision on Hopper), sections 实现拆解 and 关键源码片段,
+ *     and vLLM PR #45000 summary (GDN KKT compile time on RDNA), 关键源码片段: the GDN kernel
+ *     forms the product of beta-scaled keys with the raw keys and applies the gate g only
+ *     afterwards, which a gate shared by all key channels of a token allows.
  *
  * Readings where the pages are silent (each is also listed in the design notes):
  *   - L2-norm epsilon 1e-6 inside the square root.
@@ -33,6 +39,9 @@
  *   - BNSD/BSND with cu_seqlens: batch row b holds cu[b+1]-cu[b] valid tokens at its start;
  *     out rows past that length are left untouched by this oracle.
  *   - initial_state == NULL means a zero state; final_state == NULL means it is not returned.
+ *   - Scalar gate: one fp32 value per (token, value head), the natural-log decay of every key
+ *     channel of that token (the GDN pages show the gate applied after the key product, which
+ *     only a channel-independent gate permits).
  *
  * Parity pins for this function live in the CPU test suite: a hand-worked two-token example,
  * an independent brute-force evaluation of the chunk equations, and closed-form invariants.
@@ -52,7 +61,7 @@
 #endif
 
 enum { ORACLE_BNSD = 0, ORACLE_BSND = 1, ORACLE_TND = 2 };
-enum { ORACLE_QK_L2NORM = 1u, ORACLE_BETA_SIGMOID = 2u };
+enum { ORACLE_QK_L2NORM = 1u, ORACLE_BETA_SIGMOID = 2u, ORACLE_SCALAR_GATE = 4u };
 
 static double bf16_bits_to_double(uint16_t bits) {
     uint32_t u = ((uint32_t)bits) << 16;
@@ -114,6 +123,7 @@ int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_
     if (!q || !k || !v || !g || !beta || !out) return -6;
 
     const int group = n_v / n_qk;
+    const int scalar_gate = (flags & ORACLE_SCALAR_GATE) != 0;
     (void)group;
     (void)scale;
     const int rows_per_chain = 16;
@@ -184,15 +194,26 @@ int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_
                 if (flags & ORACLE_BETA_SIGMOID) bt = 1.0 / (1.0 + exp(-bt));
 #endif
                 for (int j = 0; j < d_k; ++j) {
+                    /* gate of channel j: its own value, or the token's one value (scalar gate) */
+#if KDA_ORACLE_MUTANT == 13
+                    /* planted: scalar gate of the query/key head instead of the value head */
+                    const size_t gi = scalar_gate
+                        ? beta_offset(layout, b, t, hq, n_v, seq_len, cu_seqlens) : og + (size_t)j;
+#else
+                    const size_t gi = scalar_gate ? ob : og + (size_t)j;
+#endif
 #if KDA_ORACLE_MUTANT == 11
                     /* planted: gate taken from the previous token */
-                    const size_t ogp = (t > 0) ? row_offset(layout, b, t - 1, h, n_v, seq_len,
-                                                            cu_seqlens, d_k) : og;
-                    dec[j] = (t > 0) ? exp((double)g[ogp + j]) : 1.0;
+                    size_t gip = gi;
+                    if (t > 0)
+                        gip = scalar_gate ? beta_offset(layout, b, t - 1, h, n_v, seq_len, cu_seqlens)
+                                          : row_offset(layout, b, t - 1, h, n_v, seq_len,
+                                                       cu_seqlens, d_k) + (size_t)j;
+                    dec[j] = (t > 0) ? exp((double)g[gip]) : 1.0;
 #elif KDA_ORACLE_MUTANT == 12
-                    dec[j] = exp2((double)g[og + j]);  /* planted: wrong base */
+                    dec[j] = exp2((double)g[gi]);  /* planted: wrong base */
 #else
-                    dec[j] = exp((double)g[og + j]);
+                    dec[j] = exp((double)g[gi]);
 #endif
                 }
 
@@ -201,7 +222,7 @@ int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_
                     const int dv = r0 + i;
 #if KDA_ORACLE_MUTANT == 3
                     /* planted: decay the value rows instead of the key columns */
-                    const double drow = (dv < d_k) ? exp((double)g[og + dv]) : 1.0;
+                    const double drow = (dv < d_k) ? exp((double)g[scalar_gate ? ob : og + dv]) : 1.0;
                     for (int j = 0; j < d_k; ++j) Si[j] *= drow;
 #elif KDA_ORACLE_MUTANT == 1
                     /* planted: decay applied after the write (below) */

@@ -20,6 +20,7 @@ LIB = os.path.join(HERE, "liboracle_kda.so")
 LAYOUTS = {"BNSD": 0, "BSND": 1, "TND": 2}
 QK_L2NORM = 1
 BETA_SIGMOID = 2
+SCALAR_GATE = 4      # g holds one value per (token, value head), shaped like beta
 
 _loaded: dict = {}
 
@@ -114,6 +115,9 @@ def kda_oracle(q, k, v, g, beta, scale: float, initial_state=None, cu_seqlens=No
         if cu_seqlens is None:
             raise ValueError("TND needs cu_seqlens")
         batch = int(np.asarray(cu_seqlens).shape[0]) - 1
+    want_g = bb.shape if (int(flags) & SCALAR_GATE) else vb.shape
+    if ga.shape != want_g:
+        raise ValueError(f"g has shape {ga.shape}, expected {want_g}")
     cu = None if cu_seqlens is None else _arr(cu_seqlens, np.int32)
     init = None if initial_state is None else _arr(initial_state, np.float32)
     lo, hi = (0, d_v) if dv_range is None else (int(dv_range[0]), int(dv_range[1]))

@@ -16,6 +16,9 @@ when that library disagrees with the pages or with mathematics:
   fused options     sigmoid(0) = 1/2; L2-normalising c*u equals u for a unit u
   valid lengths     cu_seqlens with BNSD truncates each batch row
   row subsets       computing a subset of state rows equals the full run
+  scalar gate       one gate per (token, head): the gated delta rule in the form
+                    S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T, and the per-channel
+                    form with the gate repeated over the channels, in every layout
 
 The same functions run against compile-time planted mistakes in the oracle
 (tests/test_oracle_mutants.py) to show that each mistake is caught by at least one pin.
@@ -29,7 +32,7 @@ import os
 import numpy as np
 import torch
 
-from oracle import kda_oracle, QK_L2NORM, BETA_SIGMOID
+from oracle import kda_oracle, QK_L2NORM, BETA_SIGMOID, SCALAR_GATE
 from bruteforce_chunked import bruteforce
 from kimi_delta_attention_chunk_amd.workloads import make_inputs, Inputs
 
@@ -37,7 +40,8 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def _run(lib, inp: Inputs, **kw):
-    flags = (QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+    flags = ((QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+             | (SCALAR_GATE if inp.scalar_gate else 0))
     return kda_oracle(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
                       inp.cu_seqlens, inp.layout, flags, lib_path=lib, **kw)
 
@@ -291,7 +295,48 @@ def pin_row_subset(lib):
     assert np.isnan(so[..., :5]).all() and np.isnan(sf[:, :, 21:]).all()
 
 
+def pin_scalar_gate(lib):
+    """One gate per (token, value head), shared by every key channel (the GDN form).
+
+    (a) Two value heads reading one q/k head, against the gated delta rule written as
+        S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T with a_t = exp(g_t), token by token
+        in numpy fp64.
+    (b) In BNSD, BSND and TND, the same numbers as the per-channel form with each token's gate
+        repeated over the channels.
+    """
+    d, n = 16, 37
+    inp = make_inputs("BNSD", 1, n, 1, 2, g_kind="unit", init=True, seed=131, d=d,
+                      scalar_gate=True)
+    assert inp.scalar_gate and tuple(inp.g.shape) == (1, 2, n)
+    out, fin = _run(lib, inp)
+    q = inp.q[0, 0].double().numpy()
+    k = inp.k[0, 0].double().numpy()
+    q = q / np.sqrt((q * q).sum(1, keepdims=True) + 1e-6)
+    k = k / np.sqrt((k * k).sum(1, keepdims=True) + 1e-6)
+    for h in range(2):
+        v = inp.v[0, h].double().numpy()
+        b = 1 / (1 + np.exp(-inp.beta[0, h].double().numpy()))
+        a = np.exp(inp.g[0, h].double().numpy())
+        S = inp.initial_state[0, h].double().numpy()
+        eo = np.zeros((n, d))
+        for t in range(n):
+            S = a[t] * S @ (np.eye(d) - b[t] * np.outer(k[t], k[t])) + b[t] * np.outer(v[t], k[t])
+            eo[t] = inp.scale * S @ q[t]
+        _close(out[0, h], eo, 1e-10, f"scalar gate out, head {h}")
+        _close(fin[0, h], S, 1e-10, f"scalar gate final_state, head {h}")
+    for layout, kw in (("BNSD", {}), ("BSND", {}), ("TND", dict(lengths=[13, 24]))):
+        sc = make_inputs(layout, 2, 19, 1, 2, g_kind="strong", init=True, seed=132, d=d,
+                         scalar_gate=True, **kw)
+        pc = make_inputs(layout, 2, 19, 1, 2, g_kind="strong", init=True, seed=132, d=d, **kw)
+        pc.q, pc.k, pc.v, pc.beta, pc.initial_state = sc.q, sc.k, sc.v, sc.beta, sc.initial_state
+        pc.g = sc.g[..., None].expand(*sc.g.shape, d).contiguous()
+        so, sf = _run(lib, sc)
+        po, pf = _run(lib, pc)
+        _close(so, po, 0.0, f"scalar vs repeated gate out ({layout})")
+        _close(sf, pf, 0.0, f"scalar vs repeated gate final_state ({layout})")
+
+
 ALL_PINS = [pin_hand_example, pin_bruteforce_chunked, pin_beta_zero, pin_plain_delta_rule,
             pin_perfect_retrieval, pin_linearity, pin_resume_split, pin_layout_invariance,
             pin_packing_invariance, pin_gqa, pin_fused_options, pin_valid_lengths,
-            pin_row_subset]
+            pin_row_subset, pin_scalar_gate]

@@ -1,9 +1,10 @@
 """Every planted mistake in the oracle must be caught by at least one pin.
 
-The oracle source carries compile-time mutants (KDA_ORACLE_MUTANT=1..12): decay after the
+The oracle source carries compile-time mutants (KDA_ORACLE_MUTANT=1..13): decay after the
 write, read before the write, decay of the value rows, a flipped delta sign, a wrong GQA head
 map, a dropped scale, a skipped sigmoid, a skipped L2 norm, a transposed initial state, beta on
-v only, the gate of the previous token, and base-2 instead of natural exp.  Each is built
+v only, the gate of the previous token, base-2 instead of natural exp, and a scalar gate read
+from the query/key head instead of the value head.  Each is built
 into its own library here and run through the pin set.
 """
 import os
@@ -13,7 +14,7 @@ import pytest
 from oracle import build_oracle
 import oracle_pins
 
-MUTANTS = list(range(1, 13))
+MUTANTS = list(range(1, 14))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
