@@ -31,11 +31,16 @@ MALL_BYTES = 256 << 20     # last-level (Infinity) cache
 METRIC = "KDA prefill tokens/s (all heads) at D=128, T=8K; % of MFMA/HBM roofline"
 
 
+def gate_bytes(inp) -> int:
+    """Bytes of g per token-head: 128 fp32 per-channel gates, or one fp32 with the scalar gate."""
+    return 4 if inp.scalar_gate else 128 * 4
+
+
 def path_bytes(inp) -> int:
     """Algorithmic bytes of one call: q,k (bf16) per q/k head, v (bf16), g (fp32), beta (bf16),
     out (bf16) per value head, plus one fp32 state read and one written per (sequence, head)."""
     t = inp.tokens
-    b = t * inp.n_qk * 128 * 2 * 2 + t * inp.n_v * (128 * 2 + 128 * 4 + 2 + 128 * 2)
+    b = t * inp.n_qk * 128 * 2 * 2 + t * inp.n_v * (128 * 2 + gate_bytes(inp) + 2 + 128 * 2)
     states = inp.batch * inp.n_v * 128 * 128 * 4
     return b + states * ((inp.initial_state is not None) + 1)
 
@@ -68,7 +73,7 @@ def intra_bytes(inp) -> int:
     """Compulsory bytes of the intra kernel: q,k,v,g,beta in, the per-chunk record out."""
     chunks = sum((L + 63) // 64 for L in inp.lengths)
     t = inp.tokens
-    rd = t * inp.n_v * (128 * 2 * 3 + 128 * 4 + 2)   # q,k re-read per value head
+    rd = t * inp.n_v * (128 * 2 * 3 + gate_bytes(inp) + 2)   # q,k re-read per value head
     wr = chunks * inp.n_v * (64 * 128 * (2 + 2 + 4 + 4 + 2) + 128 * 4)
     return rd + wr
 

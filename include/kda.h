@@ -54,10 +54,15 @@ typedef enum {
 
 /* Fused prologue options (FlashKDA README, section 功能说明: q/k row L2 normalise and the beta
  * sigmoid are fused into the operator).  KDA_QK_L2NORM replaces each q and k row x by
- * x / sqrt(sum(x^2) + 1e-6); KDA_BETA_SIGMOID reads beta as a logit and applies 1/(1+e^-x). */
+ * x / sqrt(sum(x^2) + 1e-6); KDA_BETA_SIGMOID reads beta as a logit and applies 1/(1+e^-x).
+ * KDA_SCALAR_GATE selects the scalar-gate (GDN) form: g holds one value per (token, value head),
+ * laid out like beta, and exp(g_t) decays every key channel alike (the GDN kernels of the vLLM
+ * PR #42076 and #45000 summaries, sections 关键源码片段, apply the gate after the key product,
+ * which only a channel-independent gate allows). */
 enum {
     KDA_QK_L2NORM = 1u << 0,
-    KDA_BETA_SIGMOID = 1u << 1
+    KDA_BETA_SIGMOID = 1u << 1,
+    KDA_SCALAR_GATE = 1u << 2
 };
 
 typedef enum {
@@ -77,7 +82,7 @@ typedef struct {
     int32_t d_k;       /* must be 128                                                         */
     int32_t d_v;       /* must be 128                                                         */
     float scale;       /* output scale, typically d_k ** -0.5; must be finite                 */
-    uint32_t flags;    /* KDA_QK_L2NORM | KDA_BETA_SIGMOID                                    */
+    uint32_t flags;    /* KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE                  */
 } kda_shape;
 
 /* Bytes of device workspace kda_chunk_fwd needs for `shape` (FlashKDA README, section 功能说明:
@@ -89,7 +94,8 @@ kda_status kda_chunk_fwd_workspace(const kda_shape* shape, size_t* bytes);
 /* The chunked forward (prefill) of KDA.  Semantics: see the top of this file.
  *   q, k           bf16 in `layout`; raw rows when KDA_QK_L2NORM is set
  *   v              bf16 in `layout`
- *   g              fp32, same shape as v: activated natural-log decay per token and key channel
+ *   g              fp32, same shape as v: activated natural-log decay per token and key channel;
+ *                  with KDA_SCALAR_GATE, beta's shape: one decay per token and value head
  *   beta           bf16 (logits when KDA_BETA_SIGMOID is set)
  *   initial_state  fp32 [batch, n_v, d_v, d_k] or NULL (zero state); never written
  *   cu_seqlens     int32 [batch + 1] prefix sum: required for TND; for BNSD/BSND optional, then

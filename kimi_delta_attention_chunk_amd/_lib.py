@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(PKG, "libkda.so")
 KDA_LAYOUT = {"BNSD": 0, "BSND": 1, "TND": 2}
 KDA_QK_L2NORM = 1
 KDA_BETA_SIGMOID = 2
+KDA_SCALAR_GATE = 4
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 
 EXPORTED = ["kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",

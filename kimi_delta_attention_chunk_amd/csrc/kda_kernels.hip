@@ -331,15 +331,26 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         const __bf16* qr = p.q + qb + size_t(tc) * qs;
         const __bf16* kr = p.k + qb + size_t(tc) * qs;
         const __bf16* vr = p.v + vb + size_t(tc) * vs;
-        const float* gr = p.g + vb + size_t(tc) * vs;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int c = 32 * kb + 8 * q4;
             xq[kb] = *reinterpret_cast<const bf16x8*>(qr + c);
             xk[kb] = *reinterpret_cast<const bf16x8*>(kr + c);
             xv[kb] = *reinterpret_cast<const bf16x8*>(vr + c);
-            xg[2 * kb] = *reinterpret_cast<const f32x4*>(gr + c);
-            xg[2 * kb + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
+        }
+        if (p.flags & KDA_SCALAR_GATE) {
+            // one gate per (token, value head), laid out like beta, for every key channel
+            const float gs = p.g[bb + size_t(tc) * bs];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) xg[u] = f32x4{gs, gs, gs, gs};
+        } else {
+            const float* gr = p.g + vb + size_t(tc) * vs;
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const int c = 32 * kb + 8 * q4;
+                xg[2 * kb] = *reinterpret_cast<const f32x4*>(gr + c);
+                xg[2 * kb + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
+            }
         }
         braw = (float)p.beta[bb + size_t(tc) * bs];
     }

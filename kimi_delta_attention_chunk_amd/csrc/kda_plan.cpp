@@ -32,7 +32,8 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     if (s->d_k < 1 || s->d_v < 1) return KDA_ERR_INVALID_ARG;
     if (s->d_k != kHead || s->d_v != kHead) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(s->scale)) return KDA_ERR_INVALID_ARG;
-    if (s->flags & ~uint32_t(KDA_QK_L2NORM | KDA_BETA_SIGMOID)) return KDA_ERR_INVALID_ARG;
+    if (s->flags & ~uint32_t(KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE))
+        return KDA_ERR_INVALID_ARG;
     if (s->layout == KDA_LAYOUT_TND && s->seq_len < s->batch) return KDA_ERR_INVALID_ARG;
 
     Plan p;

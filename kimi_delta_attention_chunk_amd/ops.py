@@ -12,7 +12,7 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import KdaShape, KDA_LAYOUT, KDA_QK_L2NORM, KDA_BETA_SIGMOID, KDA_OK
+from ._lib import KdaShape, KDA_LAYOUT, KDA_QK_L2NORM, KDA_BETA_SIGMOID, KDA_SCALAR_GATE, KDA_OK
 
 D = 128
 
@@ -37,10 +37,11 @@ def kda_stage_name(i: int) -> str:
 
 def make_shape(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, scale: float,
                qk_l2norm: bool = True, beta_sigmoid: bool = True, d_k: int = D,
-               d_v: int = D) -> KdaShape:
+               d_v: int = D, scalar_gate: bool = False) -> KdaShape:
     if layout not in KDA_LAYOUT:
         raise ValueError(f"unknown layout {layout!r}")
-    flags = (KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0)
+    flags = ((KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0)
+             | (KDA_SCALAR_GATE if scalar_gate else 0))
     return KdaShape(KDA_LAYOUT[layout], int(batch), int(seq_len), int(n_qk), int(n_v),
                     int(d_k), int(d_v), float(scale), flags)
 
@@ -82,9 +83,11 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   stage_events: Optional[Sequence] = None):
     """KDA chunked forward on the current HIP device and stream.  Returns (out, final_state).
 
-    q, k: bf16; v: bf16; g: fp32 natural-log decay (v's shape); beta: bf16 (logits when
-    beta_sigmoid); initial_state: fp32 [batch, n_v, 128, 128] or None; cu_seqlens: int32
-    [batch+1] (required for TND).  All tensors must be contiguous and on one GPU.
+    q, k: bf16; v: bf16; g: fp32 natural-log decay, either v's shape (one gate per key
+    channel) or beta's shape (one gate per token and value head, shared by every key channel:
+    the library's scalar-gate option); beta: bf16 (logits when beta_sigmoid); initial_state:
+    fp32 [batch, n_v, 128, 128] or None; cu_seqlens: int32 [batch+1] (required for TND).  All
+    tensors must be contiguous and on one GPU.
     """
     batch, seq_len, n_qk, n_v = infer_shape(q, v, layout, cu_seqlens)
     if scale is None:
@@ -98,8 +101,14 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
             raise ValueError(f"{name} must be a GPU tensor")
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
-    if k.shape != q.shape or g.shape != v.shape:
-        raise ValueError("k must match q and g must match v")
+    if k.shape != q.shape:
+        raise ValueError("k must match q")
+    if g.shape == v.shape:
+        scalar_gate = False
+    elif g.shape == beta.shape:
+        scalar_gate = True
+    else:
+        raise ValueError("g must have v's shape (per channel) or beta's shape (scalar gate)")
     if initial_state is not None and (initial_state.dtype != torch.float32
                                       or not initial_state.is_contiguous()
                                       or tuple(initial_state.shape) != (batch, n_v, v.shape[-1],
@@ -108,7 +117,7 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
         raise ValueError("cu_seqlens must be an int32 GPU tensor")
     shape = make_shape(layout, batch, seq_len, n_qk, n_v, scale, qk_l2norm, beta_sigmoid,
-                       q.shape[-1], v.shape[-1])
+                       q.shape[-1], v.shape[-1], scalar_gate)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(v)

@@ -77,7 +77,8 @@ def test_workspace_sizes(lib):
 @pytest.mark.parametrize("bad, code", [
     (dict(layout=7), 1), (dict(batch=0), 1), (dict(seq_len=0), 1), (dict(n_qk=0), 1),
     (dict(n_qk=4, n_v=2), 1), (dict(n_qk=3, n_v=4), 1), (dict(d_k=64), 2), (dict(d_v=256), 2),
-    (dict(scale=float("nan")), 1), (dict(flags=8), 1),
+    (dict(scale=float("nan")), 1), (dict(flags=8), 1), (dict(flags=16), 1),
+    (dict(flags=7), 0), (dict(flags=4), 0),
 ])
 def test_shape_rejections(lib, bad, code):
     kw = dict(layout="BNSD", batch=1, seq_len=100, n_qk=1, n_v=2, scale=0.1)

@@ -1,10 +1,10 @@
 """GPU parity: the gfx950 library against the fp64 oracle, through the C ABI.
 
 Small cases (several chunks, ragged tails, every layout, GQA, both fused-option settings) are
-compared in full.  The five named workloads run at their full sizes in the launch configuration
-the benchmark times; the oracle checks every output of the tiny and 8K workloads and one full
-16-row Dv tile (all tokens, all heads) of the three large ones, since state rows evolve
-independently in the recurrence.  Further tests check invariants that hold at any size.
+compared in full, for the per-channel gate and the scalar (GDN) gate.  The named workloads run
+at their full sizes in the launch configuration the benchmark times; the oracle checks every
+output of the tiny and both 8K workloads and one full 16-row Dv tile (all tokens, all heads) of
+the three large ones, since state rows evolve independently in the recurrence.  Further tests check invariants that hold at any size.
 """
 import json
 import math
@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import kda_oracle, QK_L2NORM, BETA_SIGMOID
+from oracle import kda_oracle, QK_L2NORM, BETA_SIGMOID, SCALAR_GATE
 from parity import assert_parity
 from kimi_delta_attention_chunk_amd import kda_chunk_fwd, chunk_fwd
 from kimi_delta_attention_chunk_amd.workloads import (Inputs, make_inputs, workload_inputs,
@@ -34,7 +34,8 @@ def need_gpu():
 
 
 def oracle_of(inp: Inputs, dv_range=None):
-    flags = (QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+    flags = ((QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+             | (SCALAR_GATE if inp.scalar_gate else 0))
     return kda_oracle(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
                       inp.cu_seqlens, inp.layout, flags, dv_range=dv_range)
 
@@ -92,7 +93,31 @@ SMALL = [
                               g_kind="floor", init=True, seed=9)),
     ("bnsd_no_decay", dict(layout="BNSD", batch=1, seq_len=192, n_qk=1, n_v=1,
                            g_kind="zero", init=True, seed=10)),
+    # no decay over 64 chunks: the state never forgets, so rounding accumulates longest here
+    ("bnsd_no_decay_s4096", dict(layout="BNSD", batch=1, seq_len=4096, n_qk=1, n_v=1,
+                                 g_kind="zero", init=True, seed=11)),
 ]
+
+# One gate per (token, value head) (KDA_SCALAR_GATE, the GDN form): every layout, GQA, ragged
+# tails, valid lengths, and a sequence long enough for the two-level scan.
+SCALAR_GATE_CASES = [
+    ("gdn_bnsd_gqa_tail", dict(layout="BNSD", batch=2, seq_len=300, n_qk=1, n_v=2,
+                               g_kind="strong", init=True, seed=41, scalar_gate=True)),
+    ("gdn_bsnd_valid_lengths", dict(layout="BSND", batch=2, seq_len=200, n_qk=2, n_v=2,
+                                    g_kind="unit", init=False, seed=42, valid_lengths=[200, 77],
+                                    scalar_gate=True)),
+    ("gdn_tnd_ragged", dict(layout="TND", batch=4, seq_len=0, n_qk=2, n_v=4, g_kind="strong",
+                            init=True, seed=43, lengths=[150, 64, 1, 90], scalar_gate=True)),
+    ("gdn_bnsd_two_level", dict(layout="BNSD", batch=1, seq_len=64 * 40 + 5, n_qk=1, n_v=1,
+                                g_kind="small", init=True, seed=44, scalar_gate=True)),
+]
+
+
+@pytest.mark.parametrize("name,kw", SCALAR_GATE_CASES, ids=[s[0] for s in SCALAR_GATE_CASES])
+def test_scalar_gate(name, kw):
+    inp = make_inputs(**kw)
+    assert inp.scalar_gate
+    compare(inp, name)
 
 
 # Few (sequence, head) chains and long enough sequences: the library runs the two-level scan
@@ -134,7 +159,8 @@ def test_flags_off_prenormalised_inputs():
 
 
 WL_ROWS = {"tiny_s256": None, "prefill_s8k_n3": None, "gqa_tail_s4100": (16, 32),
-           "varlen_tnd_32seq": (48, 64), "long_s128k_n32": (112, 128)}
+           "varlen_tnd_32seq": (48, 64), "long_s128k_n32": (112, 128),
+           "gdn_prefill_s8k_n3": None}
 
 
 @pytest.mark.parametrize("name", [w.name for w in WORKLOADS])
