@@ -259,6 +259,8 @@ __device__ __forceinline__ void blk_row8(const float* m, int I, int s, int q4, i
     }
 }
 
+// SG: one gate per (token, value head) (KDA_SCALAR_GATE), broadcast over the key channels.
+template <bool SG>
 __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) unsigned char smem[INTRA_LDS];
     float* sAqk = reinterpret_cast<float*>(smem + OFF_AQK);
@@ -324,9 +326,24 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     const int tc = tv ? tok : n - 1;     // rows past the tail are read clamped, then zeroed
 
     // ---- phase 0: every global load of the workgroup, in row layout --------------------------
+    // The gate first (the prefix scan needs it first), then q, k, v and beta.  Rows past the
+    // tail are read clamped and masked where they are consumed, so that no register written
+    // here is rewritten before its load returns (which would make the wave wait for it).
     bf16x8 xq[4], xk[4], xv[4];
     f32x4 xg[8];
+    float gsv;   // the one gate of this token with KDA_SCALAR_GATE (beta's layout)
     float braw;
+    if constexpr (SG) {
+        gsv = p.g[bb + size_t(tc) * bs];
+    } else {
+        const float* gr = p.g + vb + size_t(tc) * vs;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int c = 32 * kb + 8 * q4;
+            xg[2 * kb] = *reinterpret_cast<const f32x4*>(gr + c);
+            xg[2 * kb + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
+        }
+    }
     {
         const __bf16* qr = p.q + qb + size_t(tc) * qs;
         const __bf16* kr = p.k + qb + size_t(tc) * qs;
@@ -334,37 +351,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             const int c = 32 * kb + 8 * q4;
-            xq[kb] = *reinterpret_cast<const bf16x8*>(qr + c);
             xk[kb] = *reinterpret_cast<const bf16x8*>(kr + c);
-            xv[kb] = *reinterpret_cast<const bf16x8*>(vr + c);
+            xq[kb] = *reinterpret_cast<const bf16x8*>(qr + c);
         }
-        if (p.flags & KDA_SCALAR_GATE) {
-            // one gate per (token, value head), laid out like beta, for every key channel
-            const float gs = p.g[bb + size_t(tc) * bs];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) xg[u] = f32x4{gs, gs, gs, gs};
-        } else {
-            const float* gr = p.g + vb + size_t(tc) * vs;
-#pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int c = 32 * kb + 8 * q4;
-                xg[2 * kb] = *reinterpret_cast<const f32x4*>(gr + c);
-                xg[2 * kb + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
-            }
-        }
-        braw = (float)p.beta[bb + size_t(tc) * bs];
-    }
-    if (!tv) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                xq[kb][e] = (__bf16)0.f;
-                xk[kb][e] = (__bf16)0.f;
-                xv[kb][e] = (__bf16)0.f;
-            }
-#pragma unroll
-        for (int u = 0; u < 8; ++u) xg[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+            xv[kb] = *reinterpret_cast<const bf16x8*>(vr + 32 * kb + 8 * q4);
+        braw = (float)p.beta[bb + size_t(tc) * bs];
     }
 
     // ---- phase 0a: gate sums -------------------------------------------------------------------
@@ -375,7 +368,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     float d[32];
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-        const float gi = xg[i >> 2][i & 3];
+        float gi;
+        if constexpr (SG) gi = gsv; else gi = xg[i >> 2][i & 3];
+        gi = tv ? gi : 0.f;
         d[i] = row_scan16(n16 == 0 ? 0.f : gi);
         if (n16 == 0) sFirst[I * 128 + 32 * (i >> 3) + 8 * q4 + (i & 7)] = gi;
         if (n16 == 15) sDlast[I * 128 + 32 * (i >> 3) + 8 * q4 + (i & 7)] = d[i];
@@ -421,8 +416,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         sk += __shfl_xor(sk, 16);
         sk += __shfl_xor(sk, 32);
         const bool l2 = (p.flags & KDA_QK_L2NORM) != 0;
-        qn = l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f;
-        kn = l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f;
+        // a zero factor removes the clamped rows past the tail from every q/k product
+        qn = !tv ? 0.f : (l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f);
+        kn = !tv ? 0.f : (l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f);
         bt = 0.f;
         if (tv) bt = (p.flags & KDA_BETA_SIGMOID) ? 1.0f / (1.0f + expf(-braw)) : braw;
     }
@@ -574,6 +570,12 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     __syncthreads();   // Ainv ready; T and the staging tiles dead
 
     // ---- phase 3b: token-major tiles of (beta K~) hi/lo (phi channel order) and V ----------------
+    if (!tv) {   // rows past the tail (v was read clamped)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[kb][e] = (__bf16)0.f;
+    }
     {
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1221,8 +1223,10 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
 
     (void)hipGetLastError();  // clear a stale error so the checks below see only ours
     auto e = [&](int i) { return ev ? ev[i] : hipEvent_t(nullptr); };
-    kda_status st2 = launch_kernel(reinterpret_cast<const void*>(&kda_intra_kernel),
-                                   unsigned(plan.intra_blocks), stream, e(0), e(1), p);
+    const void* intra = (p.flags & KDA_SCALAR_GATE)
+                            ? reinterpret_cast<const void*>(&kda_intra_kernel<true>)
+                            : reinterpret_cast<const void*>(&kda_intra_kernel<false>);
+    kda_status st2 = launch_kernel(intra, unsigned(plan.intra_blocks), stream, e(0), e(1), p);
     if (st2 != KDA_OK) return st2;
     if (plan.seg_p > 1) {
         st2 = launch_kernel(reinterpret_cast<const void*>(&kda_seg_kernel),
