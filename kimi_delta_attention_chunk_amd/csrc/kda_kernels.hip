@@ -506,7 +506,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             qb2[(4 * q4 + r) * BLK_LD + n16] = (i >= jj) ? p.scale * aQ[r] : 0.f;
         }
     }
-    // operands kept for later phases: Q~ = scale * q * exp(G) and (beta K~) hi/lo
+    // operands kept for later phases: Q~ = scale * q * exp(G) and K~ hi/lo
     float Qt[32];
     bf16x8 bkh[4], bkl[4];
 #pragma unroll
@@ -515,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         for (int e = 0; e < 8; ++e) {
             const float a = sVecA[I * 128 + 32 * kb + 8 * q4 + e];
             Qt[8 * kb + e] = p.scale * Lq[8 * kb + e] * a;
-            SPLIT_BF16(bt * Lk[8 * kb + e] * a, bkh[kb][e], bkl[kb][e]);
+            SPLIT_BF16(Lk[8 * kb + e] * a, bkh[kb][e], bkl[kb][e]);   // K~ (beta goes with Ainv)
         }
     __syncthreads();   // T, Aqk ready
 
@@ -569,7 +569,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     }
     __syncthreads();   // Ainv ready; T and the staging tiles dead
 
-    // ---- phase 3b: token-major tiles of (beta K~) hi/lo (phi channel order) and V ----------------
+    // ---- phase 3b: token-major tiles of K~ hi/lo (phi channel order) and V ---------------------
     if (!tv) {   // rows past the tail (v was read clamped)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
@@ -604,16 +604,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             accU[f] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         for (int s = 0; s < nks; ++s) {
-            // Ainv[16I + n16][32s + 8q4 + e]: B fragment of W^T = (beta K~)^T Ainv^T and A
-            // fragment of U = Ainv (beta V)
+            // (Ainv diag beta)[16I + n16][32s + 8q4 + e]: B fragment of
+            // W^T = K~^T (Ainv diag beta)^T and A fragment of U = (Ainv diag beta) V, as hi/lo
             float ai[8];
             blk_row8(sAi, I, s, q4, n16, ai);
             bf16x8 ah, al;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) SPLIT_BF16(ai[e], ah[e], al[e]);
-            float b8[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) b8[e] = sBeta[32 * s + 8 * q4 + e];
+            for (int e = 0; e < 8; ++e) SPLIT_BF16(ai[e] * sBeta[32 * s + 8 * q4 + e], ah[e], al[e]);
 #pragma unroll
             for (int ft = 0; ft < 8; ++ft) {
                 const bf16x8 xh = tile_get(sKtH, ft, 4 * s + q4, n16);
@@ -622,15 +619,12 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 accW[ft] = mfma(xl, ah, accW[ft]);
                 accW[ft] = mfma(xh, al, accW[ft]);
             }
+            // V is exact in bf16: two terms carry the product to the split's precision
 #pragma unroll
             for (int nt = 0; nt < 8; ++nt) {
                 const bf16x8 vv = tile_get(sVt, nt, 4 * s + q4, n16);
-                bf16x8 vh, vl;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) SPLIT_BF16((float)vv[e] * b8[e], vh[e], vl[e]);
-                accU[nt] = mfma(ah, vh, accU[nt]);
-                accU[nt] = mfma(al, vh, accU[nt]);
-                accU[nt] = mfma(ah, vl, accU[nt]);
+                accU[nt] = mfma(ah, vv, accU[nt]);
+                accU[nt] = mfma(al, vv, accU[nt]);
             }
         }
         // W^T accumulator: lane (q4, n16) holds W[token 16I + n16][32kb + 8q4 + 4hf + r] for
@@ -658,7 +652,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             uT[nt] = to_bf16x4(accU[nt]);
         }
     }
-    __syncthreads();   // every wave is done with the (beta K~) and V tiles
+    __syncthreads();   // every wave is done with the K~ and V tiles
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         tile_put(sW, t, I, q4, n16, wT[t]);
