@@ -156,27 +156,28 @@ constexpr int OFF_BETA = OFF_AI + N_BLK * BLK_SZ * 4;      // beta[64]          
 constexpr int OFF_X = OFF_BETA + 256;                      // phase-shared region 49152
 // inside region X, by phase:
 //   gate sums      first[4][128], dlast[4][128] fp32                        at X + 0
-//   T/Aqk          sKF [wave 4][kb 4][lane 64] bf16x8 (16384)              at X + 0
-//                  sT blocks (12800)                                        at X + 16384
-//                  vec: BV[6][128], C[4][128] fp32 (5120)                   at X + 29184
-//                  vecA[4][128] fp32 (2048)                                 at X + 34304
-//   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                    at X + 29184
+//   T/Aqk          sR [pair 6][kb 4][lane 64] bf16x8 (24576)               at X + 0
+//                  sT blocks (12800)                                        at X + 24576
+//                  vec: BV[6][128], C[4][128] fp32 (5120)                   at X + 37376
+//                  vecA[4][128] fp32 (2048)                                 at X + 42496
+//   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                    at X + 37376
 //   W, U           sKt hi/lo tiles (32768)                                  at X + 0
 //                  sVt tile (16384)                                         at X + 32768
-//   O_intra, Q'    sW tile (16384)                                          at X + 0
+//   O_intra, Q'    sW tile (-W, 16384)                                      at X + 0
 //                  sU tile (16384)                                          at X + 16384
-constexpr int X_KF = 0;
-constexpr int X_T = 16384;
-constexpr int X_VEC = 29184;
-constexpr int X_VECA = 34304;
-constexpr int X_TMP = 29184;
+constexpr int X_R = 0;
+constexpr int X_T = 24576;
+constexpr int X_VEC = 37376;
+constexpr int X_VECA = 42496;
+constexpr int X_TMP = 37376;
 constexpr int X_KT = 0;
 constexpr int X_VT = 32768;
 constexpr int X_W = 0;
 constexpr int X_U = 16384;
 constexpr int X_BYTES = 49152;
 constexpr int INTRA_LDS = OFF_X + X_BYTES;
-static_assert(X_VECA + 2048 <= X_VT + TILE_BYTES, "vector rows fit region X");
+static_assert(X_VECA + 2048 <= X_BYTES, "vector rows fit region X");
+static_assert(X_R + 6 * 4 * 64 * 16 <= X_T, "scaled key blocks end before the T blocks");
 static_assert(X_T + N_BLK * BLK_SZ * 4 <= X_VEC, "T blocks end before the vector rows");
 static_assert(X_TMP + 4 * BLK_SZ * 4 <= X_BYTES, "inverse staging fits region X");
 static_assert(2 * INTRA_LDS <= 160 * 1024, "two intra workgroups fit one compute unit");
@@ -215,11 +216,11 @@ __device__ __forceinline__ bf16x8 sel_nat(int h, int q4, int n16) {
     for (int j = 0; j < 8; ++j) r[j] = (8 * q4 + j == 16 * h + n16) ? (__bf16)1.f : (__bf16)0.f;
     return r;
 }
-__device__ __forceinline__ bf16x8 sel_phi(int h, int q4, int n16) {
+__device__ __forceinline__ bf16x8 sel_phi(int h, int q4, int n16, float one = 1.f) {
     bf16x8 r;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-        r[j] = (q4 == (n16 >> 2) && j == 4 * h + (n16 & 3)) ? (__bf16)1.f : (__bf16)0.f;
+        r[j] = (q4 == (n16 >> 2) && j == 4 * h + (n16 & 3)) ? (__bf16)one : (__bf16)0.f;
     return r;
 }
 
@@ -269,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     unsigned char* X = smem + OFF_X;
     float* sFirst = reinterpret_cast<float*>(X);               // [4][128]
     float* sDlast = sFirst + 512;                              // [4][128]
-    bf16x8* sKF = reinterpret_cast<bf16x8*>(X + X_KF);         // [4][4][64]
+    bf16x8* sR = reinterpret_cast<bf16x8*>(X + X_R);           // [pair 6][kb 4][lane 64]
     float* sT = reinterpret_cast<float*>(X + X_T);
     float* sVec = reinterpret_cast<float*>(X + X_VEC);
     float* sVecA = reinterpret_cast<float*>(X + X_VECA);
@@ -435,6 +436,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             bf16x8 kdh, kdl;
+            float kf[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int i = 8 * kb + e;
@@ -446,11 +448,19 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 const float kv = (float)xk[kb][e] * kn;
                 Lk[i] = kv * ef;
                 Lq[i] = (float)xq[kb][e] * qn * ef;
-                const float kf = kv * ff;
-                KFb[kb][e] = (__bf16)kf;
-                SPLIT_BF16(kf * sVec[(VEC_C + I) * 128 + c], kdh[e], kdl[e]);   // K_dec <= 1
+                kf[e] = kv * ff;
+                KFb[kb][e] = (__bf16)kf[e];
+                SPLIT_BF16(kf[e] * sVec[(VEC_C + I) * 128 + c], kdh[e], kdl[e]);   // K_dec <= 1
             }
-            sKF[(I * 4 + kb) * 64 + lane] = KFb[kb];
+            // the key operand of every later row block I2 > I: k_j exp(G[16 I2] - G_j) <= 1
+            for (int I2 = I + 1; I2 < 4; ++I2) {
+                const int pi = pair_index(I2, I);
+                const float* bv = sVec + (VEC_BV + pi) * 128 + 32 * kb + 8 * q4;
+                bf16x8 r;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r[e] = (__bf16)(kf[e] * bv[e]);
+                sR[(pi * 4 + kb) * 64 + lane] = r;
+            }
             // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [hi/lo][mt 8][s 2][lane 64][8]
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -464,37 +474,31 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             }
         }
     }
-    __syncthreads();   // sKF, sBeta ready
+    __syncthreads();   // scaled key blocks, sBeta ready
 
     // ---- phase 2: T and Aqk blocks of row block I on MFMA -------------------------------------
-    // Off-diagonal (I > J): key j relative to the first token of block J (KF of wave J, factor
-    // <= 2^109), query/key i scaled by exp(G_i - G[16J]) <= 1.  Diagonal: both relative to 16I.
-    // Masked entries of a diagonal block may be huge and are removed by select.
+    // Both products use the row block's own operands relative to its first token 16I,
+    // k_i exp(G_i - G[16I]) <= 1 and q_i exp(G_i - G[16I]).  Diagonal: the key side is KF,
+    // exp(G[16I] - G_j) < 2^109; masked entries may be huge and are removed by select.
+    // Off-diagonal (I > J): the key side arrives scaled by its owner wave to k_j exp(G[16I] - G_j)
+    // <= 1.
+    bf16x8 Lkb[4], Lqb[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            Lkb[kb][e] = (__bf16)Lk[8 * kb + e];
+            Lqb[kb][e] = (__bf16)Lq[8 * kb + e];
+        }
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         if (J > I) continue;
         f32x4 aT = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-            bf16x8 ak, aq, bf;
-            if (J == I) {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ak[e] = (__bf16)Lk[8 * kb + e];
-                    aq[e] = (__bf16)Lq[8 * kb + e];
-                }
-                bf = KFb[kb];
-            } else {
-                const float* bv = sVec + (VEC_BV + pair_index(I, J)) * 128 + 32 * kb + 8 * q4;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    ak[e] = (__bf16)(Lk[8 * kb + e] * bv[e]);
-                    aq[e] = (__bf16)(Lq[8 * kb + e] * bv[e]);
-                }
-                bf = sKF[(J * 4 + kb) * 64 + lane];
-            }
-            aT = mfma(ak, bf, aT);
-            aQ = mfma(aq, bf, aQ);
+            const bf16x8 bf = (J == I) ? KFb[kb] : sR[(pair_index(I, J) * 4 + kb) * 64 + lane];
+            aT = mfma(Lkb[kb], bf, aT);
+            aQ = mfma(Lqb[kb], bf, aQ);
         }
         float* tb = sT + blk(I, J) * BLK_SZ;
         float* qb2 = sAqk + blk(I, J) * BLK_SZ;
@@ -640,9 +644,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 oh[4 + r] = (__bf16)accW[2 * kb + 1][r];
             }
             *reinterpret_cast<bf16x8*>(wdst + ((I * 4 + kb) * 64 + lane) * 8) = oh;
-            // token-major W (phi channel order) for Q' = Q~ - Aqk W
-            wT[2 * kb] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16), zero));
-            wT[2 * kb + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16), zero));
+            // token-major -W (phi channel order) for Q' = Q~ + Aqk (-W): a selection with -1
+            wT[2 * kb] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, -1.f), zero));
+            wT[2 * kb + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, -1.f), zero));
         }
         // U accumulator: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
         float* udst = p.Uf + size_t(rec) * (kUBytes / 4);
@@ -684,9 +688,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             }
 #pragma unroll
             for (int ft = 0; ft < 8; ++ft) {
-                bf16x8 a = tile_get(sW, ft, 4 * s + q4, n16);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = -a[e];
+                const bf16x8 a = tile_get(sW, ft, 4 * s + q4, n16);   // -W
                 accQ[ft] = mfma(a, qh, accQ[ft]);
                 accQ[ft] = mfma(a, ql, accQ[ft]);
             }
