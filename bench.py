@@ -31,51 +31,60 @@ MALL_BYTES = 256 << 20     # last-level (Infinity) cache
 METRIC = "KDA prefill tokens/s (all heads) at D=128, T=8K; % of MFMA/HBM roofline"
 
 
+def head_dim(inp) -> int:
+    return int(inp.q.shape[-1])
+
+
 def gate_bytes(inp) -> int:
-    """Bytes of g per token-head: 128 fp32 per-channel gates, or one fp32 with the scalar gate."""
-    return 4 if inp.scalar_gate else 128 * 4
+    """Bytes of g per token-head: D fp32 per-channel gates, or one fp32 with the scalar gate."""
+    return 4 if inp.scalar_gate else head_dim(inp) * 4
 
 
 def path_bytes(inp) -> int:
     """Algorithmic bytes of one call: q,k (bf16) per q/k head, v (bf16), g (fp32), beta (bf16),
     out (bf16) per value head, plus one fp32 state read and one written per (sequence, head)."""
-    t = inp.tokens
-    b = t * inp.n_qk * 128 * 2 * 2 + t * inp.n_v * (128 * 2 + gate_bytes(inp) + 2 + 128 * 2)
-    states = inp.batch * inp.n_v * 128 * 128 * 4
+    t, d = inp.tokens, head_dim(inp)
+    b = t * inp.n_qk * d * 2 * 2 + t * inp.n_v * (d * 2 + gate_bytes(inp) + 2 + d * 2)
+    states = inp.batch * inp.n_v * d * d * 4
     return b + states * ((inp.initial_state is not None) + 1)
 
 
 def seg_p_of(inp) -> int:
     """Segments per sequence chosen by the library's plan (kda_plan.cpp) for this shape."""
     bh = inp.batch * inp.n_v
-    if bh * 8 >= 256:
+    tiles = head_dim(inp) // 16
+    if bh * tiles >= 256:
         return 1
     nc = -(-inp.seq_len // 64) if inp.layout != "TND" else -(-(inp.seq_len // inp.batch) // 64)
-    sp = min((256 // (bh * 8) + 3) // 2, nc // 8, 16)
+    sp = min((256 // (bh * tiles) + 3) // 2, nc // 8, 16)
     return sp if sp >= 2 else 1
 
 
+def record_bytes(d: int) -> int:
+    """Workspace record per (chunk, value head): W, Q' (bf16), K_dec (bf16 hi+lo), U (fp32),
+    O_intra (bf16), gamma (fp32 per channel)."""
+    return 64 * d * (2 + 2 + 4 + 4 + 2) + d * 4
+
+
 def scan_bytes(inp) -> int:
-    """Compulsory bytes of the scan kernel: per (64-token chunk, value head) it reads W (bf16),
-    Q' (bf16), K_dec (bf16 hi+lo), U (fp32), O_intra (bf16), gamma (fp32 x128) and writes out;
-    plus the states, and with a two-level scan the segment matrices it combines."""
+    """Compulsory bytes of the scan kernel: the record of every (chunk, value head) and the
+    output; plus the states, and with a two-level scan the segment matrices it combines."""
+    d = head_dim(inp)
     chunks = sum((L + 63) // 64 for L in inp.lengths)
-    per_chunk = 64 * 128 * (2 + 2 + 4 + 4 + 2) + 128 * 4
-    out = inp.tokens * inp.n_v * 128 * 2
-    states = inp.batch * inp.n_v * 128 * 128 * 4
+    out = inp.tokens * inp.n_v * d * 2
+    states = inp.batch * inp.n_v * d * d * 4
     sp = seg_p_of(inp)
-    mats = inp.batch * inp.n_v * max(sp - 1, 0) * 2 * 128 * 128 * 4
-    return (chunks * inp.n_v * per_chunk + out + states * ((inp.initial_state is not None) + 1)
-            + mats)
+    mats = inp.batch * inp.n_v * max(sp - 1, 0) * 2 * d * d * 4
+    return (chunks * inp.n_v * record_bytes(d) + out
+            + states * ((inp.initial_state is not None) + 1) + mats)
 
 
 def intra_bytes(inp) -> int:
     """Compulsory bytes of the intra kernel: q,k,v,g,beta in, the per-chunk record out."""
+    d = head_dim(inp)
     chunks = sum((L + 63) // 64 for L in inp.lengths)
-    t = inp.tokens
-    rd = t * inp.n_v * (128 * 2 * 3 + gate_bytes(inp) + 2)   # q,k re-read per value head
-    wr = chunks * inp.n_v * (64 * 128 * (2 + 2 + 4 + 4 + 2) + 128 * 4)
-    return rd + wr
+    rd = inp.tokens * inp.n_v * (d * 2 * 3 + gate_bytes(inp) + 2)   # q,k re-read per value head
+    return rd + chunks * inp.n_v * record_bytes(d)
 
 
 def seg_bytes(inp) -> int:
@@ -84,13 +93,14 @@ def seg_bytes(inp) -> int:
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
+    d = head_dim(inp)
     frac = 0
     for L in inp.lengths:
         nc = (L + 63) // 64
         frac += min((sp - 1) * (-(-nc // sp)), nc)   # chunks outside the last segment
-    per_chunk = 64 * 128 * (2 + 4 + 4) + 128 * 4
-    states = inp.batch * inp.n_v * 128 * 128 * 4
-    mats = inp.batch * inp.n_v * (sp - 1) * 2 * 128 * 128 * 4
+    per_chunk = 64 * d * (2 + 4 + 4) + d * 4
+    states = inp.batch * inp.n_v * d * d * 4
+    mats = inp.batch * inp.n_v * (sp - 1) * 2 * d * d * 4
     return frac * inp.n_v * per_chunk + states * (inp.initial_state is not None) + mats
 
 
@@ -185,9 +195,10 @@ def main() -> int:
     dev = torch.device("cuda", 0)
     sets = [host.to(dev) for _ in range(copies)]
     out = torch.empty_like(sets[0].v)
-    fin = torch.empty((host.batch, host.n_v, 128, 128), dtype=torch.float32, device=dev)
+    d = head_dim(host)
+    fin = torch.empty((host.batch, host.n_v, d, d), dtype=torch.float32, device=dev)
     shape = make_shape(host.layout, host.batch, host.seq_len, host.n_qk, host.n_v, host.scale,
-                       host.qk_l2norm, host.beta_sigmoid)
+                       host.qk_l2norm, host.beta_sigmoid, d, d, host.scalar_gate)
     ws = torch.empty(kda_chunk_fwd_workspace(shape), dtype=torch.uint8, device=dev)
     nst = kda_num_stages()
 
@@ -233,7 +244,8 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and distributions of the workload)",
         "config": {"workload": wl.name, "layout": host.layout, "batch": host.batch,
                    "seq_len": host.seq_len, "tokens": host.tokens, "n_qk": host.n_qk,
-                   "n_v": host.n_v, "head_dim": 128, "input_copies": copies,
+                   "n_v": host.n_v, "head_dim": d, "scalar_gate": host.scalar_gate,
+                   "input_copies": copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kda_stage_name(dom), "achieved": achieved / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,

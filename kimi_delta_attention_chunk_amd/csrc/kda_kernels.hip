@@ -261,8 +261,11 @@ __device__ __forceinline__ void blk_row8(const float* m, int I, int s, int q4, i
 }
 
 // SG: one gate per (token, value head) (KDA_SCALAR_GATE), broadcast over the key channels.
-template <bool SG>
+// D: head dim (d_k = d_v), 128 or 64.
+template <bool SG, int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
+    constexpr int KB = D / 32;    // 32-channel K steps of a product over channels
+    constexpr int NTD = D / 16;   // 16-wide channel (or Dv) tiles
     __shared__ __attribute__((aligned(16))) unsigned char smem[INTRA_LDS];
     float* sAqk = reinterpret_cast<float*>(smem + OFF_AQK);
     float* sAi = reinterpret_cast<float*>(smem + OFF_AI);
@@ -314,8 +317,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     const int n = (len - t0) < kChunk ? (len - t0) : kChunk;
 
     size_t qb, qs, vb, vs, bb, bs;
-    row_geom(p, b, hq, p.n_qk, kHead, c0, qb, qs);
-    row_geom(p, b, h, p.n_v, kHead, c0, vb, vs);
+    row_geom(p, b, hq, p.n_qk, D, c0, qb, qs);
+    row_geom(p, b, h, p.n_v, D, c0, vb, vs);
     row_geom(p, b, h, p.n_v, 1, c0, bb, bs);
     qb += size_t(t0) * qs;
     vb += size_t(t0) * vs;
@@ -330,8 +333,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     // The gate first (the prefix scan needs it first), then q, k, v and beta.  Rows past the
     // tail are read clamped and masked where they are consumed, so that no register written
     // here is rewritten before its load returns (which would make the wave wait for it).
-    bf16x8 xq[4], xk[4], xv[4];
-    f32x4 xg[8];
+    bf16x8 xq[KB], xk[KB], xv[KB];
+    f32x4 xg[2 * KB];
     float gsv;   // the one gate of this token with KDA_SCALAR_GATE (beta's layout)
     float braw;
     if constexpr (SG) {
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     } else {
         const float* gr = p.g + vb + size_t(tc) * vs;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             const int c = 32 * kb + 8 * q4;
             xg[2 * kb] = *reinterpret_cast<const f32x4*>(gr + c);
             xg[2 * kb + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
@@ -350,13 +353,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         const __bf16* kr = p.k + qb + size_t(tc) * qs;
         const __bf16* vr = p.v + vb + size_t(tc) * vs;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             const int c = 32 * kb + 8 * q4;
             xk[kb] = *reinterpret_cast<const bf16x8*>(kr + c);
             xq[kb] = *reinterpret_cast<const bf16x8*>(qr + c);
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
             xv[kb] = *reinterpret_cast<const bf16x8*>(vr + 32 * kb + 8 * q4);
         braw = (float)p.beta[bb + size_t(tc) * bs];
     }
@@ -366,9 +369,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     // token, natural log), a prefix sum across the 16 lanes of a DPP row with the first token's
     // term removed.  The block sums go through LDS to give, per channel, G at each block's
     // first token (G[16I]) and G_last = G at the last valid token.
-    float d[32];
+    float d[8 * KB];
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < 8 * KB; ++i) {
         float gi;
         if constexpr (SG) gi = gsv; else gi = xg[i >> 2][i & 3];
         gi = tv ? gi : 0.f;
@@ -377,7 +380,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         if (n16 == 15) sDlast[I * 128 + 32 * (i >> 3) + 8 * q4 + (i & 7)] = d[i];
     }
     __syncthreads();
-    if (tid < 128) {
+    if (tid < D) {
         const int c = tid;
         float Gr[4];
         float acc = 0.f;
@@ -397,7 +400,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             sVec[(VEC_C + J) * 128 + c] = exp2_fast((Gl - Gr[J]) * kLog2e);
             sVecA[J * 128 + c] = exp2_fast(Gr[J] * kLog2e);
         }
-        p.Gf[size_t(rec) * kHead + c] = exp2_fast(Gl * kLog2e);
+        p.Gf[size_t(rec) * D + c] = exp2_fast(Gl * kLog2e);
     }
 
     // ---- phase 1: normalised, decayed operands in registers; K_dec record ---------------------
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     {
         float sq = 0.f, sk = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float fq = (float)xq[kb][e], fk = (float)xk[kb][e];
@@ -426,15 +429,15 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     __syncthreads();   // vector rows ready; first/dlast dead
     if (q4 == 0) sBeta[tok] = bt;
 
-    float Lk[32], Lq[32];
-    bf16x8 KFb[4];
+    float Lk[8 * KB], Lq[8 * KB];
+    bf16x8 KFb[KB];
     {
-        __bf16* kdst = p.Kf + size_t(rec) * (kKBytes / 2);
+        __bf16* kdst = p.Kf + size_t(rec) * (64 * D * 2);
         const int s_k = I >> 1;
         const int lane_k = (2 * (I & 1) + (q4 >> 1)) * 16 + n16;
         const int j0 = 4 * (q4 & 1);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             bf16x8 kdh, kdl;
             float kf[8];
 #pragma unroll
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 for (int e = 0; e < 8; ++e) r[e] = (__bf16)(kf[e] * bv[e]);
                 sR[(pi * 4 + kb) * 64 + lane] = r;
             }
-            // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [hi/lo][mt 8][s 2][lane 64][8]
+            // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [hi/lo][mt D/16][s 2][lane 64][8]
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
                 const bf16x8 sel = sel_nat(hh, q4, n16);
@@ -470,7 +473,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 const bf16x4 tl = to_bf16x4(mfma(kdl, sel, zero));
                 const int mt = 2 * kb + hh;
                 *reinterpret_cast<bf16x4*>(kdst + ((size_t(mt) * 2 + s_k) * 64 + lane_k) * 8 + j0) = th;
-                *reinterpret_cast<bf16x4*>(kdst + 8192 + ((size_t(mt) * 2 + s_k) * 64 + lane_k) * 8 + j0) = tl;
+                *reinterpret_cast<bf16x4*>(kdst + 64 * D + ((size_t(mt) * 2 + s_k) * 64 + lane_k) * 8 + j0) = tl;
             }
         }
     }
@@ -482,9 +485,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     // exp(G[16I] - G_j) < 2^109; masked entries may be huge and are removed by select.
     // Off-diagonal (I > J): the key side arrives scaled by its owner wave to k_j exp(G[16I] - G_j)
     // <= 1.
-    bf16x8 Lkb[4], Lqb[4];
+    bf16x8 Lkb[KB], Lqb[KB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             Lkb[kb][e] = (__bf16)Lk[8 * kb + e];
@@ -495,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         if (J > I) continue;
         f32x4 aT = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             const bf16x8 bf = (J == I) ? KFb[kb] : sR[(pair_index(I, J) * 4 + kb) * 64 + lane];
             aT = mfma(Lkb[kb], bf, aT);
             aQ = mfma(Lqb[kb], bf, aQ);
@@ -511,10 +514,10 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         }
     }
     // operands kept for later phases: Q~ = scale * q * exp(G) and K~ hi/lo
-    float Qt[32];
-    bf16x8 bkh[4], bkl[4];
+    float Qt[8 * KB];
+    bf16x8 bkh[KB], bkl[KB];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float a = sVecA[I * 128 + 32 * kb + 8 * q4 + e];
@@ -576,7 +579,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     // ---- phase 3b: token-major tiles of K~ hi/lo (phi channel order) and V ---------------------
     if (!tv) {   // rows past the tail (v was read clamped)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 8; ++e) xv[kb][e] = (__bf16)0.f;
     }
@@ -587,7 +590,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             const bf16x8 sp = sel_phi(hh, q4, n16);
             const bf16x8 sn = sel_nat(hh, q4, n16);
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < KB; ++kb) {
                 const int t = 2 * kb + hh;
                 tile_put(sKtH, t, I, q4, n16, to_bf16x4(mfma(bkh[kb], sp, zero)));
                 tile_put(sKtL, t, I, q4, n16, to_bf16x4(mfma(bkl[kb], sp, zero)));
@@ -599,11 +602,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 
     // ---- phase 4: W^T (phi channel tiles) and U for token block I, three-term hi/lo ----------
     const int nks = (I >= 2) ? 2 : 1;  // 32-token K steps that reach the diagonal
-    bf16x4 wT[8], uT[8];
+    bf16x4 wT[NTD], uT[NTD];
     {
-        f32x4 accW[8], accU[8];
+        f32x4 accW[NTD], accU[NTD];
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
+        for (int f = 0; f < NTD; ++f) {
             accW[f] = f32x4{0.f, 0.f, 0.f, 0.f};
             accU[f] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -616,7 +619,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) SPLIT_BF16(ai[e] * sBeta[32 * s + 8 * q4 + e], ah[e], al[e]);
 #pragma unroll
-            for (int ft = 0; ft < 8; ++ft) {
+            for (int ft = 0; ft < NTD; ++ft) {
                 const bf16x8 xh = tile_get(sKtH, ft, 4 * s + q4, n16);
                 const bf16x8 xl = tile_get(sKtL, ft, 4 * s + q4, n16);
                 accW[ft] = mfma(xh, ah, accW[ft]);
@@ -625,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             }
             // V is exact in bf16: two terms carry the product to the split's precision
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int nt = 0; nt < NTD; ++nt) {
                 const bf16x8 vv = tile_get(sVt, nt, 4 * s + q4, n16);
                 accU[nt] = mfma(ah, vv, accU[nt]);
                 accU[nt] = mfma(al, vv, accU[nt]);
@@ -633,32 +636,32 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         }
         // W^T accumulator: lane (q4, n16) holds W[token 16I + n16][32kb + 8q4 + 4hf + r] for
         // tile 2kb + hf, so the pair of tiles is the W fragment the scan multiplies.
-        __bf16* wdst = p.Wf + size_t(rec) * (kWBytes / 2);
+        __bf16* wdst = p.Wf + size_t(rec) * (64 * D);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             bf16x8 oh;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 oh[r] = (__bf16)accW[2 * kb][r];
                 oh[4 + r] = (__bf16)accW[2 * kb + 1][r];
             }
-            *reinterpret_cast<bf16x8*>(wdst + ((I * 4 + kb) * 64 + lane) * 8) = oh;
+            *reinterpret_cast<bf16x8*>(wdst + ((I * KB + kb) * 64 + lane) * 8) = oh;
             // token-major -W (phi channel order) for Q' = Q~ + Aqk (-W): a selection with -1
             wT[2 * kb] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, -1.f), zero));
             wT[2 * kb + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, -1.f), zero));
         }
         // U accumulator: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
-        float* udst = p.Uf + size_t(rec) * (kUBytes / 4);
+        float* udst = p.Uf + size_t(rec) * (64 * D);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt) {
+        for (int nt = 0; nt < NTD; ++nt) {
             *reinterpret_cast<f32x4*>(udst + ((nt * 4 + I) * 64 + lane) * 4) = accU[nt];
             uT[nt] = to_bf16x4(accU[nt]);
         }
     }
     __syncthreads();   // every wave is done with the K~ and V tiles
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < NTD; ++t) {
         tile_put(sW, t, I, q4, n16, wT[t]);
         tile_put(sU, t, I, q4, n16, uT[t]);
     }
@@ -666,9 +669,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 
     // ---- phase 5: O_intra^T = U^T Aqk^T and Q'^T = Q~^T - W^T Aqk^T (token block I) --------
     {
-        f32x4 accO[8], accQ[8];
+        f32x4 accO[NTD], accQ[NTD];
 #pragma unroll
-        for (int f = 0; f < 8; ++f) {
+        for (int f = 0; f < NTD; ++f) {
             accO[f] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int kb = f >> 1, hf = f & 1;
 #pragma unroll
@@ -681,32 +684,32 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) SPLIT_BF16(aq[e], qh[e], ql[e]);
 #pragma unroll
-            for (int nt = 0; nt < 8; ++nt) {
+            for (int nt = 0; nt < NTD; ++nt) {
                 const bf16x8 a = tile_get(sU, nt, 4 * s + q4, n16);
                 accO[nt] = mfma(a, qh, accO[nt]);
                 accO[nt] = mfma(a, ql, accO[nt]);
             }
 #pragma unroll
-            for (int ft = 0; ft < 8; ++ft) {
+            for (int ft = 0; ft < NTD; ++ft) {
                 const bf16x8 a = tile_get(sW, ft, 4 * s + q4, n16);   // -W
                 accQ[ft] = mfma(a, qh, accQ[ft]);
                 accQ[ft] = mfma(a, ql, accQ[ft]);
             }
         }
-        __bf16* odst = p.Of + size_t(rec) * (kOBytes / 2);
+        __bf16* odst = p.Of + size_t(rec) * (64 * D);
 #pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
+        for (int nt = 0; nt < NTD; ++nt)
             *reinterpret_cast<bf16x4*>(odst + ((nt * 4 + I) * 64 + lane) * 4) = to_bf16x4(accO[nt]);
-        __bf16* qdst = p.Qf + size_t(rec) * (kQBytes / 2);
+        __bf16* qdst = p.Qf + size_t(rec) * (64 * D);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < KB; ++kb) {
             bf16x8 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 o[r] = (__bf16)accQ[2 * kb][r];
                 o[4 + r] = (__bf16)accQ[2 * kb + 1][r];
             }
-            *reinterpret_cast<bf16x8*>(qdst + ((I * 4 + kb) * 64 + lane) * 8) = o;
+            *reinterpret_cast<bf16x8*>(qdst + ((I * KB + kb) * 64 + lane) * 8) = o;
         }
     }
 }
@@ -728,45 +731,53 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 // the identity (giving P_s, 8 workgroups of 16 identity rows); kda_scan_kernel then forms
 // S_in(s) = S_in(s-1) P_{s-1} + N_{s-1} on MFMA and reruns segment s with outputs.
 
-constexpr int S_LD = 136;   // bf16 [BV][136]  state tile (hi or lo), row = value channel
+// Head-dim constants of the scan kernels (d_k = d_v = D; four waves split the Dk rows).
+template <int D>
+struct HD {
+    static constexpr int KB = D / 32;    // 32-channel K steps of a product over Dk
+    static constexpr int MW = D / 64;    // 16-row Dk tiles per wave
+    static constexpr int TILES = D / 16; // 16-row Dv tiles per head
+    static constexpr int SLD = D + 8;    // bf16 row stride of the LDS state tile (hi or lo)
+};
 constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = value channel
 
-template <int NT>
+template <int NT, int D>
 struct ChunkFrags {
-    bf16x8 w[4];              // W, token tile w, 32-channel block kb
-    bf16x8 qp[4];             // Q', token tile w
-    bf16x8 kh[2][2], kl[2][2];// K_dec^T hi/lo, Dk tile 2w+mt, token step s
-    f32x4 gm[2];              // gamma_last for the lane's Dk rows
-    f32x4 u[NT];              // U (fp32), token tile w, Dv tile
-    bf16x4 o[NT];             // O_intra (bf16), token tile w, Dv tile
+    bf16x8 w[HD<D>::KB];                          // W, token tile w, 32-channel block kb
+    bf16x8 qp[HD<D>::KB];                         // Q', token tile w
+    bf16x8 kh[HD<D>::MW][2], kl[HD<D>::MW][2];    // K_dec^T hi/lo, Dk tile MW*w+mt, token step s
+    f32x4 gm[HD<D>::MW];                          // gamma_last for the lane's Dk rows
+    f32x4 u[NT];                                  // U (fp32), token tile w, Dv tile
+    bf16x4 o[NT];                                 // O_intra (bf16), token tile w, Dv tile
 };
 
-template <int NT, bool WITH_U, bool WITH_OUT>
+template <int NT, bool WITH_U, bool WITH_OUT, int D>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
-                                           int dv_tile0, ChunkFrags<NT>& f) {
-    const __bf16* wsrc = p.Wf + size_t(rec) * (kWBytes / 2);
-    const __bf16* qsrc = p.Qf + size_t(rec) * (kQBytes / 2);
-    const __bf16* ksrc = p.Kf + size_t(rec) * (kKBytes / 2);
+                                           int dv_tile0, ChunkFrags<NT, D>& f) {
+    constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
+    const __bf16* wsrc = p.Wf + size_t(rec) * (64 * D);
+    const __bf16* qsrc = p.Qf + size_t(rec) * (64 * D);
+    const __bf16* ksrc = p.Kf + size_t(rec) * (64 * D * 2);
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-        f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * 4 + kb) * 64 + lane) * 8);
+    for (int kb = 0; kb < KB; ++kb) {
+        f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * KB + kb) * 64 + lane) * 8);
         if constexpr (WITH_OUT)
-            f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * 4 + kb) * 64 + lane) * 8);
+            f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * KB + kb) * 64 + lane) * 8);
     }
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-            const int off = (((2 * w + mt) * 2 + s) * 64 + lane) * 8;
+            const int off = (((MW * w + mt) * 2 + s) * 64 + lane) * 8;
             f.kh[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + off);
-            f.kl[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + 8192 + off);
+            f.kl[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + 64 * D + off);
         }
-    const float* gsrc = p.Gf + size_t(rec) * kHead;
+    const float* gsrc = p.Gf + size_t(rec) * D;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-        f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (2 * w + mt) + 4 * (lane >> 4));
-    const float* usrc = p.Uf + size_t(rec) * (kUBytes / 4);
-    const __bf16* osrc = p.Of + size_t(rec) * (kOBytes / 2);
+    for (int mt = 0; mt < MW; ++mt)
+        f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (MW * w + mt) + 4 * (lane >> 4));
+    const float* usrc = p.Uf + size_t(rec) * (64 * D);
+    const __bf16* osrc = p.Of + size_t(rec) * (64 * D);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int dt = dv_tile0 + nt;
@@ -778,13 +789,14 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
 }
 
 // Writes one fp32 state fragment (4 consecutive Dk values of one Dv row) as hi/lo bf16.
+template <int D>
 __device__ __forceinline__ void put_state(__bf16* sSh, __bf16* sSl, int row, int col,
                                           f32x4 x) {
     bf16x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) SPLIT_BF16(x[i], h[i], l[i]);
-    *reinterpret_cast<bf16x4*>(sSh + row * S_LD + col) = h;
-    *reinterpret_cast<bf16x4*>(sSl + row * S_LD + col) = l;
+    *reinterpret_cast<bf16x4*>(sSh + row * HD<D>::SLD + col) = h;
+    *reinterpret_cast<bf16x4*>(sSl + row * HD<D>::SLD + col) = l;
 }
 
 struct ScanLds {
@@ -796,12 +808,13 @@ struct ScanLds {
 
 // One chunk of the scan for this workgroup's Dv tile(s):
 //   X = W S^T and (with outputs) Y^T = S Q'^T for token tile w; V_new = U - X (U = 0 for the
-//   transfer-matrix pass); out = Y + O_intra; S^T <- gamma * S^T + K_dec^T V_new for Dk rows
-//   32w..32w+31.
-template <int NT, bool WITH_U, bool WITH_OUT>
-__device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>& cur,
-                                          f32x4 (&S)[2][NT], const ScanLds& L, int jc, int len,
-                                          size_t ob, size_t os, int dv_tile0) {
+//   transfer-matrix pass); out = Y + O_intra; S^T <- gamma * S^T + K_dec^T V_new for this
+//   wave's D/4 Dk rows.
+template <int NT, bool WITH_U, bool WITH_OUT, int D>
+__device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, D>& cur,
+                                          f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L, int jc,
+                                          int len, size_t ob, size_t os, int dv_tile0) {
+    constexpr int KB = HD<D>::KB, MW = HD<D>::MW, SLD = HD<D>::SLD;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
@@ -815,8 +828,8 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
         accX[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
         accY[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
+        for (int kb = 0; kb < KB; ++kb) {
+            const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
             const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
             const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
             accX[nt] = mfma(cur.w[kb], sh, accX[nt]);
@@ -859,7 +872,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
             vl[s] = *reinterpret_cast<const bf16x8*>(L.vl + off);
         }
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < MW; ++mt) {
             f32x4 acc = S[mt][nt] * cur.gm[mt];
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
@@ -868,7 +881,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
                 acc = mfma(cur.kh[mt][s], vl[s], acc);
             }
             S[mt][nt] = acc;
-            put_state(L.sh, L.sl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, acc);
+            put_state<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, acc);
         }
     }
     lds_barrier();
@@ -878,24 +891,25 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT>&
 // The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
 // record, never used): with the same number of loads in flight on every path, the compiler's
 // wait counts let each step wait only for its own operands, not for the next chunk's.
-template <int NT, bool WITH_U, bool WITH_OUT>
-__device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[2][NT], const ScanLds& L,
+template <int NT, bool WITH_U, bool WITH_OUT, int D>
+__device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW][NT],
+                                           const ScanLds& L,
                                            int64_t rec0, int cb, int ce, int len, size_t ob,
                                            size_t os, int dv_tile0) {
     if (cb >= ce) return;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int last = ce - 1;
-    ChunkFrags<NT> fa, fb;
-    load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
+    ChunkFrags<NT, D> fa, fb;
+    load_chunk<NT, WITH_U, WITH_OUT, D>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
     for (int jc = cb; jc < ce; jc += 2) {
         const int c1 = jc + 1 < last ? jc + 1 : last;
-        load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
-        scan_step<NT, WITH_U, WITH_OUT>(p, fa, S, L, jc, len, ob, os, dv_tile0);
+        load_chunk<NT, WITH_U, WITH_OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
+        scan_step<NT, WITH_U, WITH_OUT, D>(p, fa, S, L, jc, len, ob, os, dv_tile0);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
-        load_chunk<NT, WITH_U, WITH_OUT>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
-        scan_step<NT, WITH_U, WITH_OUT>(p, fb, S, L, jc + 1, len, ob, os, dv_tile0);
+        load_chunk<NT, WITH_U, WITH_OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
+        scan_step<NT, WITH_U, WITH_OUT, D>(p, fb, S, L, jc + 1, len, ob, os, dv_tile0);
     }
 }
 
@@ -910,49 +924,52 @@ __device__ __forceinline__ void segment_range(int nchunks, int seg_p, int seg, i
 
 // Operands of one combine step S <- S P_s + N_s for this wave's Dk rows: rows 16(2w+mt)+n16 of
 // P_s^T (stored transposed: Pt[dk'][dk] = P_s[dk][dk']) and this workgroup's tiles of N_s.
-template <int NT>
+template <int NT, int D>
 struct CombFrags {
-    f32x4 pa[2][4], pb[2][4];   // Pt[16(2w+mt)+n16][32kb+8q4 .. +3] and [.. +4 .. +7]
-    f32x4 n[NT][2];             // N_s[16(dv_tile0+nt)+n16][16(2w+mt)+4q4 .. +3]
+    f32x4 pa[HD<D>::MW][HD<D>::KB];   // Pt[16(MW w+mt)+n16][32kb+8q4 .. +3]
+    f32x4 pb[HD<D>::MW][HD<D>::KB];   //                     [32kb+8q4+4 .. +7]
+    f32x4 n[NT][HD<D>::MW];           // N_s[16(dv_tile0+nt)+n16][16(MW w+mt)+4q4 .. +3]
 };
 
-template <int NT>
+template <int NT, int D>
 __device__ __forceinline__ void load_comb(const float* Pt, const float* Nst, int dv_tile0,
-                                          CombFrags<NT>& f) {
+                                          CombFrags<NT, D>& f) {
+    constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const float* src = Pt + size_t(16 * (2 * w + mt) + n16) * kHead + 32 * kb + 8 * q4;
+        for (int kb = 0; kb < KB; ++kb) {
+            const float* src = Pt + size_t(16 * (MW * w + mt) + n16) * D + 32 * kb + 8 * q4;
             f.pa[mt][kb] = *reinterpret_cast<const f32x4*>(src);
             f.pb[mt][kb] = *reinterpret_cast<const f32x4*>(src + 4);
         }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MW; ++mt)
             f.n[nt][mt] = *reinterpret_cast<const f32x4*>(
-                Nst + size_t(16 * (dv_tile0 + nt) + n16) * kHead + 16 * (2 * w + mt) + 4 * q4);
+                Nst + size_t(16 * (dv_tile0 + nt) + n16) * D + 16 * (MW * w + mt) + 4 * q4);
 }
 
 // S^T <- P_s^T S^T + N_s^T for this wave's Dk rows, i.e. S <- S P_s + N_s, with the state in S
 // (registers) and in LDS (B operand); three-term hi/lo products.
-template <int NT>
-__device__ __forceinline__ void combine_step(const CombFrags<NT>& f, f32x4 (&S)[2][NT],
-                                             const ScanLds& L) {
+template <int NT, int D>
+__device__ __forceinline__ void combine_step(const CombFrags<NT, D>& f,
+                                             f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L) {
+    constexpr int KB = HD<D>::KB, MW = HD<D>::MW, SLD = HD<D>::SLD;
     const int lane = threadIdx.x & 63;
     const int w = threadIdx.x >> 6;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
-    bf16x8 ph[2][4], pl[2][4];
+    bf16x8 ph[MW][KB], pl[MW][KB];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 SPLIT_BF16(f.pa[mt][kb][e], ph[mt][kb][e], pl[mt][kb][e]);
@@ -961,11 +978,11 @@ __device__ __forceinline__ void combine_step(const CombFrags<NT>& f, f32x4 (&S)[
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
+        for (int mt = 0; mt < MW; ++mt) {
             f32x4 acc = f.n[nt][mt];
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
-                const int off = (16 * nt + n16) * S_LD + 32 * kb + 8 * q4;
+            for (int kb = 0; kb < KB; ++kb) {
+                const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
                 const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
                 const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
                 acc = mfma(ph[mt][kb], sh, acc);
@@ -979,40 +996,41 @@ __device__ __forceinline__ void combine_step(const CombFrags<NT>& f, f32x4 (&S)[
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-            put_state(L.sh, L.sl, 16 * nt + n16, 16 * (2 * w + mt) + 4 * q4, S[mt][nt]);
+        for (int mt = 0; mt < MW; ++mt)
+            put_state<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, S[mt][nt]);
     lds_barrier();
 }
 
 // S_in(seg) = (((N_0) P_1 + N_1) P_2 + ...) P_{seg-1} + N_{seg-1}, with S = N_0 on entry.  The
 // next step's operands load while the current one multiplies (two register sets; the load is
 // issued on every step, past the end as a reload of the last matrices, never used).
-template <int NT>
+template <int NT, int D>
 __device__ __forceinline__ void combine_segments(const Params& p, int bh, int seg,
-                                                 f32x4 (&S)[2][NT], const ScanLds& L,
+                                                 f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L,
                                                  int dv_tile0) {
     if (seg < 2) return;
     auto mat = [&](int sp) {
-        return (size_t(bh) * p.seg_p + (sp < seg - 1 ? sp : seg - 1)) * kHead * kHead;
+        return (size_t(bh) * p.seg_p + (sp < seg - 1 ? sp : seg - 1)) * D * D;
     };
-    CombFrags<NT> ca, cb;
-    load_comb<NT>(p.Pt + mat(1), p.Nst + mat(1), dv_tile0, ca);
+    CombFrags<NT, D> ca, cb;
+    load_comb<NT, D>(p.Pt + mat(1), p.Nst + mat(1), dv_tile0, ca);
     int sp = 1;
     for (; sp + 2 <= seg; sp += 2) {
-        load_comb<NT>(p.Pt + mat(sp + 1), p.Nst + mat(sp + 1), dv_tile0, cb);
-        combine_step<NT>(ca, S, L);
-        load_comb<NT>(p.Pt + mat(sp + 2), p.Nst + mat(sp + 2), dv_tile0, ca);
-        combine_step<NT>(cb, S, L);
+        load_comb<NT, D>(p.Pt + mat(sp + 1), p.Nst + mat(sp + 1), dv_tile0, cb);
+        combine_step<NT, D>(ca, S, L);
+        load_comb<NT, D>(p.Pt + mat(sp + 2), p.Nst + mat(sp + 2), dv_tile0, ca);
+        combine_step<NT, D>(cb, S, L);
     }
-    if (sp < seg) combine_step<NT>(ca, S, L);
+    if (sp < seg) combine_step<NT, D>(ca, S, L);
 }
 
 // The one-tile form keeps under 256 registers so that two workgroups share a compute unit.
-template <int NT>
+template <int NT, int D>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Params p) {
     constexpr int BV = 16 * NT;
-    __shared__ __attribute__((aligned(16))) __bf16 sSh[BV * S_LD];
-    __shared__ __attribute__((aligned(16))) __bf16 sSl[BV * S_LD];
+    constexpr int MW = HD<D>::MW;
+    __shared__ __attribute__((aligned(16))) __bf16 sSh[BV * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) __bf16 sSl[BV * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[BV * VN_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sVl[BV * VN_LD];
     const ScanLds L{sSh, sSl, sVh, sVl};
@@ -1042,37 +1060,37 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Par
     int cb, ce;
     segment_range(nchunks, p.seg_p, seg, cb, ce);
     size_t ob, os;
-    row_geom(p, b, h, p.n_v, kHead, c0, ob, os);
+    row_geom(p, b, h, p.n_v, D, c0, ob, os);
 
-    // state tile: S[mt][nt][i] = S[dv = 16(dv_tile0+nt) + n16][dk = 16(2w+mt) + 4q4 + i]
-    f32x4 S[2][NT];
-    const size_t st_base = (size_t(b) * p.n_v + h) * kHead * kHead;
+    // state tile: S[mt][nt][i] = S[dv = 16(dv_tile0+nt) + n16][dk = 16(MW w+mt) + 4q4 + i]
+    f32x4 S[MW][NT];
+    const size_t st_base = (size_t(b) * p.n_v + h) * D * D;
     const float* s0 = p.init ? p.init + st_base : nullptr;
-    if (seg > 0) s0 = p.Nst + (size_t(bh) * p.seg_p + 0) * kHead * kHead;   // N_0
+    if (seg > 0) s0 = p.Nst + (size_t(bh) * p.seg_p + 0) * D * D;   // N_0
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int dv = 16 * (dv_tile0 + nt) + n16;
-            const int dk = 16 * (2 * w + mt) + 4 * q4;
-            S[mt][nt] = s0 ? *reinterpret_cast<const f32x4*>(s0 + size_t(dv) * kHead + dk)
+            const int dk = 16 * (MW * w + mt) + 4 * q4;
+            S[mt][nt] = s0 ? *reinterpret_cast<const f32x4*>(s0 + size_t(dv) * D + dk)
                            : f32x4{0.f, 0.f, 0.f, 0.f};
-            put_state(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
+            put_state<D>(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
         }
     lds_barrier();
-    combine_segments<NT>(p, bh, seg, S, L, dv_tile0);
+    combine_segments<NT, D>(p, bh, seg, S, L, dv_tile0);
 
-    run_chunks<NT, true, true>(p, S, L, int64_t(slot0) * p.n_v + h, cb, ce, len, ob, os,
-                               dv_tile0);
+    run_chunks<NT, true, true, D>(p, S, L, int64_t(slot0) * p.n_v + h, cb, ce, len, ob, os,
+                                  dv_tile0);
 
     if (p.fin && seg == p.seg_p - 1) {
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
             for (int nt = 0; nt < NT; ++nt) {
                 const int dv = 16 * (dv_tile0 + nt) + n16;
-                const int dk = 16 * (2 * w + mt) + 4 * q4;
-                *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * kHead + dk) = S[mt][nt];
+                const int dk = 16 * (MW * w + mt) + 4 * q4;
+                *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * D + dk) = S[mt][nt];
             }
     }
     // rows past a batch row's valid length (BNSD/BSND with cu_seqlens) are written as zeros
@@ -1089,12 +1107,14 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Par
     }
 }
 
-// Segment pass of the two-level scan: 16 workgroups per (sequence, head, segment s < seg_p-1).
-// Slots 0..7: N_s tiles (from S = 0, or from the initial state for s = 0, with U); slots 8..15:
-// P_s tiles (from 16 identity rows each, without U; not needed for s = 0).
+// Segment pass of the two-level scan: 2 D/16 workgroups per (sequence, head, segment
+// s < seg_p-1).  Slots 0..D/16-1: N_s tiles (from S = 0, or from the initial state for s = 0,
+// with U); slots D/16..: P_s tiles (from 16 identity rows each, without U; not needed for s = 0).
+template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
-    __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * S_LD];
-    __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * S_LD];
+    constexpr int MW = HD<D>::MW, TILES = HD<D>::TILES;
+    __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[16 * VN_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sVl[16 * VN_LD];
     const ScanLds L{sSh, sSl, sVh, sVl};
@@ -1107,13 +1127,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
 
     const int pid = blockIdx.x;
     const int xcd = pid & 7, r8 = pid >> 3;
-    const int grp = (r8 >> 4) * 8 + xcd;
-    const int slot = r8 & 15;
+    const int grp = (r8 / (2 * TILES)) * 8 + xcd;
+    const int slot = r8 % (2 * TILES);
     if (grp >= p.batch * p.n_v * (p.seg_p - 1)) return;
     const int bh = grp / (p.seg_p - 1);
     const int seg = grp % (p.seg_p - 1);
-    const bool is_p = slot >= 8;
-    const int tile = slot & 7;
+    const bool is_p = slot >= TILES;
+    const int tile = slot % TILES;
     if (is_p && seg == 0) return;
     const int b = bh / p.n_v;
     const int h = bh % p.n_v;
@@ -1124,39 +1144,39 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     int cb, ce;
     segment_range(nchunks, p.seg_p, seg, cb, ce);
 
-    f32x4 S[2][1];
-    const size_t st_base = (size_t(b) * p.n_v + h) * kHead * kHead;
+    f32x4 S[MW][1];
+    const size_t st_base = (size_t(b) * p.n_v + h) * D * D;
     const int row = 16 * tile + n16;   // state row (value channel, or identity row)
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-        const int dk = 16 * (2 * w + mt) + 4 * q4;
+    for (int mt = 0; mt < MW; ++mt) {
+        const int dk = 16 * (MW * w + mt) + 4 * q4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (is_p) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) x[i] = (dk + i == row) ? 1.f : 0.f;
         } else if (seg == 0 && p.init) {
-            x = *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(row) * kHead + dk);
+            x = *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(row) * D + dk);
         }
         S[mt][0] = x;
-        put_state(sSh, sSl, n16, dk, x);
+        put_state<D>(sSh, sSl, n16, dk, x);
     }
     lds_barrier();
 
     const int64_t rec0 = int64_t(slot0) * p.n_v + h;
-    const size_t m = (size_t(bh) * p.seg_p + seg) * kHead * kHead;
+    const size_t m = (size_t(bh) * p.seg_p + seg) * D * D;
     if (is_p) {
-        run_chunks<1, false, false>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
+        run_chunks<1, false, false, D>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
         // rows 16 tile .. of P_s, stored transposed: Pt[dk'][row]
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
+        for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                p.Pt[m + size_t(16 * (2 * w + mt) + 4 * q4 + i) * kHead + row] = S[mt][0][i];
+                p.Pt[m + size_t(16 * (MW * w + mt) + 4 * q4 + i) * D + row] = S[mt][0][i];
     } else {
-        run_chunks<1, true, false>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
+        run_chunks<1, true, false, D>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-            *reinterpret_cast<f32x4*>(p.Nst + m + size_t(row) * kHead + 16 * (2 * w + mt) +
+        for (int mt = 0; mt < MW; ++mt)
+            *reinterpret_cast<f32x4*>(p.Nst + m + size_t(row) * D + 16 * (MW * w + mt) +
                                       4 * q4) = S[mt][0];
     }
 }
@@ -1219,23 +1239,32 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
 
     (void)hipGetLastError();  // clear a stale error so the checks below see only ours
     auto e = [&](int i) { return ev ? ev[i] : hipEvent_t(nullptr); };
-    const void* intra = (p.flags & KDA_SCALAR_GATE)
-                            ? reinterpret_cast<const void*>(&kda_intra_kernel<true>)
-                            : reinterpret_cast<const void*>(&kda_intra_kernel<false>);
+    const bool sg = (p.flags & KDA_SCALAR_GATE) != 0;
+    const bool d64 = plan.d == 64;
+    auto fn = [](auto f) { return reinterpret_cast<const void*>(f); };
+    const void* intra =
+        d64 ? (sg ? fn(&kda_intra_kernel<true, 64>) : fn(&kda_intra_kernel<false, 64>))
+            : (sg ? fn(&kda_intra_kernel<true, 128>) : fn(&kda_intra_kernel<false, 128>));
     kda_status st2 = launch_kernel(intra, unsigned(plan.intra_blocks), stream, e(0), e(1), p);
     if (st2 != KDA_OK) return st2;
     if (plan.seg_p > 1) {
-        st2 = launch_kernel(reinterpret_cast<const void*>(&kda_seg_kernel),
-                            unsigned(plan.seg_blocks), stream, e(2), e(3), p);
+        const void* segk = d64 ? fn(&kda_seg_kernel<64>) : fn(&kda_seg_kernel<128>);
+        st2 = launch_kernel(segk, unsigned(plan.seg_blocks), stream, e(2), e(3), p);
         if (st2 != KDA_OK) return st2;
     } else if (ev) {   // no segment pass: an empty stage
         if (hipEventRecord(ev[2], stream) != hipSuccess ||
             hipEventRecord(ev[3], stream) != hipSuccess)
             return KDA_ERR_HIP;
     }
-    const void* scan = plan.scan_nt == 4   ? reinterpret_cast<const void*>(&kda_scan_kernel<4>)
-                       : plan.scan_nt == 2 ? reinterpret_cast<const void*>(&kda_scan_kernel<2>)
-                                           : reinterpret_cast<const void*>(&kda_scan_kernel<1>);
+    const void* scan;
+    if (d64)
+        scan = plan.scan_nt == 4   ? fn(&kda_scan_kernel<4, 64>)
+               : plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 64>)
+                                   : fn(&kda_scan_kernel<1, 64>);
+    else
+        scan = plan.scan_nt == 4   ? fn(&kda_scan_kernel<4, 128>)
+               : plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 128>)
+                                   : fn(&kda_scan_kernel<1, 128>);
     st2 = launch_kernel(scan, unsigned(plan.scan_blocks), stream, e(4), e(5), p);
     if (st2 != KDA_OK) return st2;
     return KDA_OK;

@@ -1,6 +1,7 @@
 // kda_plan.cpp -- host-side validation and planning for the KDA chunked forward.
 //
-// The accepted argument space follows the FlashKDA README, section 约束说明: Dk = Dv = 128,
+// The accepted argument space follows the FlashKDA README, section 约束说明: Dk = Dv = 128 (and
+// here also Dk = Dv = 64),
 // B >= 1, stored length > 0, layouts BNSD / BSND / TND, 1 <= Nqk <= Nv with Nv % Nqk == 0,
 // TND needs an int32 cu_seqlens of B+1 entries, and final_state is a new tensor (here: it must
 // not overlap initial_state).  Only shapes and pointers are inspected; device data is never read.
@@ -30,7 +31,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     if (s->batch < 1 || s->seq_len < 1) return KDA_ERR_INVALID_ARG;
     if (s->n_qk < 1 || s->n_v < s->n_qk || s->n_v % s->n_qk != 0) return KDA_ERR_INVALID_ARG;
     if (s->d_k < 1 || s->d_v < 1) return KDA_ERR_INVALID_ARG;
-    if (s->d_k != kHead || s->d_v != kHead) return KDA_ERR_UNSUPPORTED;
+    if (s->d_k != s->d_v || !head_dim_ok(s->d_k)) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(s->scale)) return KDA_ERR_INVALID_ARG;
     if (s->flags & ~uint32_t(KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE))
         return KDA_ERR_INVALID_ARG;
@@ -38,6 +39,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
 
     Plan p;
     p.layout = s->layout;
+    p.d = s->d_k;
     p.batch = s->batch;
     p.seq_len = s->seq_len;
     p.n_qk = s->n_qk;
@@ -58,30 +60,31 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     // wider tile cuts the bytes streamed per unit of work; it is taken only while enough
     // workgroups remain to occupy all 256 compute units of an MI355X.
     const int64_t bh = int64_t(s->batch) * s->n_v;
+    const int tiles = p.d / 16;   // 16-row Dv tiles per head
     p.scan_nt = 1;
     for (int nt = 4; nt >= 2; nt /= 2)
-        if (bh * (8 / nt) >= 256) { p.scan_nt = nt; break; }
+        if (bh * (tiles / nt) >= 256) { p.scan_nt = nt; break; }
     // Few (sequence, head) chains leave most compute units idle through a long sequential scan.
     // Then each sequence is cut into seg_p segments: a segment pass runs every segment but the
-    // last from a zero state and from identity rows (8 + 8 workgroups per segment), giving its
-    // end state N_s and transfer matrix P_s, and the output pass starts segment s from
-    // S_in(s) = S_in(s-1) P_{s-1} + N_{s-1}.  seg_p is the largest count whose segment pass
-    // fits 256 workgroups, with at least 8 chunks per segment.
+    // last from a zero state and from identity rows (d/16 + d/16 workgroups per segment),
+    // giving its end state N_s and transfer matrix P_s, and the output pass starts segment s
+    // from S_in(s) = S_in(s-1) P_{s-1} + N_{s-1}.  seg_p is the largest count whose segment
+    // pass fits 256 workgroups, with at least 8 chunks per segment.
     p.seg_p = 1;
-    if (bh * 8 < 256) {
+    if (bh * tiles < 256) {
         const int64_t nc_est = (s->layout == KDA_LAYOUT_TND)
                                    ? (int64_t(s->seq_len) / s->batch + kChunk - 1) / kChunk
                                    : p.nc_max;
-        int64_t sp = (256 / (bh * 8) + 3) / 2;
+        int64_t sp = (256 / (bh * tiles) + 3) / 2;
         if (sp > nc_est / 8) sp = nc_est / 8;
         if (sp > 16) sp = 16;
         if (sp >= 2) p.seg_p = int(sp);
     }
     if (p.seg_p > 1) p.scan_nt = 1;
-    p.scan_tiles = 8 / p.scan_nt;
+    p.scan_tiles = tiles / p.scan_nt;
     const int64_t out_groups = bh * p.seg_p;
     p.scan_blocks = ((out_groups + 7) / 8) * 8 * p.scan_tiles;
-    p.seg_blocks = (p.seg_p > 1) ? ((bh * (p.seg_p - 1) + 7) / 8) * 8 * 16 : 0;
+    p.seg_blocks = (p.seg_p > 1) ? ((bh * (p.seg_p - 1) + 7) / 8) * 8 * 2 * tiles : 0;
     const int64_t max_grid = std::numeric_limits<int32_t>::max();
     if (p.intra_blocks > max_grid || p.scan_blocks > max_grid || p.seg_blocks > max_grid)
         return KDA_ERR_UNSUPPORTED;
@@ -89,18 +92,19 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     // element counts of the largest tensors must fit the 64-bit offsets used on the device
     const double tokens = (s->layout == KDA_LAYOUT_TND) ? double(s->seq_len)
                                                         : double(s->batch) * s->seq_len;
-    if (tokens * s->n_v * kHead > 9.0e18) return KDA_ERR_UNSUPPORTED;
+    if (tokens * s->n_v * p.d > 9.0e18) return KDA_ERR_UNSUPPORTED;
 
     const size_t n = size_t(p.n_records);
+    const int d = p.d;
     size_t off = 0;
-    p.off_w = off; off = align_up(off + n * kWBytes, 256);
-    p.off_q = off; off = align_up(off + n * kQBytes, 256);
-    p.off_k = off; off = align_up(off + n * kKBytes, 256);
-    p.off_u = off; off = align_up(off + n * kUBytes, 256);
-    p.off_o = off; off = align_up(off + n * kOBytes, 256);
-    p.off_g = off; off = align_up(off + n * kGBytes, 256);
+    p.off_w = off; off = align_up(off + n * rec_w_bytes(d), 256);
+    p.off_q = off; off = align_up(off + n * rec_q_bytes(d), 256);
+    p.off_k = off; off = align_up(off + n * rec_k_bytes(d), 256);
+    p.off_u = off; off = align_up(off + n * rec_u_bytes(d), 256);
+    p.off_o = off; off = align_up(off + n * rec_o_bytes(d), 256);
+    p.off_g = off; off = align_up(off + n * rec_g_bytes(d), 256);
     if (p.seg_p > 1) {
-        const size_t mats = size_t(bh) * p.seg_p * kHead * kHead * sizeof(float);
+        const size_t mats = size_t(bh) * p.seg_p * d * d * sizeof(float);
         p.off_pt = off; off = align_up(off + mats, 256);
         p.off_n = off; off = align_up(off + mats, 256);
     }
@@ -123,7 +127,7 @@ kda_status check_call(const kda_shape* s, const Plan& p, const void* q, const vo
     if (initial_state && !aligned(initial_state, 16)) return KDA_ERR_INVALID_ARG;
     if (final_state && !aligned(final_state, 16)) return KDA_ERR_INVALID_ARG;
     if (cu_seqlens && !aligned(cu_seqlens, 4)) return KDA_ERR_INVALID_ARG;
-    const size_t state_bytes = size_t(p.batch) * p.n_v * kHead * kHead * sizeof(float);
+    const size_t state_bytes = size_t(p.batch) * p.n_v * p.d * p.d * sizeof(float);
     if (initial_state && final_state &&
         overlap(initial_state, state_bytes, final_state, state_bytes))
         return KDA_ERR_INVALID_ARG;

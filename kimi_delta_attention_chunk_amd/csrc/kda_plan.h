@@ -10,23 +10,29 @@
 namespace kda {
 
 constexpr int kChunk = 64;   // tokens per chunk (FlashKDA README, section 功能说明: 64-token chunks)
-constexpr int kHead = 128;   // d_k = d_v = 128 (FlashKDA README, section 约束说明)
 constexpr int kThreads = 256;
+// Head dims: d_k = d_v = D with D = 128 (FlashKDA README, section 约束说明) or D = 64.
+constexpr bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
-// Per (chunk slot, value head) workspace record, in bytes.  Layouts are the MFMA fragment
-// orders the scan kernel reads (see kda_kernels.hip).  K_dec is kept as a bf16 hi/lo pair and
-// U in fp32, so that the innovation V_new = U - W S^T (a small difference of large terms once
-// the state predicts v well) and the state update keep about 16 mantissa bits.
-constexpr size_t kWBytes = size_t(kChunk) * kHead * 2;       // W       bf16
-constexpr size_t kQBytes = size_t(kChunk) * kHead * 2;       // Q'      bf16
-constexpr size_t kKBytes = size_t(kChunk) * kHead * 2 * 2;   // K_dec   bf16 hi + lo
-constexpr size_t kUBytes = size_t(kChunk) * kHead * 4;       // U       fp32
-constexpr size_t kOBytes = size_t(kChunk) * kHead * 2;       // O_intra bf16
-constexpr size_t kGBytes = size_t(kHead) * 4;                // gamma_last fp32
-constexpr size_t kRecordBytes = kWBytes + kQBytes + kKBytes + kUBytes + kOBytes + kGBytes;
+// Per (chunk slot, value head) workspace record for head dim D, in bytes.  Layouts are the MFMA
+// fragment orders the scan kernel reads (see kda_kernels.hip).  K_dec is kept as a bf16 hi/lo
+// pair and U in fp32, so that the innovation V_new = U - W S^T (a small difference of large
+// terms once the state predicts v well) and the state update keep about 16 mantissa bits.
+constexpr size_t rec_w_bytes(int d) { return size_t(kChunk) * d * 2; }       // W       bf16
+constexpr size_t rec_q_bytes(int d) { return size_t(kChunk) * d * 2; }       // Q'      bf16
+constexpr size_t rec_k_bytes(int d) { return size_t(kChunk) * d * 2 * 2; }   // K_dec   bf16 hi + lo
+constexpr size_t rec_u_bytes(int d) { return size_t(kChunk) * d * 4; }       // U       fp32
+constexpr size_t rec_o_bytes(int d) { return size_t(kChunk) * d * 2; }       // O_intra bf16
+constexpr size_t rec_g_bytes(int d) { return size_t(d) * 4; }                // gamma_last fp32
+constexpr size_t rec_bytes(int d) {
+    return rec_w_bytes(d) + rec_q_bytes(d) + rec_k_bytes(d) + rec_u_bytes(d) + rec_o_bytes(d) +
+           rec_g_bytes(d);
+}
+static_assert(rec_bytes(128) == 115200, "record of a 128-dim head");
 
 struct Plan {
     int layout = 0;
+    int d = 128;               // head dim (d_k = d_v)
     int batch = 0, seq_len = 0, n_qk = 0, n_v = 0, group = 0;
     int nc_max = 0;            // BNSD/BSND: chunk slots per batch row, ceil(S / 64)
     int64_t n_slots = 0;       // chunk slots: B * nc_max, or floor(T / 64) + N for TND
@@ -34,7 +40,7 @@ struct Plan {
     int64_t intra_blocks = 0;  // one workgroup per record
     int64_t scan_blocks = 0;   // one workgroup per (sequence, value head, Dv tile), XCD padded
     int scan_nt = 1;           // 16-row Dv tiles per scan workgroup (1, 2 or 4)
-    int scan_tiles = 0;        // scan workgroups per (sequence, head, segment) = 8 / scan_nt
+    int scan_tiles = 0;        // scan workgroups per (sequence, head, segment) = (d/16) / scan_nt
     int seg_p = 1;             // segments per sequence of the two-level scan (1 = one level)
     int64_t seg_blocks = 0;    // workgroups of the segment pass (0 when seg_p == 1)
     // byte offsets of each workspace array (256-byte aligned)

@@ -35,6 +35,7 @@ class Workload:
     tnd_max_len: int = 0        # TND: lengths uniform in [1, tnd_max_len]
     note: str = ""
     scalar_gate: bool = False   # one gate per (token, value head), shaped like beta
+    d: int = D                  # head dim d_k = d_v (128 or 64)
 
 
 WORKLOADS = [
@@ -51,6 +52,9 @@ WORKLOADS = [
     Workload("gdn_prefill_s8k_n3", "BNSD", 1, 8192, 3, 3, "strong", True, 1005,
              note="the 8K prefill with one gate per (token, head) (the GDN form); "
                   "g = -5*sigmoid(N(0,1))", scalar_gate=True),
+    Workload("prefill_s8k_n6_d64", "BNSD", 1, 8192, 6, 6, "strong", True, 1006,
+             note="the 8K prefill at head dim 64 with six heads (the same q/k/v bytes as three "
+                  "128-dim heads); g = -5*sigmoid(N(0,1)); state N(0,0.1^2)", d=64),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
@@ -172,9 +176,9 @@ def workload_inputs(w, seed: Optional[int] = None) -> Inputs:
         gen = torch.Generator().manual_seed(s + 7919)
         lengths = torch.randint(1, w.tnd_max_len + 1, (w.batch,), generator=gen).tolist()
         inp = make_inputs("TND", w.batch, 0, w.n_qk, w.n_v, g_kind=w.g_kind, init=w.init,
-                          seed=s, lengths=lengths, scalar_gate=w.scalar_gate)
+                          seed=s, lengths=lengths, scalar_gate=w.scalar_gate, d=w.d)
     else:
         inp = make_inputs(w.layout, w.batch, w.seq_len, w.n_qk, w.n_v, g_kind=w.g_kind,
-                          init=w.init, seed=s, scalar_gate=w.scalar_gate)
+                          init=w.init, seed=s, scalar_gate=w.scalar_gate, d=w.d)
     inp.meta["workload"] = w.name
     return inp

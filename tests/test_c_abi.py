@@ -72,11 +72,20 @@ def test_workspace_sizes(lib):
     # a ragged tail adds one chunk slot per batch row
     st, n3 = ws(lib, make_shape("BSND", 4, 4100, 4, 16, 0.088))
     assert st == 0 and n3 >= 4 * 65 * 16 * 115200
+    # head dim 64: a record of 64 x 64 x 14 + 64 x 4 bytes; six heads at 8K use the two-level
+    # scan (256 / (6 x 4) tiles -> 6 segments) with 64 x 64 fp32 matrices
+    rec64 = 64 * 64 * 14 + 64 * 4
+    assert rec64 == 57600
+    st, n5 = ws(lib, make_shape("BNSD", 1, 8192, 6, 6, 0.125, d_k=64, d_v=64))
+    assert st == 0
+    assert n5 >= 128 * 6 * rec64 + 6 * 6 * 2 * 64 * 64 * 4
+    assert n5 < 128 * 6 * rec64 + 6 * 6 * 2 * 64 * 64 * 4 + 16 * 256
 
 
 @pytest.mark.parametrize("bad, code", [
     (dict(layout=7), 1), (dict(batch=0), 1), (dict(seq_len=0), 1), (dict(n_qk=0), 1),
     (dict(n_qk=4, n_v=2), 1), (dict(n_qk=3, n_v=4), 1), (dict(d_k=64), 2), (dict(d_v=256), 2),
+    (dict(d_k=64, d_v=64), 0), (dict(d_k=32, d_v=32), 2), (dict(d_k=256, d_v=256), 2),
     (dict(scale=float("nan")), 1), (dict(flags=8), 1), (dict(flags=16), 1),
     (dict(flags=7), 0), (dict(flags=4), 0),
 ])

@@ -113,6 +113,34 @@ SCALAR_GATE_CASES = [
 ]
 
 
+# Head dim 64 (d_k = d_v = 64): every layout, GQA, ragged tails, valid lengths, no decay, the
+# scalar gate, and a sequence long enough for the two-level scan.
+D64_CASES = [
+    ("d64_bnsd_b2_s200", dict(layout="BNSD", batch=2, seq_len=200, n_qk=2, n_v=2,
+                              g_kind="strong", init=True, seed=51, d=64)),
+    ("d64_bsnd_gqa_tail", dict(layout="BSND", batch=2, seq_len=150, n_qk=1, n_v=4,
+                               g_kind="unit", init=False, seed=52, d=64)),
+    ("d64_tnd_ragged", dict(layout="TND", batch=5, seq_len=0, n_qk=2, n_v=2, g_kind="strong",
+                            init=True, seed=53, lengths=[1, 63, 65, 130, 17], d=64)),
+    ("d64_bnsd_valid_lengths", dict(layout="BNSD", batch=3, seq_len=140, n_qk=1, n_v=1,
+                                    g_kind="small", init=True, seed=54,
+                                    valid_lengths=[140, 65, 3], d=64)),
+    ("d64_bnsd_no_decay", dict(layout="BNSD", batch=1, seq_len=1024, n_qk=1, n_v=1,
+                               g_kind="zero", init=True, seed=55, d=64)),
+    ("d64_two_level", dict(layout="BNSD", batch=1, seq_len=64 * 40 + 17, n_qk=1, n_v=1,
+                           g_kind="strong", init=True, seed=56, d=64)),
+    ("d64_gdn_tnd", dict(layout="TND", batch=3, seq_len=0, n_qk=1, n_v=2, g_kind="strong",
+                         init=True, seed=57, lengths=[100, 64, 33], scalar_gate=True, d=64)),
+]
+
+
+@pytest.mark.parametrize("name,kw", D64_CASES, ids=[s[0] for s in D64_CASES])
+def test_head_dim_64(name, kw):
+    inp = make_inputs(**kw)
+    assert inp.q.shape[-1] == 64
+    compare(inp, name)
+
+
 @pytest.mark.parametrize("name,kw", SCALAR_GATE_CASES, ids=[s[0] for s in SCALAR_GATE_CASES])
 def test_scalar_gate(name, kw):
     inp = make_inputs(**kw)
@@ -160,7 +188,7 @@ def test_flags_off_prenormalised_inputs():
 
 WL_ROWS = {"tiny_s256": None, "prefill_s8k_n3": None, "gqa_tail_s4100": (16, 32),
            "varlen_tnd_32seq": (48, 64), "long_s128k_n32": (112, 128),
-           "gdn_prefill_s8k_n3": None}
+           "gdn_prefill_s8k_n3": None, "prefill_s8k_n6_d64": None}
 
 
 @pytest.mark.parametrize("name", [w.name for w in WORKLOADS])
