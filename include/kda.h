@@ -42,7 +42,7 @@ extern "C" {
 #endif
 
 /* Physical layouts (FlashKDA README, section 参数说明).  B = batch, N = heads, S = stored
- * length, T = packed tokens, D = 128:
+ * length, T = packed tokens, D = d_k = d_v (128, or 64):
  *   BNSD: q,k [B,n_qk,S,D]  v,g,out [B,n_v,S,D]  beta [B,n_v,S]
  *   BSND: q,k [B,S,n_qk,D]  v,g,out [B,S,n_v,D]  beta [B,S,n_v]
  *   TND:  q,k [T,n_qk,D]    v,g,out [T,n_v,D]    beta [T,n_v]   (packed; cu_seqlens required) */
@@ -68,7 +68,7 @@ enum {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,  /* a NULL or misaligned pointer, bad enum, negative size, alias */
-    KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (d_k != 128) */
+    KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (head dim)   */
     KDA_ERR_WORKSPACE = 3,    /* workspace pointer NULL or workspace_bytes too small */
     KDA_ERR_HIP = 4           /* a HIP launch or event call failed (hipGetLastError) */
 } kda_status;
@@ -79,8 +79,8 @@ typedef struct {
     int32_t seq_len;   /* S (stored length) for BNSD/BSND; T (total packed tokens) for TND    */
     int32_t n_qk;      /* query/key heads, 1 <= n_qk <= n_v                                   */
     int32_t n_v;       /* value heads, n_v % n_qk == 0 (GQA groups of n_v / n_qk)            */
-    int32_t d_k;       /* must be 128                                                         */
-    int32_t d_v;       /* must be 128                                                         */
+    int32_t d_k;       /* head dim of q/k: 128 (FlashKDA README, 约束说明) or 64; equal to d_v  */
+    int32_t d_v;       /* head dim of v and out: equal to d_k                                 */
     float scale;       /* output scale, typically d_k ** -0.5; must be finite                 */
     uint32_t flags;    /* KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE                  */
 } kda_shape;

@@ -133,7 +133,7 @@ __device__ __forceinline__ void row_geom(const Params& p, int b, int h, int head
 //
 // One workgroup of four waves per (64-token chunk, value head); wave w owns token block I = w
 // (tokens 16I .. 16I+15).  Lane (q4, n16) holds token 16I + n16 and channels 32kb + 8q4 + e
-// (kb, e = 0..3, 0..7) of q, k, v and g, loaded straight from HBM in this "row layout", which
+// (kb < D/32, e < 8) of q, k, v and g, loaded straight from HBM in this "row layout", which
 // is at once the A operand of an MFMA over channels and its B operand with tokens as columns.
 //
 // Products over tokens (W, U, O_intra, Q') need operands with eight consecutive tokens per
