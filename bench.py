@@ -56,7 +56,7 @@ def seg_p_of(inp) -> int:
     if bh * tiles >= 256:
         return 1
     nc = -(-inp.seq_len // 64) if inp.layout != "TND" else -(-(inp.seq_len // inp.batch) // 64)
-    sp = min((256 // (bh * tiles) + 3) // 2, nc // 8, 16)
+    sp = min((256 // (bh * tiles) + 1) // 2, nc // 8, 16)
     return sp if sp >= 2 else 1
 
 
@@ -66,17 +66,28 @@ def record_bytes(d: int) -> int:
     return 64 * d * (2 + 2 + 4 + 4 + 2) + d * 4
 
 
+def chunk_counts(inp, sp: int):
+    """(chunks in segment 0, chunks in later segments) over all sequences, per value head."""
+    first = later = 0
+    for L in inp.lengths:
+        nc = (L + 63) // 64
+        n0 = min(-(-nc // sp), nc)
+        first += n0
+        later += nc - n0
+    return first, later
+
+
 def scan_bytes(inp) -> int:
-    """Compulsory bytes of the scan kernel: the record of every (chunk, value head) and the
-    output; plus the states, and with a two-level scan the segment matrices it combines."""
+    """Compulsory bytes of the one-level scan: the record of every (chunk, value head), the
+    output, and the initial and final states."""
+    if seg_p_of(inp) > 1:
+        return 0
     d = head_dim(inp)
     chunks = sum((L + 63) // 64 for L in inp.lengths)
     out = inp.tokens * inp.n_v * d * 2
     states = inp.batch * inp.n_v * d * d * 4
-    sp = seg_p_of(inp)
-    mats = inp.batch * inp.n_v * max(sp - 1, 0) * 2 * d * d * 4
     return (chunks * inp.n_v * record_bytes(d) + out
-            + states * ((inp.initial_state is not None) + 1) + mats)
+            + states * ((inp.initial_state is not None) + 1))
 
 
 def intra_bytes(inp) -> int:
@@ -88,20 +99,46 @@ def intra_bytes(inp) -> int:
 
 
 def seg_bytes(inp) -> int:
-    """Compulsory bytes of the segment pass of the two-level scan: W, K_dec (hi+lo), gamma and
-    U of every chunk outside the last segment, the initial states, and the N and P matrices."""
+    """Compulsory bytes of the segment pass: every record, the initial states, the final
+    outputs of segment 0 (bf16), O0 and R of the later segments' chunks (fp32), and the N and
+    P matrices of every segment."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
-    frac = 0
-    for L in inp.lengths:
-        nc = (L + 63) // 64
-        frac += min((sp - 1) * (-(-nc // sp)), nc)   # chunks outside the last segment
-    per_chunk = 64 * d * (2 + 4 + 4) + d * 4
+    first, later = chunk_counts(inp, sp)
     states = inp.batch * inp.n_v * d * d * 4
-    mats = inp.batch * inp.n_v * (sp - 1) * 2 * d * d * 4
-    return frac * inp.n_v * per_chunk + states * (inp.initial_state is not None) + mats
+    mats = inp.batch * inp.n_v * sp * 2 * d * d * 4
+    return (inp.n_v * ((first + later) * record_bytes(d) + first * 64 * d * 2
+                       + later * 64 * d * 4 * 2)
+            + states * (inp.initial_state is not None) + mats)
+
+
+def combine_bytes(inp) -> int:
+    """Compulsory bytes of the combine pass: N and P of every segment in, S_in of segments
+    1.. and the final state out."""
+    sp = seg_p_of(inp)
+    if sp == 1:
+        return 0
+    d = head_dim(inp)
+    m = inp.batch * inp.n_v * d * d * 4
+    return m * (2 * sp - 1) + m * (sp - 1) + m
+
+
+def out_bytes(inp) -> int:
+    """Compulsory bytes of the completion pass: O0 and R (fp32) of every chunk of segments
+    1.. and S_in of those segments in, the outputs (bf16) out."""
+    sp = seg_p_of(inp)
+    if sp == 1:
+        return 0
+    d = head_dim(inp)
+    _, later = chunk_counts(inp, sp)
+    return inp.n_v * later * 64 * d * (4 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 4
+
+
+KERNEL_BYTES = {"kda_intra_kernel": intra_bytes, "kda_seg_kernel": seg_bytes,
+                "kda_combine_kernel": combine_bytes, "kda_out_kernel": out_bytes,
+                "kda_scan_kernel": scan_bytes}
 
 
 def source_hash() -> str:
@@ -232,7 +269,7 @@ def main() -> int:
     stage_ms = [sum(events[i][2 * s].elapsed_time(events[i][2 * s + 1]) for i in range(args.steps))
                 / args.steps for s in range(nst)]
     dom = max(range(nst), key=lambda s: stage_ms[s])
-    kbytes = [intra_bytes(host), seg_bytes(host), scan_bytes(host)]
+    kbytes = [KERNEL_BYTES[kda_stage_name(s)](host) for s in range(nst)]
     achieved = kbytes[dom] / (stage_ms[dom] * 1e-3)
     pbytes = path_bytes(host)
     value = host.tokens / (ms_step * 1e-3)

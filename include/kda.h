@@ -114,10 +114,12 @@ kda_status kda_chunk_fwd(const kda_shape* shape,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
-/* Number of stages of one kda_chunk_fwd call and the name of each: the intra-chunk kernel, the
- * segment pass of the two-level scan (enqueued only when few (sequence, head) chains would
- * leave the GPU idle through a long sequential scan; otherwise the stage is empty), and the
- * scan with outputs. */
+/* Number of stages of one kda_chunk_fwd call and the name of each, one kernel per stage: the
+ * intra-chunk kernel; then, when few (sequence, head) chains would leave the GPU idle through a
+ * long sequential scan, the two-level scan's segment pass (every segment walked at once from a
+ * zero state and from the identity), combine (segment entry states) and completion (outputs of
+ * segments after the first) kernels; otherwise the one-level scan with outputs.  Stages the
+ * plan does not enqueue are empty. */
 int32_t kda_num_stages(void);
 const char* kda_stage_name(int32_t stage);
 

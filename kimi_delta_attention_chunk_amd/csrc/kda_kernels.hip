@@ -58,8 +58,12 @@ struct Params {
     float* Uf;    // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n]
     __bf16* Of;   // [record][nt 8][tt 4][lane 64][4]         O_intra[16tt+n][16nt+4q+i]
     float* Gf;    // [record][128]                            2^(G2_last)
-    float* Pt;    // [seq*head][segment][128][128]  segment transfer matrix, transposed
-    float* Nst;   // [seq*head][segment][128][128]  segment end state from a zero start
+    // two-level scan, per (sequence*head, segment) and per record, in MFMA fragment order:
+    __bf16* Pt;   // [hi/lo][M 8][kb 4][lane 64][8]  P_s[32kb+8q+j][16M+m]      transfer matrix
+    float* Nst;   // [t 8][M 8][lane 64][4]          N_s[16t+m][16M+4q+i]       zero-start end state
+    __bf16* Sin;  // [hi/lo][t 8][kb 4][lane 64][8]  S_in[16t+m][32kb+8q+j]     entry state
+    float* O0;    // [t 8][tt 4][lane 64][4]         O0[16tt+m][16t+4q+i]       zero-start outputs
+    __bf16* Rf;   // [hi/lo][tt 4][kb 4][lane 64][8] R[16tt+m][32kb+8q+j]       R = Q' P^T
     int layout, batch, seq_len, n_qk, n_v, group, nc_max;
     int scan_tiles;
     int seg_p;     // segments per sequence of the two-level scan (1 = one level)
@@ -109,6 +113,19 @@ __device__ __forceinline__ void seq_info(const Params& p, int b, int& c0, int& l
         len = l;
         slot0 = b * p.nc_max;
     }
+}
+
+// Sequence of a chunk slot: the last b whose first slot is <= slot (TND), or slot / nc_max.
+__device__ __forceinline__ int slot_batch(const Params& p, int slot) {
+    if (p.layout != KDA_LAYOUT_TND) return slot / p.nc_max;
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        int cm = p.cu[mid];
+        cm = cm < 0 ? 0 : (cm > p.seq_len ? p.seq_len : cm);
+        if (cm / kChunk + mid <= slot) lo = mid; else hi = mid - 1;
+    }
+    return lo;
 }
 
 // Element offset of token 0 and the token stride for (sequence b, head h) of a tensor with
@@ -296,19 +313,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     const int hq = h / p.group;
 
     // chunk slot -> (sequence b, chunk j)
-    int b;
-    if (p.layout == KDA_LAYOUT_TND) {
-        int lo = 0, hi = p.batch - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            int cm = p.cu[mid];
-            cm = cm < 0 ? 0 : (cm > p.seq_len ? p.seq_len : cm);
-            if (cm / kChunk + mid <= slot) lo = mid; else hi = mid - 1;
-        }
-        b = lo;
-    } else {
-        b = slot / p.nc_max;
-    }
+    const int b = slot_batch(p, slot);
     int c0, len, slot0;
     seq_info(p, b, c0, len, slot0);
     const int j = slot - slot0;
@@ -726,10 +731,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
 //
 // Two-level form for few (sequence, head) chains: a sequence of C chunks is cut into P
 // segments.  Chunk c maps the state affinely, S -> S M_c + N_c with M_c = Diag(gamma_c) -
-// W_c^T K_dec,c, so segment s has S_out = S_in P_s + N_s.  kda_seg_kernel runs each segment but
-// the last from S = 0 (giving N_s; segment 0 starts from the initial state instead) and from
-// the identity (giving P_s, 8 workgroups of 16 identity rows); kda_scan_kernel then forms
-// S_in(s) = S_in(s-1) P_{s-1} + N_{s-1} on MFMA and reruns segment s with outputs.
+// W_c^T K_dec,c, so segment s has S_out = S_in P_s + N_s, and inside segment s the state
+// entering chunk c is S_in P_(..c) + N_(..c) (products and sums over the segment's earlier
+// chunks).  kda_seg_kernel walks every segment at once from S = 0 (segment 0 from the initial
+// state), writing N_s and the outputs O0_c = Q'_c N_(..c)^T + O_intra,c, and from the identity,
+// writing P_s and R_c = Q'_c P_(..c)^T; kda_combine_kernel forms S_in(s) on MFMA, and
+// kda_out_kernel completes out_c = O0_c + R_c S_in(s)^T for every chunk of segment s >= 1 at
+// once.  The sequential depth is C/P chunk steps plus P - 1 combine steps.
 
 // Head-dim constants of the scan kernels (d_k = d_v = D; four waves split the Dk rows).
 template <int D>
@@ -741,6 +749,14 @@ struct HD {
 };
 constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = value channel
 
+// What a chunk step writes besides the state update.
+enum OutMode {
+    OUT_NONE = 0,    // nothing (segment end state and transfer matrix only)
+    OUT_FINAL = 1,   // out = Q' S^T + O_intra in bf16, valid tokens only
+    OUT_O0 = 2,      // O0 = Q' S^T + O_intra in fp32, workspace (state from a zero start)
+    OUT_R = 3,       // R = Q' S^T in fp32, workspace (state rows of the transfer matrix)
+};
+
 template <int NT, int D>
 struct ChunkFrags {
     bf16x8 w[HD<D>::KB];                          // W, token tile w, 32-channel block kb
@@ -751,7 +767,7 @@ struct ChunkFrags {
     bf16x4 o[NT];                                 // O_intra (bf16), token tile w, Dv tile
 };
 
-template <int NT, bool WITH_U, bool WITH_OUT, int D>
+template <int NT, bool WITH_U, int OUT, int D>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
                                            int dv_tile0, ChunkFrags<NT, D>& f) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
@@ -761,7 +777,7 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * KB + kb) * 64 + lane) * 8);
-        if constexpr (WITH_OUT)
+        if constexpr (OUT != OUT_NONE)
             f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * KB + kb) * 64 + lane) * 8);
     }
 #pragma unroll
@@ -783,7 +799,7 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
         const int dt = dv_tile0 + nt;
         if constexpr (WITH_U)
             f.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
-        if constexpr (WITH_OUT)
+        if constexpr (OUT == OUT_FINAL || OUT == OUT_O0)
             f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
     }
 }
@@ -808,12 +824,13 @@ struct ScanLds {
 
 // One chunk of the scan for this workgroup's Dv tile(s):
 //   X = W S^T and (with outputs) Y^T = S Q'^T for token tile w; V_new = U - X (U = 0 for the
-//   transfer-matrix pass); out = Y + O_intra; S^T <- gamma * S^T + K_dec^T V_new for this
-//   wave's D/4 Dk rows.
-template <int NT, bool WITH_U, bool WITH_OUT, int D>
+//   transfer-matrix pass); out = Y + O_intra (or R = Y); S^T <- gamma * S^T + K_dec^T V_new
+//   for this wave's D/4 Dk rows.  `rec` is the chunk's record (workspace outputs).
+template <int NT, bool WITH_U, int OUT, int D>
 __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, D>& cur,
                                           f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L, int jc,
-                                          int len, size_t ob, size_t os, int dv_tile0) {
+                                          int len, size_t ob, size_t os, int dv_tile0,
+                                          int64_t rec) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW, SLD = HD<D>::SLD;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -821,7 +838,8 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
-    // X = W (S_hi + S_lo)^T (tokens of tile w x Dv); Y^T = S_hi Q'^T (Dv x tokens)
+    // X = W (S_hi + S_lo)^T (tokens of tile w x Dv); Y^T = S_hi Q'^T (Dv x tokens), with S_lo
+    // too for R (the transfer matrix rows are not rounded again by a state of their own)
     f32x4 accX[NT], accY[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -834,7 +852,8 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
             const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
             accX[nt] = mfma(cur.w[kb], sh, accX[nt]);
             accX[nt] = mfma(cur.w[kb], sl, accX[nt]);
-            if constexpr (WITH_OUT) accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
+            if constexpr (OUT != OUT_NONE) accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
+            if constexpr (OUT == OUT_R) accY[nt] = mfma(sl, cur.qp[kb], accY[nt]);
         }
     }
     const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
@@ -849,13 +868,33 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
         const int off = (16 * nt + n16) * VN_LD + 16 * w + 4 * q4;
         *reinterpret_cast<bf16x4*>(L.vh + off) = vh;
         *reinterpret_cast<bf16x4*>(L.vl + off) = vl;
-        if constexpr (WITH_OUT) {
+        if constexpr (OUT == OUT_FINAL) {
             if (tok < len) {
                 bf16x4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)cur.o[nt][r]);
                 *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os +
                                            16 * (dv_tile0 + nt) + 4 * q4) = o;
+            }
+        } else if constexpr (OUT == OUT_O0 || OUT == OUT_R) {
+            // every row, so the completion pass reads no unwritten memory (rows past the
+            // tail are zero: their q and every Aqk entry are)
+            const int t = dv_tile0 + nt;
+            f32x4 y = accY[nt];
+            if constexpr (OUT == OUT_O0) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) y[r] += (float)cur.o[nt][r];
+                *reinterpret_cast<f32x4*>(p.O0 + size_t(rec) * (64 * D) +
+                                          ((t * 4 + w) * 64 + lane) * 4) = y;
+            } else {   // R as a hi/lo pair in the completion pass's B-operand order
+                bf16x4 yh, yl;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) SPLIT_BF16(y[r], yh[r], yl[r]);
+                const int lb = (2 * (t & 1) + (q4 >> 1)) * 16 + n16;
+                __bf16* dst = p.Rf + size_t(rec) * (2 * 64 * D) +
+                              ((w * KB + (t >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1);
+                *reinterpret_cast<bf16x4*>(dst) = yh;
+                *reinterpret_cast<bf16x4*>(dst + 64 * D) = yl;
             }
         }
     }
@@ -891,7 +930,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
 // The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
 // record, never used): with the same number of loads in flight on every path, the compiler's
 // wait counts let each step wait only for its own operands, not for the next chunk's.
-template <int NT, bool WITH_U, bool WITH_OUT, int D>
+template <int NT, bool WITH_U, int OUT, int D>
 __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW][NT],
                                            const ScanLds& L,
                                            int64_t rec0, int cb, int ce, int len, size_t ob,
@@ -901,15 +940,17 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     const int lane = threadIdx.x & 63;
     const int last = ce - 1;
     ChunkFrags<NT, D> fa, fb;
-    load_chunk<NT, WITH_U, WITH_OUT, D>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
+    load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
     for (int jc = cb; jc < ce; jc += 2) {
         const int c1 = jc + 1 < last ? jc + 1 : last;
-        load_chunk<NT, WITH_U, WITH_OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
-        scan_step<NT, WITH_U, WITH_OUT, D>(p, fa, S, L, jc, len, ob, os, dv_tile0);
+        load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
+        scan_step<NT, WITH_U, OUT, D>(p, fa, S, L, jc, len, ob, os, dv_tile0,
+                                      rec0 + int64_t(jc) * p.n_v);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
-        load_chunk<NT, WITH_U, WITH_OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
-        scan_step<NT, WITH_U, WITH_OUT, D>(p, fb, S, L, jc + 1, len, ob, os, dv_tile0);
+        load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
+        scan_step<NT, WITH_U, OUT, D>(p, fb, S, L, jc + 1, len, ob, os, dv_tile0,
+                                      rec0 + int64_t(jc + 1) * p.n_v);
     }
 }
 
@@ -922,37 +963,36 @@ __device__ __forceinline__ void segment_range(int nchunks, int seg_p, int seg, i
     if (cb > nchunks) cb = nchunks;
 }
 
-// Operands of one combine step S <- S P_s + N_s for this wave's Dk rows: rows 16(2w+mt)+n16 of
-// P_s^T (stored transposed: Pt[dk'][dk] = P_s[dk][dk']) and this workgroup's tiles of N_s.
+// Operands of one combine step S <- S P_s + N_s for this wave's Dk tiles M = MW w + mt: the
+// A fragments of P_s^T (hi/lo) and the accumulator fragments of this workgroup's N_s tiles.
 template <int NT, int D>
 struct CombFrags {
-    f32x4 pa[HD<D>::MW][HD<D>::KB];   // Pt[16(MW w+mt)+n16][32kb+8q4 .. +3]
-    f32x4 pb[HD<D>::MW][HD<D>::KB];   //                     [32kb+8q4+4 .. +7]
-    f32x4 n[NT][HD<D>::MW];           // N_s[16(dv_tile0+nt)+n16][16(MW w+mt)+4q4 .. +3]
+    bf16x8 ph[HD<D>::MW][HD<D>::KB];   // P_s[32kb+8q4 .. +7][16M+n16] hi
+    bf16x8 pl[HD<D>::MW][HD<D>::KB];   // lo
+    f32x4 n[NT][HD<D>::MW];            // N_s[16(dv_tile0+nt)+n16][16M+4q4 .. +3]
 };
 
 template <int NT, int D>
-__device__ __forceinline__ void load_comb(const float* Pt, const float* Nst, int dv_tile0,
+__device__ __forceinline__ void load_comb(const __bf16* Pt, const float* Nst, int dv_tile0,
                                           CombFrags<NT, D>& f) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
+    constexpr int TILES = HD<D>::TILES;
     const int w = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
-    const int q4 = lane >> 4;
-    const int n16 = lane & 15;
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const float* src = Pt + size_t(16 * (MW * w + mt) + n16) * D + 32 * kb + 8 * q4;
-            f.pa[mt][kb] = *reinterpret_cast<const f32x4*>(src);
-            f.pb[mt][kb] = *reinterpret_cast<const f32x4*>(src + 4);
+            const __bf16* src = Pt + (((MW * w + mt) * KB + kb) * 64 + lane) * 8;
+            f.ph[mt][kb] = *reinterpret_cast<const bf16x8*>(src);
+            f.pl[mt][kb] = *reinterpret_cast<const bf16x8*>(src + D * D);
         }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
             f.n[nt][mt] = *reinterpret_cast<const f32x4*>(
-                Nst + size_t(16 * (dv_tile0 + nt) + n16) * D + 16 * (MW * w + mt) + 4 * q4);
+                Nst + (((dv_tile0 + nt) * TILES + MW * w + mt) * 64 + lane) * 4);
 }
 
 // S^T <- P_s^T S^T + N_s^T for this wave's Dk rows, i.e. S <- S P_s + N_s, with the state in S
@@ -965,16 +1005,6 @@ __device__ __forceinline__ void combine_step(const CombFrags<NT, D>& f,
     const int w = threadIdx.x >> 6;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
-    bf16x8 ph[MW][KB], pl[MW][KB];
-#pragma unroll
-    for (int mt = 0; mt < MW; ++mt)
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                SPLIT_BF16(f.pa[mt][kb][e], ph[mt][kb][e], pl[mt][kb][e]);
-                SPLIT_BF16(f.pb[mt][kb][e], ph[mt][kb][4 + e], pl[mt][kb][4 + e]);
-            }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -985,9 +1015,9 @@ __device__ __forceinline__ void combine_step(const CombFrags<NT, D>& f,
                 const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
                 const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
                 const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
-                acc = mfma(ph[mt][kb], sh, acc);
-                acc = mfma(pl[mt][kb], sh, acc);
-                acc = mfma(ph[mt][kb], sl, acc);
+                acc = mfma(f.ph[mt][kb], sh, acc);
+                acc = mfma(f.pl[mt][kb], sh, acc);
+                acc = mfma(f.ph[mt][kb], sl, acc);
             }
             S[mt][nt] = acc;
         }
@@ -1001,30 +1031,25 @@ __device__ __forceinline__ void combine_step(const CombFrags<NT, D>& f,
     lds_barrier();
 }
 
-// S_in(seg) = (((N_0) P_1 + N_1) P_2 + ...) P_{seg-1} + N_{seg-1}, with S = N_0 on entry.  The
-// next step's operands load while the current one multiplies (two register sets; the load is
-// issued on every step, past the end as a reload of the last matrices, never used).
-template <int NT, int D>
-__device__ __forceinline__ void combine_segments(const Params& p, int bh, int seg,
-                                                 f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L,
-                                                 int dv_tile0) {
-    if (seg < 2) return;
-    auto mat = [&](int sp) {
-        return (size_t(bh) * p.seg_p + (sp < seg - 1 ? sp : seg - 1)) * D * D;
-    };
-    CombFrags<NT, D> ca, cb;
-    load_comb<NT, D>(p.Pt + mat(1), p.Nst + mat(1), dv_tile0, ca);
-    int sp = 1;
-    for (; sp + 2 <= seg; sp += 2) {
-        load_comb<NT, D>(p.Pt + mat(sp + 1), p.Nst + mat(sp + 1), dv_tile0, cb);
-        combine_step<NT, D>(ca, S, L);
-        load_comb<NT, D>(p.Pt + mat(sp + 2), p.Nst + mat(sp + 2), dv_tile0, ca);
-        combine_step<NT, D>(cb, S, L);
+// Rows past a batch row's valid length (BNSD/BSND with cu_seqlens) are written as zeros, for
+// output columns [col0, col0 + ncols) (ncols a multiple of 4).
+__device__ __forceinline__ void zero_rows_past_len(const Params& p, int len, size_t ob, size_t os,
+                                                   int col0, int ncols) {
+    if (p.layout == KDA_LAYOUT_TND || len >= p.seq_len) return;
+    const int parts = ncols / 4;
+    const int rows = p.seq_len - len;
+    bf16x4 z;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) z[i] = (__bf16)0.f;
+    for (int e = threadIdx.x; e < rows * parts; e += kThreads) {
+        const int t = len + e / parts;
+        *reinterpret_cast<bf16x4*>(p.out + ob + size_t(t) * os + col0 + 4 * (e % parts)) = z;
     }
-    if (sp < seg) combine_step<NT, D>(ca, S, L);
 }
 
-// The one-tile form keeps under 256 registers so that two workgroups share a compute unit.
+// The one-level scan: one workgroup per (sequence, value head, NT Dv tiles) walks every chunk
+// of the sequence from the initial state.  The one-tile form keeps under 256 registers so that
+// two workgroups share a compute unit.
 template <int NT, int D>
 __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Params p) {
     constexpr int BV = 16 * NT;
@@ -1041,15 +1066,13 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Par
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
-    // XCD-aware decode: the Dv tiles of one (sequence, head, segment) share blockIdx.x mod 8,
-    // so they run on one XCD and share its L2 for the chunk operands they all read.
+    // XCD-aware decode: the Dv tiles of one (sequence, head) share blockIdx.x mod 8, so they
+    // run on one XCD and share its L2 for the chunk operands they all read.
     const int pid = blockIdx.x;
     const int xcd = pid & 7, r8 = pid >> 3;
-    const int grp = (r8 / p.scan_tiles) * 8 + xcd;
+    const int bh = (r8 / p.scan_tiles) * 8 + xcd;
     const int tile = r8 % p.scan_tiles;
-    if (grp >= p.batch * p.n_v * p.seg_p) return;
-    const int bh = grp / p.seg_p;
-    const int seg = grp % p.seg_p;
+    if (bh >= p.batch * p.n_v) return;
     const int b = bh / p.n_v;
     const int h = bh % p.n_v;
     const int dv_tile0 = tile * NT;   // first 16-wide Dv tile of this workgroup
@@ -1057,33 +1080,28 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Par
     int c0, len, slot0;
     seq_info(p, b, c0, len, slot0);
     const int nchunks = (len + kChunk - 1) / kChunk;
-    int cb, ce;
-    segment_range(nchunks, p.seg_p, seg, cb, ce);
     size_t ob, os;
     row_geom(p, b, h, p.n_v, D, c0, ob, os);
 
     // state tile: S[mt][nt][i] = S[dv = 16(dv_tile0+nt) + n16][dk = 16(MW w+mt) + 4q4 + i]
     f32x4 S[MW][NT];
     const size_t st_base = (size_t(b) * p.n_v + h) * D * D;
-    const float* s0 = p.init ? p.init + st_base : nullptr;
-    if (seg > 0) s0 = p.Nst + (size_t(bh) * p.seg_p + 0) * D * D;   // N_0
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int dv = 16 * (dv_tile0 + nt) + n16;
             const int dk = 16 * (MW * w + mt) + 4 * q4;
-            S[mt][nt] = s0 ? *reinterpret_cast<const f32x4*>(s0 + size_t(dv) * D + dk)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
+            S[mt][nt] = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
+                               : f32x4{0.f, 0.f, 0.f, 0.f};
             put_state<D>(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
         }
     lds_barrier();
-    combine_segments<NT, D>(p, bh, seg, S, L, dv_tile0);
 
-    run_chunks<NT, true, true, D>(p, S, L, int64_t(slot0) * p.n_v + h, cb, ce, len, ob, os,
-                                  dv_tile0);
+    run_chunks<NT, true, OUT_FINAL, D>(p, S, L, int64_t(slot0) * p.n_v + h, 0, nchunks, len, ob,
+                                       os, dv_tile0);
 
-    if (p.fin && seg == p.seg_p - 1) {
+    if (p.fin) {
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
@@ -1093,23 +1111,14 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Par
                 *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * D + dk) = S[mt][nt];
             }
     }
-    // rows past a batch row's valid length (BNSD/BSND with cu_seqlens) are written as zeros
-    if (p.layout != KDA_LAYOUT_TND && len < p.seq_len && seg == p.seg_p - 1) {
-        const int rows = p.seq_len - len;
-        for (int e = tid; e < rows * NT * 4; e += kThreads) {
-            const int t = len + e / (NT * 4);
-            const int part = e % (NT * 4);
-            bf16x4 z;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) z[i] = (__bf16)0.f;
-            *reinterpret_cast<bf16x4*>(p.out + ob + size_t(t) * os + 16 * dv_tile0 + 4 * part) = z;
-        }
-    }
+    zero_rows_past_len(p, len, ob, os, 16 * dv_tile0, 16 * NT);
 }
 
-// Segment pass of the two-level scan: 2 D/16 workgroups per (sequence, head, segment
-// s < seg_p-1).  Slots 0..D/16-1: N_s tiles (from S = 0, or from the initial state for s = 0,
-// with U); slots D/16..: P_s tiles (from 16 identity rows each, without U; not needed for s = 0).
+// Segment pass of the two-level scan: 2 D/16 workgroups per (sequence, head, segment s).
+// Slots 0..D/16-1 walk the segment from S = 0 (from the initial state for s = 0) with U: the
+// outputs of segment 0 are final, those of later segments go to O0, and the end state is N_s.
+// Slots D/16.. walk it from 16 identity rows each without U (not needed for s = 0): their
+// outputs are the columns of R = Q' P^T, and their end rows those of P_s.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     constexpr int MW = HD<D>::MW, TILES = HD<D>::TILES;
@@ -1125,13 +1134,14 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
+    // XCD-aware decode: the 2 D/16 workgroups of one (sequence, head, segment) share an XCD.
     const int pid = blockIdx.x;
     const int xcd = pid & 7, r8 = pid >> 3;
     const int grp = (r8 / (2 * TILES)) * 8 + xcd;
     const int slot = r8 % (2 * TILES);
-    if (grp >= p.batch * p.n_v * (p.seg_p - 1)) return;
-    const int bh = grp / (p.seg_p - 1);
-    const int seg = grp % (p.seg_p - 1);
+    if (grp >= p.batch * p.n_v * p.seg_p) return;
+    const int bh = grp / p.seg_p;
+    const int seg = grp % p.seg_p;
     const bool is_p = slot >= TILES;
     const int tile = slot % TILES;
     if (is_p && seg == 0) return;
@@ -1143,6 +1153,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     const int nchunks = (len + kChunk - 1) / kChunk;
     int cb, ce;
     segment_range(nchunks, p.seg_p, seg, cb, ce);
+    size_t ob, os;
+    row_geom(p, b, h, p.n_v, D, c0, ob, os);
 
     f32x4 S[MW][1];
     const size_t st_base = (size_t(b) * p.n_v + h) * D * D;
@@ -1165,23 +1177,217 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     const int64_t rec0 = int64_t(slot0) * p.n_v + h;
     const size_t m = (size_t(bh) * p.seg_p + seg) * D * D;
     if (is_p) {
-        run_chunks<1, false, false, D>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
-        // rows 16 tile .. of P_s, stored transposed: Pt[dk'][row]
+        run_chunks<1, false, OUT_R, D>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+        // rows 16 tile .. of P_s, split, into the combine's A fragments of P_s^T: element
+        // P_s[16 tile + n16][16 M + 4 q4 + i] is lane (2 (tile & 1) + (n16 >> 3), 4 q4 + i),
+        // entry n16 & 7, of fragment (M, tile >> 1)
+        __bf16* pt = p.Pt + 2 * m;
+        constexpr int KB = HD<D>::KB;
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                p.Pt[m + size_t(16 * (MW * w + mt) + 4 * q4 + i) * D + row] = S[mt][0][i];
+            for (int i = 0; i < 4; ++i) {
+                const int lp = (2 * (tile & 1) + (n16 >> 3)) * 16 + 4 * q4 + i;
+                const int at = (((MW * w + mt) * KB + (tile >> 1)) * 64 + lp) * 8 + (n16 & 7);
+                SPLIT_BF16(S[mt][0][i], pt[at], pt[D * D + at]);
+            }
     } else {
-        run_chunks<1, true, false, D>(p, S, L, rec0, cb, ce, len, 0, 0, tile);
+        if (seg == 0)
+            run_chunks<1, true, OUT_FINAL, D>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+        else
+            run_chunks<1, true, OUT_O0, D>(p, S, L, rec0, cb, ce, len, ob, os, tile);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
-            *reinterpret_cast<f32x4*>(p.Nst + m + size_t(row) * D + 16 * (MW * w + mt) +
-                                      4 * q4) = S[mt][0];
+            *reinterpret_cast<f32x4*>(p.Nst + m + ((tile * TILES + MW * w + mt) * 64 + lane) * 4) =
+                S[mt][0];
     }
 }
 
-constexpr int kStages = 3;   // intra, segment pass, scan
+// Combine pass of the two-level scan: D/16 workgroups per (sequence, head), one 16-row Dv tile
+// each, form S_in(1) = N_0 and S_in(s+1) = S_in(s) P_s + N_s, store every S_in(s) and, with a
+// final state, S_in(seg_p-1) P_last + N_last.  No step's operands depend on an earlier step,
+// so they load two steps ahead, in three register sets (a load past the end rereads the last
+// step's matrices, never used).  Few workgroups: the register budget of one per compute unit.
+template <int D>
+__global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
+    constexpr int MW = HD<D>::MW, KB = HD<D>::KB, TILES = HD<D>::TILES;
+    __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
+    const ScanLds L{sSh, sSl, nullptr, nullptr};
+
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+
+    const int pid = blockIdx.x;
+    const int xcd = pid & 7, r8 = pid >> 3;
+    const int bh = (r8 / TILES) * 8 + xcd;
+    const int tile = r8 % TILES;
+    if (bh >= p.batch * p.n_v) return;
+    const int b = bh / p.n_v;
+    const int h = bh % p.n_v;
+    auto mat = [&](int s) { return (size_t(bh) * p.seg_p + s) * D * D; };
+
+    const int last = p.fin ? p.seg_p - 1 : p.seg_p - 2;   // steps 1 .. last
+    auto at = [&](int s) { return mat(s < last ? s : (last > 0 ? last : 1)); };
+    f32x4 S[MW][1];
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+        S[mt][0] = *reinterpret_cast<const f32x4*>(p.Nst + mat(0) +
+                                                   ((tile * TILES + MW * w + mt) * 64 + lane) * 4);
+    CombFrags<1, D> c0f, c1f, c2f;
+    load_comb<1, D>(p.Pt + 2 * at(1), p.Nst + at(1), tile, c0f);
+    load_comb<1, D>(p.Pt + 2 * at(2), p.Nst + at(2), tile, c1f);
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+        put_state<D>(sSh, sSl, n16, 16 * (MW * w + mt) + 4 * q4, S[mt][0]);
+    lds_barrier();
+
+    // S_in(s) as the completion pass's A fragments (hi/lo): element S[16 tile + n16][16 M +
+    // 4 q4 + i] is lane (2 (M & 1) + (q4 >> 1), n16), entries 4 (q4 & 1) + i, of fragment
+    // (tile, M >> 1)
+    auto store_in = [&](int s) {
+        __bf16* dst = p.Sin + 2 * mat(s);
+#pragma unroll
+        for (int mt = 0; mt < MW; ++mt) {
+            const int M = MW * w + mt;
+            bf16x4 hh, ll;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) SPLIT_BF16(S[mt][0][i], hh[i], ll[i]);
+            const int lb = (2 * (M & 1) + (q4 >> 1)) * 16 + n16;
+            const int off = ((tile * KB + (M >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1);
+            *reinterpret_cast<bf16x4*>(dst + off) = hh;
+            *reinterpret_cast<bf16x4*>(dst + D * D + off) = ll;
+        }
+    };
+    int s = 1;
+    for (; s + 2 <= last; s += 3) {
+        load_comb<1, D>(p.Pt + 2 * at(s + 2), p.Nst + at(s + 2), tile, c2f);
+        store_in(s);
+        combine_step<1, D>(c0f, S, L);
+        load_comb<1, D>(p.Pt + 2 * at(s + 3), p.Nst + at(s + 3), tile, c0f);
+        store_in(s + 1);
+        combine_step<1, D>(c1f, S, L);
+        load_comb<1, D>(p.Pt + 2 * at(s + 4), p.Nst + at(s + 4), tile, c1f);
+        store_in(s + 2);
+        combine_step<1, D>(c2f, S, L);
+    }
+    if (s <= last) {
+        store_in(s);
+        combine_step<1, D>(c0f, S, L);
+        ++s;
+    }
+    if (s <= last) {
+        store_in(s);
+        combine_step<1, D>(c1f, S, L);
+        ++s;
+    }
+    if (s < p.seg_p) store_in(s);   // S_in(seg_p - 1) without a final state
+    const int row = 16 * tile + n16;
+    if (p.fin) {
+        float* dst = p.fin + (size_t(b) * p.n_v + h) * D * D;
+#pragma unroll
+        for (int mt = 0; mt < MW; ++mt)
+            *reinterpret_cast<f32x4*>(dst + size_t(row) * D + 16 * (MW * w + mt) + 4 * q4) =
+                S[mt][0];
+    }
+
+    int c0, len, slot0;
+    seq_info(p, b, c0, len, slot0);
+    size_t ob, os;
+    row_geom(p, b, h, p.n_v, D, c0, ob, os);
+    zero_rows_past_len(p, len, ob, os, 16 * tile, 16);
+}
+
+// Completion pass of the two-level scan: one workgroup per record of a chunk in segment
+// s >= 1, out = O0 + R S_in(s)^T with three-term hi/lo products (as O^T = S_in R^T: the
+// accumulator holds four consecutive value channels of one token per lane).  Wave w takes Dv
+// tiles D/64 w .. of all 64 tokens.  R, which every wave multiplies, is read from HBM once into
+// LDS; every operand is loaded before the first output is stored.
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
+    constexpr int KB = HD<D>::KB, NTW = D / 64;
+    constexpr int R_U4 = 2 * 64 * D * 2 / 16;   // R hi/lo in 16-byte units
+    __shared__ __attribute__((aligned(16))) bf16x8 sR[R_U4];
+    const int tid = threadIdx.x;
+    const int w = tid >> 6;
+    const int lane = tid & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+
+    const int64_t rec = blockIdx.x;
+    const int slot = int(rec / p.n_v);
+    const int h = int(rec % p.n_v);
+    const int b = slot_batch(p, slot);
+    int c0, len, slot0;
+    seq_info(p, b, c0, len, slot0);
+    const int j = slot - slot0;
+    if (j < 0 || j * kChunk >= len) return;   // an unused slot
+    const int nchunks = (len + kChunk - 1) / kChunk;
+    const int seg = j / ((nchunks + p.seg_p - 1) / p.seg_p);
+    if (seg == 0) return;                     // written final by the segment pass
+    size_t ob, os;
+    row_geom(p, b, h, p.n_v, D, c0, ob, os);
+
+    const __bf16* sin = p.Sin + 2 * ((size_t(b) * p.n_v + h) * p.seg_p + seg) * D * D;
+    const float* o0 = p.O0 + size_t(rec) * (64 * D);
+    const __bf16* rr = p.Rf + size_t(rec) * (2 * 64 * D);
+
+    bf16x8 ah[NTW][KB], al[NTW][KB];   // S_in[16 nt + n16][32 kb + 8 q4 ..]
+    f32x4 acc[4][NTW];                 // O0[16 tt + n16][16 nt + 4 q4 ..]
+    {
+        bf16x8 x[R_U4 / kThreads];
+#pragma unroll
+        for (int u = 0; u < R_U4 / kThreads; ++u)
+            x[u] = *reinterpret_cast<const bf16x8*>(rr + size_t(u * kThreads + tid) * 8);
+#pragma unroll
+        for (int u = 0; u < R_U4 / kThreads; ++u) sR[u * kThreads + tid] = x[u];
+    }
+#pragma unroll
+    for (int i = 0; i < NTW; ++i)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const __bf16* src = sin + (((NTW * w + i) * KB + kb) * 64 + lane) * 8;
+            ah[i][kb] = *reinterpret_cast<const bf16x8*>(src);
+            al[i][kb] = *reinterpret_cast<const bf16x8*>(src + D * D);
+        }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+            acc[tt][i] = *reinterpret_cast<const f32x4*>(o0 + (((NTW * w + i) * 4 + tt) * 64 + lane) * 4);
+    __syncthreads();
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            const bf16x8 bh = sR[(tt * KB + kb) * 64 + lane];            // R[16 tt + n16][32 kb + 8 q4 ..]
+            const bf16x8 bl = sR[R_U4 / 2 + (tt * KB + kb) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+                acc[tt][i] = mfma(ah[i][kb], bh, acc[tt][i]);
+                acc[tt][i] = mfma(al[i][kb], bh, acc[tt][i]);
+                acc[tt][i] = mfma(ah[i][kb], bl, acc[tt][i]);
+            }
+        }
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt) {
+        const int tok = j * kChunk + 16 * tt + n16;
+        if (tok < len) {
+#pragma unroll
+            for (int i = 0; i < NTW; ++i)
+                *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os +
+                                           16 * (NTW * w + i) + 4 * q4) = to_bf16x4(acc[tt][i]);
+        }
+    }
+}
+
+// Stages of one call, each one kernel (empty when the plan does not enqueue it): intra, then
+// either the one-level scan or the segment, combine and completion passes.
+constexpr int kStages = 5;
+enum Stage { ST_INTRA = 0, ST_SEG = 1, ST_COMB = 2, ST_OUT = 3, ST_SCAN = 4 };
 
 // One kernel launch.  With events, the dispatch itself records e0 when the kernel starts and
 // e1 when it ends (hipExtLaunchKernel), so no marker packet sits between the kernels.
@@ -1232,8 +1438,12 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.nc_max = plan.nc_max;
     p.scan_tiles = plan.scan_tiles;
     p.seg_p = plan.seg_p;
-    p.Pt = plan.seg_p > 1 ? reinterpret_cast<float*>(ws + plan.off_pt) : nullptr;
-    p.Nst = plan.seg_p > 1 ? reinterpret_cast<float*>(ws + plan.off_n) : nullptr;
+    const bool two = plan.seg_p > 1;
+    p.Pt = two ? reinterpret_cast<__bf16*>(ws + plan.off_pt) : nullptr;
+    p.Nst = two ? reinterpret_cast<float*>(ws + plan.off_n) : nullptr;
+    p.Sin = two ? reinterpret_cast<__bf16*>(ws + plan.off_sin) : nullptr;
+    p.O0 = two ? reinterpret_cast<float*>(ws + plan.off_o0) : nullptr;
+    p.Rf = two ? reinterpret_cast<__bf16*>(ws + plan.off_r) : nullptr;
     p.scale = shape->scale;
     p.flags = shape->flags;
 
@@ -1245,29 +1455,36 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     const void* intra =
         d64 ? (sg ? fn(&kda_intra_kernel<true, 64>) : fn(&kda_intra_kernel<false, 64>))
             : (sg ? fn(&kda_intra_kernel<true, 128>) : fn(&kda_intra_kernel<false, 128>));
-    kda_status st2 = launch_kernel(intra, unsigned(plan.intra_blocks), stream, e(0), e(1), p);
-    if (st2 != KDA_OK) return st2;
-    if (plan.seg_p > 1) {
-        const void* segk = d64 ? fn(&kda_seg_kernel<64>) : fn(&kda_seg_kernel<128>);
-        st2 = launch_kernel(segk, unsigned(plan.seg_blocks), stream, e(2), e(3), p);
-        if (st2 != KDA_OK) return st2;
-    } else if (ev) {   // no segment pass: an empty stage
-        if (hipEventRecord(ev[2], stream) != hipSuccess ||
-            hipEventRecord(ev[3], stream) != hipSuccess)
+    // one stage: its kernel, or (not enqueued by this plan) its two events back to back
+    auto stage = [&](int sidx, const void* kernel, int64_t grid) -> kda_status {
+        if (kernel) return launch_kernel(kernel, unsigned(grid), stream, e(2 * sidx), e(2 * sidx + 1), p);
+        if (ev && (hipEventRecord(ev[2 * sidx], stream) != hipSuccess ||
+                   hipEventRecord(ev[2 * sidx + 1], stream) != hipSuccess))
             return KDA_ERR_HIP;
-    }
-    const void* scan;
-    if (d64)
+        return KDA_OK;
+    };
+    const void* segk = nullptr;
+    const void* combk = nullptr;
+    const void* outk = nullptr;
+    const void* scan = nullptr;
+    if (two) {
+        segk = d64 ? fn(&kda_seg_kernel<64>) : fn(&kda_seg_kernel<128>);
+        combk = d64 ? fn(&kda_combine_kernel<64>) : fn(&kda_combine_kernel<128>);
+        outk = d64 ? fn(&kda_out_kernel<64>) : fn(&kda_out_kernel<128>);
+    } else if (d64) {
         scan = plan.scan_nt == 4   ? fn(&kda_scan_kernel<4, 64>)
                : plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 64>)
                                    : fn(&kda_scan_kernel<1, 64>);
-    else
+    } else {
         scan = plan.scan_nt == 4   ? fn(&kda_scan_kernel<4, 128>)
                : plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 128>)
                                    : fn(&kda_scan_kernel<1, 128>);
-    st2 = launch_kernel(scan, unsigned(plan.scan_blocks), stream, e(4), e(5), p);
-    if (st2 != KDA_OK) return st2;
-    return KDA_OK;
+    }
+    if ((st = stage(ST_INTRA, intra, plan.intra_blocks)) != KDA_OK) return st;
+    if ((st = stage(ST_SEG, segk, plan.seg_blocks)) != KDA_OK) return st;
+    if ((st = stage(ST_COMB, combk, plan.comb_blocks)) != KDA_OK) return st;
+    if ((st = stage(ST_OUT, outk, plan.out_blocks)) != KDA_OK) return st;
+    return stage(ST_SCAN, scan, plan.scan_blocks);
 }
 
 }  // namespace kda
@@ -1306,9 +1523,11 @@ int32_t kda_num_stages(void) { return kda::kStages; }
 
 const char* kda_stage_name(int32_t stage) {
     switch (stage) {
-    case 0: return "kda_intra_kernel";
-    case 1: return "kda_seg_kernel";
-    case 2: return "kda_scan_kernel";
+    case kda::ST_INTRA: return "kda_intra_kernel";
+    case kda::ST_SEG: return "kda_seg_kernel";
+    case kda::ST_COMB: return "kda_combine_kernel";
+    case kda::ST_OUT: return "kda_out_kernel";
+    case kda::ST_SCAN: return "kda_scan_kernel";
     default: return "unknown stage";
     }
 }

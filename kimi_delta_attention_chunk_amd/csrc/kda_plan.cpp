@@ -65,28 +65,38 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     for (int nt = 4; nt >= 2; nt /= 2)
         if (bh * (tiles / nt) >= 256) { p.scan_nt = nt; break; }
     // Few (sequence, head) chains leave most compute units idle through a long sequential scan.
-    // Then each sequence is cut into seg_p segments: a segment pass runs every segment but the
-    // last from a zero state and from identity rows (d/16 + d/16 workgroups per segment),
-    // giving its end state N_s and transfer matrix P_s, and the output pass starts segment s
-    // from S_in(s) = S_in(s-1) P_{s-1} + N_{s-1}.  seg_p is the largest count whose segment
-    // pass fits 256 workgroups, with at least 8 chunks per segment.
+    // Then each sequence is cut into seg_p segments and every segment is walked at once: from
+    // a zero state (from the initial state for segment 0), giving its end state N_s and the
+    // outputs O0 of its chunks, and from the identity, giving its transfer matrix P_s and the
+    // queries R = Q' P^T carried back to the segment start (d/16 + d/16 workgroups per
+    // segment).  A short combine then forms S_in(s) = S_in(s-1) P_{s-1} + N_{s-1}, and the
+    // outputs of segment s >= 1 are completed in parallel as O0 + R S_in(s)^T.  seg_p is the
+    // largest count whose segment pass fits 256 workgroups, with at least 8 chunks per
+    // segment.
     p.seg_p = 1;
     if (bh * tiles < 256) {
         const int64_t nc_est = (s->layout == KDA_LAYOUT_TND)
                                    ? (int64_t(s->seq_len) / s->batch + kChunk - 1) / kChunk
                                    : p.nc_max;
-        int64_t sp = (256 / (bh * tiles) + 3) / 2;
+        int64_t sp = (256 / (bh * tiles) + 1) / 2;
         if (sp > nc_est / 8) sp = nc_est / 8;
         if (sp > 16) sp = 16;
         if (sp >= 2) p.seg_p = int(sp);
     }
     if (p.seg_p > 1) p.scan_nt = 1;
     p.scan_tiles = tiles / p.scan_nt;
-    const int64_t out_groups = bh * p.seg_p;
-    p.scan_blocks = ((out_groups + 7) / 8) * 8 * p.scan_tiles;
-    p.seg_blocks = (p.seg_p > 1) ? ((bh * (p.seg_p - 1) + 7) / 8) * 8 * 2 * tiles : 0;
+    const int64_t bh8 = (bh + 7) / 8 * 8;
+    if (p.seg_p > 1) {
+        p.scan_blocks = 0;
+        p.seg_blocks = ((bh * p.seg_p + 7) / 8) * 8 * 2 * tiles;
+        p.comb_blocks = bh8 * tiles;
+        p.out_blocks = p.n_records;
+    } else {
+        p.scan_blocks = bh8 * p.scan_tiles;
+    }
     const int64_t max_grid = std::numeric_limits<int32_t>::max();
-    if (p.intra_blocks > max_grid || p.scan_blocks > max_grid || p.seg_blocks > max_grid)
+    if (p.intra_blocks > max_grid || p.scan_blocks > max_grid || p.seg_blocks > max_grid ||
+        p.comb_blocks > max_grid || p.out_blocks > max_grid)
         return KDA_ERR_UNSUPPORTED;
 
     // element counts of the largest tensors must fit the 64-bit offsets used on the device
@@ -105,8 +115,12 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     p.off_g = off; off = align_up(off + n * rec_g_bytes(d), 256);
     if (p.seg_p > 1) {
         const size_t mats = size_t(bh) * p.seg_p * d * d * sizeof(float);
+        const size_t rows = n * kChunk * d * sizeof(float);
         p.off_pt = off; off = align_up(off + mats, 256);
         p.off_n = off; off = align_up(off + mats, 256);
+        p.off_sin = off; off = align_up(off + mats, 256);
+        p.off_o0 = off; off = align_up(off + rows, 256);
+        p.off_r = off; off = align_up(off + rows, 256);
     }
     p.total = off;
     *plan = p;

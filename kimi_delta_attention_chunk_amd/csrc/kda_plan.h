@@ -42,10 +42,15 @@ struct Plan {
     int scan_nt = 1;           // 16-row Dv tiles per scan workgroup (1, 2 or 4)
     int scan_tiles = 0;        // scan workgroups per (sequence, head, segment) = (d/16) / scan_nt
     int seg_p = 1;             // segments per sequence of the two-level scan (1 = one level)
-    int64_t seg_blocks = 0;    // workgroups of the segment pass (0 when seg_p == 1)
+    int64_t seg_blocks = 0;    // two-level: segment pass, 2 d/16 per (sequence, head, segment)
+    int64_t comb_blocks = 0;   // two-level: segment combine, d/16 per (sequence, head)
+    int64_t out_blocks = 0;    // two-level: output completion, one per record
     // byte offsets of each workspace array (256-byte aligned)
     size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0;
-    size_t off_pt = 0, off_n = 0;   // segment transfer matrices and zero-start end states
+    // two-level only: per (sequence, head, segment) transfer matrix P_s (transposed), zero-start
+    // end state N_s and entry state S_in(s), d x d fp32 each; per record the zero-start outputs
+    // O0 and the propagated queries R = Q' P^T of the segment's chunks, 64 x d fp32 each
+    size_t off_pt = 0, off_n = 0, off_sin = 0, off_o0 = 0, off_r = 0;
     size_t total = 0;
 };
 

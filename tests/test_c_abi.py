@@ -43,9 +43,11 @@ def test_status_strings(lib):
     assert lib.kda_status_str(0) == b"KDA_OK"
     assert lib.kda_status_str(3) == b"KDA_ERR_WORKSPACE"
     assert lib.kda_status_str(99) == b"unknown kda_status"
-    assert lib.kda_num_stages() == 3
-    assert lib.kda_stage_name(1) == b"kda_seg_kernel"
-    assert lib.kda_stage_name(2) == b"kda_scan_kernel"
+    assert lib.kda_num_stages() == 5
+    names = [lib.kda_stage_name(i) for i in range(5)]
+    assert names == [b"kda_intra_kernel", b"kda_seg_kernel", b"kda_combine_kernel",
+                     b"kda_out_kernel", b"kda_scan_kernel"]
+    assert lib.kda_stage_name(5) == b"unknown stage"
     assert lib.kda_version() >= 100
 
 
@@ -59,11 +61,13 @@ def test_workspace_sizes(lib):
     st, n1 = ws(lib, make_shape("BNSD", 1, 8192, 3, 3, 0.088))
     assert st == 0
     # 128 chunks x 3 heads x (W, K_dec hi+lo, U fp32, Q', O_intra bf16, gamma), plus the
-    # two-level scan's matrices: 3 heads x 6 segments x (P_s, N_s) fp32 128x128
+    # two-level scan (3 x (2 x 5 - 1) x 8 = 216 segment-pass workgroups -> 5 segments): per
+    # segment P_s, N_s and S_in (fp32 128x128), per record O0 and R (fp32 64x128)
     rec = 16384 + 16384 + 32768 + 32768 + 16384 + 512
     assert rec == 115200
-    assert n1 >= 128 * 3 * rec + 3 * 6 * 2 * 65536
-    assert n1 < 128 * 3 * rec + 3 * 6 * 2 * 65536 + 16 * 256
+    two = 3 * 5 * 3 * 65536 + 384 * 2 * 32768
+    assert n1 >= 128 * 3 * rec + two
+    assert n1 < 128 * 3 * rec + two + 16 * 256
     # many heads: one-level scan, no matrices
     st, n4 = ws(lib, make_shape("BNSD", 1, 8192, 32, 32, 0.088))
     assert st == 0 and n4 < 128 * 32 * rec + 16 * 256
@@ -73,13 +77,14 @@ def test_workspace_sizes(lib):
     st, n3 = ws(lib, make_shape("BSND", 4, 4100, 4, 16, 0.088))
     assert st == 0 and n3 >= 4 * 65 * 16 * 115200
     # head dim 64: a record of 64 x 64 x 14 + 64 x 4 bytes; six heads at 8K use the two-level
-    # scan (256 / (6 x 4) tiles -> 6 segments) with 64 x 64 fp32 matrices
+    # scan (6 x (2 x 5 - 1) x 4 = 216 workgroups -> 5 segments) with 64 x 64 fp32 matrices
     rec64 = 64 * 64 * 14 + 64 * 4
     assert rec64 == 57600
     st, n5 = ws(lib, make_shape("BNSD", 1, 8192, 6, 6, 0.125, d_k=64, d_v=64))
     assert st == 0
-    assert n5 >= 128 * 6 * rec64 + 6 * 6 * 2 * 64 * 64 * 4
-    assert n5 < 128 * 6 * rec64 + 6 * 6 * 2 * 64 * 64 * 4 + 16 * 256
+    two64 = 6 * 5 * 3 * 64 * 64 * 4 + 768 * 2 * 64 * 64 * 4
+    assert n5 >= 128 * 6 * rec64 + two64
+    assert n5 < 128 * 6 * rec64 + two64 + 16 * 256
 
 
 @pytest.mark.parametrize("bad, code", [

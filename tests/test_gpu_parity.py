@@ -304,10 +304,14 @@ def test_output_guard_bands_and_padding_rows():
     assert_parity(fin, rf, "guarded final_state")
 
 
-def test_null_states():
-    inp = make_inputs("BNSD", 1, 100, 1, 1, g_kind="strong", init=False, seed=27)
+@pytest.mark.parametrize("seq_len,init", [(100, False), (64 * 40 + 9, False), (64 * 40 + 9, True)],
+                         ids=["one_level", "two_level", "two_level_init"])
+def test_null_states(seq_len, init):
+    """No final state requested (and no initial state), on both scan forms: the two-level
+    combine then stops one step early."""
+    inp = make_inputs("BNSD", 1, seq_len, 1, 1, g_kind="strong", init=init, seed=27)
     d = inp.to("cuda")
-    out, fin = kda_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.scale, None, None, "BNSD",
+    out, fin = kda_chunk_fwd(d.q, d.k, d.v, d.g, d.beta, d.scale, d.initial_state, None, "BNSD",
                              output_final_state=False)
     torch.cuda.synchronize()
     assert fin is None
