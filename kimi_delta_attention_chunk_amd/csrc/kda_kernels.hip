@@ -374,15 +374,39 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     // token, natural log), a prefix sum across the 16 lanes of a DPP row with the first token's
     // term removed.  The block sums go through LDS to give, per channel, G at each block's
     // first token (G[16I]) and G_last = G at the last valid token.
-    float d[8 * KB];
+    // (With the scalar gate every channel of a token has the same gate: one scan per lane.)
+    float gv[8 * KB], d[8 * KB];
+    if constexpr (SG) {
+        const float gs = tv ? gsv : 0.f;
+        const float ds = row_scan16(n16 == 0 ? 0.f : gs);
 #pragma unroll
-    for (int i = 0; i < 8 * KB; ++i) {
-        float gi;
-        if constexpr (SG) gi = gsv; else gi = xg[i >> 2][i & 3];
-        gi = tv ? gi : 0.f;
-        d[i] = row_scan16(n16 == 0 ? 0.f : gi);
-        if (n16 == 0) sFirst[I * 128 + 32 * (i >> 3) + 8 * q4 + (i & 7)] = gi;
-        if (n16 == 15) sDlast[I * 128 + 32 * (i >> 3) + 8 * q4 + (i & 7)] = d[i];
+        for (int i = 0; i < 8 * KB; ++i) {
+            gv[i] = gs;
+            d[i] = ds;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8 * KB; ++i) gv[i] = xg[i >> 2][i & 3];
+        if (n < kChunk) {   // a tail chunk: rows past it add nothing
+#pragma unroll
+            for (int i = 0; i < 8 * KB; ++i) gv[i] = tv ? gv[i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 8 * KB; ++i) d[i] = row_scan16(n16 == 0 ? 0.f : gv[i]);
+    }
+    if (n16 == 0 || n16 == 15) {   // block-first gates and block sums, 8 channels per store pair
+        float* dst = (n16 == 0 ? sFirst : sDlast) + I * 128 + 8 * q4;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+            f32x4 a, c;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[e] = n16 == 0 ? gv[8 * kb + e] : d[8 * kb + e];
+                c[e] = n16 == 0 ? gv[8 * kb + 4 + e] : d[8 * kb + 4 + e];
+            }
+            *reinterpret_cast<f32x4*>(dst + 32 * kb) = a;
+            *reinterpret_cast<f32x4*>(dst + 32 * kb + 4) = c;
+        }
     }
     __syncthreads();
     if (tid < D) {
