@@ -1138,11 +1138,12 @@ __global__ __launch_bounds__(kThreads, NT == 1 ? 2 : 1) void kda_scan_kernel(Par
     zero_rows_past_len(p, len, ob, os, 16 * dv_tile0, 16 * NT);
 }
 
-// Segment pass of the two-level scan: 2 D/16 workgroups per (sequence, head, segment s).
-// Slots 0..D/16-1 walk the segment from S = 0 (from the initial state for s = 0) with U: the
-// outputs of segment 0 are final, those of later segments go to O0, and the end state is N_s.
-// Slots D/16.. walk it from 16 identity rows each without U (not needed for s = 0): their
-// outputs are the columns of R = Q' P^T, and their end rows those of P_s.
+// Segment pass of the two-level scan: 2 D/16 workgroups per (sequence, head, segment s >= 1),
+// D/16 for segment 0.  The zero-start walk (D/16 workgroups, one 16-row Dv tile each) starts
+// from S = 0 (from the initial state for s = 0) with U: the outputs of segment 0 are final,
+// those of later segments go to O0, and the end state is N_s.  The identity walk (D/16
+// workgroups from 16 identity rows each, without U) writes the columns of R = Q' P^T as its
+// outputs and ends with the rows of P_s.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     constexpr int MW = HD<D>::MW, TILES = HD<D>::TILES;
@@ -1158,17 +1159,20 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
-    // XCD-aware decode: the 2 D/16 workgroups of one (sequence, head, segment) share an XCD.
+    // XCD-aware decode.  Units of D/16 workgroups: per (sequence, head) the zero-start walk of
+    // segment 0, then for s >= 1 the zero-start and the identity walks of segment s (2 seg_p - 1
+    // units).  Unit u runs on XCD u mod 8, so its workgroups share that XCD's L2 for the records
+    // they all read, and the XCDs receive equal numbers of units.
     const int pid = blockIdx.x;
     const int xcd = pid & 7, r8 = pid >> 3;
-    const int grp = (r8 / (2 * TILES)) * 8 + xcd;
-    const int slot = r8 % (2 * TILES);
-    if (grp >= p.batch * p.n_v * p.seg_p) return;
-    const int bh = grp / p.seg_p;
-    const int seg = grp % p.seg_p;
-    const bool is_p = slot >= TILES;
-    const int tile = slot % TILES;
-    if (is_p && seg == 0) return;
+    const int unit = (r8 / TILES) * 8 + xcd;
+    const int tile = r8 % TILES;
+    const int per_bh = 2 * p.seg_p - 1;
+    if (unit >= p.batch * p.n_v * per_bh) return;
+    const int bh = unit / per_bh;
+    const int k = unit % per_bh;
+    const bool is_p = k > 0 && (k & 1) == 0;
+    const int seg = (k + 1) >> 1;
     const int b = bh / p.n_v;
     const int h = bh % p.n_v;
 

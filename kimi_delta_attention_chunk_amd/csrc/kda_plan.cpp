@@ -88,7 +88,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     const int64_t bh8 = (bh + 7) / 8 * 8;
     if (p.seg_p > 1) {
         p.scan_blocks = 0;
-        p.seg_blocks = ((bh * p.seg_p + 7) / 8) * 8 * 2 * tiles;
+        p.seg_blocks = ((bh * (2 * p.seg_p - 1) + 7) / 8) * 8 * tiles;
         p.comb_blocks = bh8 * tiles;
         p.out_blocks = p.n_records;
     } else {

@@ -42,7 +42,7 @@ struct Plan {
     int scan_nt = 1;           // 16-row Dv tiles per scan workgroup (1, 2 or 4)
     int scan_tiles = 0;        // scan workgroups per (sequence, head, segment) = (d/16) / scan_nt
     int seg_p = 1;             // segments per sequence of the two-level scan (1 = one level)
-    int64_t seg_blocks = 0;    // two-level: segment pass, 2 d/16 per (sequence, head, segment)
+    int64_t seg_blocks = 0;    // two-level: segment pass, (2 seg_p - 1) d/16 per (sequence, head)
     int64_t comb_blocks = 0;   // two-level: segment combine, d/16 per (sequence, head)
     int64_t out_blocks = 0;    // two-level: output completion, one per record
     // byte offsets of each workspace array (256-byte aligned)
