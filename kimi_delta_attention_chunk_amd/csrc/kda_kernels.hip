@@ -308,8 +308,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     const int n16 = lane & 15;
 
     const int64_t rec = blockIdx.x;
-    const int slot = int(rec / p.n_v);
-    const int h = int(rec % p.n_v);
+    const int slot = int(blockIdx.x / unsigned(p.n_v));   // 32-bit: grids stay below 2^31
+    const int h = int(blockIdx.x - unsigned(slot) * unsigned(p.n_v));
     const int hq = h / p.group;
 
     // chunk slot -> (sequence b, chunk j)
@@ -1346,8 +1346,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     const int n16 = lane & 15;
 
     const int64_t rec = blockIdx.x;
-    const int slot = int(rec / p.n_v);
-    const int h = int(rec % p.n_v);
+    const int slot = int(blockIdx.x / unsigned(p.n_v));
+    const int h = int(blockIdx.x - unsigned(slot) * unsigned(p.n_v));
     const int b = slot_batch(p, slot);
     int c0, len, slot0;
     seq_info(p, b, c0, len, slot0);
