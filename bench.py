@@ -49,15 +49,17 @@ def path_bytes(inp) -> int:
     return b + states * ((inp.initial_state is not None) + 1)
 
 
+def shape_of(inp):
+    from kimi_delta_attention_chunk_amd import make_shape
+    d = head_dim(inp)
+    return make_shape(inp.layout, inp.batch, inp.seq_len, inp.n_qk, inp.n_v, inp.scale,
+                      inp.qk_l2norm, inp.beta_sigmoid, d, d, inp.scalar_gate)
+
+
 def seg_p_of(inp) -> int:
-    """Segments per sequence chosen by the library's plan (kda_plan.cpp) for this shape."""
-    bh = inp.batch * inp.n_v
-    tiles = head_dim(inp) // 16
-    if bh * tiles >= 256:
-        return 1
-    nc = -(-inp.seq_len // 64) if inp.layout != "TND" else -(-(inp.seq_len // inp.batch) // 64)
-    sp = min((256 // (bh * tiles) + 1) // 2, nc // 8, 16)
-    return sp if sp >= 2 else 1
+    """Segments per sequence of the library's plan for this shape (kda_chunk_fwd_plan)."""
+    from kimi_delta_attention_chunk_amd import kda_chunk_fwd_plan
+    return kda_chunk_fwd_plan(shape_of(inp))[1]
 
 
 def record_bytes(d: int) -> int:
@@ -221,7 +223,8 @@ def main() -> int:
         print(json.dumps({"copy_bytes": n, "ms": dt * 1e3, "GB/s (read+write)": 2 * n / dt / 1e9}))
         return 0
     from kimi_delta_attention_chunk_amd import (chunk_fwd, kda_chunk_fwd_workspace,
-                                                kda_num_stages, kda_stage_name, make_shape)
+                                                kda_num_stages, kda_stage_name, make_shape,
+                                                kda_chunk_fwd_plan)
     from kimi_delta_attention_chunk_amd.workloads import workload_inputs, BY_NAME
 
     wl = BY_NAME[args.workload]
@@ -268,7 +271,11 @@ def main() -> int:
     ms_step = (t1 - t0) * 1e3 / args.steps
     stage_ms = [sum(events[i][2 * s].elapsed_time(events[i][2 * s + 1]) for i in range(args.steps))
                 / args.steps for s in range(nst)]
-    dom = max(range(nst), key=lambda s: stage_ms[s])
+    # stages the plan enqueues (an empty stage's two back-to-back events measure only the
+    # marker packets between them)
+    mask, segments = kda_chunk_fwd_plan(shape)
+    live = [s for s in range(nst) if mask >> s & 1]
+    dom = max(live, key=lambda s: stage_ms[s])
     kbytes = [KERNEL_BYTES[kda_stage_name(s)](host) for s in range(nst)]
     achieved = kbytes[dom] / (stage_ms[dom] * 1e-3)
     pbytes = path_bytes(host)
@@ -292,7 +299,8 @@ def main() -> int:
         "path_roofline": {"bound": "hbm", "algorithmic_bytes": pbytes,
                           "achieved": pbytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
                           "frac": pbytes / (ms_step * 1e-3) / HBM_PEAK},
-        "stages_ms": {kda_stage_name(s): stage_ms[s] for s in range(nst)},
+        "stages_ms": {kda_stage_name(s): stage_ms[s] for s in live},
+        "segments": segments,
         "ms_per_step_with_stage_events": (t3 - t2) * 1e3 / args.steps,
         "token_heads_per_s": host.tokens * host.n_v / (ms_step * 1e-3),
     }

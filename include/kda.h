@@ -123,6 +123,13 @@ kda_status kda_chunk_fwd(const kda_shape* shape,
 int32_t kda_num_stages(void);
 const char* kda_stage_name(int32_t stage);
 
+/* The plan kda_chunk_fwd follows for `shape`, from the shape alone (nothing is launched):
+ *   stage_mask  bit s set when stage s enqueues a kernel (the others are empty);
+ *   segments    segments per sequence of the two-level scan, 1 for the one-level scan.
+ * Either output pointer may be NULL.  Returns the status kda_chunk_fwd_workspace returns for
+ * the same shape, and leaves the outputs untouched unless it is KDA_OK. */
+kda_status kda_chunk_fwd_plan(const kda_shape* shape, uint32_t* stage_mask, int32_t* segments);
+
 /* Profiling variant of kda_chunk_fwd: identical work.  For each stage s, the kernel's own
  * dispatch records stage_events[2s] when the kernel starts and stage_events[2s+1] when it ends
  * (hipExtLaunchKernel; no marker packet between the kernels), so hipEventElapsedTime of the pair

@@ -7,6 +7,7 @@ from .ops import (  # noqa: F401
     KdaError,
     chunk_fwd,
     kda_chunk_fwd,
+    kda_chunk_fwd_plan,
     kda_chunk_fwd_workspace,
     kda_num_stages,
     kda_stage_name,
@@ -14,5 +15,5 @@ from .ops import (  # noqa: F401
     make_shape,
 )
 
-__all__ = ["KdaError", "chunk_fwd", "kda_chunk_fwd", "kda_chunk_fwd_workspace",
-           "kda_num_stages", "kda_stage_name", "kda_status_str", "make_shape"]
+__all__ = ["KdaError", "chunk_fwd", "kda_chunk_fwd", "kda_chunk_fwd_plan",
+           "kda_chunk_fwd_workspace", "kda_num_stages", "kda_stage_name", "kda_status_str", "make_shape"]

@@ -17,7 +17,8 @@ KDA_SCALAR_GATE = 4
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 
 EXPORTED = ["kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
-            "kda_num_stages", "kda_stage_name", "kda_status_str", "kda_version"]
+            "kda_num_stages", "kda_stage_name", "kda_chunk_fwd_plan", "kda_status_str",
+            "kda_version"]
 
 
 class KdaShape(ctypes.Structure):
@@ -54,6 +55,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_num_stages.restype = ctypes.c_int32
     lib.kda_stage_name.argtypes = [ctypes.c_int32]
     lib.kda_stage_name.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_plan.argtypes = [S, ctypes.POINTER(ctypes.c_uint32),
+                                       ctypes.POINTER(ctypes.c_int32)]
+    lib.kda_chunk_fwd_plan.restype = ctypes.c_int
     lib.kda_status_str.argtypes = [ctypes.c_int]
     lib.kda_status_str.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []

@@ -1549,6 +1549,19 @@ kda_status kda_chunk_fwd_timed(const kda_shape* shape, const void* q, const void
 
 int32_t kda_num_stages(void) { return kda::kStages; }
 
+kda_status kda_chunk_fwd_plan(const kda_shape* shape, uint32_t* stage_mask, int32_t* segments) {
+    kda::Plan plan;
+    const kda_status st = kda::make_plan(shape, &plan);
+    if (st != KDA_OK) return st;
+    const bool two = plan.seg_p > 1;
+    if (stage_mask)
+        *stage_mask = (1u << kda::ST_INTRA) |
+                      (two ? (1u << kda::ST_SEG) | (1u << kda::ST_COMB) | (1u << kda::ST_OUT)
+                           : (1u << kda::ST_SCAN));
+    if (segments) *segments = plan.seg_p;
+    return KDA_OK;
+}
+
 const char* kda_stage_name(int32_t stage) {
     switch (stage) {
     case kda::ST_INTRA: return "kda_intra_kernel";

@@ -54,6 +54,17 @@ def kda_chunk_fwd_workspace(shape: KdaShape) -> int:
     return int(n.value)
 
 
+def kda_chunk_fwd_plan(shape: KdaShape):
+    """(stage mask, segments per sequence) of the plan for `shape` (kda_chunk_fwd_plan)."""
+    mask = ctypes.c_uint32(0)
+    segs = ctypes.c_int32(0)
+    st = _lib.load().kda_chunk_fwd_plan(ctypes.byref(shape), ctypes.byref(mask),
+                                        ctypes.byref(segs))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_fwd_plan")
+    return int(mask.value), int(segs.value)
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 

@@ -87,6 +87,32 @@ def test_workspace_sizes(lib):
     assert n5 < 128 * 6 * rec64 + two64 + 16 * 256
 
 
+def plan(lib, shape):
+    mask, segs = ctypes.c_uint32(99), ctypes.c_int32(99)
+    st = lib.kda_chunk_fwd_plan(ctypes.byref(shape), ctypes.byref(mask), ctypes.byref(segs))
+    return st, mask.value, segs.value
+
+
+def test_plan_query(lib):
+    """Stage mask and segment count: the two-level scan when few chains would idle the GPU."""
+    two = 0b01111    # intra, segment pass, combine, completion
+    one = 0b10001    # intra, one-level scan
+    # 3 heads x 8 tiles: (2P - 1) x 24 <= 256 -> P = 5
+    assert plan(lib, make_shape("BNSD", 1, 8192, 3, 3, 0.088)) == (0, two, 5)
+    # head dim 64: 6 heads x 4 tiles -> P = 5
+    assert plan(lib, make_shape("BNSD", 1, 8192, 6, 6, 0.125, d_k=64, d_v=64)) == (0, two, 5)
+    # 32 heads fill 256 workgroups: one level
+    assert plan(lib, make_shape("BNSD", 1, 131072, 32, 32, 0.088)) == (0, one, 1)
+    # 4 chunks cannot be cut into segments of at least 8 chunks
+    assert plan(lib, make_shape("BNSD", 1, 256, 1, 1, 0.088)) == (0, one, 1)
+    # 41 chunks of one head: 256 / 8 tiles -> 16, capped by 41 / 8
+    assert plan(lib, make_shape("BNSD", 1, 64 * 40 + 9, 1, 1, 0.088)) == (0, two, 5)
+    # an invalid shape: the workspace query's status, outputs untouched
+    assert plan(lib, make_shape("BNSD", 1, 8192, 3, 3, 0.088, d_k=256, d_v=256)) == (2, 99, 99)
+    assert lib.kda_chunk_fwd_plan(ctypes.byref(make_shape("BNSD", 1, 8192, 3, 3, 0.088)),
+                                  None, None) == 0
+
+
 @pytest.mark.parametrize("bad, code", [
     (dict(layout=7), 1), (dict(batch=0), 1), (dict(seq_len=0), 1), (dict(n_qk=0), 1),
     (dict(n_qk=4, n_v=2), 1), (dict(n_qk=3, n_v=4), 1), (dict(d_k=64), 2), (dict(d_v=256), 2),
