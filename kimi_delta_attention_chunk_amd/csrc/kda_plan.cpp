@@ -93,6 +93,10 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
         p.out_blocks = p.n_records;
     } else {
         p.scan_blocks = bh8 * p.scan_tiles;
+        // a prefetch wave costs the second workgroup per compute unit: only when one per unit
+        // is all there is, and not for the four-tile form (its registers would not fit two
+        // waves per SIMD)
+        p.scan_pf = bh * p.scan_tiles <= 256 && p.scan_nt <= 2;
     }
     const int64_t max_grid = std::numeric_limits<int32_t>::max();
     if (p.intra_blocks > max_grid || p.scan_blocks > max_grid || p.seg_blocks > max_grid ||

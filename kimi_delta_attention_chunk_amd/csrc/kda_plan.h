@@ -40,7 +40,9 @@ struct Plan {
     int64_t intra_blocks = 0;  // one workgroup per record
     int64_t scan_blocks = 0;   // one workgroup per (sequence, value head, Dv tile), XCD padded
     int scan_nt = 1;           // 16-row Dv tiles per scan workgroup (1, 2 or 4)
-    int scan_tiles = 0;        // scan workgroups per (sequence, head, segment) = (d/16) / scan_nt
+    int scan_tiles = 0;        // scan workgroups per (sequence, head) = (d/16) / scan_nt
+    bool scan_pf = false;      // one-level scan with a record prefetch wave (<= 256 workgroups,
+                               // scan_nt <= 2)
     int seg_p = 1;             // segments per sequence of the two-level scan (1 = one level)
     int64_t seg_blocks = 0;    // two-level: segment pass, (2 seg_p - 1) d/16 per (sequence, head)
     int64_t comb_blocks = 0;   // two-level: segment combine, d/16 per (sequence, head)
