@@ -791,40 +791,46 @@ struct ChunkFrags {
     bf16x4 o[NT];                                 // O_intra (bf16), token tile w, Dv tile
 };
 
-template <int NT, bool WITH_U, int OUT, int D>
+// PART 1: the operands of a step's first products (W, Q', U, O_intra); PART 2: those of its
+// state update (K_dec, gamma); PART 0: all.
+template <int NT, bool WITH_U, int OUT, int D, int PART = 0>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
                                            int dv_tile0, ChunkFrags<NT, D>& f) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
-    const __bf16* wsrc = p.Wf + size_t(rec) * (64 * D);
-    const __bf16* qsrc = p.Qf + size_t(rec) * (64 * D);
-    const __bf16* ksrc = p.Kf + size_t(rec) * (64 * D * 2);
+    if constexpr (PART != 2) {
+        const __bf16* wsrc = p.Wf + size_t(rec) * (64 * D);
+        const __bf16* qsrc = p.Qf + size_t(rec) * (64 * D);
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * KB + kb) * 64 + lane) * 8);
-        if constexpr (OUT != OUT_NONE)
-            f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * KB + kb) * 64 + lane) * 8);
-    }
-#pragma unroll
-    for (int mt = 0; mt < MW; ++mt)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int off = (((MW * w + mt) * 2 + s) * 64 + lane) * 8;
-            f.kh[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + off);
-            f.kl[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + 64 * D + off);
+        for (int kb = 0; kb < KB; ++kb) {
+            f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * KB + kb) * 64 + lane) * 8);
+            if constexpr (OUT != OUT_NONE)
+                f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * KB + kb) * 64 + lane) * 8);
         }
-    const float* gsrc = p.Gf + size_t(rec) * D;
+        const float* usrc = p.Uf + size_t(rec) * (64 * D);
+        const __bf16* osrc = p.Of + size_t(rec) * (64 * D);
 #pragma unroll
-    for (int mt = 0; mt < MW; ++mt)
-        f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (MW * w + mt) + 4 * (lane >> 4));
-    const float* usrc = p.Uf + size_t(rec) * (64 * D);
-    const __bf16* osrc = p.Of + size_t(rec) * (64 * D);
+        for (int nt = 0; nt < NT; ++nt) {
+            const int dt = dv_tile0 + nt;
+            if constexpr (WITH_U)
+                f.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
+            if constexpr (OUT == OUT_FINAL || OUT == OUT_O0)
+                f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
+        }
+    }
+    if constexpr (PART != 1) {
+        const __bf16* ksrc = p.Kf + size_t(rec) * (64 * D * 2);
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-        const int dt = dv_tile0 + nt;
-        if constexpr (WITH_U)
-            f.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
-        if constexpr (OUT == OUT_FINAL || OUT == OUT_O0)
-            f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
+        for (int mt = 0; mt < MW; ++mt)
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int off = (((MW * w + mt) * 2 + s) * 64 + lane) * 8;
+                f.kh[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + off);
+                f.kl[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + 64 * D + off);
+            }
+        const float* gsrc = p.Gf + size_t(rec) * D;
+#pragma unroll
+        for (int mt = 0; mt < MW; ++mt)
+            f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (MW * w + mt) + 4 * (lane >> 4));
     }
 }
 
@@ -850,8 +856,13 @@ struct ScanLds {
 //   X = W S^T and (with outputs) Y^T = S Q'^T for token tile w; V_new = U - X (U = 0 for the
 //   transfer-matrix pass); out = Y + O_intra (or R = Y); S^T <- gamma * S^T + K_dec^T V_new
 //   for this wave's D/4 Dk rows.  `rec` is the chunk's record (workspace outputs).
-template <int NT, bool WITH_U, int OUT, int D>
+//   With SPLIT the next chunk's operands (record rec_nxt) load into `nxt` here, in two parts,
+//   each issued after the products it must not delay (a wave that issues a burst of loads
+//   waits at issue while the compute unit's address unit takes them); without it the caller
+//   has issued them all before the step.  Which is faster depends on the kernel (measured).
+template <int NT, bool WITH_U, int OUT, int D, bool SPLIT>
 __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, D>& cur,
+                                          ChunkFrags<NT, D>& nxt, int64_t rec_nxt,
                                           f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L, int jc,
                                           int len, size_t ob, size_t os, int dv_tile0,
                                           int64_t rec) {
@@ -879,6 +890,11 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
             if constexpr (OUT != OUT_NONE) accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
             if constexpr (OUT == OUT_R) accY[nt] = mfma(sl, cur.qp[kb], accY[nt]);
         }
+    }
+    if constexpr (SPLIT) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk<NT, WITH_U, OUT, D, 1>(p, rec_nxt, w, lane, dv_tile0, nxt);
+        __builtin_amdgcn_sched_barrier(0);
     }
     const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
 #pragma unroll
@@ -947,6 +963,10 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
             put_state<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, acc);
         }
     }
+    if constexpr (SPLIT) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_chunk<NT, WITH_U, OUT, D, 2>(p, rec_nxt, w, lane, dv_tile0, nxt);
+    }
     lds_barrier();
 }
 
@@ -954,7 +974,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
 // The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
 // record, never used): with the same number of loads in flight on every path, the compiler's
 // wait counts let each step wait only for its own operands, not for the next chunk's.
-template <int NT, bool WITH_U, int OUT, int D>
+template <int NT, bool WITH_U, int OUT, int D, bool SPLIT>
 __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW][NT],
                                            const ScanLds& L,
                                            int64_t rec0, int cb, int ce, int len, size_t ob,
@@ -967,14 +987,17 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
     for (int jc = cb; jc < ce; jc += 2) {
         const int c1 = jc + 1 < last ? jc + 1 : last;
-        load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
-        scan_step<NT, WITH_U, OUT, D>(p, fa, S, L, jc, len, ob, os, dv_tile0,
-                                      rec0 + int64_t(jc) * p.n_v);
+        if constexpr (!SPLIT)
+            load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
+        scan_step<NT, WITH_U, OUT, D, SPLIT>(p, fa, fb, rec0 + int64_t(c1) * p.n_v, S, L, jc,
+                                             len, ob, os, dv_tile0, rec0 + int64_t(jc) * p.n_v);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
-        load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
-        scan_step<NT, WITH_U, OUT, D>(p, fb, S, L, jc + 1, len, ob, os, dv_tile0,
-                                      rec0 + int64_t(jc + 1) * p.n_v);
+        if constexpr (!SPLIT)
+            load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
+        scan_step<NT, WITH_U, OUT, D, SPLIT>(p, fb, fa, rec0 + int64_t(c2) * p.n_v, S, L,
+                                             jc + 1, len, ob, os, dv_tile0,
+                                             rec0 + int64_t(jc + 1) * p.n_v);
     }
 }
 
@@ -1256,7 +1279,9 @@ void kda_scan_kernel(Params p) {
         }
     lds_barrier();
 
-    run_chunks<NT, true, OUT_FINAL, D>(p, S, L, rec0, 0, nchunks, len, ob, os, dv_tile0);
+    // split loads measured faster for the wider tiles, slower for the one-tile prefetched form
+    run_chunks<NT, true, OUT_FINAL, D, (NT > 1)>(p, S, L, rec0, 0, nchunks, len, ob, os,
+                                                 dv_tile0);
 
     if (p.fin) {
 #pragma unroll
@@ -1280,6 +1305,7 @@ void kda_scan_kernel(Params p) {
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     constexpr int MW = HD<D>::MW, TILES = HD<D>::TILES;
+    constexpr bool SEG_SPLIT = D == 128;   // split loads: faster at D = 128, slower at 64 (measured)
     __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[16 * VN_LD];
@@ -1338,7 +1364,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
 
     const size_t m = (size_t(bh) * p.seg_p + seg) * D * D;
     if (is_p) {
-        run_chunks<1, false, OUT_R, D>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+        run_chunks<1, false, OUT_R, D, SEG_SPLIT>(p, S, L, rec0, cb, ce, len, ob, os, tile);
         // rows 16 tile .. of P_s, split, into the combine's A fragments of P_s^T: element
         // P_s[16 tile + n16][16 M + 4 q4 + i] is lane (2 (tile & 1) + (n16 >> 3), 4 q4 + i),
         // entry n16 & 7, of fragment (M, tile >> 1)
@@ -1354,9 +1380,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
             }
     } else {
         if (seg == 0)
-            run_chunks<1, true, OUT_FINAL, D>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+            run_chunks<1, true, OUT_FINAL, D, SEG_SPLIT>(p, S, L, rec0, cb, ce, len, ob, os, tile);
         else
-            run_chunks<1, true, OUT_O0, D>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+            run_chunks<1, true, OUT_O0, D, SEG_SPLIT>(p, S, L, rec0, cb, ce, len, ob, os, tile);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
             *reinterpret_cast<f32x4*>(p.Nst + m + ((tile * TILES + MW * w + mt) * 64 + lane) * 4) =
