@@ -1318,20 +1318,34 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
-    // XCD-aware decode.  Units of D/16 workgroups: per (sequence, head) the zero-start walk of
-    // segment 0, then for s >= 1 the zero-start and the identity walks of segment s (2 seg_p - 1
-    // units).  Unit u runs on XCD u mod 8, so its workgroups share that XCD's L2 for the records
-    // they all read, and the XCDs receive equal numbers of units.
+    // XCD-aware decode.  Both walks of a segment s >= 1 (2 D/16 workgroups, a "pair") run on
+    // one XCD, so the segment's records are fetched into one L2 once; pair q = bh (seg_p - 1) +
+    // s - 1 goes to XCD q mod 8.  The zero-start walks of segment 0 (D/16 workgroups, a
+    // "single" per (sequence, head)) follow round-robin from the XCD after the last pair, so
+    // that the XCDs receive nearly equal numbers of workgroups.
     const int pid = blockIdx.x;
     const int xcd = pid & 7, r8 = pid >> 3;
-    const int unit = (r8 / TILES) * 8 + xcd;
-    const int tile = r8 % TILES;
-    const int per_bh = 2 * p.seg_p - 1;
-    if (unit >= p.batch * p.n_v * per_bh) return;
-    const int bh = unit / per_bh;
-    const int k = unit % per_bh;
-    const bool is_p = k > 0 && (k & 1) == 0;
-    const int seg = (k + 1) >> 1;
+    const int n_bh = p.batch * p.n_v;
+    const int np = n_bh * (p.seg_p - 1);           // pairs
+    const int npx = (np + 7 - xcd) / 8;            // pairs on this XCD
+    int bh, seg, tile;
+    bool is_p;
+    if (r8 < npx * 2 * TILES) {
+        const int q = (r8 / (2 * TILES)) * 8 + xcd;
+        const int slot = r8 % (2 * TILES);
+        bh = q / (p.seg_p - 1);
+        seg = q % (p.seg_p - 1) + 1;
+        is_p = slot >= TILES;
+        tile = slot % TILES;
+    } else {
+        const int r = r8 - npx * 2 * TILES;
+        const int q = (xcd - np % 8 + 8) % 8 + 8 * (r / TILES);   // single q runs on XCD (np + q) mod 8
+        if (q >= n_bh) return;
+        bh = q;
+        seg = 0;
+        is_p = false;
+        tile = r % TILES;
+    }
     const int b = bh / p.n_v;
     const int h = bh % p.n_v;
 

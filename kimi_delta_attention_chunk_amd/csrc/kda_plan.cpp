@@ -88,7 +88,18 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     const int64_t bh8 = (bh + 7) / 8 * 8;
     if (p.seg_p > 1) {
         p.scan_blocks = 0;
-        p.seg_blocks = ((bh * (2 * p.seg_p - 1) + 7) / 8) * 8 * tiles;
+        // per XCD x: its pairs ((np + 7 - x) / 8, 2 tiles workgroups each), then its singles
+        // (segment 0 of sequence-head q runs on XCD (np + q) mod 8, tiles workgroups each)
+        const int64_t np = bh * (p.seg_p - 1);
+        int64_t rows = 0;
+        for (int x = 0; x < 8; ++x) {
+            const int64_t npx = (np + 7 - x) / 8;
+            const int64_t q0 = (x - np % 8 + 8) % 8;   // first single on XCD x
+            const int64_t nsx = q0 < bh ? (bh - q0 + 7) / 8 : 0;
+            const int64_t r = npx * 2 * tiles + nsx * tiles;
+            rows = r > rows ? r : rows;
+        }
+        p.seg_blocks = rows * 8;
         p.comb_blocks = bh8 * tiles;
         p.out_blocks = p.n_records;
     } else {
