@@ -159,6 +159,11 @@ TWO_LEVEL = [
                           init=True, seed=33, lengths=[2100, 700])),
     ("bsnd_gqa", dict(layout="BSND", batch=1, seq_len=1600, n_qk=1, n_v=2, g_kind="mixed",
                       init=False, seed=34)),
+    # the most segments (16: one head, 128 chunks) and two heads (8 segments)
+    ("bnsd_1head_16seg", dict(layout="BNSD", batch=1, seq_len=8192, n_qk=1, n_v=1,
+                              g_kind="strong", init=True, seed=35)),
+    ("bnsd_2head_8seg", dict(layout="BNSD", batch=1, seq_len=4096 + 30, n_qk=2, n_v=2,
+                             g_kind="small", init=True, seed=36)),
 ]
 
 
