@@ -87,8 +87,8 @@ typedef struct {
 
 /* Bytes of device workspace kda_chunk_fwd needs for `shape` (FlashKDA README, section 功能说明:
  * the per-chunk intermediates of the chunk equations, W, U, the q-side operand, the decayed
- * keys and the intra-chunk output, live here between the two kernels).  Depends only on the
- * shape.  Returns KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED for shapes kda_chunk_fwd rejects. */
+ * keys and the intra-chunk output, live here between the kernels of one call, with the
+ * two-level scan's segment matrices and partial outputs).  Depends only on the shape.  Returns KDA_ERR_INVALID_ARG / KDA_ERR_UNSUPPORTED for shapes kda_chunk_fwd rejects. */
 kda_status kda_chunk_fwd_workspace(const kda_shape* shape, size_t* bytes);
 
 /* The chunked forward (prefill) of KDA.  Semantics: see the top of this file.

@@ -10,15 +10,19 @@
 // h and v_new and an output kernel o = q h + A v_new):
 //     V_new = U - W S^T,   O = Qt S^T + Aqk V_new,   Aqk = lower-with-diagonal(Qt Kb^T),
 //     S <- S diag(exp(G_last)) + V_new^T (K * exp(G_last - G)).
-// Two kernels:
+// Kernels:
 //   kda_intra_kernel  one workgroup per (64-token chunk, value head), fully parallel.  Computes
 //                     the log2-space running gate sum, the decayed operands, T and Aqk on bf16
 //                     MFMA, the fp32 blocked inverse, W and U, and folds the chunk-local terms:
 //                     Q' = Qt - Aqk W and O_intra = Aqk U, so that O = Q' S^T + O_intra.
 //                     Writes W, Q', K_dec, U, O_intra and gamma_last in MFMA fragment order.
-//   kda_scan_kernel   one workgroup per (sequence, value head, 16-row Dv tile) walks the chunks
-//                     in order with its state tile resident in registers:
+//   kda_scan_kernel   one workgroup per (sequence, value head, Dv tiles) walks the chunks in
+//                     order with its state tiles resident in registers:
 //                     V_new = U - W S^T, O = Q' S^T + O_intra, S <- gamma*S + K_dec^T V_new.
+//   When few (sequence, head) chains would leave most compute units idle, the two-level scan
+//   replaces kda_scan_kernel: kda_seg_kernel walks every segment of a sequence at once (from a
+//   zero state and from identity rows), kda_combine_kernel chains the segment entry states, and
+//   kda_out_kernel completes the outputs of every segment after the first in parallel.
 //
 // Overflow safety (vLLM #43195 summary, 实现拆解 / 关键源码片段: gates kept in log2 space and
 // every decay an exp2 of a difference; flash-linear-attention PR #656: 16-token sub-blocks).
