@@ -258,6 +258,26 @@ def test_run_to_run_determinism():
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
+def test_concurrent_streams_bitwise():
+    """Calls on two streams at once, each with its own workspace (the library keeps no state),
+    give the results of the same calls made one after the other: a two-level call beside a
+    one-level call, three rounds."""
+    a = make_inputs("BNSD", 1, 64 * 40 + 9, 1, 2, g_kind="strong", init=True, seed=28).to("cuda")
+    b = make_inputs("BSND", 2, 300, 2, 4, g_kind="unit", init=False, seed=29).to("cuda")
+    oa, fa = chunk_fwd(a)
+    ob, fb = chunk_fwd(b)
+    torch.cuda.synchronize()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            oa2, fa2 = chunk_fwd(a)
+        with torch.cuda.stream(s2):
+            ob2, fb2 = chunk_fwd(b)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, oa2) and torch.equal(fa, fa2)
+        assert torch.equal(ob, ob2) and torch.equal(fb, fb2)
+
+
 def test_resume_split():
     full = make_inputs("BNSD", 1, 300, 1, 2, g_kind="strong", init=True, seed=25)
     o, f = run_gpu(full)
