@@ -102,8 +102,8 @@ def intra_bytes(inp) -> int:
 
 def seg_bytes(inp) -> int:
     """Compulsory bytes of the segment pass: every record, the initial states, the final
-    outputs of segment 0 (bf16), O0 and R of the later segments' chunks (fp32), and the N and
-    P matrices of every segment."""
+    outputs of segment 0, O0 and R of the later segments' chunks (all bf16), and the N and P
+    matrices of every segment."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
@@ -112,7 +112,7 @@ def seg_bytes(inp) -> int:
     states = inp.batch * inp.n_v * d * d * 4
     mats = inp.batch * inp.n_v * sp * 2 * d * d * 4
     return (inp.n_v * ((first + later) * record_bytes(d) + first * 64 * d * 2
-                       + later * 64 * d * 4 * 2)
+                       + later * 64 * d * 2 * 2)
             + states * (inp.initial_state is not None) + mats)
 
 
@@ -128,14 +128,14 @@ def combine_bytes(inp) -> int:
 
 
 def out_bytes(inp) -> int:
-    """Compulsory bytes of the completion pass: O0 and R (fp32) of every chunk of segments
+    """Compulsory bytes of the completion pass: O0 and R (bf16) of every chunk of segments
     1.. and S_in of those segments in, the outputs (bf16) out."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     _, later = chunk_counts(inp, sp)
-    return inp.n_v * later * 64 * d * (4 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 4
+    return inp.n_v * later * 64 * d * (2 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 4
 
 
 KERNEL_BYTES = {"kda_intra_kernel": intra_bytes, "kda_seg_kernel": seg_bytes,

@@ -66,8 +66,8 @@ struct Params {
     __bf16* Pt;   // [hi/lo][M 8][kb 4][lane 64][8]  P_s[32kb+8q+j][16M+m]      transfer matrix
     float* Nst;   // [t 8][M 8][lane 64][4]          N_s[16t+m][16M+4q+i]       zero-start end state
     __bf16* Sin;  // [hi/lo][t 8][kb 4][lane 64][8]  S_in[16t+m][32kb+8q+j]     entry state
-    float* O0;    // [t 8][tt 4][lane 64][4]         O0[16tt+m][16t+4q+i]       zero-start outputs
-    __bf16* Rf;   // [hi/lo][tt 4][kb 4][lane 64][8] R[16tt+m][32kb+8q+j]       R = Q' P^T
+    __bf16* O0;   // [t 8][tt 4][lane 64][4]         O0[16tt+m][16t+4q+i]       zero-start outputs
+    __bf16* Rf;   // [tt 4][kb 4][lane 64][8]        R[16tt+m][32kb+8q+j]       R = Q' P^T
     int layout, batch, seq_len, n_qk, n_v, group, nc_max;
     int scan_tiles;
     int seg_p;     // segments per sequence of the two-level scan (1 = one level)
@@ -781,7 +781,7 @@ constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = va
 enum OutMode {
     OUT_NONE = 0,    // nothing (segment end state and transfer matrix only)
     OUT_FINAL = 1,   // out = Q' S^T + O_intra in bf16, valid tokens only
-    OUT_O0 = 2,      // O0 = Q' S^T + O_intra in fp32, workspace (state from a zero start)
+    OUT_O0 = 2,      // O0 = Q' S^T + O_intra in bf16, workspace (state from a zero start)
     OUT_R = 3,       // R = Q' S^T in fp32, workspace (state rows of the transfer matrix)
 };
 
@@ -925,20 +925,20 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
             // tail are zero: their q and every Aqk entry are)
             const int t = dv_tile0 + nt;
             f32x4 y = accY[nt];
+            // both in bf16: each adds one bf16 rounding to an output that is itself rounded
+            // to bf16, against the fp32 sums of the completion pass
+            bf16x4 yb;
             if constexpr (OUT == OUT_O0) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) y[r] += (float)cur.o[nt][r];
-                *reinterpret_cast<f32x4*>(p.O0 + size_t(rec) * (64 * D) +
-                                          ((t * 4 + w) * 64 + lane) * 4) = y;
-            } else {   // R as a hi/lo pair in the completion pass's B-operand order
-                bf16x4 yh, yl;
+                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(y[r] + (float)cur.o[nt][r]);
+                *reinterpret_cast<bf16x4*>(p.O0 + size_t(rec) * (64 * D) +
+                                           ((t * 4 + w) * 64 + lane) * 4) = yb;
+            } else {   // R in the completion pass's B-operand order
 #pragma unroll
-                for (int r = 0; r < 4; ++r) SPLIT_BF16(y[r], yh[r], yl[r]);
+                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)y[r];
                 const int lb = (2 * (t & 1) + (q4 >> 1)) * 16 + n16;
-                __bf16* dst = p.Rf + size_t(rec) * (2 * 64 * D) +
-                              ((w * KB + (t >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1);
-                *reinterpret_cast<bf16x4*>(dst) = yh;
-                *reinterpret_cast<bf16x4*>(dst + 64 * D) = yl;
+                *reinterpret_cast<bf16x4*>(p.Rf + size_t(rec) * (64 * D) +
+                                           ((w * KB + (t >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1)) = yb;
             }
         }
     }
@@ -1507,14 +1507,14 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
 }
 
 // Completion pass of the two-level scan: one workgroup per record of a chunk in segment
-// s >= 1, out = O0 + R S_in(s)^T with three-term hi/lo products (as O^T = S_in R^T: the
-// accumulator holds four consecutive value channels of one token per lane).  Wave w takes Dv
+// s >= 1, out = O0 + R S_in(s)^T with S_in as a hi/lo pair and R and O0 in bf16 (as
+// O^T = S_in R^T: the accumulator holds four consecutive value channels of one token per lane).  Wave w takes Dv
 // tiles D/64 w .. of all 64 tokens.  R, which every wave multiplies, is read from HBM once into
 // LDS; every operand is loaded before the first output is stored.
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     constexpr int KB = HD<D>::KB, NTW = D / 64;
-    constexpr int R_U4 = 2 * 64 * D * 2 / 16;   // R hi/lo in 16-byte units
+    constexpr int R_U4 = 64 * D * 2 / 16;   // R in 16-byte units
     __shared__ __attribute__((aligned(16))) bf16x8 sR[R_U4];
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1537,11 +1537,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     row_geom(p, b, h, p.n_v, D, c0, ob, os);
 
     const __bf16* sin = p.Sin + 2 * ((size_t(b) * p.n_v + h) * p.seg_p + seg) * D * D;
-    const float* o0 = p.O0 + size_t(rec) * (64 * D);
-    const __bf16* rr = p.Rf + size_t(rec) * (2 * 64 * D);
+    const __bf16* o0 = p.O0 + size_t(rec) * (64 * D);
+    const __bf16* rr = p.Rf + size_t(rec) * (64 * D);
 
     bf16x8 ah[NTW][KB], al[NTW][KB];   // S_in[16 nt + n16][32 kb + 8 q4 ..]
-    f32x4 acc[4][NTW];                 // O0[16 tt + n16][16 nt + 4 q4 ..]
+    bf16x4 ob4[4][NTW];                // O0[16 tt + n16][16 nt + 4 q4 ..]
     {
         bf16x8 x[R_U4 / kThreads];
 #pragma unroll
@@ -1562,19 +1562,24 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int i = 0; i < NTW; ++i)
-            acc[tt][i] = *reinterpret_cast<const f32x4*>(o0 + (((NTW * w + i) * 4 + tt) * 64 + lane) * 4);
+            ob4[tt][i] = *reinterpret_cast<const bf16x4*>(o0 + (((NTW * w + i) * 4 + tt) * 64 + lane) * 4);
     __syncthreads();
+    f32x4 acc[4][NTW];
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int i = 0; i < NTW; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[tt][i][r] = (float)ob4[tt][i][r];
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8 bh = sR[(tt * KB + kb) * 64 + lane];            // R[16 tt + n16][32 kb + 8 q4 ..]
-            const bf16x8 bl = sR[R_U4 / 2 + (tt * KB + kb) * 64 + lane];
+            const bf16x8 br = sR[(tt * KB + kb) * 64 + lane];   // R[16 tt + n16][32 kb + 8 q4 ..]
 #pragma unroll
             for (int i = 0; i < NTW; ++i) {
-                acc[tt][i] = mfma(ah[i][kb], bh, acc[tt][i]);
-                acc[tt][i] = mfma(al[i][kb], bh, acc[tt][i]);
-                acc[tt][i] = mfma(ah[i][kb], bl, acc[tt][i]);
+                acc[tt][i] = mfma(ah[i][kb], br, acc[tt][i]);
+                acc[tt][i] = mfma(al[i][kb], br, acc[tt][i]);
             }
         }
 #pragma unroll
@@ -1647,7 +1652,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.Pt = two ? reinterpret_cast<__bf16*>(ws + plan.off_pt) : nullptr;
     p.Nst = two ? reinterpret_cast<float*>(ws + plan.off_n) : nullptr;
     p.Sin = two ? reinterpret_cast<__bf16*>(ws + plan.off_sin) : nullptr;
-    p.O0 = two ? reinterpret_cast<float*>(ws + plan.off_o0) : nullptr;
+    p.O0 = two ? reinterpret_cast<__bf16*>(ws + plan.off_o0) : nullptr;
     p.Rf = two ? reinterpret_cast<__bf16*>(ws + plan.off_r) : nullptr;
     p.scale = shape->scale;
     p.flags = shape->flags;

@@ -130,7 +130,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     p.off_g = off; off = align_up(off + n * rec_g_bytes(d), 256);
     if (p.seg_p > 1) {
         const size_t mats = size_t(bh) * p.seg_p * d * d * sizeof(float);
-        const size_t rows = n * kChunk * d * sizeof(float);
+        const size_t rows = n * kChunk * d * 2;   // bf16
         p.off_pt = off; off = align_up(off + mats, 256);
         p.off_n = off; off = align_up(off + mats, 256);
         p.off_sin = off; off = align_up(off + mats, 256);
