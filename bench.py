@@ -117,25 +117,25 @@ def seg_bytes(inp) -> int:
 
 
 def combine_bytes(inp) -> int:
-    """Compulsory bytes of the combine pass: N and P of every segment in, S_in of segments
-    1.. and the final state out."""
+    """Compulsory bytes of the combine pass: N and P of every segment in (4 bytes a value),
+    S_in of segments 1.. (bf16) and the final state (fp32) out."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     m = inp.batch * inp.n_v * d * d * 4
-    return m * (2 * sp - 1) + m * (sp - 1) + m
+    return m * (2 * sp - 1) + m // 2 * (sp - 1) + m
 
 
 def out_bytes(inp) -> int:
-    """Compulsory bytes of the completion pass: O0 and R (bf16) of every chunk of segments
-    1.. and S_in of those segments in, the outputs (bf16) out."""
+    """Compulsory bytes of the completion pass: O0 and R of every chunk of segments 1.. and
+    S_in of those segments in, the outputs out (all bf16)."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     _, later = chunk_counts(inp, sp)
-    return inp.n_v * later * 64 * d * (2 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 4
+    return inp.n_v * later * 64 * d * (2 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 2
 
 
 KERNEL_BYTES = {"kda_intra_kernel": intra_bytes, "kda_seg_kernel": seg_bytes,

@@ -65,7 +65,7 @@ struct Params {
     // two-level scan, per (sequence*head, segment) and per record, in MFMA fragment order:
     __bf16* Pt;   // [hi/lo][M 8][kb 4][lane 64][8]  P_s[32kb+8q+j][16M+m]      transfer matrix
     float* Nst;   // [t 8][M 8][lane 64][4]          N_s[16t+m][16M+4q+i]       zero-start end state
-    __bf16* Sin;  // [hi/lo][t 8][kb 4][lane 64][8]  S_in[16t+m][32kb+8q+j]     entry state
+    __bf16* Sin;  // [t 8][kb 4][lane 64][8]         S_in[16t+m][32kb+8q+j]     entry state
     __bf16* O0;   // [t 8][tt 4][lane 64][4]         O0[16tt+m][16t+4q+i]       zero-start outputs
     __bf16* Rf;   // [tt 4][kb 4][lane 64][8]        R[16tt+m][32kb+8q+j]       R = Q' P^T
     int layout, batch, seq_len, n_qk, n_v, group, nc_max;
@@ -1450,21 +1450,17 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
         put_state<D>(sSh, sSl, n16, 16 * (MW * w + mt) + 4 * q4, S[mt][0]);
     lds_barrier();
 
-    // S_in(s) as the completion pass's A fragments (hi/lo): element S[16 tile + n16][16 M +
+    // S_in(s) in bf16 as the completion pass's A fragments: element S[16 tile + n16][16 M +
     // 4 q4 + i] is lane (2 (M & 1) + (q4 >> 1), n16), entries 4 (q4 & 1) + i, of fragment
-    // (tile, M >> 1)
+    // (tile, M >> 1).  (The chain itself keeps S in fp32.)
     auto store_in = [&](int s) {
-        __bf16* dst = p.Sin + 2 * mat(s);
+        __bf16* dst = p.Sin + mat(s);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt) {
             const int M = MW * w + mt;
-            bf16x4 hh, ll;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) SPLIT_BF16(S[mt][0][i], hh[i], ll[i]);
             const int lb = (2 * (M & 1) + (q4 >> 1)) * 16 + n16;
             const int off = ((tile * KB + (M >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1);
-            *reinterpret_cast<bf16x4*>(dst + off) = hh;
-            *reinterpret_cast<bf16x4*>(dst + D * D + off) = ll;
+            *reinterpret_cast<bf16x4*>(dst + off) = to_bf16x4(S[mt][0]);
         }
     };
     int s = 1;
@@ -1507,8 +1503,8 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
 }
 
 // Completion pass of the two-level scan: one workgroup per record of a chunk in segment
-// s >= 1, out = O0 + R S_in(s)^T with S_in as a hi/lo pair and R and O0 in bf16 (as
-// O^T = S_in R^T: the accumulator holds four consecutive value channels of one token per lane).  Wave w takes Dv
+// s >= 1, out = O0 + R S_in(s)^T from bf16 S_in, R and O0 with fp32 sums (as O^T = S_in R^T:
+// the accumulator holds four consecutive value channels of one token per lane).  Wave w takes Dv
 // tiles D/64 w .. of all 64 tokens.  R, which every wave multiplies, is read from HBM once into
 // LDS; every operand is loaded before the first output is stored.
 template <int D>
@@ -1536,11 +1532,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     size_t ob, os;
     row_geom(p, b, h, p.n_v, D, c0, ob, os);
 
-    const __bf16* sin = p.Sin + 2 * ((size_t(b) * p.n_v + h) * p.seg_p + seg) * D * D;
+    const __bf16* sin = p.Sin + ((size_t(b) * p.n_v + h) * p.seg_p + seg) * D * D;
     const __bf16* o0 = p.O0 + size_t(rec) * (64 * D);
     const __bf16* rr = p.Rf + size_t(rec) * (64 * D);
 
-    bf16x8 ah[NTW][KB], al[NTW][KB];   // S_in[16 nt + n16][32 kb + 8 q4 ..]
+    bf16x8 ah[NTW][KB];                // S_in[16 nt + n16][32 kb + 8 q4 ..]
     bf16x4 ob4[4][NTW];                // O0[16 tt + n16][16 nt + 4 q4 ..]
     {
         bf16x8 x[R_U4 / kThreads];
@@ -1554,9 +1550,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     for (int i = 0; i < NTW; ++i)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const __bf16* src = sin + (((NTW * w + i) * KB + kb) * 64 + lane) * 8;
-            ah[i][kb] = *reinterpret_cast<const bf16x8*>(src);
-            al[i][kb] = *reinterpret_cast<const bf16x8*>(src + D * D);
+            ah[i][kb] = *reinterpret_cast<const bf16x8*>(
+                sin + (((NTW * w + i) * KB + kb) * 64 + lane) * 8);
         }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -1577,10 +1572,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
         for (int kb = 0; kb < KB; ++kb) {
             const bf16x8 br = sR[(tt * KB + kb) * 64 + lane];   // R[16 tt + n16][32 kb + 8 q4 ..]
 #pragma unroll
-            for (int i = 0; i < NTW; ++i) {
-                acc[tt][i] = mfma(ah[i][kb], br, acc[tt][i]);
-                acc[tt][i] = mfma(al[i][kb], br, acc[tt][i]);
-            }
+            for (int i = 0; i < NTW; ++i) acc[tt][i] = mfma(ah[i][kb], br, acc[tt][i]);
         }
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {

@@ -133,7 +133,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
         const size_t rows = n * kChunk * d * 2;   // bf16
         p.off_pt = off; off = align_up(off + mats, 256);
         p.off_n = off; off = align_up(off + mats, 256);
-        p.off_sin = off; off = align_up(off + mats, 256);
+        p.off_sin = off; off = align_up(off + mats / 2, 256);   // bf16
         p.off_o0 = off; off = align_up(off + rows, 256);
         p.off_r = off; off = align_up(off + rows, 256);
     }

@@ -49,8 +49,9 @@ struct Plan {
     int64_t out_blocks = 0;    // two-level: output completion, one per record
     // byte offsets of each workspace array (256-byte aligned)
     size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0;
-    // two-level only: per (sequence, head, segment) transfer matrix P_s (transposed), zero-start
-    // end state N_s and entry state S_in(s), d x d fp32 each; per record the zero-start outputs
+    // two-level only: per (sequence, head, segment) transfer matrix P_s (transposed, hi/lo
+    // bf16) and zero-start end state N_s (fp32), d x d 4-byte values each, and entry state
+    // S_in(s), d x d bf16; per record the zero-start outputs
     // O0 and the propagated queries R = Q' P^T of the segment's chunks, 64 x d bf16 each
     size_t off_pt = 0, off_n = 0, off_sin = 0, off_o0 = 0, off_r = 0;
     size_t total = 0;
