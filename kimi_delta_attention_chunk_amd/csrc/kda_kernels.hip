@@ -790,14 +790,18 @@ struct ChunkFrags {
     bf16x8 w[HD<D>::KB];                          // W, token tile w, 32-channel block kb
     bf16x8 qp[HD<D>::KB];                         // Q', token tile w
     bf16x8 kh[HD<D>::MW][2], kl[HD<D>::MW][2];    // K_dec^T hi/lo, Dk tile MW*w+mt, token step s
-    f32x4 gm[HD<D>::MW];                          // gamma_last for the lane's Dk rows
+    f32x4 gm[HD<D>::MW];                          // gamma_last for the lane's Dk rows, or
+    float g[D / 64];                              // gamma_last[lane D/64 ..] (wave 0, GLDS)
     f32x4 u[NT];                                  // U (fp32), token tile w, Dv tile
     bf16x4 o[NT];                                 // O_intra (bf16), token tile w, Dv tile
 };
 
 // PART 1: the operands of a step's first products (W, Q', U, O_intra); PART 2: those of its
 // state update (K_dec, gamma); PART 0: all.
-template <int NT, bool WITH_U, int OUT, int D, int PART = 0>
+// GLDS: wave 0 loads gamma for the workgroup (one load instead of one per wave and Dk tile) and
+// the step passes it on through LDS.  Taken by the one-tile scan with the record prefetch wave
+// (128K scan 2.54 -> 2.31 ms); slower for the segment pass.
+template <int NT, bool WITH_U, int OUT, int D, int PART = 0, bool GLDS = false>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
                                            int dv_tile0, ChunkFrags<NT, D>& f) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
@@ -831,10 +835,24 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
                 f.kh[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + off);
                 f.kl[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + 64 * D + off);
             }
-        const float* gsrc = p.Gf + size_t(rec) * D;
+        if constexpr (GLDS) {
+            if (w == 0) {
+                const float* gsrc = p.Gf + size_t(rec) * D + lane * (D / 64);
+                if constexpr (D == 128) {
+                    const float2 x = *reinterpret_cast<const float2*>(gsrc);
+                    f.g[0] = x.x;
+                    f.g[D / 64 - 1] = x.y;
+                } else {
+                    f.g[0] = *gsrc;
+                }
+            }
+        } else {
+            const float* gsrc = p.Gf + size_t(rec) * D;
 #pragma unroll
-        for (int mt = 0; mt < MW; ++mt)
-            f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (MW * w + mt) + 4 * (lane >> 4));
+            for (int mt = 0; mt < MW; ++mt)
+                f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (MW * w + mt) +
+                                                           4 * (lane >> 4));
+        }
     }
 }
 
@@ -854,6 +872,7 @@ struct ScanLds {
     __bf16* sl;
     __bf16* vh;
     __bf16* vl;
+    float* g;   // gamma_last of the current chunk [D]
 };
 
 // One chunk of the scan for this workgroup's Dv tile(s):
@@ -864,7 +883,7 @@ struct ScanLds {
 //   each issued after the products it must not delay (a wave that issues a burst of loads
 //   waits at issue while the compute unit's address unit takes them); without it the caller
 //   has issued them all before the step.  Which is faster depends on the kernel (measured).
-template <int NT, bool WITH_U, int OUT, int D, bool SPLIT>
+template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS>
 __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, D>& cur,
                                           ChunkFrags<NT, D>& nxt, int64_t rec_nxt,
                                           f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L, int jc,
@@ -942,6 +961,13 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
             }
         }
     }
+    static_assert(!(GLDS && SPLIT), "gamma through LDS comes with unsplit loads");
+    if constexpr (GLDS) {
+        if (w == 0) {
+#pragma unroll
+            for (int e = 0; e < D / 64; ++e) L.g[lane * (D / 64) + e] = cur.g[e];
+        }
+    }
     lds_barrier();
 
     // S^T <- gamma * S^T + K_dec^T V_new  (Dk rows of this wave x Dv), three-term hi/lo
@@ -956,7 +982,9 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
         }
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt) {
-            f32x4 acc = S[mt][nt] * cur.gm[mt];
+            f32x4 acc = S[mt][nt] * (GLDS ? *reinterpret_cast<const f32x4*>(
+                                                L.g + 16 * (MW * w + mt) + 4 * q4)
+                                          : cur.gm[mt]);
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 acc = mfma(cur.kh[mt][s], vh[s], acc);
@@ -978,7 +1006,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
 // The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
 // record, never used): with the same number of loads in flight on every path, the compiler's
 // wait counts let each step wait only for its own operands, not for the next chunk's.
-template <int NT, bool WITH_U, int OUT, int D, bool SPLIT>
+template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS = false>
 __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW][NT],
                                            const ScanLds& L,
                                            int64_t rec0, int cb, int ce, int len, size_t ob,
@@ -988,20 +1016,24 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     const int lane = threadIdx.x & 63;
     const int last = ce - 1;
     ChunkFrags<NT, D> fa, fb;
-    load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
+    load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0,
+                                            fa);
     for (int jc = cb; jc < ce; jc += 2) {
         const int c1 = jc + 1 < last ? jc + 1 : last;
         if constexpr (!SPLIT)
-            load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
-        scan_step<NT, WITH_U, OUT, D, SPLIT>(p, fa, fb, rec0 + int64_t(c1) * p.n_v, S, L, jc,
-                                             len, ob, os, dv_tile0, rec0 + int64_t(jc) * p.n_v);
+            load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(c1) * p.n_v, w, lane,
+                                                    dv_tile0, fb);
+        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS>(p, fa, fb, rec0 + int64_t(c1) * p.n_v, S, L,
+                                                   jc, len, ob, os, dv_tile0,
+                                                   rec0 + int64_t(jc) * p.n_v);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
         if constexpr (!SPLIT)
-            load_chunk<NT, WITH_U, OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
-        scan_step<NT, WITH_U, OUT, D, SPLIT>(p, fb, fa, rec0 + int64_t(c2) * p.n_v, S, L,
-                                             jc + 1, len, ob, os, dv_tile0,
-                                             rec0 + int64_t(jc + 1) * p.n_v);
+            load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(c2) * p.n_v, w, lane,
+                                                    dv_tile0, fa);
+        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS>(p, fb, fa, rec0 + int64_t(c2) * p.n_v, S, L,
+                                                   jc + 1, len, ob, os, dv_tile0,
+                                                   rec0 + int64_t(jc + 1) * p.n_v);
     }
 }
 
@@ -1231,7 +1263,8 @@ void kda_scan_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) __bf16 sSl[BV * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[BV * VN_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sVl[BV * VN_LD];
-    const ScanLds L{sSh, sSl, sVh, sVl};
+    __shared__ __attribute__((aligned(16))) float sG[D];
+    const ScanLds L{sSh, sSl, sVh, sVl, sG};
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1283,9 +1316,11 @@ void kda_scan_kernel(Params p) {
         }
     lds_barrier();
 
-    // split loads measured faster for the wider tiles, slower for the one-tile prefetched form
-    run_chunks<NT, true, OUT_FINAL, D, (NT > 1)>(p, S, L, rec0, 0, nchunks, len, ob, os,
-                                                 dv_tile0);
+    // split loads measured faster for the wider tiles, slower for the one-tile prefetched form,
+    // which takes gamma through LDS instead
+    constexpr bool SPLIT = NT > 1, GLDS = PFW && NT == 1;
+    run_chunks<NT, true, OUT_FINAL, D, SPLIT, GLDS>(p, S, L, rec0, 0, nchunks, len, ob, os,
+                                                   dv_tile0);
 
     if (p.fin) {
 #pragma unroll
@@ -1314,7 +1349,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[16 * VN_LD];
     __shared__ __attribute__((aligned(16))) __bf16 sVl[16 * VN_LD];
-    const ScanLds L{sSh, sSl, sVh, sVl};
+    __shared__ __attribute__((aligned(16))) float sG[D];
+    const ScanLds L{sSh, sSl, sVh, sVl, sG};
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1418,7 +1454,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
     constexpr int MW = HD<D>::MW, KB = HD<D>::KB, TILES = HD<D>::TILES;
     __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
-    const ScanLds L{sSh, sSl, nullptr, nullptr};
+    const ScanLds L{sSh, sSl, nullptr, nullptr, nullptr};
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
