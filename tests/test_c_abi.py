@@ -174,3 +174,16 @@ def test_timed_needs_events(lib):
                                  P(0x40000), P(0x50000), P(None), P(None), P(0x60000),
                                  P(None), P(0x100000), ctypes.c_size_t(1 << 40), P(None), None, 6)
     assert st == 1
+
+
+def test_bench_record_model_matches_workspace(lib):
+    """The benchmark's compulsory-byte model uses the library's record size: a one-level shape's
+    workspace is chunk slots x value heads x that record, plus 256-byte alignment per array."""
+    import sys
+    sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    import bench
+    for d, nv in ((128, 32), (64, 64)):
+        st, n = ws(lib, make_shape("BNSD", 1, 64 * 300, nv, nv, 0.1, d_k=d, d_v=d))
+        assert st == 0
+        body = 300 * nv * bench.record_bytes(d)
+        assert body <= n < body + 8 * 256, (d, n, body)
