@@ -43,6 +43,8 @@ namespace kda {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -84,6 +86,29 @@ __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_ex
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): about 16 mantissa bits in two MFMA
 // operands; a product of two such pairs drops only the lo*lo term.
 __device__ __forceinline__ __bf16 bf16_lo(float x, __bf16 hi) { return (__bf16)(x - (float)hi); }
+// Stores into one workgroup's share of a workspace array at device scope (cache policy sc1):
+// they are written through the L2, so the kernel's end does not wait for a write-back of every
+// dirty record line, and the next kernel, on any XCD, reads them from the memory-side cache.
+// Raw buffer stores: the hardware drops any store past `bytes`.
+struct DevStore {
+    __amdgpu_buffer_rsrc_t r;
+    static constexpr int kDevScope = 16;   // sc1
+    __device__ __forceinline__ DevStore(void* base, unsigned bytes)
+        : r(__builtin_amdgcn_make_buffer_rsrc(base, 0, int(bytes), 0x00020000)) {}
+    template <typename T>
+    __device__ __forceinline__ void put(unsigned byte_off, const T& v) const {
+        if constexpr (sizeof(T) == 16)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, int(byte_off), 0,
+                                                   kDevScope);
+        else if constexpr (sizeof(T) == 8)
+            __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, int(byte_off), 0,
+                                                  kDevScope);
+        else
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, int(byte_off), 0,
+                                                  kDevScope);
+    }
+};
+
 #define SPLIT_BF16(x, hi, lo)          \
     do {                               \
         const float x_ = (x);          \
@@ -433,7 +458,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
             sVec[(VEC_C + J) * 128 + c] = exp2_fast((Gl - Gr[J]) * kLog2e);
             sVecA[J * 128 + c] = exp2_fast(Gr[J] * kLog2e);
         }
-        p.Gf[size_t(rec) * D + c] = exp2_fast(Gl * kLog2e);
+        DevStore(p.Gf + size_t(rec) * D, D * 4).put(unsigned(c) * 4, exp2_fast(Gl * kLog2e));
     }
 
     // ---- phase 1: normalised, decayed operands in registers; K_dec record ---------------------
@@ -465,7 +490,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
     float Lk[8 * KB], Lq[8 * KB];
     bf16x8 KFb[KB];
     {
-        __bf16* kdst = p.Kf + size_t(rec) * (64 * D * 2);
+        const DevStore kdst(p.Kf + size_t(rec) * (64 * D * 2), 64 * D * 2 * 2);
         const int s_k = I >> 1;
         const int lane_k = (2 * (I & 1) + (q4 >> 1)) * 16 + n16;
         const int j0 = 4 * (q4 & 1);
@@ -505,8 +530,9 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 const bf16x4 th = to_bf16x4(mfma(kdh, sel, zero));
                 const bf16x4 tl = to_bf16x4(mfma(kdl, sel, zero));
                 const int mt = 2 * kb + hh;
-                *reinterpret_cast<bf16x4*>(kdst + ((size_t(mt) * 2 + s_k) * 64 + lane_k) * 8 + j0) = th;
-                *reinterpret_cast<bf16x4*>(kdst + 64 * D + ((size_t(mt) * 2 + s_k) * 64 + lane_k) * 8 + j0) = tl;
+                const unsigned at = unsigned(((mt * 2 + s_k) * 64 + lane_k) * 8 + j0) * 2;
+                kdst.put(at, th);
+                kdst.put(at + 64 * D * 2, tl);
             }
         }
     }
@@ -669,7 +695,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         }
         // W^T accumulator: lane (q4, n16) holds W[token 16I + n16][32kb + 8q4 + 4hf + r] for
         // tile 2kb + hf, so the pair of tiles is the W fragment the scan multiplies.
-        __bf16* wdst = p.Wf + size_t(rec) * (64 * D);
+        const DevStore wdst(p.Wf + size_t(rec) * (64 * D), 64 * D * 2);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -679,16 +705,16 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 oh[r] = (__bf16)accW[2 * kb][r];
                 oh[4 + r] = (__bf16)accW[2 * kb + 1][r];
             }
-            *reinterpret_cast<bf16x8*>(wdst + ((I * KB + kb) * 64 + lane) * 8) = oh;
+            wdst.put(unsigned((I * KB + kb) * 64 + lane) * 16, oh);
             // token-major -W (phi channel order) for Q' = Q~ + Aqk (-W): a selection with -1
             wT[2 * kb] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, -1.f), zero));
             wT[2 * kb + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, -1.f), zero));
         }
         // U accumulator: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
-        float* udst = p.Uf + size_t(rec) * (64 * D);
+        const DevStore udst(p.Uf + size_t(rec) * (64 * D), 64 * D * 4);
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt) {
-            *reinterpret_cast<f32x4*>(udst + ((nt * 4 + I) * 64 + lane) * 4) = accU[nt];
+            udst.put(unsigned((nt * 4 + I) * 64 + lane) * 16, accU[nt]);
             uT[nt] = to_bf16x4(accU[nt]);
         }
     }
@@ -729,11 +755,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 accQ[ft] = mfma(a, ql, accQ[ft]);
             }
         }
-        __bf16* odst = p.Of + size_t(rec) * (64 * D);
+        const DevStore odst(p.Of + size_t(rec) * (64 * D), 64 * D * 2);
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt)
-            *reinterpret_cast<bf16x4*>(odst + ((nt * 4 + I) * 64 + lane) * 4) = to_bf16x4(accO[nt]);
-        __bf16* qdst = p.Qf + size_t(rec) * (64 * D);
+            odst.put(unsigned((nt * 4 + I) * 64 + lane) * 8, to_bf16x4(accO[nt]));
+        const DevStore qdst(p.Qf + size_t(rec) * (64 * D), 64 * D * 2);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             bf16x8 o;
@@ -742,7 +768,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 o[r] = (__bf16)accQ[2 * kb][r];
                 o[4 + r] = (__bf16)accQ[2 * kb + 1][r];
             }
-            *reinterpret_cast<bf16x8*>(qdst + ((I * KB + kb) * 64 + lane) * 8) = o;
+            qdst.put(unsigned((I * KB + kb) * 64 + lane) * 16, o);
         }
     }
 }
@@ -883,7 +909,7 @@ struct ScanLds {
 //   each issued after the products it must not delay (a wave that issues a burst of loads
 //   waits at issue while the compute unit's address unit takes them); without it the caller
 //   has issued them all before the step.  Which is faster depends on the kernel (measured).
-template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS>
+template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS, bool DEVST>
 __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, D>& cur,
                                           ChunkFrags<NT, D>& nxt, int64_t rec_nxt,
                                           f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L, int jc,
@@ -936,8 +962,15 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
                 bf16x4 o;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)cur.o[nt][r]);
-                *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os +
-                                           16 * (dv_tile0 + nt) + 4 * q4) = o;
+                if constexpr (DEVST) {   // the chunk's 64 output rows as one store region
+                    const DevStore dst(p.out + ob + size_t(jc) * kChunk * os,
+                                       unsigned(kChunk * os * 2));
+                    dst.put(unsigned((tok - jc * kChunk) * os + 16 * (dv_tile0 + nt) + 4 * q4) * 2,
+                            o);
+                } else {
+                    *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os +
+                                               16 * (dv_tile0 + nt) + 4 * q4) = o;
+                }
             }
         } else if constexpr (OUT == OUT_O0 || OUT == OUT_R) {
             // every row, so the completion pass reads no unwritten memory (rows past the
@@ -950,14 +983,14 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
             if constexpr (OUT == OUT_O0) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(y[r] + (float)cur.o[nt][r]);
-                *reinterpret_cast<bf16x4*>(p.O0 + size_t(rec) * (64 * D) +
-                                           ((t * 4 + w) * 64 + lane) * 4) = yb;
+                DevStore(p.O0 + size_t(rec) * (64 * D), 64 * D * 2)
+                    .put(unsigned((t * 4 + w) * 64 + lane) * 8, yb);
             } else {   // R in the completion pass's B-operand order
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yb[r] = (__bf16)y[r];
                 const int lb = (2 * (t & 1) + (q4 >> 1)) * 16 + n16;
-                *reinterpret_cast<bf16x4*>(p.Rf + size_t(rec) * (64 * D) +
-                                           ((w * KB + (t >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1)) = yb;
+                DevStore(p.Rf + size_t(rec) * (64 * D), 64 * D * 2)
+                    .put(unsigned(((w * KB + (t >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1)) * 2, yb);
             }
         }
     }
@@ -1003,10 +1036,12 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
 }
 
 // Chunks [cb, ce) of one sequence (records rec0 + c * n_v), state in S and in LDS on entry.
+// DEVST: the step's outputs are stored at device scope (the segment pass; measured slower for
+// the one-level scan's output stream).
 // The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
 // record, never used): with the same number of loads in flight on every path, the compiler's
 // wait counts let each step wait only for its own operands, not for the next chunk's.
-template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS = false>
+template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS = false, bool DEVST = false>
 __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW][NT],
                                            const ScanLds& L,
                                            int64_t rec0, int cb, int ce, int len, size_t ob,
@@ -1023,17 +1058,17 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
         if constexpr (!SPLIT)
             load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(c1) * p.n_v, w, lane,
                                                     dv_tile0, fb);
-        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS>(p, fa, fb, rec0 + int64_t(c1) * p.n_v, S, L,
-                                                   jc, len, ob, os, dv_tile0,
-                                                   rec0 + int64_t(jc) * p.n_v);
+        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS, DEVST>(
+            p, fa, fb, rec0 + int64_t(c1) * p.n_v, S, L, jc, len, ob, os, dv_tile0,
+            rec0 + int64_t(jc) * p.n_v);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
         if constexpr (!SPLIT)
             load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(c2) * p.n_v, w, lane,
                                                     dv_tile0, fa);
-        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS>(p, fb, fa, rec0 + int64_t(c2) * p.n_v, S, L,
-                                                   jc + 1, len, ob, os, dv_tile0,
-                                                   rec0 + int64_t(jc + 1) * p.n_v);
+        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS, DEVST>(
+            p, fb, fa, rec0 + int64_t(c2) * p.n_v, S, L, jc + 1, len, ob, os, dv_tile0,
+            rec0 + int64_t(jc + 1) * p.n_v);
     }
 }
 
@@ -1418,7 +1453,8 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
 
     const size_t m = (size_t(bh) * p.seg_p + seg) * D * D;
     if (is_p) {
-        run_chunks<1, false, OUT_R, D, SEG_SPLIT>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+        run_chunks<1, false, OUT_R, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len, ob, os,
+                                                              tile);
         // rows 16 tile .. of P_s, split, into the combine's A fragments of P_s^T: element
         // P_s[16 tile + n16][16 M + 4 q4 + i] is lane (2 (tile & 1) + (n16 >> 3), 4 q4 + i),
         // entry n16 & 7, of fragment (M, tile >> 1)
@@ -1434,9 +1470,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
             }
     } else {
         if (seg == 0)
-            run_chunks<1, true, OUT_FINAL, D, SEG_SPLIT>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+            run_chunks<1, true, OUT_FINAL, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len,
+                                                                     ob, os, tile);
         else
-            run_chunks<1, true, OUT_O0, D, SEG_SPLIT>(p, S, L, rec0, cb, ce, len, ob, os, tile);
+            run_chunks<1, true, OUT_O0, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len, ob,
+                                                                  os, tile);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
             *reinterpret_cast<f32x4*>(p.Nst + m + ((tile * TILES + MW * w + mt) * 64 + lane) * 4) =
