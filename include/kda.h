@@ -68,7 +68,9 @@ enum {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,  /* a NULL or misaligned pointer, bad enum, negative size, alias */
-    KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement (head dim)   */
+    KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement: head dim, or
+                                 sizes past its limits (n_v * d_k >= 2^24; more than 2^31 - 1
+                                 workgroups in a kernel; tensors of 2^63 elements or more) */
     KDA_ERR_WORKSPACE = 3,    /* workspace pointer NULL or workspace_bytes too small */
     KDA_ERR_HIP = 4           /* a HIP launch or event call failed (hipGetLastError) */
 } kda_status;

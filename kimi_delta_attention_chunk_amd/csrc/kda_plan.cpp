@@ -118,6 +118,8 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     const double tokens = (s->layout == KDA_LAYOUT_TND) ? double(s->seq_len)
                                                         : double(s->batch) * s->seq_len;
     if (tokens * s->n_v * p.d > 9.0e18) return KDA_ERR_UNSUPPORTED;
+    // the 64 output rows of one chunk are one buffer-store region with 32-bit byte offsets
+    if (int64_t(kChunk) * s->n_v * p.d * 2 >= (int64_t(1) << 31)) return KDA_ERR_UNSUPPORTED;
 
     const size_t n = size_t(p.n_records);
     const int d = p.d;

@@ -120,6 +120,7 @@ def test_plan_query(lib):
     (dict(d_k=64, d_v=64), 0), (dict(d_k=32, d_v=32), 2), (dict(d_k=256, d_v=256), 2),
     (dict(scale=float("nan")), 1), (dict(flags=8), 1), (dict(flags=16), 1),
     (dict(flags=7), 0), (dict(flags=4), 0),
+    (dict(layout=1, n_v=1 << 17), 2), (dict(layout=1, n_v=(1 << 17) - 2), 0),
 ])
 def test_shape_rejections(lib, bad, code):
     kw = dict(layout="BNSD", batch=1, seq_len=100, n_qk=1, n_v=2, scale=0.1)
