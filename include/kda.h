@@ -107,6 +107,8 @@ kda_status kda_chunk_fwd_workspace(const kda_shape* shape, size_t* bytes);
  *   final_state    fp32 [batch, n_v, d_v, d_k] or NULL (not produced); must not overlap
  *                  initial_state
  *   workspace      device buffer of at least kda_chunk_fwd_workspace() bytes, 256-byte aligned
+ * Buffers the call writes (out, final_state, the first kda_chunk_fwd_workspace() bytes of the
+ * workspace) must not overlap each other or any input; overlap is KDA_ERR_INVALID_ARG.
  * Returns KDA_OK once the kernels are enqueued on `stream`. */
 kda_status kda_chunk_fwd(const kda_shape* shape,
                          const void* q, const void* k, const void* v,

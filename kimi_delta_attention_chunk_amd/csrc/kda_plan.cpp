@@ -164,6 +164,36 @@ kda_status check_call(const kda_shape* s, const Plan& p, const void* q, const vo
         return KDA_ERR_INVALID_ARG;
     if (!workspace || workspace_bytes < p.total) return KDA_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return KDA_ERR_WORKSPACE;
+
+    // nothing the call writes (out, final_state, the workspace it uses) may overlap anything
+    // else it reads or writes
+    const size_t tokens = (s->layout == KDA_LAYOUT_TND) ? size_t(s->seq_len)
+                                                        : size_t(s->batch) * s->seq_len;
+    const size_t per_v = tokens * p.n_v;
+    const bool sg = (s->flags & KDA_SCALAR_GATE) != 0;
+    struct Region {
+        const void* ptr;
+        size_t bytes;
+        bool written;
+    };
+    const Region r[] = {
+        {q, tokens * p.n_qk * p.d * 2, false},
+        {k, tokens * p.n_qk * p.d * 2, false},
+        {v, per_v * p.d * 2, false},
+        {g, per_v * (sg ? 1 : p.d) * sizeof(float), false},
+        {beta, per_v * 2, false},
+        {initial_state, initial_state ? state_bytes : 0, false},
+        {cu_seqlens, cu_seqlens ? (size_t(s->batch) + 1) * sizeof(int32_t) : 0, false},
+        {out, per_v * p.d * 2, true},
+        {final_state, final_state ? state_bytes : 0, true},
+        {workspace, p.total, true},
+    };
+    constexpr int nr = sizeof(r) / sizeof(r[0]);
+    for (int i = 0; i < nr; ++i)
+        for (int j = i + 1; j < nr; ++j)
+            if ((r[i].written || r[j].written) && r[i].bytes && r[j].bytes &&
+                overlap(r[i].ptr, r[i].bytes, r[j].ptr, r[j].bytes))
+                return KDA_ERR_INVALID_ARG;
     return KDA_OK;
 }
 

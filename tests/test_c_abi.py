@@ -148,6 +148,10 @@ def call(lib, shape, **ptrs):
     (dict(out=0x60002), 1), (dict(init=0x80000, fin=0x80000), 1),
     (dict(init=0x80000, fin=0x80000 + 4096), 1), (dict(ws=None), 3), (dict(ws_bytes=1024), 3),
     (dict(ws=0x100010), 3),
+    # what the call writes may overlap nothing else: out over v, out over the workspace, the
+    # final state over q, the workspace over g
+    (dict(out=0x30000 + 256), 1), (dict(out=0x100000 - 512), 1), (dict(fin=0x10000), 1),
+    (dict(ws=0x40000, ws_bytes=1 << 20), 1),
 ])
 def test_call_rejections(lib, ptrs, code):
     shape = make_shape("BNSD", 1, 100, 1, 2, 0.1)
