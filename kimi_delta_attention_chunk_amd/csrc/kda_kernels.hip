@@ -808,7 +808,7 @@ enum OutMode {
     OUT_NONE = 0,    // nothing (segment end state and transfer matrix only)
     OUT_FINAL = 1,   // out = Q' S^T + O_intra in bf16, valid tokens only
     OUT_O0 = 2,      // O0 = Q' S^T + O_intra in bf16, workspace (state from a zero start)
-    OUT_R = 3,       // R = Q' S^T in fp32, workspace (state rows of the transfer matrix)
+    OUT_R = 3,       // R = Q' S^T in bf16, workspace (state rows of the transfer matrix)
 };
 
 template <int NT, int D>
