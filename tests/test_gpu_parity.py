@@ -164,6 +164,10 @@ TWO_LEVEL = [
                               g_kind="strong", init=True, seed=35)),
     ("bnsd_2head_8seg", dict(layout="BNSD", batch=1, seq_len=4096 + 30, n_qk=2, n_v=2,
                              g_kind="small", init=True, seed=36)),
+    # packed sequences of very different lengths: the short ones leave later segments empty
+    # (their walks return at once, the combine meets identity transfers and zero end states)
+    ("tnd_length_mix", dict(layout="TND", batch=5, seq_len=0, n_qk=1, n_v=1, g_kind="strong",
+                            init=True, seed=37, lengths=[1, 5000, 64, 65, 700])),
 ]
 
 
