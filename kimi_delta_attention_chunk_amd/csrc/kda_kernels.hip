@@ -189,46 +189,53 @@ __device__ __forceinline__ void row_geom(const Params& p, int b, int h, int head
 // into token-grouped LDS tiles that the consumers read back with 16-byte loads.
 //
 // The workgroup keeps its LDS under 80 KB and its registers under 256 per lane, so two
-// workgroups share a compute unit and one's memory phase overlaps the other's arithmetic.
+// workgroups share a compute unit and one's memory phase overlaps the other's arithmetic; at
+// head dim 64 under 53 KB and 168 registers, so three do.
 
 constexpr int BLK_LD = 20;              // fp32 row stride of a stored 16 x 16 block
 constexpr int BLK_SZ = 16 * BLK_LD;     // floats per stored block
 constexpr int N_BLK = 10;               // lower-triangular 16 x 16 blocks of a 64 x 64 matrix
-constexpr int TILE_BYTES = 8 * 8 * 16 * 16;   // [tile 8][token group 8][n16][8] bf16 = 16 KB
+constexpr int TILE = 8 * 16 * 8 * 2;    // one token-grouped tile [group 8][n16][8] bf16: 2 KB
 
-constexpr int OFF_AQK = 0;                                 // Aqk blocks          12800
-constexpr int OFF_AI = OFF_AQK + N_BLK * BLK_SZ * 4;       // Ainv blocks         12800
-constexpr int OFF_BETA = OFF_AI + N_BLK * BLK_SZ * 4;      // beta[64]              256
-constexpr int OFF_X = OFF_BETA + 256;                      // phase-shared region 49152
-// inside region X, by phase:
-//   gate sums      first[4][128], dlast[4][128] fp32                        at X + 0
-//   T/Aqk          sR [pair 6][kb 4][lane 64] bf16x8 (24576)               at X + 0
-//                  sT blocks (12800)                                        at X + 24576
-//                  vec: BV[6][128], C[4][128] fp32 (5120)                   at X + 37376
-//                  vecA[4][128] fp32 (2048)                                 at X + 42496
-//   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                    at X + 37376
-//   W, U           sKt hi/lo tiles (32768)                                  at X + 0
-//                  sVt tile (16384)                                         at X + 32768
-//   O_intra, Q'    sW tile (-W, 16384)                                      at X + 0
-//                  sU tile (16384)                                          at X + 16384
-constexpr int X_R = 0;
-constexpr int X_T = 24576;
-constexpr int X_VEC = 37376;
-constexpr int X_VECA = 42496;
-constexpr int X_TMP = 37376;
-constexpr int X_KT = 0;
-constexpr int X_VT = 32768;
-constexpr int X_W = 0;
-constexpr int X_U = 16384;
-constexpr int X_BYTES = 49152;
-constexpr int INTRA_LDS = OFF_X + X_BYTES;
-static_assert(X_VECA + 2048 <= X_BYTES, "vector rows fit region X");
-static_assert(X_R + 6 * 4 * 64 * 16 <= X_T, "scaled key blocks end before the T blocks");
-static_assert(X_T + N_BLK * BLK_SZ * 4 <= X_VEC, "T blocks end before the vector rows");
-static_assert(X_TMP + 4 * BLK_SZ * 4 <= X_BYTES, "inverse staging fits region X");
-static_assert(2 * INTRA_LDS <= 160 * 1024, "two intra workgroups fit one compute unit");
+// LDS of the intra kernel for head dim D:
+//   Aqk blocks (12800) | Ainv blocks (12800) | beta[64] (256) | region X
+// The Ainv region holds, until the inverse is formed, the per-channel factor rows:
+//   vec: BV[6][128], C[4][128] fp32 (5120) at Ainv + 0;  vecA[4][128] fp32 (2048) at + 5120.
+// Region X, by phase:
+//   gate sums      first[4][128], dlast[4][128] fp32 (4096)                  at X + 0
+//   T/Aqk          sR [pair 6][kb D/32][lane 64] bf16x8 (6 D/32 KB)           at X + 0
+//                  sT blocks (12800)                                          at X + X_T
+//   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                      at X + 0
+//   W, U           sKt hi/lo tiles (2 D/16 tiles), sVt (D/16 tiles)           at X + 0
+//   O_intra, Q'    sW (-W, D/16 tiles), sU (D/16 tiles)                       at X + 0
+// D = 128: 75,008 B (two workgroups per compute unit); D = 64: 50,944 B (three).
+template <int D>
+struct IntraLds {
+    static constexpr int OFF_AQK = 0;
+    static constexpr int OFF_AI = OFF_AQK + N_BLK * BLK_SZ * 4;
+    static constexpr int OFF_BETA = OFF_AI + N_BLK * BLK_SZ * 4;
+    static constexpr int OFF_X = OFF_BETA + 256;
+    static constexpr int AI_VEC = 0;
+    static constexpr int AI_VECA = 5120;
+    static constexpr int TILES = D / 16;
+    static constexpr int X_R = 0;
+    static constexpr int X_T = 6 * (D / 32) * 64 * 16;
+    static constexpr int X_TMP = 0;
+    static constexpr int X_KT = 0;
+    static constexpr int X_KTL = TILES * TILE;
+    static constexpr int X_VT = 2 * TILES * TILE;
+    static constexpr int X_W = 0;
+    static constexpr int X_U = TILES * TILE;
+    static constexpr int X_BYTES = (X_T + N_BLK * BLK_SZ * 4) > 3 * TILES * TILE
+                                       ? (X_T + N_BLK * BLK_SZ * 4) : 3 * TILES * TILE;
+    static constexpr int BYTES = OFF_X + X_BYTES;
+    static constexpr int PER_CU = D == 64 ? 3 : 2;   // workgroups per compute unit
+    static_assert(AI_VECA + 2048 <= N_BLK * BLK_SZ * 4, "factor rows fit the Ainv region");
+    static_assert(X_BYTES >= 4096 && X_BYTES >= 4 * BLK_SZ * 4, "gate sums and staging fit X");
+    static_assert(PER_CU * BYTES <= 160 * 1024, "the workgroups of one compute unit fit its LDS");
+};
 
-// vector rows inside vec (X + X_VEC), 128 floats each
+// vector rows inside vec (the Ainv region until the inverse), 128 floats each
 constexpr int VEC_BV = 0;   // 6 rows: exp(G[16I] - G[16J]) for (I,J) = (1,0),(2,0),(2,1),(3,0),(3,1),(3,2)
 constexpr int VEC_C = 6;    // 4 rows: exp(G_last - G[16I])
 
@@ -309,26 +316,27 @@ __device__ __forceinline__ void blk_row8(const float* m, int I, int s, int q4, i
 // SG: one gate per (token, value head) (KDA_SCALAR_GATE), broadcast over the key channels.
 // D: head dim (d_k = d_v), 128 or 64.
 template <bool SG, int D>
-__global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kernel(Params p) {
     constexpr int KB = D / 32;    // 32-channel K steps of a product over channels
     constexpr int NTD = D / 16;   // 16-wide channel (or Dv) tiles
-    __shared__ __attribute__((aligned(16))) unsigned char smem[INTRA_LDS];
-    float* sAqk = reinterpret_cast<float*>(smem + OFF_AQK);
-    float* sAi = reinterpret_cast<float*>(smem + OFF_AI);
-    float* sBeta = reinterpret_cast<float*>(smem + OFF_BETA);
-    unsigned char* X = smem + OFF_X;
+    using LY = IntraLds<D>;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LY::BYTES];
+    float* sAqk = reinterpret_cast<float*>(smem + LY::OFF_AQK);
+    float* sAi = reinterpret_cast<float*>(smem + LY::OFF_AI);
+    float* sBeta = reinterpret_cast<float*>(smem + LY::OFF_BETA);
+    float* sVec = reinterpret_cast<float*>(smem + LY::OFF_AI + LY::AI_VEC);
+    float* sVecA = reinterpret_cast<float*>(smem + LY::OFF_AI + LY::AI_VECA);
+    unsigned char* X = smem + LY::OFF_X;
     float* sFirst = reinterpret_cast<float*>(X);               // [4][128]
     float* sDlast = sFirst + 512;                              // [4][128]
-    bf16x8* sR = reinterpret_cast<bf16x8*>(X + X_R);           // [pair 6][kb 4][lane 64]
-    float* sT = reinterpret_cast<float*>(X + X_T);
-    float* sVec = reinterpret_cast<float*>(X + X_VEC);
-    float* sVecA = reinterpret_cast<float*>(X + X_VECA);
-    float* sTmp = reinterpret_cast<float*>(X + X_TMP);
-    __bf16* sKtH = reinterpret_cast<__bf16*>(X + X_KT);
-    __bf16* sKtL = reinterpret_cast<__bf16*>(X + X_KT + TILE_BYTES);
-    __bf16* sVt = reinterpret_cast<__bf16*>(X + X_VT);
-    __bf16* sW = reinterpret_cast<__bf16*>(X + X_W);
-    __bf16* sU = reinterpret_cast<__bf16*>(X + X_U);
+    bf16x8* sR = reinterpret_cast<bf16x8*>(X + LY::X_R);       // [pair 6][kb KB][lane 64]
+    float* sT = reinterpret_cast<float*>(X + LY::X_T);
+    float* sTmp = reinterpret_cast<float*>(X + LY::X_TMP);
+    __bf16* sKtH = reinterpret_cast<__bf16*>(X + LY::X_KT);
+    __bf16* sKtL = reinterpret_cast<__bf16*>(X + LY::X_KTL);
+    __bf16* sVt = reinterpret_cast<__bf16*>(X + LY::X_VT);
+    __bf16* sW = reinterpret_cast<__bf16*>(X + LY::X_W);
+    __bf16* sU = reinterpret_cast<__bf16*>(X + LY::X_U);
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -520,7 +528,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
                 bf16x8 r;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) r[e] = (__bf16)(kf[e] * bv[e]);
-                sR[(pi * 4 + kb) * 64 + lane] = r;
+                sR[(pi * KB + kb) * 64 + lane] = r;
             }
             // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [hi/lo][mt D/16][s 2][lane 64][8]
 #pragma unroll
@@ -558,7 +566,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_intra_kernel(Params p) {
         f32x4 aT = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8 bf = (J == I) ? KFb[kb] : sR[(pair_index(I, J) * 4 + kb) * 64 + lane];
+            const bf16x8 bf = (J == I) ? KFb[kb] : sR[(pair_index(I, J) * KB + kb) * 64 + lane];
             aT = mfma(Lkb[kb], bf, aT);
             aQ = mfma(Lqb[kb], bf, aQ);
         }
