@@ -232,6 +232,7 @@ struct IntraLds {
     static constexpr int PER_CU = D == 64 ? 3 : 2;   // workgroups per compute unit
     static_assert(AI_VECA + 2048 <= N_BLK * BLK_SZ * 4, "factor rows fit the Ainv region");
     static_assert(X_BYTES >= 4096 && X_BYTES >= 4 * BLK_SZ * 4, "gate sums and staging fit X");
+    static_assert(X_TMP + 4 * BLK_SZ * 4 <= X_T, "inverse staging ends before the T blocks");
     static_assert(PER_CU * BYTES <= 160 * 1024, "the workgroups of one compute unit fit its LDS");
 };
 
