@@ -1081,6 +1081,35 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     }
 }
 
+// Sequences of different lengths (cu_seqlens given) are walked longest first: workgroup rank r
+// takes the sequence of rank r in the order of decreasing valid length (ties by index), so the
+// long walks start first and the short ones fill the end of the grid (longest processing time
+// first).  Every workgroup ranks the lengths itself, from LDS; with more than kRankMax sequences
+// the order stays the index order.  Uniform for the workgroup (all its threads call it).
+constexpr int kRankMax = 256;
+__device__ __forceinline__ int seq_by_rank(const Params& p, int r) {
+    if (!p.cu || p.batch <= 1 || p.batch > kRankMax) return r;
+    __shared__ int sLen[kRankMax];
+    __shared__ int sSeq;
+    for (int t = threadIdx.x; t < p.batch; t += blockDim.x) {
+        int c0, len, slot0;
+        seq_info(p, t, c0, len, slot0);
+        sLen[t] = len;
+    }
+    __syncthreads();
+    for (int t = threadIdx.x; t < p.batch; t += blockDim.x) {
+        const int lt = sLen[t];
+        int rank = 0;
+        for (int u = 0; u < p.batch; ++u) {
+            const int lu = sLen[u];
+            rank += (lu > lt || (lu == lt && u < t)) ? 1 : 0;
+        }
+        if (rank == r) sSeq = t;
+    }
+    __syncthreads();
+    return sSeq;
+}
+
 // Chunk range [cb, ce) of segment `seg` of a sequence with `nchunks` chunks cut into seg_p
 // segments of ceil(nchunks / seg_p) chunks.
 __device__ __forceinline__ void segment_range(int nchunks, int seg_p, int seg, int& cb, int& ce) {
@@ -1323,7 +1352,7 @@ void kda_scan_kernel(Params p) {
     const int bh = (r8 / p.scan_tiles) * 8 + xcd;
     const int tile = r8 % p.scan_tiles;
     if (bh >= p.batch * p.n_v) return;
-    const int b = bh / p.n_v;
+    const int b = seq_by_rank(p, bh / p.n_v);
     const int h = bh % p.n_v;
     const int dv_tile0 = tile * NT;   // first 16-wide Dv tile of this workgroup
 

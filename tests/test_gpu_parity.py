@@ -96,6 +96,14 @@ SMALL = [
     # no decay over 64 chunks: the state never forgets, so rounding accumulates longest here
     ("bnsd_no_decay_s4096", dict(layout="BNSD", batch=1, seq_len=4096, n_qk=1, n_v=1,
                                  g_kind="zero", init=True, seed=11)),
+    # the scan walks sequences longest first: equal lengths (ties broken by index) and more
+    # sequences than it ranks (index order)
+    ("tnd_equal_lengths", dict(layout="TND", batch=6, seq_len=0, n_qk=1, n_v=2,
+                               g_kind="strong", init=True, seed=12,
+                               lengths=[100, 3, 100, 100, 64, 100])),
+    ("tnd_300_short_seqs", dict(layout="TND", batch=300, seq_len=0, n_qk=1, n_v=1,
+                                g_kind="strong", init=True, seed=13,
+                                lengths=[1 + (37 * i) % 90 for i in range(300)])),
 ]
 
 # One gate per (token, value head) (KDA_SCALAR_GATE, the GDN form): every layout, GQA, ragged
