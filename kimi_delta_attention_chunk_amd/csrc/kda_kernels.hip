@@ -190,7 +190,9 @@ __device__ __forceinline__ void row_geom(const Params& p, int b, int h, int head
 //
 // The workgroup keeps its LDS under 80 KB and its registers under 256 per lane, so two
 // workgroups share a compute unit and one's memory phase overlaps the other's arithmetic; at
-// head dim 64 under 53 KB and 168 registers, so three do.
+// head dim 64 under 53 KB and 168 registers, so three do.  When every workgroup has a compute
+// unit to itself, an eight-wave form (two waves per token block, each with half the channels)
+// shortens the workgroup's latency instead.
 
 constexpr int BLK_LD = 20;              // fp32 row stride of a stored 16 x 16 block
 constexpr int BLK_SZ = 16 * BLK_LD;     // floats per stored block
@@ -208,8 +210,10 @@ constexpr int TILE = 8 * 16 * 8 * 2;    // one token-grouped tile [group 8][n16]
 //   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                      at X + 0
 //   W, U           sKt hi/lo tiles (2 D/16 tiles), sVt (D/16 tiles)           at X + 0
 //   O_intra, Q'    sW (-W, D/16 tiles), sU (D/16 tiles)                       at X + 0
-// D = 128: 75,008 B (two workgroups per compute unit); D = 64: 50,944 B (three).
-template <int D>
+// D = 128: 75,008 B (two workgroups per compute unit); D = 64: 50,944 B (three).  The eight-wave
+// form (HV = 2) also keeps, through phases 1 and 2, the half sums of squares [2][64][2] fp32 and
+// the second channel half's T products [block 10][lane 64][4] fp32 after the T blocks.
+template <int D, int HV = 1>
 struct IntraLds {
     static constexpr int OFF_AQK = 0;
     static constexpr int OFF_AI = OFF_AQK + N_BLK * BLK_SZ * 4;
@@ -226,10 +230,12 @@ struct IntraLds {
     static constexpr int X_VT = 2 * TILES * TILE;
     static constexpr int X_W = 0;
     static constexpr int X_U = TILES * TILE;
-    static constexpr int X_BYTES = (X_T + N_BLK * BLK_SZ * 4) > 3 * TILES * TILE
-                                       ? (X_T + N_BLK * BLK_SZ * 4) : 3 * TILES * TILE;
+    static constexpr int X_NRM = X_T + N_BLK * BLK_SZ * 4;   // eight waves: half sums [2][64][2]
+    static constexpr int X_TP = X_NRM + 1024;                  // eight waves: T half products
+    static constexpr int X_P2 = HV == 2 ? X_TP + N_BLK * 1024 : X_NRM;   // end of phase 1-2 use
+    static constexpr int X_BYTES = X_P2 > 3 * TILES * TILE ? X_P2 : 3 * TILES * TILE;
     static constexpr int BYTES = OFF_X + X_BYTES;
-    static constexpr int PER_CU = D == 64 ? 3 : 2;   // workgroups per compute unit
+    static constexpr int PER_CU = HV == 2 ? 1 : (D == 64 ? 3 : 2);   // workgroups per compute unit
     static_assert(AI_VECA + 2048 <= N_BLK * BLK_SZ * 4, "factor rows fit the Ainv region");
     static_assert(X_BYTES >= 4096 && X_BYTES >= 4 * BLK_SZ * 4, "gate sums and staging fit X");
     static_assert(X_TMP + 4 * BLK_SZ * 4 <= X_T, "inverse staging ends before the T blocks");
@@ -316,11 +322,19 @@ __device__ __forceinline__ void blk_row8(const float* m, int I, int s, int q4, i
 
 // SG: one gate per (token, value head) (KDA_SCALAR_GATE), broadcast over the key channels.
 // D: head dim (d_k = d_v), 128 or 64.
-template <bool SG, int D>
-__global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kernel(Params p) {
+// HV: waves per 16-token block.  With HV = 2 (eight waves) wave w owns token block I = w >> 1
+// and channel half hc = w & 1: its loads, gate sums, decayed operands and transposes cover
+// channels [hc D/2, (hc+1) D/2), its W, Q' tiles are the Dk tiles of that half and its U,
+// O_intra tiles the Dv tiles of the same index range; the T/Aqk products over channels are
+// summed from the two halves through LDS.
+template <bool SG, int D, int HV>
+__global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void kda_intra_kernel(Params p) {
     constexpr int KB = D / 32;    // 32-channel K steps of a product over channels
     constexpr int NTD = D / 16;   // 16-wide channel (or Dv) tiles
-    using LY = IntraLds<D>;
+    constexpr int KBW = KB / HV;  // channel blocks of this wave
+    constexpr int NTW = NTD / HV; // W/Q' (Dk) and U/O_intra (Dv) tiles of this wave
+    static_assert(HV == 1 || HV == 2, "one or two waves per token block");
+    using LY = IntraLds<D, HV>;
     __shared__ __attribute__((aligned(16))) unsigned char smem[LY::BYTES];
     float* sAqk = reinterpret_cast<float*>(smem + LY::OFF_AQK);
     float* sAi = reinterpret_cast<float*>(smem + LY::OFF_AI);
@@ -332,6 +346,8 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     float* sDlast = sFirst + 512;                              // [4][128]
     bf16x8* sR = reinterpret_cast<bf16x8*>(X + LY::X_R);       // [pair 6][kb KB][lane 64]
     float* sT = reinterpret_cast<float*>(X + LY::X_T);
+    float* sNrm = reinterpret_cast<float*>(X + LY::X_NRM);     // [half 2][token 64][q, k]
+    float* sTp = reinterpret_cast<float*>(X + LY::X_TP);       // [block 10][lane 64][4]
     float* sTmp = reinterpret_cast<float*>(X + LY::X_TMP);
     __bf16* sKtH = reinterpret_cast<__bf16*>(X + LY::X_KT);
     __bf16* sKtL = reinterpret_cast<__bf16*>(X + LY::X_KTL);
@@ -344,6 +360,10 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     const int lane = tid & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
+    const int I = HV == 2 ? (w >> 1) : w;     // token block
+    const int hc = HV == 2 ? (w & 1) : 0;     // channel half
+    const int kb0 = hc * KBW;                 // first channel block of this wave
+    const int tw0 = hc * NTW;                 // first W/Q' and U/O_intra tile of this wave
 
     const int64_t rec = blockIdx.x;
     const int slot = int(blockIdx.x / unsigned(p.n_v));   // 32-bit: grids stay below 2^31
@@ -367,7 +387,6 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     vb += size_t(t0) * vs;
     bb += size_t(t0) * bs;
 
-    const int I = w;
     const int tok = 16 * I + n16;        // this lane's token inside the chunk
     const bool tv = tok < n;
     const int tc = tv ? tok : n - 1;     // rows past the tail are read clamped, then zeroed
@@ -376,8 +395,8 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     // The gate first (the prefix scan needs it first), then q, k, v and beta.  Rows past the
     // tail are read clamped and masked where they are consumed, so that no register written
     // here is rewritten before its load returns (which would make the wave wait for it).
-    bf16x8 xq[KB], xk[KB], xv[KB];
-    f32x4 xg[2 * KB];
+    bf16x8 xq[KBW], xk[KBW], xv[KBW];
+    f32x4 xg[2 * KBW];
     float gsv;   // the one gate of this token with KDA_SCALAR_GATE (beta's layout)
     float braw;
     if constexpr (SG) {
@@ -385,10 +404,10 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     } else {
         const float* gr = p.g + vb + size_t(tc) * vs;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int c = 32 * kb + 8 * q4;
-            xg[2 * kb] = *reinterpret_cast<const f32x4*>(gr + c);
-            xg[2 * kb + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
+        for (int i = 0; i < KBW; ++i) {
+            const int c = 32 * (kb0 + i) + 8 * q4;
+            xg[2 * i] = *reinterpret_cast<const f32x4*>(gr + c);
+            xg[2 * i + 1] = *reinterpret_cast<const f32x4*>(gr + c + 4);
         }
     }
     {
@@ -396,14 +415,14 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
         const __bf16* kr = p.k + qb + size_t(tc) * qs;
         const __bf16* vr = p.v + vb + size_t(tc) * vs;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const int c = 32 * kb + 8 * q4;
-            xk[kb] = *reinterpret_cast<const bf16x8*>(kr + c);
-            xq[kb] = *reinterpret_cast<const bf16x8*>(qr + c);
+        for (int i = 0; i < KBW; ++i) {
+            const int c = 32 * (kb0 + i) + 8 * q4;
+            xk[i] = *reinterpret_cast<const bf16x8*>(kr + c);
+            xq[i] = *reinterpret_cast<const bf16x8*>(qr + c);
         }
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-            xv[kb] = *reinterpret_cast<const bf16x8*>(vr + 32 * kb + 8 * q4);
+        for (int i = 0; i < KBW; ++i)
+            xv[i] = *reinterpret_cast<const bf16x8*>(vr + 32 * (kb0 + i) + 8 * q4);
         braw = (float)p.beta[bb + size_t(tc) * bs];
     }
 
@@ -413,37 +432,37 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     // term removed.  The block sums go through LDS to give, per channel, G at each block's
     // first token (G[16I]) and G_last = G at the last valid token.
     // (With the scalar gate every channel of a token has the same gate: one scan per lane.)
-    float gv[8 * KB], d[8 * KB];
+    float gv[8 * KBW], d[8 * KBW];
     if constexpr (SG) {
         const float gs = tv ? gsv : 0.f;
         const float ds = row_scan16(n16 == 0 ? 0.f : gs);
 #pragma unroll
-        for (int i = 0; i < 8 * KB; ++i) {
+        for (int i = 0; i < 8 * KBW; ++i) {
             gv[i] = gs;
             d[i] = ds;
         }
     } else {
 #pragma unroll
-        for (int i = 0; i < 8 * KB; ++i) gv[i] = xg[i >> 2][i & 3];
+        for (int i = 0; i < 8 * KBW; ++i) gv[i] = xg[i >> 2][i & 3];
         if (n < kChunk) {   // a tail chunk: rows past it add nothing
 #pragma unroll
-            for (int i = 0; i < 8 * KB; ++i) gv[i] = tv ? gv[i] : 0.f;
+            for (int i = 0; i < 8 * KBW; ++i) gv[i] = tv ? gv[i] : 0.f;
         }
 #pragma unroll
-        for (int i = 0; i < 8 * KB; ++i) d[i] = row_scan16(n16 == 0 ? 0.f : gv[i]);
+        for (int i = 0; i < 8 * KBW; ++i) d[i] = row_scan16(n16 == 0 ? 0.f : gv[i]);
     }
     if (n16 == 0 || n16 == 15) {   // block-first gates and block sums, 8 channels per store pair
         float* dst = (n16 == 0 ? sFirst : sDlast) + I * 128 + 8 * q4;
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int i = 0; i < KBW; ++i) {
             f32x4 a, c;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                a[e] = n16 == 0 ? gv[8 * kb + e] : d[8 * kb + e];
-                c[e] = n16 == 0 ? gv[8 * kb + 4 + e] : d[8 * kb + 4 + e];
+                a[e] = n16 == 0 ? gv[8 * i + e] : d[8 * i + e];
+                c[e] = n16 == 0 ? gv[8 * i + 4 + e] : d[8 * i + 4 + e];
             }
-            *reinterpret_cast<f32x4*>(dst + 32 * kb) = a;
-            *reinterpret_cast<f32x4*>(dst + 32 * kb + 4) = c;
+            *reinterpret_cast<f32x4*>(dst + 32 * (kb0 + i)) = a;
+            *reinterpret_cast<f32x4*>(dst + 32 * (kb0 + i) + 4) = c;
         }
     }
     __syncthreads();
@@ -471,21 +490,32 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     }
 
     // ---- phase 1: normalised, decayed operands in registers; K_dec record ---------------------
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int i = 0; i < KBW; ++i)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float fq = (float)xq[i][e], fk = (float)xk[i][e];
+            sq += fq * fq;
+            sk += fk * fk;
+        }
+    sq += __shfl_xor(sq, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 16);
+    sk += __shfl_xor(sk, 32);
+    if constexpr (HV == 2) {   // this half's sums of squares for the other half's wave
+        if (q4 == 0) {
+            sNrm[(hc * 64 + tok) * 2] = sq;
+            sNrm[(hc * 64 + tok) * 2 + 1] = sk;
+        }
+    }
+    __syncthreads();   // vector rows (and the half sums) ready; first/dlast dead
+    if constexpr (HV == 2) {
+        sq += sNrm[((hc ^ 1) * 64 + tok) * 2];
+        sk += sNrm[((hc ^ 1) * 64 + tok) * 2 + 1];
+    }
     float qn, kn, bt;
     {
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float fq = (float)xq[kb][e], fk = (float)xk[kb][e];
-                sq += fq * fq;
-                sk += fk * fk;
-            }
-        sq += __shfl_xor(sq, 16);
-        sq += __shfl_xor(sq, 32);
-        sk += __shfl_xor(sk, 16);
-        sk += __shfl_xor(sk, 32);
         const bool l2 = (p.flags & KDA_QK_L2NORM) != 0;
         // a zero factor removes the clamped rows past the tail from every q/k product
         qn = !tv ? 0.f : (l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f);
@@ -493,33 +523,33 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
         bt = 0.f;
         if (tv) bt = (p.flags & KDA_BETA_SIGMOID) ? 1.0f / (1.0f + expf(-braw)) : braw;
     }
-    __syncthreads();   // vector rows ready; first/dlast dead
-    if (q4 == 0) sBeta[tok] = bt;
+    if (q4 == 0 && hc == 0) sBeta[tok] = bt;
 
-    float Lk[8 * KB], Lq[8 * KB];
-    bf16x8 KFb[KB];
+    float Lk[8 * KBW], Lq[8 * KBW];
+    bf16x8 KFb[KBW];
     {
         const DevStore kdst(p.Kf + size_t(rec) * (64 * D * 2), 64 * D * 2 * 2);
         const int s_k = I >> 1;
         const int lane_k = (2 * (I & 1) + (q4 >> 1)) * 16 + n16;
         const int j0 = 4 * (q4 & 1);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int i = 0; i < KBW; ++i) {
+            const int kb = kb0 + i;
             bf16x8 kdh, kdl;
             float kf[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int i = 8 * kb + e;
+                const int ii = 8 * i + e;
                 const int c = 32 * kb + 8 * q4 + e;
                 // e^{d} <= 1 and e^{-d} < 2^109 (d over at most 15 tokens, g >= -5)
-                const float dd = d[i] * kLog2e;
+                const float dd = d[ii] * kLog2e;
                 const float ef = exp2_fast(dd);
                 const float ff = exp2_fast(-dd);
-                const float kv = (float)xk[kb][e] * kn;
-                Lk[i] = kv * ef;
-                Lq[i] = (float)xq[kb][e] * qn * ef;
+                const float kv = (float)xk[i][e] * kn;
+                Lk[ii] = kv * ef;
+                Lq[ii] = (float)xq[i][e] * qn * ef;
                 kf[e] = kv * ff;
-                KFb[kb][e] = (__bf16)kf[e];
+                KFb[i][e] = (__bf16)kf[e];
                 SPLIT_BF16(kf[e] * sVec[(VEC_C + I) * 128 + c], kdh[e], kdl[e]);   // K_dec <= 1
             }
             // the key operand of every later row block I2 > I: k_j exp(G[16 I2] - G_j) <= 1
@@ -552,51 +582,77 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     // k_i exp(G_i - G[16I]) <= 1 and q_i exp(G_i - G[16I]).  Diagonal: the key side is KF,
     // exp(G[16I] - G_j) < 2^109; masked entries may be huge and are removed by select.
     // Off-diagonal (I > J): the key side arrives scaled by its owner wave to k_j exp(G[16I] - G_j)
-    // <= 1.
-    bf16x8 Lkb[KB], Lqb[KB];
+    // <= 1.  With two waves per block each sums over its channel half; the second half's sums
+    // pass through LDS (T's after the T blocks, Aqk's in its own not yet written block slots) to
+    // the first half's wave, which adds them and stores T and Aqk.
+    bf16x8 Lkb[KBW], Lqb[KBW];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int i = 0; i < KBW; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            Lkb[kb][e] = (__bf16)Lk[8 * kb + e];
-            Lqb[kb][e] = (__bf16)Lq[8 * kb + e];
+            Lkb[i][e] = (__bf16)Lk[8 * i + e];
+            Lqb[i][e] = (__bf16)Lq[8 * i + e];
         }
+    f32x4 aT[4], aQ[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
+        aT[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        aQ[J] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (J > I) continue;
-        f32x4 aT = {0.f, 0.f, 0.f, 0.f}, aQ = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-            const bf16x8 bf = (J == I) ? KFb[kb] : sR[(pair_index(I, J) * KB + kb) * 64 + lane];
-            aT = mfma(Lkb[kb], bf, aT);
-            aQ = mfma(Lqb[kb], bf, aQ);
+        for (int i = 0; i < KBW; ++i) {
+            const int kb = kb0 + i;
+            const bf16x8 bf = (J == I) ? KFb[i] : sR[(pair_index(I, J) * KB + kb) * 64 + lane];
+            aT[J] = mfma(Lkb[i], bf, aT[J]);
+            aQ[J] = mfma(Lqb[i], bf, aQ[J]);
         }
-        float* tb = sT + blk(I, J) * BLK_SZ;
-        float* qb2 = sAqk + blk(I, J) * BLK_SZ;
+    }
+    if constexpr (HV == 2) {
+        if (hc == 1) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int i = 16 * I + 4 * q4 + r;
-            const int jj = 16 * J + n16;
-            tb[(4 * q4 + r) * BLK_LD + n16] = (i > jj) ? sBeta[i] * aT[r] : 0.f;
-            qb2[(4 * q4 + r) * BLK_LD + n16] = (i >= jj) ? p.scale * aQ[r] : 0.f;
+            for (int J = 0; J < 4; ++J) {
+                if (J > I) continue;
+                *reinterpret_cast<f32x4*>(sTp + blk(I, J) * 256 + 4 * lane) = aT[J];
+                *reinterpret_cast<f32x4*>(sAqk + blk(I, J) * BLK_SZ + 4 * lane) = aQ[J];
+            }
+        }
+        __syncthreads();   // the second halves' sums
+    }
+    if (hc == 0) {
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J > I) continue;
+            float* tb = sT + blk(I, J) * BLK_SZ;
+            float* qb2 = sAqk + blk(I, J) * BLK_SZ;
+            if constexpr (HV == 2) {
+                aT[J] += *reinterpret_cast<const f32x4*>(sTp + blk(I, J) * 256 + 4 * lane);
+                aQ[J] += *reinterpret_cast<const f32x4*>(qb2 + 4 * lane);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int i = 16 * I + 4 * q4 + r;
+                const int jj = 16 * J + n16;
+                tb[(4 * q4 + r) * BLK_LD + n16] = (i > jj) ? sBeta[i] * aT[J][r] : 0.f;
+                qb2[(4 * q4 + r) * BLK_LD + n16] = (i >= jj) ? p.scale * aQ[J][r] : 0.f;
+            }
         }
     }
     // operands kept for later phases: Q~ = scale * q * exp(G) and K~ hi/lo
-    float Qt[8 * KB];
-    bf16x8 bkh[KB], bkl[KB];
+    float Qt[8 * KBW];
+    bf16x8 bkh[KBW], bkl[KBW];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb)
+    for (int i = 0; i < KBW; ++i)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float a = sVecA[I * 128 + 32 * kb + 8 * q4 + e];
-            Qt[8 * kb + e] = p.scale * Lq[8 * kb + e] * a;
-            SPLIT_BF16(Lk[8 * kb + e] * a, bkh[kb][e], bkl[kb][e]);   // K~ (beta goes with Ainv)
+            const float a = sVecA[I * 128 + 32 * (kb0 + i) + 8 * q4 + e];
+            Qt[8 * i + e] = p.scale * Lq[8 * i + e] * a;
+            SPLIT_BF16(Lk[8 * i + e] * a, bkh[i][e], bkl[i][e]);   // K~ (beta goes with Ainv)
         }
     __syncthreads();   // T, Aqk ready
 
-    // ---- phase 3: Ainv = (I + T)^-1 in fp32 ---------------------------------------------------
-    if (lane < 16) {  // diagonal block I by forward substitution, column `lane`
-        const float* tb = sT + blk(I, I) * BLK_SZ;
+    // ---- phase 3: Ainv = (I + T)^-1 in fp32 (waves 0..3) ----------------------------------------
+    if (w < 4 && lane < 16) {  // diagonal block w by forward substitution, column `lane`
+        const float* tb = sT + blk(w, w) * BLK_SZ;
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -605,16 +661,16 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
             for (int m = 0; m < i; ++m) s -= tb[i * BLK_LD + m] * x[m];
             x[i] = s;
         }
-        float* ab = sAi + blk(I, I) * BLK_SZ;
+        float* ab = sAi + blk(w, w) * BLK_SZ;
 #pragma unroll
         for (int i = 0; i < 16; ++i) ab[i * BLK_LD + lane] = x[i];
     }
     __syncthreads();
-    // Below the diagonal, wave w fills block column w, top to bottom:
+    // Below the diagonal, wave w < 4 fills block column w, top to bottom:
     //     Ainv[I2][w] = -Ainv[I2][I2] * sum_{K=w}^{I2-1} T[I2][K] Ainv[K][w]
     // (block forward substitution of (I + T) X = I); every block it reads in column w is its
     // own earlier result.  Products on fp32 MFMA.
-    {
+    if (w < 4) {
         float* sP = sTmp + w * BLK_SZ;
         const int lr = lane & 15, lk = lane >> 4;
         for (int I2 = w + 1; I2 < 4; ++I2) {
@@ -647,9 +703,9 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
     // ---- phase 3b: token-major tiles of K~ hi/lo (phi channel order) and V ---------------------
     if (!tv) {   // rows past the tail (v was read clamped)
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+        for (int i = 0; i < KBW; ++i)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xv[kb][e] = (__bf16)0.f;
+            for (int e = 0; e < 8; ++e) xv[i][e] = (__bf16)0.f;
     }
     {
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -658,11 +714,11 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
             const bf16x8 sp = sel_phi(hh, q4, n16);
             const bf16x8 sn = sel_nat(hh, q4, n16);
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb) {
-                const int t = 2 * kb + hh;
-                tile_put(sKtH, t, I, q4, n16, to_bf16x4(mfma(bkh[kb], sp, zero)));
-                tile_put(sKtL, t, I, q4, n16, to_bf16x4(mfma(bkl[kb], sp, zero)));
-                tile_put(sVt, t, I, q4, n16, to_bf16x4(mfma(xv[kb], sn, zero)));
+            for (int i = 0; i < KBW; ++i) {
+                const int t = 2 * (kb0 + i) + hh;
+                tile_put(sKtH, t, I, q4, n16, to_bf16x4(mfma(bkh[i], sp, zero)));
+                tile_put(sKtL, t, I, q4, n16, to_bf16x4(mfma(bkl[i], sp, zero)));
+                tile_put(sVt, t, I, q4, n16, to_bf16x4(mfma(xv[i], sn, zero)));
             }
         }
     }
@@ -670,11 +726,11 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
 
     // ---- phase 4: W^T (phi channel tiles) and U for token block I, three-term hi/lo ----------
     const int nks = (I >= 2) ? 2 : 1;  // 32-token K steps that reach the diagonal
-    bf16x4 wT[NTD], uT[NTD];
+    bf16x4 wT[NTW], uT[NTW];
     {
-        f32x4 accW[NTD], accU[NTD];
+        f32x4 accW[NTW], accU[NTW];
 #pragma unroll
-        for (int f = 0; f < NTD; ++f) {
+        for (int f = 0; f < NTW; ++f) {
             accW[f] = f32x4{0.f, 0.f, 0.f, 0.f};
             accU[f] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
@@ -687,19 +743,19 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
 #pragma unroll
             for (int e = 0; e < 8; ++e) SPLIT_BF16(ai[e] * sBeta[32 * s + 8 * q4 + e], ah[e], al[e]);
 #pragma unroll
-            for (int ft = 0; ft < NTD; ++ft) {
-                const bf16x8 xh = tile_get(sKtH, ft, 4 * s + q4, n16);
-                const bf16x8 xl = tile_get(sKtL, ft, 4 * s + q4, n16);
-                accW[ft] = mfma(xh, ah, accW[ft]);
-                accW[ft] = mfma(xl, ah, accW[ft]);
-                accW[ft] = mfma(xh, al, accW[ft]);
+            for (int f = 0; f < NTW; ++f) {
+                const bf16x8 xh = tile_get(sKtH, tw0 + f, 4 * s + q4, n16);
+                const bf16x8 xl = tile_get(sKtL, tw0 + f, 4 * s + q4, n16);
+                accW[f] = mfma(xh, ah, accW[f]);
+                accW[f] = mfma(xl, ah, accW[f]);
+                accW[f] = mfma(xh, al, accW[f]);
             }
             // V is exact in bf16: two terms carry the product to the split's precision
 #pragma unroll
-            for (int nt = 0; nt < NTD; ++nt) {
-                const bf16x8 vv = tile_get(sVt, nt, 4 * s + q4, n16);
-                accU[nt] = mfma(ah, vv, accU[nt]);
-                accU[nt] = mfma(al, vv, accU[nt]);
+            for (int f = 0; f < NTW; ++f) {
+                const bf16x8 vv = tile_get(sVt, tw0 + f, 4 * s + q4, n16);
+                accU[f] = mfma(ah, vv, accU[f]);
+                accU[f] = mfma(al, vv, accU[f]);
             }
         }
         // W^T accumulator: lane (q4, n16) holds W[token 16I + n16][32kb + 8q4 + 4hf + r] for
@@ -707,43 +763,43 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
         const DevStore wdst(p.Wf + size_t(rec) * (64 * D), 64 * D * 2);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int i = 0; i < KBW; ++i) {
             bf16x8 oh;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                oh[r] = (__bf16)accW[2 * kb][r];
-                oh[4 + r] = (__bf16)accW[2 * kb + 1][r];
+                oh[r] = (__bf16)accW[2 * i][r];
+                oh[4 + r] = (__bf16)accW[2 * i + 1][r];
             }
-            wdst.put(unsigned((I * KB + kb) * 64 + lane) * 16, oh);
+            wdst.put(unsigned((I * KB + kb0 + i) * 64 + lane) * 16, oh);
             // token-major -W (phi channel order) for Q' = Q~ + Aqk (-W): a selection with -1
-            wT[2 * kb] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, -1.f), zero));
-            wT[2 * kb + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, -1.f), zero));
+            wT[2 * i] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, -1.f), zero));
+            wT[2 * i + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, -1.f), zero));
         }
         // U accumulator: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
         const DevStore udst(p.Uf + size_t(rec) * (64 * D), 64 * D * 4);
 #pragma unroll
-        for (int nt = 0; nt < NTD; ++nt) {
-            udst.put(unsigned((nt * 4 + I) * 64 + lane) * 16, accU[nt]);
-            uT[nt] = to_bf16x4(accU[nt]);
+        for (int f = 0; f < NTW; ++f) {
+            udst.put(unsigned(((tw0 + f) * 4 + I) * 64 + lane) * 16, accU[f]);
+            uT[f] = to_bf16x4(accU[f]);
         }
     }
     __syncthreads();   // every wave is done with the K~ and V tiles
 #pragma unroll
-    for (int t = 0; t < NTD; ++t) {
-        tile_put(sW, t, I, q4, n16, wT[t]);
-        tile_put(sU, t, I, q4, n16, uT[t]);
+    for (int f = 0; f < NTW; ++f) {
+        tile_put(sW, tw0 + f, I, q4, n16, wT[f]);
+        tile_put(sU, tw0 + f, I, q4, n16, uT[f]);
     }
     __syncthreads();
 
     // ---- phase 5: O_intra^T = U^T Aqk^T and Q'^T = Q~^T - W^T Aqk^T (token block I) --------
     {
-        f32x4 accO[NTD], accQ[NTD];
+        f32x4 accO[NTW], accQ[NTW];
 #pragma unroll
-        for (int f = 0; f < NTD; ++f) {
+        for (int f = 0; f < NTW; ++f) {
             accO[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int kb = f >> 1, hf = f & 1;
+            const int i = f >> 1, hf = f & 1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) accQ[f][r] = Qt[kb * 8 + 4 * hf + r];
+            for (int r = 0; r < 4; ++r) accQ[f][r] = Qt[i * 8 + 4 * hf + r];
         }
         for (int s = 0; s < nks; ++s) {
             float aq[8];
@@ -752,32 +808,32 @@ __global__ __launch_bounds__(kThreads, IntraLds<D>::PER_CU) void kda_intra_kerne
 #pragma unroll
             for (int e = 0; e < 8; ++e) SPLIT_BF16(aq[e], qh[e], ql[e]);
 #pragma unroll
-            for (int nt = 0; nt < NTD; ++nt) {
-                const bf16x8 a = tile_get(sU, nt, 4 * s + q4, n16);
-                accO[nt] = mfma(a, qh, accO[nt]);
-                accO[nt] = mfma(a, ql, accO[nt]);
+            for (int f = 0; f < NTW; ++f) {
+                const bf16x8 a = tile_get(sU, tw0 + f, 4 * s + q4, n16);
+                accO[f] = mfma(a, qh, accO[f]);
+                accO[f] = mfma(a, ql, accO[f]);
             }
 #pragma unroll
-            for (int ft = 0; ft < NTD; ++ft) {
-                const bf16x8 a = tile_get(sW, ft, 4 * s + q4, n16);   // -W
-                accQ[ft] = mfma(a, qh, accQ[ft]);
-                accQ[ft] = mfma(a, ql, accQ[ft]);
+            for (int f = 0; f < NTW; ++f) {
+                const bf16x8 a = tile_get(sW, tw0 + f, 4 * s + q4, n16);   // -W
+                accQ[f] = mfma(a, qh, accQ[f]);
+                accQ[f] = mfma(a, ql, accQ[f]);
             }
         }
         const DevStore odst(p.Of + size_t(rec) * (64 * D), 64 * D * 2);
 #pragma unroll
-        for (int nt = 0; nt < NTD; ++nt)
-            odst.put(unsigned((nt * 4 + I) * 64 + lane) * 8, to_bf16x4(accO[nt]));
+        for (int f = 0; f < NTW; ++f)
+            odst.put(unsigned(((tw0 + f) * 4 + I) * 64 + lane) * 8, to_bf16x4(accO[f]));
         const DevStore qdst(p.Qf + size_t(rec) * (64 * D), 64 * D * 2);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
+        for (int i = 0; i < KBW; ++i) {
             bf16x8 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                o[r] = (__bf16)accQ[2 * kb][r];
-                o[4 + r] = (__bf16)accQ[2 * kb + 1][r];
+                o[r] = (__bf16)accQ[2 * i][r];
+                o[4 + r] = (__bf16)accQ[2 * i + 1][r];
             }
-            qdst.put(unsigned((I * KB + kb) * 64 + lane) * 16, o);
+            qdst.put(unsigned((I * KB + kb0 + i) * 64 + lane) * 16, o);
         }
     }
 }
@@ -1766,9 +1822,12 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     const bool sg = (p.flags & KDA_SCALAR_GATE) != 0;
     const bool d64 = plan.d == 64;
     auto fn = [](auto f) { return reinterpret_cast<const void*>(f); };
+    const bool hv2 = plan.intra_hv == 2;
     const void* intra =
-        d64 ? (sg ? fn(&kda_intra_kernel<true, 64>) : fn(&kda_intra_kernel<false, 64>))
-            : (sg ? fn(&kda_intra_kernel<true, 128>) : fn(&kda_intra_kernel<false, 128>));
+        hv2 ? (d64 ? (sg ? fn(&kda_intra_kernel<true, 64, 2>) : fn(&kda_intra_kernel<false, 64, 2>))
+                   : (sg ? fn(&kda_intra_kernel<true, 128, 2>) : fn(&kda_intra_kernel<false, 128, 2>)))
+            : (d64 ? (sg ? fn(&kda_intra_kernel<true, 64, 1>) : fn(&kda_intra_kernel<false, 64, 1>))
+                   : (sg ? fn(&kda_intra_kernel<true, 128, 1>) : fn(&kda_intra_kernel<false, 128, 1>)));
     // one stage: its kernel, or (not enqueued by this plan) its two events back to back
     auto stage = [&](int sidx, const void* kernel, int64_t grid, unsigned threads) -> kda_status {
         if (kernel)
@@ -1800,7 +1859,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
                       : plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 128, false>)
                                           : fn(&kda_scan_kernel<1, 128, false>));
     }
-    if ((st = stage(ST_INTRA, intra, plan.intra_blocks, kThreads)) != KDA_OK) return st;
+    if ((st = stage(ST_INTRA, intra, plan.intra_blocks, kThreads * plan.intra_hv)) != KDA_OK) return st;
     if ((st = stage(ST_SEG, segk, plan.seg_blocks, kThreads)) != KDA_OK) return st;
     if ((st = stage(ST_COMB, combk, plan.comb_blocks, kThreads)) != KDA_OK) return st;
     if ((st = stage(ST_OUT, outk, plan.out_blocks, kThreads)) != KDA_OK) return st;

@@ -56,6 +56,10 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     }
     p.n_records = p.n_slots * s->n_v;
     p.intra_blocks = p.n_records;
+    // At most one intra workgroup per compute unit: its latency is the stage's time, and
+    // eight waves (two per token block) shorten it; with more workgroups the four-wave form,
+    // two or three per compute unit, overlaps one's memory phases with another's arithmetic.
+    p.intra_hv = p.intra_blocks <= 256 ? 2 : 1;
     // Each scan workgroup streams a whole chunk record per step whatever its Dv width, so a
     // wider tile cuts the bytes streamed per unit of work; it is taken only while enough
     // workgroups remain to occupy all 256 compute units of an MI355X.
