@@ -73,6 +73,7 @@ struct Params {
     int layout, batch, seq_len, n_qk, n_v, group, nc_max;
     int scan_tiles;
     int seg_p;     // segments per sequence of the two-level scan (1 = one level)
+    int intra_units;   // intra kernel: records / group (chunk slot, q/k head) units
     float scale;
     uint32_t flags;
 };
@@ -365,9 +366,18 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     const int kb0 = hc * KBW;                 // first channel block of this wave
     const int tw0 = hc * NTW;                 // first W/Q' and U/O_intra tile of this wave
 
-    const int64_t rec = blockIdx.x;
-    const int slot = int(blockIdx.x / unsigned(p.n_v));   // 32-bit: grids stay below 2^31
-    const int h = int(blockIdx.x - unsigned(slot) * unsigned(p.n_v));
+    // Record rec = slot * n_v + h = unit * group + m, unit = slot * n_qk + hq.  With GQA the
+    // group value heads of a unit (one chunk of one q/k head) run on one XCD, dispatched one
+    // after another, so its L2 fetches that q/k chunk once: workgroup 8 r + x takes unit
+    // (r / group) 8 + x, member r mod group (the identity without GQA).
+    const unsigned pid = blockIdx.x;
+    const unsigned gr = unsigned(p.group);
+    const unsigned rr = pid >> 3;
+    const unsigned unit = (rr / gr) * 8u + (pid & 7u);
+    if (unit >= unsigned(p.intra_units)) return;   // grid padding
+    const int64_t rec = int64_t(unit) * gr + rr % gr;
+    const int slot = int(rec / p.n_v);   // grids stay below 2^31
+    const int h = int(rec - int64_t(slot) * p.n_v);
     const int hq = h / p.group;
 
     // chunk slot -> (sequence b, chunk j)
@@ -1816,6 +1826,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.Rf = two ? reinterpret_cast<__bf16*>(ws + plan.off_r) : nullptr;
     p.scale = shape->scale;
     p.flags = shape->flags;
+    p.intra_units = int(plan.n_records / plan.group);
 
     (void)hipGetLastError();  // clear a stale error so the checks below see only ours
     auto e = [&](int i) { return ev ? ev[i] : hipEvent_t(nullptr); };

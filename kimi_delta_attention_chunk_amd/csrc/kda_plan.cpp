@@ -55,7 +55,8 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
         p.n_slots = int64_t(s->batch) * p.nc_max;
     }
     p.n_records = p.n_slots * s->n_v;
-    p.intra_blocks = p.n_records;
+    // intra grid: units (chunk slot, q/k head) padded to a multiple of 8, times the group
+    p.intra_blocks = (p.n_records / p.group + 7) / 8 * 8 * p.group;
     // At most one intra workgroup per compute unit: its latency is the stage's time, and
     // eight waves (two per token block) shorten it; with more workgroups the four-wave form,
     // two or three per compute unit, overlaps one's memory phases with another's arithmetic.
