@@ -117,25 +117,29 @@ def seg_bytes(inp) -> int:
 
 
 def combine_bytes(inp) -> int:
-    """Compulsory bytes of the combine pass: N and P of every segment in (4 bytes a value),
-    S_in of segments 1.. (bf16) and the final state (fp32) out."""
+    """Compulsory bytes of the combine pass: N_0 and the N and P of segments 1 .. seg_p-2 in
+    (4 bytes a value), S_in of segments 1.. out (bf16) and S_in of the last segment out in fp32
+    (for the final-state step of the completion pass)."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     m = inp.batch * inp.n_v * d * d * 4
-    return m * (2 * sp - 1) + m // 2 * (sp - 1) + m
+    return m * (2 * sp - 3) + m // 2 * (sp - 1) + m
 
 
 def out_bytes(inp) -> int:
     """Compulsory bytes of the completion pass: O0 and R of every chunk of segments 1.. and
-    S_in of those segments in, the outputs out (all bf16)."""
+    S_in of those segments in, the outputs out (all bf16); for the final state, S_in of the last
+    segment (fp32), its N and P in and the state out (4 bytes a value)."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     _, later = chunk_counts(inp, sp)
-    return inp.n_v * later * 64 * d * (2 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 2
+    m = inp.batch * inp.n_v * d * d * 4
+    return (inp.n_v * later * 64 * d * (2 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 2
+            + 4 * m)
 
 
 KERNEL_BYTES = {"kda_intra_kernel": intra_bytes, "kda_seg_kernel": seg_bytes,

@@ -1587,10 +1587,13 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
 }
 
 // Combine pass of the two-level scan: D/16 workgroups per (sequence, head), one 16-row Dv tile
-// each, form S_in(1) = N_0 and S_in(s+1) = S_in(s) P_s + N_s, store every S_in(s) and, with a
-// final state, S_in(seg_p-1) P_last + N_last.  No step's operands depend on an earlier step,
-// so they load two steps ahead, in three register sets (a load past the end rereads the last
-// step's matrices, never used).  Few workgroups: the register budget of one per compute unit.
+// each, form S_in(1) = N_0 and S_in(s+1) = S_in(s) P_s + N_s and store every S_in(s) (bf16,
+// for the completion pass).  With a final state it also keeps S_in(seg_p-1) in fp32, in the
+// place of N_0 (whose rows only this workgroup reads, at its start): the last product,
+// S_in(seg_p-1) P_last + N_last, runs in the completion pass beside the outputs, so that the
+// outputs do not wait for it.  No step's operands depend on an earlier step, so they load two
+// steps ahead, in three register sets (a load past the end rereads the last step's matrices,
+// never used).  Few workgroups: the register budget of one per compute unit.
 template <int D>
 __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
     constexpr int MW = HD<D>::MW, KB = HD<D>::KB, TILES = HD<D>::TILES;
@@ -1613,7 +1616,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
     const int h = bh % p.n_v;
     auto mat = [&](int s) { return (size_t(bh) * p.seg_p + s) * D * D; };
 
-    const int last = p.fin ? p.seg_p - 1 : p.seg_p - 2;   // steps 1 .. last
+    const int last = p.seg_p - 2;   // steps 1 .. last: S_in(2) .. S_in(seg_p - 1)
     auto at = [&](int s) { return mat(s < last ? s : (last > 0 ? last : 1)); };
     f32x4 S[MW][1];
 #pragma unroll
@@ -1663,14 +1666,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
         combine_step<1, D>(c1f, S, L);
         ++s;
     }
-    if (s < p.seg_p) store_in(s);   // S_in(seg_p - 1) without a final state
-    const int row = 16 * tile + n16;
+    store_in(s);   // S_in(seg_p - 1)
     if (p.fin) {
-        float* dst = p.fin + (size_t(b) * p.n_v + h) * D * D;
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
-            *reinterpret_cast<f32x4*>(dst + size_t(row) * D + 16 * (MW * w + mt) + 4 * q4) =
-                S[mt][0];
+            *reinterpret_cast<f32x4*>(p.Nst + mat(0) +
+                                      ((tile * TILES + MW * w + mt) * 64 + lane) * 4) = S[mt][0];
     }
 
     int c0, len, slot0;
@@ -1680,15 +1681,49 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
     zero_rows_past_len(p, len, ob, os, 16 * tile, 16);
 }
 
+// Final state of one 16-row Dv tile of a (sequence, head): S_in(seg_p-1) P_last + N_last, with
+// S_in(seg_p-1) in fp32 where the combine pass left it (the place of N_0).
+template <int D>
+__device__ __forceinline__ void final_state_step(const Params& p, int f, __bf16* lds) {
+    constexpr int MW = HD<D>::MW, TILES = HD<D>::TILES;
+    const int bh = f / TILES, tile = f % TILES;
+    if (bh >= p.batch * p.n_v) return;
+    const int w = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+    const ScanLds L{lds, lds + 16 * HD<D>::SLD, nullptr, nullptr, nullptr};
+    const size_t m0 = size_t(bh) * p.seg_p * D * D;
+    const size_t ml = m0 + size_t(p.seg_p - 1) * D * D;
+    f32x4 S[MW][1];
+    CombFrags<1, D> cf;
+    load_comb<1, D>(p.Pt + 2 * ml, p.Nst + ml, tile, cf);
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt) {
+        S[mt][0] = *reinterpret_cast<const f32x4*>(p.Nst + m0 +
+                                                   ((tile * TILES + MW * w + mt) * 64 + lane) * 4);
+        put_state<D>(L.sh, L.sl, n16, 16 * (MW * w + mt) + 4 * q4, S[mt][0]);
+    }
+    lds_barrier();
+    combine_step<1, D>(cf, S, L);
+    float* dst = p.fin + size_t(bh) * D * D + size_t(16 * tile + n16) * D;
+#pragma unroll
+    for (int mt = 0; mt < MW; ++mt)
+        *reinterpret_cast<f32x4*>(dst + 16 * (MW * w + mt) + 4 * q4) = S[mt][0];
+}
+
 // Completion pass of the two-level scan: one workgroup per record of a chunk in segment
 // s >= 1, out = O0 + R S_in(s)^T from bf16 S_in, R and O0 with fp32 sums (as O^T = S_in R^T:
 // the accumulator holds four consecutive value channels of one token per lane).  Wave w takes Dv
 // tiles D/64 w .. of all 64 tokens.  R, which every wave multiplies, is read from HBM once into
-// LDS; every operand is loaded before the first output is stored.
+// LDS; every operand is loaded before the first output is stored.  The workgroups after the
+// records form the final states (final_state_step), one per 16-row Dv tile of each (sequence,
+// head).
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     constexpr int KB = HD<D>::KB, NTW = D / 64;
     constexpr int R_U4 = 64 * D * 2 / 16;   // R in 16-byte units
+    static_assert(R_U4 * 16 >= 2 * 16 * HD<D>::SLD * 2, "the state tiles fit the R buffer");
     __shared__ __attribute__((aligned(16))) bf16x8 sR[R_U4];
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1697,6 +1732,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     const int n16 = lane & 15;
 
     const int64_t rec = blockIdx.x;
+    const int64_t n_rec = int64_t(p.intra_units) * p.group;
+    if (rec >= n_rec) {
+        if (p.fin) final_state_step<D>(p, int(rec - n_rec), reinterpret_cast<__bf16*>(sR));
+        return;
+    }
     const int slot = int(blockIdx.x / unsigned(p.n_v));
     const int h = int(blockIdx.x - unsigned(slot) * unsigned(p.n_v));
     const int b = slot_batch(p, slot);

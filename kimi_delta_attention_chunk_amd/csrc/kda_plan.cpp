@@ -106,7 +106,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
         }
         p.seg_blocks = rows * 8;
         p.comb_blocks = bh8 * tiles;
-        p.out_blocks = p.n_records;
+        p.out_blocks = p.n_records + bh * tiles;   // records, then final-state tiles
     } else {
         p.scan_blocks = bh8 * p.scan_tiles;
         // a prefetch wave costs the second workgroup per compute unit: only when one per unit

@@ -49,7 +49,8 @@ struct Plan {
     int seg_p = 1;             // segments per sequence of the two-level scan (1 = one level)
     int64_t seg_blocks = 0;    // two-level: segment pass, (2 seg_p - 1) d/16 per (sequence, head)
     int64_t comb_blocks = 0;   // two-level: segment combine, d/16 per (sequence, head)
-    int64_t out_blocks = 0;    // two-level: output completion, one per record
+    int64_t out_blocks = 0;    // two-level: output completion, one per record, then one per
+                               // Dv tile of each (sequence, head) for the final state
     // byte offsets of each workspace array (256-byte aligned)
     size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0;
     // two-level only: per (sequence, head, segment) transfer matrix P_s (transposed, hi/lo
