@@ -45,6 +45,8 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -60,7 +62,7 @@ struct Params {
     float* fin;
     __bf16* Wf;   // [record][tt 4][kb 4][lane 64][8]         W[16tt+m][32kb+8q+j]
     __bf16* Qf;   // [record][tt 4][kb 4][lane 64][8]         Q'[16tt+m][32kb+8q+j]
-    __bf16* Kf;   // [record][hi/lo][mt 8][s 2][lane 64][8]   K_dec[32s+8q+j][16mt+m]
+    _Float16* Kf; // [record][mt 8][s 2][lane 64][8]          K_dec[32s+8q+j][16mt+m] (fp16)
     float* Uf;    // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n]
     __bf16* Of;   // [record][nt 8][tt 4][lane 64][4]         O_intra[16tt+n][16nt+4q+i]
     float* Gf;    // [record][128]                            2^(G2_last)
@@ -80,6 +82,9 @@ struct Params {
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma(f16x8 a, f16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -277,6 +282,12 @@ __device__ __forceinline__ bf16x8 sel_nat(int h, int q4, int n16) {
     for (int j = 0; j < 8; ++j) r[j] = (8 * q4 + j == 16 * h + n16) ? (__bf16)1.f : (__bf16)0.f;
     return r;
 }
+__device__ __forceinline__ f16x8 sel_nat16(int h, int q4, int n16) {
+    f16x8 r;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) r[j] = (8 * q4 + j == 16 * h + n16) ? (_Float16)1.f : (_Float16)0.f;
+    return r;
+}
 __device__ __forceinline__ bf16x8 sel_phi(int h, int q4, int n16, float one = 1.f) {
     bf16x8 r;
 #pragma unroll
@@ -289,6 +300,12 @@ __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
     bf16x4 r;
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[i] = (__bf16)x[i];
+    return r;
+}
+__device__ __forceinline__ f16x4 to_f16x4(f32x4 x) {
+    f16x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = (_Float16)x[i];
     return r;
 }
 
@@ -538,14 +555,14 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     float Lk[8 * KBW], Lq[8 * KBW];
     bf16x8 KFb[KBW];
     {
-        const DevStore kdst(p.Kf + size_t(rec) * (64 * D * 2), 64 * D * 2 * 2);
+        const DevStore kdst(p.Kf + size_t(rec) * (64 * D), 64 * D * 2);
         const int s_k = I >> 1;
         const int lane_k = (2 * (I & 1) + (q4 >> 1)) * 16 + n16;
         const int j0 = 4 * (q4 & 1);
 #pragma unroll
         for (int i = 0; i < KBW; ++i) {
             const int kb = kb0 + i;
-            bf16x8 kdh, kdl;
+            f16x8 kd;
             float kf[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -560,7 +577,7 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
                 Lq[ii] = (float)xq[i][e] * qn * ef;
                 kf[e] = kv * ff;
                 KFb[i][e] = (__bf16)kf[e];
-                SPLIT_BF16(kf[e] * sVec[(VEC_C + I) * 128 + c], kdh[e], kdl[e]);   // K_dec <= 1
+                kd[e] = (_Float16)(kf[e] * sVec[(VEC_C + I) * 128 + c]);   // K_dec <= |k|, one fp16 value
             }
             // the key operand of every later row block I2 > I: k_j exp(G[16 I2] - G_j) <= 1
             for (int I2 = I + 1; I2 < 4; ++I2) {
@@ -571,17 +588,13 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
                 for (int e = 0; e < 8; ++e) r[e] = (__bf16)(kf[e] * bv[e]);
                 sR[(pi * KB + kb) * 64 + lane] = r;
             }
-            // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [hi/lo][mt D/16][s 2][lane 64][8]
+            // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [mt D/16][s 2][lane 64][8] fp16
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
-                const bf16x8 sel = sel_nat(hh, q4, n16);
                 const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-                const bf16x4 th = to_bf16x4(mfma(kdh, sel, zero));
-                const bf16x4 tl = to_bf16x4(mfma(kdl, sel, zero));
+                const f16x4 th = to_f16x4(mfma(kd, sel_nat16(hh, q4, n16), zero));
                 const int mt = 2 * kb + hh;
-                const unsigned at = unsigned(((mt * 2 + s_k) * 64 + lane_k) * 8 + j0) * 2;
-                kdst.put(at, th);
-                kdst.put(at + 64 * D * 2, tl);
+                kdst.put(unsigned(((mt * 2 + s_k) * 64 + lane_k) * 8 + j0) * 2, th);
             }
         }
     }
@@ -890,7 +903,7 @@ template <int NT, int D>
 struct ChunkFrags {
     bf16x8 w[HD<D>::KB];                          // W, token tile w, 32-channel block kb
     bf16x8 qp[HD<D>::KB];                         // Q', token tile w
-    bf16x8 kh[HD<D>::MW][2], kl[HD<D>::MW][2];    // K_dec^T hi/lo, Dk tile MW*w+mt, token step s
+    f16x8 kh[HD<D>::MW][2];                       // K_dec^T (fp16), Dk tile MW*w+mt, token step s
     f32x4 gm[HD<D>::MW];                          // gamma_last for the lane's Dk rows, or
     float g[D / 64];                              // gamma_last[lane D/64 ..] (wave 0, GLDS)
     f32x4 u[NT];                                  // U (fp32), token tile w, Dv tile
@@ -927,14 +940,13 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
         }
     }
     if constexpr (PART != 1) {
-        const __bf16* ksrc = p.Kf + size_t(rec) * (64 * D * 2);
+        const _Float16* ksrc = p.Kf + size_t(rec) * (64 * D);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int off = (((MW * w + mt) * 2 + s) * 64 + lane) * 8;
-                f.kh[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + off);
-                f.kl[mt][s] = *reinterpret_cast<const bf16x8*>(ksrc + 64 * D + off);
+                f.kh[mt][s] = *reinterpret_cast<const f16x8*>(ksrc + off);
             }
         if constexpr (GLDS) {
             if (w == 0) {
@@ -1023,15 +1035,16 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
     const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        bf16x4 vh, vl;
+        f16x4 vh, vl;   // V_new as an fp16 pair, the operand of the fp16 update product
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float u = WITH_U ? cur.u[nt][r] : 0.f;
-            SPLIT_BF16(u - accX[nt][r], vh[r], vl[r]);
+            const float x = (WITH_U ? cur.u[nt][r] : 0.f) - accX[nt][r];
+            vh[r] = (_Float16)x;
+            vl[r] = (_Float16)(x - (float)vh[r]);
         }
         const int off = (16 * nt + n16) * VN_LD + 16 * w + 4 * q4;
-        *reinterpret_cast<bf16x4*>(L.vh + off) = vh;
-        *reinterpret_cast<bf16x4*>(L.vl + off) = vl;
+        *reinterpret_cast<f16x4*>(L.vh + off) = vh;
+        *reinterpret_cast<f16x4*>(L.vl + off) = vl;
         if constexpr (OUT == OUT_FINAL) {
             if (tok < len) {
                 bf16x4 o;
@@ -1078,15 +1091,16 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
     }
     lds_barrier();
 
-    // S^T <- gamma * S^T + K_dec^T V_new  (Dk rows of this wave x Dv), three-term hi/lo
+    // S^T <- gamma * S^T + K_dec^T V_new  (Dk rows of this wave x Dv) on the fp16 MFMA: K_dec
+    // (one fp16 value, at most |k|) times V_new as an fp16 hi/lo pair
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-        bf16x8 vh[2], vl[2];
+        f16x8 vh[2], vl[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             const int off = (16 * nt + n16) * VN_LD + 32 * s + 8 * q4;
-            vh[s] = *reinterpret_cast<const bf16x8*>(L.vh + off);
-            vl[s] = *reinterpret_cast<const bf16x8*>(L.vl + off);
+            vh[s] = *reinterpret_cast<const f16x8*>(L.vh + off);
+            vl[s] = *reinterpret_cast<const f16x8*>(L.vl + off);
         }
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt) {
@@ -1096,7 +1110,6 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 acc = mfma(cur.kh[mt][s], vh[s], acc);
-                acc = mfma(cur.kl[mt][s], vh[s], acc);
                 acc = mfma(cur.kh[mt][s], vl[s], acc);
             }
             S[mt][nt] = acc;
@@ -1284,7 +1297,7 @@ struct RecPrefetch {
     __device__ __forceinline__ void init(const Params& p, int part, int parts, int dv_tile0,
                                          int own_tiles) {
         constexpr int WL = 64 * D * 2 / 128;   // lines of W, and of Q'
-        constexpr int KL = 2 * WL;            // K_dec hi + lo
+        constexpr int KL = WL;                // K_dec (fp16)
         constexpr int GL = D * 4 / 128;       // gamma
         constexpr int NS = 2 * WL + KL + GL;
         const int sh = (NS + parts - 1) / parts;
@@ -1307,7 +1320,7 @@ struct RecPrefetch {
                 } else if (s < 2 * WL) {
                     b = reinterpret_cast<const unsigned char*>(p.Qf); st = 64 * D * 2; off = size_t(s - WL) * 128;
                 } else if (s < 2 * WL + KL) {
-                    b = reinterpret_cast<const unsigned char*>(p.Kf); st = 64 * D * 4; off = size_t(s - 2 * WL) * 128;
+                    b = reinterpret_cast<const unsigned char*>(p.Kf); st = 64 * D * 2; off = size_t(s - 2 * WL) * 128;
                 } else {
                     b = reinterpret_cast<const unsigned char*>(p.Gf); st = D * 4; off = size_t(s - 2 * WL - KL) * 128;
                 }
@@ -1845,7 +1858,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     p.Wf = reinterpret_cast<__bf16*>(ws + plan.off_w);
     p.Qf = reinterpret_cast<__bf16*>(ws + plan.off_q);
-    p.Kf = reinterpret_cast<__bf16*>(ws + plan.off_k);
+    p.Kf = reinterpret_cast<_Float16*>(ws + plan.off_k);
     p.Uf = reinterpret_cast<float*>(ws + plan.off_u);
     p.Of = reinterpret_cast<__bf16*>(ws + plan.off_o);
     p.Gf = reinterpret_cast<float*>(ws + plan.off_g);
