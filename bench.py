@@ -63,9 +63,9 @@ def seg_p_of(inp) -> int:
 
 
 def record_bytes(d: int) -> int:
-    """Workspace record per (chunk, value head): W, Q' (bf16), K_dec (fp16), U (fp32),
-    O_intra (bf16), gamma (fp32 per channel)."""
-    return 64 * d * (2 + 2 + 2 + 4 + 2) + d * 4
+    """Workspace record per (chunk, value head): W, Q' (bf16), K_dec, U (fp16), O_intra
+    (bf16), gamma (fp32 per channel)."""
+    return 64 * d * (2 + 2 + 2 + 2 + 2) + d * 4
 
 
 def chunk_counts(inp, sp: int):

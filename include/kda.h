@@ -29,9 +29,9 @@
  *   - Not checked (preconditions, as in the FlashKDA README, section 约束说明): cu_seqlens
  *     starts at 0, is strictly increasing and ends at seq_len (TND); with BNSD/BSND each valid
  *     length lies in [1, seq_len]; -5 <= g <= 0; all tensors live on one device.  The decayed
- *     keys (at most |k|) and the innovation v - S k of the state update are fp16 operands of one
- *     product: both stay far below the fp16 limit of 65504 with L2-normalised keys and values
- *     of ordinary size (larger magnitudes overflow to inf).
+ *     keys (at most |k|), the values transformed inside a chunk (about |v|) and the innovation
+ *     v - S k of the state update are held in fp16: they stay far below the fp16 limit of 65504
+ *     with L2-normalised keys and values of ordinary size (larger magnitudes overflow to inf).
  */
 #ifndef KDA_H_
 #define KDA_H_

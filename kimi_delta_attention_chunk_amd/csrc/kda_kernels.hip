@@ -63,7 +63,7 @@ struct Params {
     __bf16* Wf;   // [record][tt 4][kb 4][lane 64][8]         W[16tt+m][32kb+8q+j]
     __bf16* Qf;   // [record][tt 4][kb 4][lane 64][8]         Q'[16tt+m][32kb+8q+j]
     _Float16* Kf; // [record][mt 8][s 2][lane 64][8]          K_dec[32s+8q+j][16mt+m] (fp16)
-    float* Uf;    // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n]
+    _Float16* Uf; // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n] (fp16)
     __bf16* Of;   // [record][nt 8][tt 4][lane 64][4]         O_intra[16tt+n][16nt+4q+i]
     float* Gf;    // [record][128]                            2^(G2_last)
     // two-level scan, per (sequence*head, segment) and per record, in MFMA fragment order:
@@ -799,10 +799,10 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
             wT[2 * i + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, -1.f), zero));
         }
         // U accumulator: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
-        const DevStore udst(p.Uf + size_t(rec) * (64 * D), 64 * D * 4);
+        const DevStore udst(p.Uf + size_t(rec) * (64 * D), 64 * D * 2);
 #pragma unroll
         for (int f = 0; f < NTW; ++f) {
-            udst.put(unsigned(((tw0 + f) * 4 + I) * 64 + lane) * 16, accU[f]);
+            udst.put(unsigned(((tw0 + f) * 4 + I) * 64 + lane) * 8, to_f16x4(accU[f]));
             uT[f] = to_bf16x4(accU[f]);
         }
     }
@@ -906,7 +906,7 @@ struct ChunkFrags {
     f16x8 kh[HD<D>::MW][2];                       // K_dec^T (fp16), Dk tile MW*w+mt, token step s
     f32x4 gm[HD<D>::MW];                          // gamma_last for the lane's Dk rows, or
     float g[D / 64];                              // gamma_last[lane D/64 ..] (wave 0, GLDS)
-    f32x4 u[NT];                                  // U (fp32), token tile w, Dv tile
+    f16x4 u[NT];                                  // U (fp16), token tile w, Dv tile
     bf16x4 o[NT];                                 // O_intra (bf16), token tile w, Dv tile
 };
 
@@ -928,13 +928,13 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
             if constexpr (OUT != OUT_NONE)
                 f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * KB + kb) * 64 + lane) * 8);
         }
-        const float* usrc = p.Uf + size_t(rec) * (64 * D);
+        const _Float16* usrc = p.Uf + size_t(rec) * (64 * D);
         const __bf16* osrc = p.Of + size_t(rec) * (64 * D);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int dt = dv_tile0 + nt;
             if constexpr (WITH_U)
-                f.u[nt] = *reinterpret_cast<const f32x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
+                f.u[nt] = *reinterpret_cast<const f16x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
             if constexpr (OUT == OUT_FINAL || OUT == OUT_O0)
                 f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
         }
@@ -1038,7 +1038,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
         f16x4 vh, vl;   // V_new as an fp16 pair, the operand of the fp16 update product
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float x = (WITH_U ? cur.u[nt][r] : 0.f) - accX[nt][r];
+            const float x = (WITH_U ? (float)cur.u[nt][r] : 0.f) - accX[nt][r];
             vh[r] = (_Float16)x;
             vl[r] = (_Float16)(x - (float)vh[r]);
         }
@@ -1303,7 +1303,7 @@ struct RecPrefetch {
         const int sh = (NS + parts - 1) / parts;
         const int s0 = part * sh;
         const int scnt = NS - s0 < sh ? NS - s0 : sh;
-        const int ucnt = 32 * own_tiles;      // 4 KiB of U per tile
+        const int ucnt = 16 * own_tiles;      // 2 KiB of U per tile
         const int total = scnt + ucnt + 16 * own_tiles;
         const int lane = threadIdx.x & 63;
 #pragma unroll
@@ -1325,8 +1325,8 @@ struct RecPrefetch {
                     b = reinterpret_cast<const unsigned char*>(p.Gf); st = D * 4; off = size_t(s - 2 * WL - KL) * 128;
                 }
             } else if (li < scnt + ucnt) {
-                b = reinterpret_cast<const unsigned char*>(p.Uf); st = 64 * D * 4;
-                off = size_t(dv_tile0) * 4096 + size_t(li - scnt) * 128;
+                b = reinterpret_cast<const unsigned char*>(p.Uf); st = 64 * D * 2;
+                off = size_t(dv_tile0) * 2048 + size_t(li - scnt) * 128;
             } else {
                 b = reinterpret_cast<const unsigned char*>(p.Of); st = 64 * D * 2;
                 off = size_t(dv_tile0) * 2048 + size_t(li - scnt - ucnt) * 128;
@@ -1859,7 +1859,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.Wf = reinterpret_cast<__bf16*>(ws + plan.off_w);
     p.Qf = reinterpret_cast<__bf16*>(ws + plan.off_q);
     p.Kf = reinterpret_cast<_Float16*>(ws + plan.off_k);
-    p.Uf = reinterpret_cast<float*>(ws + plan.off_u);
+    p.Uf = reinterpret_cast<_Float16*>(ws + plan.off_u);
     p.Of = reinterpret_cast<__bf16*>(ws + plan.off_o);
     p.Gf = reinterpret_cast<float*>(ws + plan.off_g);
     p.layout = plan.layout;

@@ -15,21 +15,21 @@ constexpr int kThreads = 256;
 constexpr bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
 // Per (chunk slot, value head) workspace record for head dim D, in bytes.  Layouts are the MFMA
-// fragment orders the scan kernel reads (see kda_kernels.hip).  U is kept in fp32, so that the
-// innovation V_new = U - W S^T (a small difference of large terms once the state predicts v
-// well) keeps its low bits; K_dec (at most |k| <= 1 with L2-normalised keys) is one fp16 value,
-// 11 significant bits, multiplied on the fp16 MFMA with V_new as an fp16 hi/lo pair.
+// fragment orders the scan kernel reads (see kda_kernels.hip).  U and K_dec (at most |k| <= 1
+// with L2-normalised keys) are fp16, 11 significant bits, three more than bf16: the innovation
+// V_new = U - W S^T (a small difference of large terms once the state predicts v well) is formed
+// in fp32 and multiplied with K_dec on the fp16 MFMA as an fp16 hi/lo pair.
 constexpr size_t rec_w_bytes(int d) { return size_t(kChunk) * d * 2; }       // W       bf16
 constexpr size_t rec_q_bytes(int d) { return size_t(kChunk) * d * 2; }       // Q'      bf16
 constexpr size_t rec_k_bytes(int d) { return size_t(kChunk) * d * 2; }       // K_dec   fp16
-constexpr size_t rec_u_bytes(int d) { return size_t(kChunk) * d * 4; }       // U       fp32
+constexpr size_t rec_u_bytes(int d) { return size_t(kChunk) * d * 2; }       // U       fp16
 constexpr size_t rec_o_bytes(int d) { return size_t(kChunk) * d * 2; }       // O_intra bf16
 constexpr size_t rec_g_bytes(int d) { return size_t(d) * 4; }                // gamma_last fp32
 constexpr size_t rec_bytes(int d) {
     return rec_w_bytes(d) + rec_q_bytes(d) + rec_k_bytes(d) + rec_u_bytes(d) + rec_o_bytes(d) +
            rec_g_bytes(d);
 }
-static_assert(rec_bytes(128) == 98816, "record of a 128-dim head");
+static_assert(rec_bytes(128) == 82432, "record of a 128-dim head");
 
 struct Plan {
     int layout = 0;

@@ -60,12 +60,12 @@ def ws(lib, shape):
 def test_workspace_sizes(lib):
     st, n1 = ws(lib, make_shape("BNSD", 1, 8192, 3, 3, 0.088))
     assert st == 0
-    # 128 chunks x 3 heads x (W, K_dec fp16, U fp32, Q', O_intra bf16, gamma), plus the
+    # 128 chunks x 3 heads x (W, K_dec fp16, U fp16, Q', O_intra bf16, gamma), plus the
     # two-level scan (3 x (2 x 5 - 1) x 8 = 216 segment-pass workgroups -> 5 segments): per
     # segment P_s and N_s (4-byte 128x128) and S_in (bf16 128x128), per record O0 and R (bf16
     # 64x128)
-    rec = 16384 + 16384 + 16384 + 32768 + 16384 + 512
-    assert rec == 98816
+    rec = 16384 + 16384 + 16384 + 16384 + 16384 + 512
+    assert rec == 82432
     two = 3 * 5 * (2 * 65536 + 32768) + 384 * 2 * 16384
     assert n1 >= 128 * 3 * rec + two
     assert n1 < 128 * 3 * rec + two + 16 * 256
@@ -73,14 +73,14 @@ def test_workspace_sizes(lib):
     st, n4 = ws(lib, make_shape("BNSD", 1, 8192, 32, 32, 0.088))
     assert st == 0 and n4 < 128 * 32 * rec + 16 * 256
     st, n2 = ws(lib, make_shape("TND", 32, 65536, 32, 32, 0.088))
-    assert st == 0 and n2 >= (65536 // 64 + 32) * 32 * 98816
+    assert st == 0 and n2 >= (65536 // 64 + 32) * 32 * 82432
     # a ragged tail adds one chunk slot per batch row
     st, n3 = ws(lib, make_shape("BSND", 4, 4100, 4, 16, 0.088))
-    assert st == 0 and n3 >= 4 * 65 * 16 * 98816
-    # head dim 64: a record of 64 x 64 x 12 + 64 x 4 bytes; six heads at 8K use the two-level
+    assert st == 0 and n3 >= 4 * 65 * 16 * 82432
+    # head dim 64: a record of 64 x 64 x 10 + 64 x 4 bytes; six heads at 8K use the two-level
     # scan (6 x (2 x 5 - 1) x 4 = 216 workgroups -> 5 segments) with 64 x 64 fp32 matrices
-    rec64 = 64 * 64 * 12 + 64 * 4
-    assert rec64 == 49408
+    rec64 = 64 * 64 * 10 + 64 * 4
+    assert rec64 == 41216
     st, n5 = ws(lib, make_shape("BNSD", 1, 8192, 6, 6, 0.125, d_k=64, d_v=64))
     assert st == 0
     two64 = 6 * 5 * 5 * 64 * 64 * 2 + 768 * 2 * 64 * 64 * 2
