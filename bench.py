@@ -102,36 +102,36 @@ def intra_bytes(inp) -> int:
 
 def seg_bytes(inp) -> int:
     """Compulsory bytes of the segment pass: every record, the initial states, the final
-    outputs of segment 0, O0 and R of the later segments' chunks (all bf16), and the N and P
-    matrices of every segment."""
+    outputs of segment 0, O0 and R of the later segments' chunks (all bf16), and the N (fp32)
+    and P (fp16) matrices of every segment."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     first, later = chunk_counts(inp, sp)
     states = inp.batch * inp.n_v * d * d * 4
-    mats = inp.batch * inp.n_v * sp * 2 * d * d * 4
+    mats = inp.batch * inp.n_v * sp * d * d * (4 + 2)
     return (inp.n_v * ((first + later) * record_bytes(d) + first * 64 * d * 2
                        + later * 64 * d * 2 * 2)
             + states * (inp.initial_state is not None) + mats)
 
 
 def combine_bytes(inp) -> int:
-    """Compulsory bytes of the combine pass: N_0 and the N and P of segments 1 .. seg_p-2 in
-    (4 bytes a value), S_in of segments 1.. out (bf16) and S_in of the last segment out in fp32
+    """Compulsory bytes of the combine pass: N_0 and the N (fp32) and P (fp16) of segments
+    1 .. seg_p-2 in, S_in of segments 1.. out (bf16) and S_in of the last segment out in fp32
     (for the final-state step of the completion pass)."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     m = inp.batch * inp.n_v * d * d * 4
-    return m * (2 * sp - 3) + m // 2 * (sp - 1) + m
+    return m * (sp - 1) + m // 2 * (sp - 2) + m // 2 * (sp - 1) + m
 
 
 def out_bytes(inp) -> int:
     """Compulsory bytes of the completion pass: O0 and R of every chunk of segments 1.. and
     S_in of those segments in, the outputs out (all bf16); for the final state, S_in of the last
-    segment (fp32), its N and P in and the state out (4 bytes a value)."""
+    segment and its N (fp32) and P (fp16) in and the state (fp32) out."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
@@ -139,7 +139,7 @@ def out_bytes(inp) -> int:
     _, later = chunk_counts(inp, sp)
     m = inp.batch * inp.n_v * d * d * 4
     return (inp.n_v * later * 64 * d * (2 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 2
-            + 4 * m)
+            + 3 * m + m // 2)
 
 
 KERNEL_BYTES = {"kda_intra_kernel": intra_bytes, "kda_seg_kernel": seg_bytes,

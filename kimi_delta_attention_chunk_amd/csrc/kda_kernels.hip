@@ -67,7 +67,7 @@ struct Params {
     __bf16* Of;   // [record][nt 8][tt 4][lane 64][4]         O_intra[16tt+n][16nt+4q+i]
     float* Gf;    // [record][128]                            2^(G2_last)
     // two-level scan, per (sequence*head, segment) and per record, in MFMA fragment order:
-    __bf16* Pt;   // [hi/lo][M 8][kb 4][lane 64][8]  P_s[32kb+8q+j][16M+m]      transfer matrix
+    _Float16* Pt; // [M 8][kb 4][lane 64][8]         P_s[32kb+8q+j][16M+m]      transfer matrix (fp16)
     float* Nst;   // [t 8][M 8][lane 64][4]          N_s[16t+m][16M+4q+i]       zero-start end state
     __bf16* Sin;  // [t 8][kb 4][lane 64][8]         S_in[16t+m][32kb+8q+j]     entry state
     __bf16* O0;   // [t 8][tt 4][lane 64][4]         O0[16tt+m][16t+4q+i]       zero-start outputs
@@ -980,6 +980,19 @@ __device__ __forceinline__ void put_state(__bf16* sSh, __bf16* sSl, int row, int
     *reinterpret_cast<bf16x4*>(sSl + row * HD<D>::SLD + col) = l;
 }
 
+// The same fragment as an fp16 hi/lo pair (the combine's fp16 products), in the same LDS tiles.
+template <int D>
+__device__ __forceinline__ void put_state16(__bf16* sSh, __bf16* sSl, int row, int col, f32x4 x) {
+    f16x4 h, l;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        h[i] = (_Float16)x[i];
+        l[i] = (_Float16)(x[i] - (float)h[i]);
+    }
+    *reinterpret_cast<f16x4*>(sSh + row * HD<D>::SLD + col) = h;
+    *reinterpret_cast<f16x4*>(sSl + row * HD<D>::SLD + col) = l;
+}
+
 struct ScanLds {
     __bf16* sh;
     __bf16* sl;
@@ -1199,16 +1212,15 @@ __device__ __forceinline__ void segment_range(int nchunks, int seg_p, int seg, i
 }
 
 // Operands of one combine step S <- S P_s + N_s for this wave's Dk tiles M = MW w + mt: the
-// A fragments of P_s^T (hi/lo) and the accumulator fragments of this workgroup's N_s tiles.
+// A fragments of P_s^T (fp16) and the accumulator fragments of this workgroup's N_s tiles.
 template <int NT, int D>
 struct CombFrags {
-    bf16x8 ph[HD<D>::MW][HD<D>::KB];   // P_s[32kb+8q4 .. +7][16M+n16] hi
-    bf16x8 pl[HD<D>::MW][HD<D>::KB];   // lo
+    f16x8 ph[HD<D>::MW][HD<D>::KB];    // P_s[32kb+8q4 .. +7][16M+n16]
     f32x4 n[NT][HD<D>::MW];            // N_s[16(dv_tile0+nt)+n16][16M+4q4 .. +3]
 };
 
 template <int NT, int D>
-__device__ __forceinline__ void load_comb(const __bf16* Pt, const float* Nst, int dv_tile0,
+__device__ __forceinline__ void load_comb(const _Float16* Pt, const float* Nst, int dv_tile0,
                                           CombFrags<NT, D>& f) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
     constexpr int TILES = HD<D>::TILES;
@@ -1218,9 +1230,8 @@ __device__ __forceinline__ void load_comb(const __bf16* Pt, const float* Nst, in
     for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            const __bf16* src = Pt + (((MW * w + mt) * KB + kb) * 64 + lane) * 8;
-            f.ph[mt][kb] = *reinterpret_cast<const bf16x8*>(src);
-            f.pl[mt][kb] = *reinterpret_cast<const bf16x8*>(src + D * D);
+            f.ph[mt][kb] = *reinterpret_cast<const f16x8*>(
+                Pt + (((MW * w + mt) * KB + kb) * 64 + lane) * 8);
         }
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
@@ -1231,7 +1242,8 @@ __device__ __forceinline__ void load_comb(const __bf16* Pt, const float* Nst, in
 }
 
 // S^T <- P_s^T S^T + N_s^T for this wave's Dk rows, i.e. S <- S P_s + N_s, with the state in S
-// (registers) and in LDS (B operand); three-term hi/lo products.
+// (registers) and in LDS as an fp16 hi/lo pair (B operand), P_s in fp16: two products on the
+// fp16 MFMA.
 template <int NT, int D>
 __device__ __forceinline__ void combine_step(const CombFrags<NT, D>& f,
                                              f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L) {
@@ -1248,10 +1260,9 @@ __device__ __forceinline__ void combine_step(const CombFrags<NT, D>& f,
 #pragma unroll
             for (int kb = 0; kb < KB; ++kb) {
                 const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
-                const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
-                const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
+                const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
+                const f16x8 sl = *reinterpret_cast<const f16x8*>(L.sl + off);
                 acc = mfma(f.ph[mt][kb], sh, acc);
-                acc = mfma(f.pl[mt][kb], sh, acc);
                 acc = mfma(f.ph[mt][kb], sl, acc);
             }
             S[mt][nt] = acc;
@@ -1262,7 +1273,7 @@ __device__ __forceinline__ void combine_step(const CombFrags<NT, D>& f,
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
-            put_state<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, S[mt][nt]);
+            put_state16<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, S[mt][nt]);
     lds_barrier();
 }
 
@@ -1572,10 +1583,10 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     if (is_p) {
         run_chunks<1, false, OUT_R, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len, ob, os,
                                                               tile);
-        // rows 16 tile .. of P_s, split, into the combine's A fragments of P_s^T: element
+        // rows 16 tile .. of P_s, in fp16, into the combine's A fragments of P_s^T: element
         // P_s[16 tile + n16][16 M + 4 q4 + i] is lane (2 (tile & 1) + (n16 >> 3), 4 q4 + i),
         // entry n16 & 7, of fragment (M, tile >> 1)
-        __bf16* pt = p.Pt + 2 * m;
+        _Float16* pt = p.Pt + m;
         constexpr int KB = HD<D>::KB;
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
@@ -1583,7 +1594,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
             for (int i = 0; i < 4; ++i) {
                 const int lp = (2 * (tile & 1) + (n16 >> 3)) * 16 + 4 * q4 + i;
                 const int at = (((MW * w + mt) * KB + (tile >> 1)) * 64 + lp) * 8 + (n16 & 7);
-                SPLIT_BF16(S[mt][0][i], pt[at], pt[D * D + at]);
+                pt[at] = (_Float16)S[mt][0][i];
             }
     } else {
         if (seg == 0)
@@ -1637,11 +1648,11 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
         S[mt][0] = *reinterpret_cast<const f32x4*>(p.Nst + mat(0) +
                                                    ((tile * TILES + MW * w + mt) * 64 + lane) * 4);
     CombFrags<1, D> c0f, c1f, c2f;
-    load_comb<1, D>(p.Pt + 2 * at(1), p.Nst + at(1), tile, c0f);
-    load_comb<1, D>(p.Pt + 2 * at(2), p.Nst + at(2), tile, c1f);
+    load_comb<1, D>(p.Pt + at(1), p.Nst + at(1), tile, c0f);
+    load_comb<1, D>(p.Pt + at(2), p.Nst + at(2), tile, c1f);
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt)
-        put_state<D>(sSh, sSl, n16, 16 * (MW * w + mt) + 4 * q4, S[mt][0]);
+        put_state16<D>(sSh, sSl, n16, 16 * (MW * w + mt) + 4 * q4, S[mt][0]);
     lds_barrier();
 
     // S_in(s) in bf16 as the completion pass's A fragments: element S[16 tile + n16][16 M +
@@ -1659,13 +1670,13 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
     };
     int s = 1;
     for (; s + 2 <= last; s += 3) {
-        load_comb<1, D>(p.Pt + 2 * at(s + 2), p.Nst + at(s + 2), tile, c2f);
+        load_comb<1, D>(p.Pt + at(s + 2), p.Nst + at(s + 2), tile, c2f);
         store_in(s);
         combine_step<1, D>(c0f, S, L);
-        load_comb<1, D>(p.Pt + 2 * at(s + 3), p.Nst + at(s + 3), tile, c0f);
+        load_comb<1, D>(p.Pt + at(s + 3), p.Nst + at(s + 3), tile, c0f);
         store_in(s + 1);
         combine_step<1, D>(c1f, S, L);
-        load_comb<1, D>(p.Pt + 2 * at(s + 4), p.Nst + at(s + 4), tile, c1f);
+        load_comb<1, D>(p.Pt + at(s + 4), p.Nst + at(s + 4), tile, c1f);
         store_in(s + 2);
         combine_step<1, D>(c2f, S, L);
     }
@@ -1710,12 +1721,12 @@ __device__ __forceinline__ void final_state_step(const Params& p, int f, __bf16*
     const size_t ml = m0 + size_t(p.seg_p - 1) * D * D;
     f32x4 S[MW][1];
     CombFrags<1, D> cf;
-    load_comb<1, D>(p.Pt + 2 * ml, p.Nst + ml, tile, cf);
+    load_comb<1, D>(p.Pt + ml, p.Nst + ml, tile, cf);
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) {
         S[mt][0] = *reinterpret_cast<const f32x4*>(p.Nst + m0 +
                                                    ((tile * TILES + MW * w + mt) * 64 + lane) * 4);
-        put_state<D>(L.sh, L.sl, n16, 16 * (MW * w + mt) + 4 * q4, S[mt][0]);
+        put_state16<D>(L.sh, L.sl, n16, 16 * (MW * w + mt) + 4 * q4, S[mt][0]);
     }
     lds_barrier();
     combine_step<1, D>(cf, S, L);
@@ -1872,7 +1883,7 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.scan_tiles = plan.scan_tiles;
     p.seg_p = plan.seg_p;
     const bool two = plan.seg_p > 1;
-    p.Pt = two ? reinterpret_cast<__bf16*>(ws + plan.off_pt) : nullptr;
+    p.Pt = two ? reinterpret_cast<_Float16*>(ws + plan.off_pt) : nullptr;
     p.Nst = two ? reinterpret_cast<float*>(ws + plan.off_n) : nullptr;
     p.Sin = two ? reinterpret_cast<__bf16*>(ws + plan.off_sin) : nullptr;
     p.O0 = two ? reinterpret_cast<__bf16*>(ws + plan.off_o0) : nullptr;

@@ -138,7 +138,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     if (p.seg_p > 1) {
         const size_t mats = size_t(bh) * p.seg_p * d * d * sizeof(float);
         const size_t rows = n * kChunk * d * 2;   // bf16
-        p.off_pt = off; off = align_up(off + mats, 256);
+        p.off_pt = off; off = align_up(off + mats / 2, 256);   // fp16
         p.off_n = off; off = align_up(off + mats, 256);
         p.off_sin = off; off = align_up(off + mats / 2, 256);   // bf16
         p.off_o0 = off; off = align_up(off + rows, 256);

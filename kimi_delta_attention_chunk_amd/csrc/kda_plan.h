@@ -54,9 +54,9 @@ struct Plan {
                                // Dv tile of each (sequence, head) for the final state
     // byte offsets of each workspace array (256-byte aligned)
     size_t off_w = 0, off_q = 0, off_k = 0, off_u = 0, off_o = 0, off_g = 0;
-    // two-level only: per (sequence, head, segment) transfer matrix P_s (transposed, hi/lo
-    // bf16) and zero-start end state N_s (fp32), d x d 4-byte values each, and entry state
-    // S_in(s), d x d bf16; per record the zero-start outputs
+    // two-level only: per (sequence, head, segment) transfer matrix P_s (transposed, fp16),
+    // zero-start end state N_s (fp32) and entry state S_in(s) (bf16), d x d each; per record
+    // the zero-start outputs
     // O0 and the propagated queries R = Q' P^T of the segment's chunks, 64 x d bf16 each
     size_t off_pt = 0, off_n = 0, off_sin = 0, off_o0 = 0, off_r = 0;
     size_t total = 0;

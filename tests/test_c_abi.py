@@ -62,11 +62,11 @@ def test_workspace_sizes(lib):
     assert st == 0
     # 128 chunks x 3 heads x (W, K_dec fp16, U fp16, Q', O_intra bf16, gamma), plus the
     # two-level scan (3 x (2 x 5 - 1) x 8 = 216 segment-pass workgroups -> 5 segments): per
-    # segment P_s and N_s (4-byte 128x128) and S_in (bf16 128x128), per record O0 and R (bf16
+    # segment P_s (fp16 128x128), N_s (fp32 128x128) and S_in (bf16 128x128), per record O0 and R (bf16
     # 64x128)
     rec = 16384 + 16384 + 16384 + 16384 + 16384 + 512
     assert rec == 82432
-    two = 3 * 5 * (2 * 65536 + 32768) + 384 * 2 * 16384
+    two = 3 * 5 * (32768 + 65536 + 32768) + 384 * 2 * 16384
     assert n1 >= 128 * 3 * rec + two
     assert n1 < 128 * 3 * rec + two + 16 * 256
     # many heads: one-level scan, no matrices
@@ -83,7 +83,7 @@ def test_workspace_sizes(lib):
     assert rec64 == 41216
     st, n5 = ws(lib, make_shape("BNSD", 1, 8192, 6, 6, 0.125, d_k=64, d_v=64))
     assert st == 0
-    two64 = 6 * 5 * 5 * 64 * 64 * 2 + 768 * 2 * 64 * 64 * 2
+    two64 = 6 * 5 * 4 * 64 * 64 * 2 + 768 * 2 * 64 * 64 * 2
     assert n5 >= 128 * 6 * rec64 + two64
     assert n5 < 128 * 6 * rec64 + two64 + 16 * 256
 
