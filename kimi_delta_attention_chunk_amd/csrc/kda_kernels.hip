@@ -196,9 +196,9 @@ __device__ __forceinline__ void row_geom(const Params& p, int b, int h, int head
 //
 // The workgroup keeps its LDS under 80 KB and its registers under 256 per lane, so two
 // workgroups share a compute unit and one's memory phase overlaps the other's arithmetic; at
-// head dim 64 under 53 KB and 168 registers, so three do.  When every workgroup has a compute
-// unit to itself, an eight-wave form (two waves per token block, each with half the channels)
-// shortens the workgroup's latency instead.
+// head dim 64 under 53 KB and 168 registers, so three do.  When the whole grid is resident at
+// once, an eight-wave form (two waves per token block, each with half the channels) shortens
+// the workgroup's latency instead.
 
 constexpr int BLK_LD = 20;              // fp32 row stride of a stored 16 x 16 block
 constexpr int BLK_SZ = 16 * BLK_LD;     // floats per stored block

@@ -57,10 +57,12 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     p.n_records = p.n_slots * s->n_v;
     // intra grid: units (chunk slot, q/k head) padded to a multiple of 8, times the group
     p.intra_blocks = (p.n_records / p.group + 7) / 8 * 8 * p.group;
-    // At most one intra workgroup per compute unit: its latency is the stage's time, and
-    // eight waves (two per token block) shorten it; with more workgroups the four-wave form,
-    // two or three per compute unit, overlaps one's memory phases with another's arithmetic.
-    p.intra_hv = p.intra_blocks <= 256 ? 2 : 1;
+    // When the whole intra grid is resident at once (at most two workgroups per compute unit),
+    // a workgroup's latency is the stage's time, and eight waves (two per token block) shorten
+    // it (measured: 256-token call -6 %, 8K tokens x 3 or 4 heads -2 %); larger grids run in
+    // rounds, where the four-wave form, two (three at head dim 64) per compute unit, overlaps
+    // one's memory phases with another's arithmetic.
+    p.intra_hv = p.intra_blocks <= 512 ? 2 : 1;
     // Each scan workgroup streams a whole chunk record per step whatever its Dv width, so a
     // wider tile cuts the bytes streamed per unit of work; it is taken only while enough
     // workgroups remain to occupy all 256 compute units of an MI355X.

@@ -40,8 +40,8 @@ struct Plan {
     int64_t n_records = 0;     // n_slots * n_v
     int64_t intra_blocks = 0;  // one workgroup per record
     int intra_hv = 1;          // waves per 16-token block of the intra kernel: 2 (eight waves,
-                               // each with half the channels) when every workgroup has a
-                               // compute unit of its own, else 1 (four waves)
+                               // each with half the channels) when the whole grid is resident
+                               // at once (<= 512 workgroups), else 1 (four waves)
     int64_t scan_blocks = 0;   // one workgroup per (sequence, value head, Dv tile), XCD padded
     int scan_nt = 1;           // 16-row Dv tiles per scan workgroup (1, 2 or 4)
     int scan_tiles = 0;        // scan workgroups per (sequence, head) = (d/16) / scan_nt
