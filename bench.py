@@ -68,15 +68,17 @@ def record_bytes(d: int) -> int:
     return 64 * d * (2 + 2 + 2 + 2 + 2) + d * 4
 
 
-def chunk_counts(inp, sp: int):
-    """(chunks in segment 0, chunks in later segments) over all sequences, per value head."""
-    first = later = 0
+def chunk_counts(inp, sp: int, seg1: bool = False):
+    """(chunks in segment 0, chunks in later segments) over all sequences, per value head; with
+    seg1, the chunks of segment 1 alone as a third entry."""
+    first = later = one = 0
     for L in inp.lengths:
         nc = (L + 63) // 64
         n0 = min(-(-nc // sp), nc)
         first += n0
         later += nc - n0
-    return first, later
+        one += min(n0, nc - n0)
+    return (first, later, one) if seg1 else (first, later)
 
 
 def scan_bytes(inp) -> int:
@@ -102,8 +104,8 @@ def intra_bytes(inp) -> int:
 
 def seg_bytes(inp) -> int:
     """Compulsory bytes of the segment pass: every record, the initial states, the final
-    outputs of segment 0, O0 and R of the later segments' chunks (all bf16), and the N (fp32)
-    and P (fp16) matrices of every segment."""
+    outputs of segment 0, O0 and R of the later segments' chunks (all bf16), the N (fp32)
+    and P (fp16) matrices of every segment, and S_in(1) = N_0 in bf16."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
@@ -113,33 +115,36 @@ def seg_bytes(inp) -> int:
     mats = inp.batch * inp.n_v * sp * d * d * (4 + 2)
     return (inp.n_v * ((first + later) * record_bytes(d) + first * 64 * d * 2
                        + later * 64 * d * 2 * 2)
-            + states * (inp.initial_state is not None) + mats)
+            + states * (inp.initial_state is not None) + mats + inp.batch * inp.n_v * d * d * 2)
 
 
 def combine_bytes(inp) -> int:
     """Compulsory bytes of the combine pass: N_0 and the N (fp32) and P (fp16) of segments
-    1 .. seg_p-2 in, S_in of segments 1.. out (bf16) and S_in of the last segment out in fp32
-    (for the final-state step of the completion pass)."""
+    1 .. seg_p-2 in, S_in of segments 2.. out (bf16) and S_in of the last segment out in fp32
+    (for the final-state step of the completion pass); and the completion of segment 1's
+    chunks: their O0 and R and S_in(1) in, their outputs out (all bf16)."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
     m = inp.batch * inp.n_v * d * d * 4
-    return m * (sp - 1) + m // 2 * (sp - 2) + m // 2 * (sp - 1) + m
+    _, _, one = chunk_counts(inp, sp, seg1=True)
+    return (m * (sp - 1) + m // 2 * (sp - 2) + m // 2 * (sp - 2) + m
+            + inp.n_v * one * 64 * d * (2 * 2 + 2) + m // 2)
 
 
 def out_bytes(inp) -> int:
-    """Compulsory bytes of the completion pass: O0 and R of every chunk of segments 1.. and
+    """Compulsory bytes of the completion pass: O0 and R of every chunk of segments 2.. and
     S_in of those segments in, the outputs out (all bf16); for the final state, S_in of the last
     segment and its N (fp32) and P (fp16) in and the state (fp32) out."""
     sp = seg_p_of(inp)
     if sp == 1:
         return 0
     d = head_dim(inp)
-    _, later = chunk_counts(inp, sp)
+    _, later, one = chunk_counts(inp, sp, seg1=True)
     m = inp.batch * inp.n_v * d * d * 4
-    return (inp.n_v * later * 64 * d * (2 * 2 + 2) + inp.batch * inp.n_v * (sp - 1) * d * d * 2
-            + 3 * m + m // 2)
+    return (inp.n_v * (later - one) * 64 * d * (2 * 2 + 2)
+            + inp.batch * inp.n_v * (sp - 2) * d * d * 2 + 3 * m + m // 2)
 
 
 KERNEL_BYTES = {"kda_intra_kernel": intra_bytes, "kda_seg_kernel": seg_bytes,

@@ -1607,6 +1607,17 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
         for (int mt = 0; mt < MW; ++mt)
             *reinterpret_cast<f32x4*>(p.Nst + m + ((tile * TILES + MW * w + mt) * 64 + lane) * 4) =
                 S[mt][0];
+        if (seg == 0) {   // S_in(1) = N_0 for the completion of segment 1 (combine pass layout)
+            constexpr int KB = HD<D>::KB;
+            __bf16* dst = p.Sin + (size_t(bh) * p.seg_p + 1) * D * D;
+#pragma unroll
+            for (int mt = 0; mt < MW; ++mt) {
+                const int M = MW * w + mt;
+                const int lb = (2 * (M & 1) + (q4 >> 1)) * 16 + n16;
+                *reinterpret_cast<bf16x4*>(dst + ((tile * KB + (M >> 1)) * 64 + lb) * 8 +
+                                           4 * (q4 & 1)) = to_bf16x4(S[mt][0]);
+            }
+        }
     }
 }
 
@@ -1631,6 +1642,12 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
+    const int n_chain = (p.batch * p.n_v + 7) / 8 * 8 * TILES;   // chain workgroups, XCD padded
+    if (int(blockIdx.x) >= n_chain) {   // segment 1's outputs: S_in(1) = N_0 is already stored
+        __shared__ __attribute__((aligned(16))) bf16x8 sR[64 * D * 2 / 16];
+        complete_record<D>(p, int64_t(blockIdx.x) - n_chain, 1, 1, sR);
+        return;
+    }
     const int pid = blockIdx.x;
     const int xcd = pid & 7, r8 = pid >> 3;
     const int bh = (r8 / TILES) * 8 + xcd;
@@ -1659,6 +1676,7 @@ __global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
     // 4 q4 + i] is lane (2 (M & 1) + (q4 >> 1), n16), entries 4 (q4 & 1) + i, of fragment
     // (tile, M >> 1).  (The chain itself keeps S in fp32.)
     auto store_in = [&](int s) {
+        if (s == 1) return;   // S_in(1) = N_0, stored by the segment pass
         __bf16* dst = p.Sin + mat(s);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt) {
@@ -1743,26 +1761,21 @@ __device__ __forceinline__ void final_state_step(const Params& p, int f, __bf16*
 // LDS; every operand is loaded before the first output is stored.  The workgroups after the
 // records form the final states (final_state_step), one per 16-row Dv tile of each (sequence,
 // head).
+// Output completion of the chunk record `rec` when its segment lies in [seg_lo, seg_hi]:
+// out = O0 + R S_in(s)^T (the completion pass's workgroups and, for segment 1, whose S_in is
+// N_0 from the segment pass, extra workgroups of the combine pass).  sR: 64 x D bf16 of LDS.
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
+__device__ __forceinline__ void complete_record(const Params& p, int64_t rec, int seg_lo,
+                                                int seg_hi, bf16x8* sR) {
     constexpr int KB = HD<D>::KB, NTW = D / 64;
     constexpr int R_U4 = 64 * D * 2 / 16;   // R in 16-byte units
-    static_assert(R_U4 * 16 >= 2 * 16 * HD<D>::SLD * 2, "the state tiles fit the R buffer");
-    __shared__ __attribute__((aligned(16))) bf16x8 sR[R_U4];
     const int tid = threadIdx.x;
     const int w = tid >> 6;
     const int lane = tid & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
-
-    const int64_t rec = blockIdx.x;
-    const int64_t n_rec = int64_t(p.intra_units) * p.group;
-    if (rec >= n_rec) {
-        if (p.fin) final_state_step<D>(p, int(rec - n_rec), reinterpret_cast<__bf16*>(sR));
-        return;
-    }
-    const int slot = int(blockIdx.x / unsigned(p.n_v));
-    const int h = int(blockIdx.x - unsigned(slot) * unsigned(p.n_v));
+    const int slot = int(rec / p.n_v);
+    const int h = int(rec - int64_t(slot) * p.n_v);
     const int b = slot_batch(p, slot);
     int c0, len, slot0;
     seq_info(p, b, c0, len, slot0);
@@ -1770,7 +1783,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     if (j < 0 || j * kChunk >= len) return;   // an unused slot
     const int nchunks = (len + kChunk - 1) / kChunk;
     const int seg = j / ((nchunks + p.seg_p - 1) / p.seg_p);
-    if (seg == 0) return;                     // written final by the segment pass
+    if (seg < seg_lo || seg > seg_hi) return;
     size_t ob, os;
     row_geom(p, b, h, p.n_v, D, c0, ob, os);
 
@@ -1826,6 +1839,20 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
                                            16 * (NTW * w + i) + 4 * q4) = to_bf16x4(acc[tt][i]);
         }
     }
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
+    constexpr int R_U4 = 64 * D * 2 / 16;   // R in 16-byte units
+    static_assert(R_U4 * 16 >= 2 * 16 * HD<D>::SLD * 2, "the state tiles fit the R buffer");
+    __shared__ __attribute__((aligned(16))) bf16x8 sR[R_U4];
+    const int64_t rec = blockIdx.x;
+    const int64_t n_rec = int64_t(p.intra_units) * p.group;
+    if (rec >= n_rec) {
+        if (p.fin) final_state_step<D>(p, int(rec - n_rec), reinterpret_cast<__bf16*>(sR));
+        return;
+    }
+    complete_record<D>(p, rec, 2, p.seg_p - 1, sR);   // segment 1 runs in the combine pass
 }
 
 // Stages of one call, each one kernel (empty when the plan does not enqueue it): intra, then

@@ -107,7 +107,7 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
             rows = r > rows ? r : rows;
         }
         p.seg_blocks = rows * 8;
-        p.comb_blocks = bh8 * tiles;
+        p.comb_blocks = bh8 * tiles + p.n_records;   // chains, then segment-1 outputs
         p.out_blocks = p.n_records + bh * tiles;   // records, then final-state tiles
     } else {
         p.scan_blocks = bh8 * p.scan_tiles;
