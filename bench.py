@@ -160,10 +160,10 @@ def source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter summary of this
-    workload (FETCH_SIZE and WRITE_SIZE, scaled by the copy-kernel calibration), or None when
-    there is no summary or the kernel sources changed since the counters were taken."""
+def counter_summary(workload: str):
+    """The committed rocprofv3 counter summary of this workload (FETCH_SIZE and WRITE_SIZE per
+    dispatch and the copy-kernel calibration), or None when there is none or the kernel sources
+    changed since the counters were taken."""
     import re
     path = os.path.join(ROOT, "profiles", f"kda_kernels_{workload}.md")
     if not os.path.exists(path):
@@ -172,15 +172,35 @@ def measured_traffic(workload: str, kernel: str):
     if not m:
         return None
     d = json.loads(m.group(1))
-    if d.get("source_hash") != source_hash() or kernel not in d.get("kernels", {}):
+    if d.get("source_hash") != source_hash():
         return None
-    k = d["kernels"][kernel]
-    return (k["fetch_kib"] * d["fetch_scale"] + k["write_kib"] * d["write_scale"]) * 1024
+    return d
+
+
+def measured_traffic(summary, kernel: str):
+    """HBM bytes per launch of `kernel` from a counter summary (scaled FETCH_SIZE + WRITE_SIZE)."""
+    if summary is None or kernel not in summary.get("kernels", {}):
+        return None
+    k = summary["kernels"][kernel]
+    return (k["fetch_kib"] * summary["fetch_scale"] + k["write_kib"] * summary["write_scale"]) * 1024
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(inp, min_seconds: float = 10.0) -> dict:
-    from oracle import kda_oracle, oracle_threads, QK_L2NORM, BETA_SIGMOID
-    flags = (QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+    """The fp64 oracle on the host cores, on the full workload, repeated for about
+    `min_seconds`; its median run gives tokens/s."""
+    from oracle import kda_oracle, oracle_threads, QK_L2NORM, BETA_SIGMOID, SCALAR_GATE
+    flags = ((QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
+             | (SCALAR_GATE if inp.scalar_gate else 0))
     times = []
     t_start = time.perf_counter()
     while len(times) < 3 or time.perf_counter() - t_start < min_seconds:
@@ -192,11 +212,35 @@ def cpu_baseline(inp, min_seconds: float = 10.0) -> dict:
             break
     times.sort()
     med = times[len(times) // 2]
-    return {"value": inp.tokens / med, "unit": "tokens/s", "cores": oracle_threads(),
-            "kind": "oracle",
+    threads = oracle_threads()
+    affinity = len(os.sched_getaffinity(0))
+    return {"value": inp.tokens / med, "unit": "tokens/s", "cores": min(threads, affinity),
+            "kind": "oracle", "omp_threads": threads, "affinity_cores": affinity,
+            "cpu_model": cpu_model(),
             "sample": f"full workload ({inp.tokens} tokens x {inp.n_v} heads), fp64 token "
                       f"recurrence, median of {len(times)} runs over "
                       f"{time.perf_counter() - t_start:.1f} s"}
+
+
+def copy_ceiling(nbytes: int, reps: int = 20) -> dict:
+    """A plain device-to-device copy moving `nbytes` in all (nbytes / 2 read, nbytes / 2
+    written): the practical bandwidth ceiling for a kernel of that size."""
+    import torch
+    half = max(nbytes // 2, 1)
+    src = torch.ones(half, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record()
+        dst.copy_(src)
+        b.record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    return {"bytes": 2 * half, "median_ms": ms[reps // 2], "min_ms": ms[0],
+            "GB/s": 2 * half / (ms[reps // 2] * 1e-3) / 1e9}
 
 
 def main() -> int:
@@ -233,7 +277,7 @@ def main() -> int:
         return 0
     from kimi_delta_attention_chunk_amd import (chunk_fwd, kda_chunk_fwd_workspace,
                                                 kda_num_stages, kda_stage_name, make_shape,
-                                                kda_chunk_fwd_plan)
+                                                kda_chunk_fwd_plan, kda_chunk_fwd_plan_kernels)
     from kimi_delta_attention_chunk_amd.workloads import workload_inputs, BY_NAME
 
     wl = BY_NAME[args.workload]
@@ -277,6 +321,16 @@ def main() -> int:
     torch.cuda.synchronize()
     t3 = time.perf_counter()
 
+    # the same K steps a third time, an event pair around each call: per-call median and min
+    calls = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for i in range(args.steps):
+        calls[i][0].record()
+        chunk_fwd(sets[i % copies], out=out, final_state=fin, workspace=ws)
+        calls[i][1].record()
+    torch.cuda.synchronize()
+    call_ms = sorted(a.elapsed_time(b) for a, b in calls)
+
     ms_step = (t1 - t0) * 1e3 / args.steps
     stage_ms = [sum(events[i][2 * s].elapsed_time(events[i][2 * s + 1]) for i in range(args.steps))
                 / args.steps for s in range(nst)]
@@ -286,9 +340,15 @@ def main() -> int:
     live = [s for s in range(nst) if mask >> s & 1]
     dom = max(live, key=lambda s: stage_ms[s])
     kbytes = [KERNEL_BYTES[kda_stage_name(s)](host) for s in range(nst)]
-    achieved = kbytes[dom] / (stage_ms[dom] * 1e-3)
     pbytes = path_bytes(host)
     value = host.tokens / (ms_step * 1e-3)
+    summary = counter_summary(wl.name)
+    traffic = {kda_stage_name(s): measured_traffic(summary, kda_stage_name(s)) for s in live}
+    all_traffic = (sum(traffic.values()) if all(t is not None for t in traffic.values())
+                   else None)
+    # roofline of the dominant kernel: the call's algorithmic bytes (1,538 B per token-head at
+    # Nqk = Nv, plus the states) over that kernel's average launch duration
+    achieved = pbytes / (stage_ms[dom] * 1e-3)
 
     res = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1,
@@ -302,13 +362,19 @@ def main() -> int:
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kda_stage_name(dom), "achieved": achieved / 1e9,
                      "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
-                     "traffic": measured_traffic(wl.name, kda_stage_name(dom)),
-                     "bytes_per_launch": kbytes[dom],
-                     "avg_launch_ms": stage_ms[dom]},
+                     "traffic": traffic[kda_stage_name(dom)],
+                     "algorithmic_bytes": pbytes, "avg_launch_ms": stage_ms[dom]},
         "path_roofline": {"bound": "hbm", "algorithmic_bytes": pbytes,
                           "achieved": pbytes / (ms_step * 1e-3) / 1e9, "unit": "GB/s",
                           "frac": pbytes / (ms_step * 1e-3) / HBM_PEAK},
+        "traffic_ratio": None if all_traffic is None else all_traffic / pbytes,
+        "kernel_traffic": traffic,
+        "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0],
+                        "mean": sum(call_ms) / len(call_ms)},
+        "copy_ceiling": copy_ceiling(pbytes),
         "stages_ms": {kda_stage_name(s): stage_ms[s] for s in live},
+        "stage_workspace_bytes": {kda_stage_name(s): kbytes[s] for s in live},
+        "kernels": kda_chunk_fwd_plan_kernels(shape),
         "segments": segments,
         "ms_per_step_with_stage_events": (t3 - t2) * 1e3 / args.steps,
         "token_heads_per_s": host.tokens * host.n_v / (ms_step * 1e-3),

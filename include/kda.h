@@ -73,7 +73,7 @@ typedef enum {
     KDA_ERR_INVALID_ARG = 1,  /* a NULL or misaligned pointer, bad enum, negative size, alias */
     KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement: head dim, or
                                  sizes past its limits (n_v * d_k >= 2^24; more than 2^31 - 1
-                                 workgroups in a kernel; tensors of 2^63 elements or more) */
+                                 workgroups in a kernel; tensors of 2^60 elements or more) */
     KDA_ERR_WORKSPACE = 3,    /* workspace pointer NULL or workspace_bytes too small */
     KDA_ERR_HIP = 4           /* a HIP launch or event call failed (hipGetLastError) */
 } kda_status;
@@ -152,7 +152,26 @@ kda_status kda_chunk_fwd_timed(const kda_shape* shape,
                                hipStream_t stream,
                                hipEvent_t* stage_events, int32_t n_stage_events);
 
-/* Static string naming a status code ("KDA_OK", ...); "unknown kda_status" otherwise. */
+/* The kernels kda_chunk_fwd launches for `shape`, in launch order, as one NUL-terminated string:
+ * each kernel's name with its template arguments (as in "kda_intra_kernel<0,128,2>"), separated
+ * by ';'.  The choice follows from the shape alone (head dim, how many (sequence, head) chains
+ * and chunk records it has, the gate form); nothing is launched.  `names` is caller memory of
+ * `capacity` bytes.  Returns the status kda_chunk_fwd_workspace returns for the shape, or
+ * KDA_ERR_INVALID_ARG when `names` is NULL or `capacity` is too small (then nothing is written).
+ * (What the kernels compute: the FlashKDA README, section 功能说明; see the top of this file.) */
+kda_status kda_chunk_fwd_plan_kernels(const kda_shape* shape, char* names, size_t capacity);
+
+/* Every kernel variant compiled into the library: kda_num_kernel_variants() of them, named as
+ * kda_chunk_fwd_plan_kernels names them; kda_kernel_variant(i) returns a static string for
+ * 0 <= i < kda_num_kernel_variants() and NULL otherwise.  Each variant is one specialisation of
+ * the same chunk method (FlashKDA README, section 功能说明) for a head dim, a gate form or a
+ * launch shape. */
+int32_t kda_num_kernel_variants(void);
+const char* kda_kernel_variant(int32_t i);
+
+/* Static string naming a status code ("KDA_OK", ...); "unknown kda_status" otherwise.  The codes
+ * report the argument checks of the FlashKDA README, section 约束说明 (supported head dims,
+ * layouts, head counts, cu_seqlens), made on the host before anything is launched. */
 const char* kda_status_str(kda_status status);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */

@@ -8,6 +8,8 @@ from .ops import (  # noqa: F401
     chunk_fwd,
     kda_chunk_fwd,
     kda_chunk_fwd_plan,
+    kda_chunk_fwd_plan_kernels,
+    kda_kernel_variants,
     kda_chunk_fwd_workspace,
     kda_num_stages,
     kda_stage_name,
@@ -15,5 +17,5 @@ from .ops import (  # noqa: F401
     make_shape,
 )
 
-__all__ = ["KdaError", "chunk_fwd", "kda_chunk_fwd", "kda_chunk_fwd_plan",
+__all__ = ["KdaError", "chunk_fwd", "kda_chunk_fwd", "kda_chunk_fwd_plan", "kda_chunk_fwd_plan_kernels", "kda_kernel_variants",
            "kda_chunk_fwd_workspace", "kda_num_stages", "kda_stage_name", "kda_status_str", "make_shape"]

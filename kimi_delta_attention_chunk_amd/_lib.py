@@ -18,7 +18,8 @@ KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP
 
 EXPORTED = ["kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
             "kda_num_stages", "kda_stage_name", "kda_chunk_fwd_plan", "kda_status_str",
-            "kda_version"]
+            "kda_version", "kda_chunk_fwd_plan_kernels", "kda_num_kernel_variants",
+            "kda_kernel_variant"]
 
 
 class KdaShape(ctypes.Structure):
@@ -60,6 +61,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.kda_chunk_fwd_plan.restype = ctypes.c_int
     lib.kda_status_str.argtypes = [ctypes.c_int]
     lib.kda_status_str.restype = ctypes.c_char_p
+    lib.kda_chunk_fwd_plan_kernels.argtypes = [S, ctypes.c_char_p, ctypes.c_size_t]
+    lib.kda_chunk_fwd_plan_kernels.restype = ctypes.c_int
+    lib.kda_num_kernel_variants.argtypes = []
+    lib.kda_num_kernel_variants.restype = ctypes.c_int32
+    lib.kda_kernel_variant.argtypes = [ctypes.c_int32]
+    lib.kda_kernel_variant.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
     lib.kda_version.restype = ctypes.c_int32
     _lib = lib

@@ -34,6 +34,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <cstdio>
+#include <cstring>
 
 #include "kda.h"
 #include "kda_plan.h"
@@ -338,15 +340,17 @@ __device__ __forceinline__ void blk_row8(const float* m, int I, int s, int q4, i
     }
 }
 
-// SG: one gate per (token, value head) (KDA_SCALAR_GATE), broadcast over the key channels.
+// GM: gate mode.  0: one fp32 natural-log decay per (token, key channel); 1: one per (token,
+// value head) (KDA_SCALAR_GATE), broadcast over the key channels.
 // D: head dim (d_k = d_v), 128 or 64.
 // HV: waves per 16-token block.  With HV = 2 (eight waves) wave w owns token block I = w >> 1
 // and channel half hc = w & 1: its loads, gate sums, decayed operands and transposes cover
 // channels [hc D/2, (hc+1) D/2), its W, Q' tiles are the Dk tiles of that half and its U,
 // O_intra tiles the Dv tiles of the same index range; the T/Aqk products over channels are
 // summed from the two halves through LDS.
-template <bool SG, int D, int HV>
+template <int GM, int D, int HV>
 __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void kda_intra_kernel(Params p) {
+    constexpr bool SG = GM == 1;
     constexpr int KB = D / 32;    // 32-channel K steps of a product over channels
     constexpr int NTD = D / 16;   // 16-wide channel (or Dv) tiles
     constexpr int KBW = KB / HV;  // channel blocks of this wave
@@ -1621,6 +1625,10 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
     }
 }
 
+template <int D>
+__device__ __forceinline__ void complete_record(const Params& p, int64_t rec, int seg_lo,
+                                                int seg_hi, bf16x8* sR);
+
 // Combine pass of the two-level scan: D/16 workgroups per (sequence, head), one 16-row Dv tile
 // each, form S_in(1) = N_0 and S_in(s+1) = S_in(s) P_s + N_s and store every S_in(s) (bf16,
 // for the completion pass).  With a final state it also keeps S_in(seg_p-1) in fp32, in the
@@ -1871,6 +1879,68 @@ kda_status launch_kernel(const void* kernel, unsigned grid, unsigned threads, hi
     return hipGetLastError() == hipSuccess ? KDA_OK : KDA_ERR_HIP;
 }
 
+// Every kernel variant the library holds, named by its template arguments.  The plan picks one
+// per stage by name (stage_kernels), so the names a plan query reports are exactly the kernels a
+// call launches.
+struct Variant {
+    const char* name;
+    const void* fn;
+    unsigned threads;
+};
+#define KDA_VARIANT(kern, threads, ...) \
+    {#kern "<" #__VA_ARGS__ ">", reinterpret_cast<const void*>(&kern<__VA_ARGS__>), threads}
+const Variant kVariants[] = {
+    KDA_VARIANT(kda_intra_kernel, kThreads, 0,128,1),
+    KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 0,128,2),
+    KDA_VARIANT(kda_intra_kernel, kThreads, 1,128,1),
+    KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 1,128,2),
+    KDA_VARIANT(kda_intra_kernel, kThreads, 0,64,1),
+    KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 0,64,2),
+    KDA_VARIANT(kda_intra_kernel, kThreads, 1,64,1),
+    KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 1,64,2),
+    KDA_VARIANT(kda_seg_kernel, kThreads, 128),
+    KDA_VARIANT(kda_seg_kernel, kThreads, 64),
+    KDA_VARIANT(kda_combine_kernel, kThreads, 128),
+    KDA_VARIANT(kda_combine_kernel, kThreads, 64),
+    KDA_VARIANT(kda_out_kernel, kThreads, 128),
+    KDA_VARIANT(kda_out_kernel, kThreads, 64),
+    KDA_VARIANT(kda_scan_kernel, kPfThreads, 1,128,true),
+    KDA_VARIANT(kda_scan_kernel, kPfThreads, 2,128,true),
+    KDA_VARIANT(kda_scan_kernel, kThreads, 1,128,false),
+    KDA_VARIANT(kda_scan_kernel, kThreads, 2,128,false),
+    KDA_VARIANT(kda_scan_kernel, kThreads, 4,128,false),
+    KDA_VARIANT(kda_scan_kernel, kPfThreads, 1,64,true),
+    KDA_VARIANT(kda_scan_kernel, kPfThreads, 2,64,true),
+    KDA_VARIANT(kda_scan_kernel, kThreads, 1,64,false),
+    KDA_VARIANT(kda_scan_kernel, kThreads, 2,64,false),
+    KDA_VARIANT(kda_scan_kernel, kThreads, 4,64,false),
+};
+#undef KDA_VARIANT
+constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
+constexpr int kNameCap = 64;
+
+// Name of the kernel each stage of `plan` launches; an empty name for a stage the plan skips.
+void stage_kernels(const Plan& plan, uint32_t flags, char (&names)[kStages][kNameCap]) {
+    for (auto& n : names) n[0] = '\0';
+    const int gm = (flags & KDA_SCALAR_GATE) ? 1 : 0;
+    std::snprintf(names[ST_INTRA], kNameCap, "kda_intra_kernel<%d,%d,%d>", gm, plan.d,
+                  plan.intra_hv);
+    if (plan.seg_p > 1) {
+        std::snprintf(names[ST_SEG], kNameCap, "kda_seg_kernel<%d>", plan.d);
+        std::snprintf(names[ST_COMB], kNameCap, "kda_combine_kernel<%d>", plan.d);
+        std::snprintf(names[ST_OUT], kNameCap, "kda_out_kernel<%d>", plan.d);
+    } else {
+        std::snprintf(names[ST_SCAN], kNameCap, "kda_scan_kernel<%d,%d,%s>", plan.scan_nt,
+                      plan.d, plan.scan_pf ? "true" : "false");
+    }
+}
+
+const Variant* find_variant(const char* name) {
+    for (const Variant& v : kVariants)
+        if (std::strcmp(v.name, name) == 0) return &v;
+    return nullptr;
+}
+
 kda_status launch(const kda_shape* shape, const void* q, const void* k, const void* v,
                   const float* g, const void* beta, const float* initial_state,
                   const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
@@ -1919,53 +1989,25 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.flags = shape->flags;
     p.intra_units = int(plan.n_records / plan.group);
 
+    char names[kStages][kNameCap];
+    stage_kernels(plan, shape->flags, names);
+    const int64_t grid[kStages] = {plan.intra_blocks, plan.seg_blocks, plan.comb_blocks,
+                                   plan.out_blocks, plan.scan_blocks};
     (void)hipGetLastError();  // clear a stale error so the checks below see only ours
-    auto e = [&](int i) { return ev ? ev[i] : hipEvent_t(nullptr); };
-    const bool sg = (p.flags & KDA_SCALAR_GATE) != 0;
-    const bool d64 = plan.d == 64;
-    auto fn = [](auto f) { return reinterpret_cast<const void*>(f); };
-    const bool hv2 = plan.intra_hv == 2;
-    const void* intra =
-        hv2 ? (d64 ? (sg ? fn(&kda_intra_kernel<true, 64, 2>) : fn(&kda_intra_kernel<false, 64, 2>))
-                   : (sg ? fn(&kda_intra_kernel<true, 128, 2>) : fn(&kda_intra_kernel<false, 128, 2>)))
-            : (d64 ? (sg ? fn(&kda_intra_kernel<true, 64, 1>) : fn(&kda_intra_kernel<false, 64, 1>))
-                   : (sg ? fn(&kda_intra_kernel<true, 128, 1>) : fn(&kda_intra_kernel<false, 128, 1>)));
-    // one stage: its kernel, or (not enqueued by this plan) its two events back to back
-    auto stage = [&](int sidx, const void* kernel, int64_t grid, unsigned threads) -> kda_status {
-        if (kernel)
-            return launch_kernel(kernel, unsigned(grid), threads, stream, e(2 * sidx),
-                                 e(2 * sidx + 1), p);
-        if (ev && (hipEventRecord(ev[2 * sidx], stream) != hipSuccess ||
-                   hipEventRecord(ev[2 * sidx + 1], stream) != hipSuccess))
+    for (int s = 0; s < kStages; ++s) {
+        if (names[s][0]) {
+            const Variant* var = find_variant(names[s]);
+            if (!var) return KDA_ERR_UNSUPPORTED;
+            st = launch_kernel(var->fn, unsigned(grid[s]), var->threads, stream,
+                               ev ? ev[2 * s] : nullptr, ev ? ev[2 * s + 1] : nullptr, p);
+            if (st != KDA_OK) return st;
+        } else if (ev && (hipEventRecord(ev[2 * s], stream) != hipSuccess ||
+                          hipEventRecord(ev[2 * s + 1], stream) != hipSuccess)) {
+            // a stage the plan skips: its two events back to back
             return KDA_ERR_HIP;
-        return KDA_OK;
-    };
-    const void* segk = nullptr;
-    const void* combk = nullptr;
-    const void* outk = nullptr;
-    const void* scan = nullptr;
-    if (two) {
-        segk = d64 ? fn(&kda_seg_kernel<64>) : fn(&kda_seg_kernel<128>);
-        combk = d64 ? fn(&kda_combine_kernel<64>) : fn(&kda_combine_kernel<128>);
-        outk = d64 ? fn(&kda_out_kernel<64>) : fn(&kda_out_kernel<128>);
-    } else if (plan.scan_pf) {   // scan_nt is 1 or 2 here
-        scan = d64 ? (plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 64, true>)
-                                        : fn(&kda_scan_kernel<1, 64, true>))
-                   : (plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 128, true>)
-                                        : fn(&kda_scan_kernel<1, 128, true>));
-    } else {
-        scan = d64 ? (plan.scan_nt == 4   ? fn(&kda_scan_kernel<4, 64, false>)
-                      : plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 64, false>)
-                                          : fn(&kda_scan_kernel<1, 64, false>))
-                   : (plan.scan_nt == 4   ? fn(&kda_scan_kernel<4, 128, false>)
-                      : plan.scan_nt == 2 ? fn(&kda_scan_kernel<2, 128, false>)
-                                          : fn(&kda_scan_kernel<1, 128, false>));
+        }
     }
-    if ((st = stage(ST_INTRA, intra, plan.intra_blocks, kThreads * plan.intra_hv)) != KDA_OK) return st;
-    if ((st = stage(ST_SEG, segk, plan.seg_blocks, kThreads)) != KDA_OK) return st;
-    if ((st = stage(ST_COMB, combk, plan.comb_blocks, kThreads)) != KDA_OK) return st;
-    if ((st = stage(ST_OUT, outk, plan.out_blocks, kThreads)) != KDA_OK) return st;
-    return stage(ST_SCAN, scan, plan.scan_blocks, plan.scan_pf ? kPfThreads : kThreads);
+    return KDA_OK;
 }
 
 }  // namespace kda
@@ -2013,6 +2055,33 @@ kda_status kda_chunk_fwd_plan(const kda_shape* shape, uint32_t* stage_mask, int3
                            : (1u << kda::ST_SCAN));
     if (segments) *segments = plan.seg_p;
     return KDA_OK;
+}
+
+kda_status kda_chunk_fwd_plan_kernels(const kda_shape* shape, char* names, size_t capacity) {
+    if (!names) return KDA_ERR_INVALID_ARG;
+    kda::Plan plan;
+    const kda_status st = kda::make_plan(shape, &plan);
+    if (st != KDA_OK) return st;
+    char stage[kda::kStages][kda::kNameCap];
+    kda::stage_kernels(plan, shape->flags, stage);
+    size_t need = 1;   // the NUL, and one ';' between two names
+    int count = 0;
+    for (const auto& n : stage)
+        if (n[0]) need += std::strlen(n) + (count++ ? 1 : 0);
+    if (capacity < need) return KDA_ERR_INVALID_ARG;
+    names[0] = '\0';
+    for (const auto& n : stage) {
+        if (!n[0]) continue;
+        if (names[0]) std::strcat(names, ";");
+        std::strcat(names, n);
+    }
+    return KDA_OK;
+}
+
+int32_t kda_num_kernel_variants(void) { return kda::kNumVariants; }
+
+const char* kda_kernel_variant(int32_t i) {
+    return (i >= 0 && i < kda::kNumVariants) ? kda::kVariants[i].name : nullptr;
 }
 
 const char* kda_stage_name(int32_t stage) {

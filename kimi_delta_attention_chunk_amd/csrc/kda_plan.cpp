@@ -51,9 +51,13 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
         p.nc_max = 0;
         p.n_slots = int64_t(s->seq_len) / kChunk + s->batch;
     } else {
-        p.nc_max = (s->seq_len + kChunk - 1) / kChunk;
+        p.nc_max = int((int64_t(s->seq_len) + kChunk - 1) / kChunk);
         p.n_slots = int64_t(s->batch) * p.nc_max;
     }
+    // one intra workgroup per record: more than 2^31 - 1 records cannot be launched (checked
+    // here, before any product that could overflow)
+    if (double(p.n_slots) * double(s->n_v) >= double(std::numeric_limits<int32_t>::max()))
+        return KDA_ERR_UNSUPPORTED;
     p.n_records = p.n_slots * s->n_v;
     // intra grid: units (chunk slot, q/k head) padded to a multiple of 8, times the group
     p.intra_blocks = (p.n_records / p.group + 7) / 8 * 8 * p.group;
@@ -124,7 +128,8 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     // element counts of the largest tensors must fit the 64-bit offsets used on the device
     const double tokens = (s->layout == KDA_LAYOUT_TND) ? double(s->seq_len)
                                                         : double(s->batch) * s->seq_len;
-    if (tokens * s->n_v * p.d > 9.0e18) return KDA_ERR_UNSUPPORTED;
+    // (below 2^60 elements, so byte counts of every tensor, fp32 g included, stay below 2^62)
+    if (tokens * s->n_v * p.d >= 1152921504606846976.0) return KDA_ERR_UNSUPPORTED;
     // the 64 output rows of one chunk are one buffer-store region with 32-bit byte offsets
     if (int64_t(kChunk) * s->n_v * p.d * 2 >= (int64_t(1) << 31)) return KDA_ERR_UNSUPPORTED;
 

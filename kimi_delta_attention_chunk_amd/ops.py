@@ -65,6 +65,21 @@ def kda_chunk_fwd_plan(shape: KdaShape):
     return int(mask.value), int(segs.value)
 
 
+def kda_chunk_fwd_plan_kernels(shape: KdaShape) -> list:
+    """Names (with template arguments) of the kernels a call with `shape` launches, in order."""
+    buf = ctypes.create_string_buffer(1024)
+    st = _lib.load().kda_chunk_fwd_plan_kernels(ctypes.byref(shape), buf, len(buf))
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_fwd_plan_kernels")
+    return buf.value.decode().split(";")
+
+
+def kda_kernel_variants() -> list:
+    """Every kernel variant compiled into the library."""
+    lib = _lib.load()
+    return [lib.kda_kernel_variant(i).decode() for i in range(lib.kda_num_kernel_variants())]
+
+
 def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
@@ -72,15 +87,69 @@ def _ptr(t: Optional[torch.Tensor]):
 def infer_shape(q: torch.Tensor, v: torch.Tensor, layout: str,
                 cu_seqlens: Optional[torch.Tensor]):
     """(batch, seq_len, n_qk, n_v) from tensor shapes, as the FlashKDA README lays them out."""
+    want = 3 if layout == "TND" else 4
+    if layout not in KDA_LAYOUT:
+        raise ValueError(f"unknown layout {layout!r}")
+    if q.dim() != want or v.dim() != want:
+        raise ValueError(f"{layout}: q and v must have {want} dimensions")
     if layout == "BNSD":
         return q.shape[0], q.shape[2], q.shape[1], v.shape[1]
     if layout == "BSND":
         return q.shape[0], q.shape[1], q.shape[2], v.shape[2]
-    if layout == "TND":
-        if cu_seqlens is None:
-            raise ValueError("TND needs cu_seqlens")
-        return cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1]
-    raise ValueError(f"unknown layout {layout!r}")
+    if cu_seqlens is None:
+        raise ValueError("TND needs cu_seqlens")
+    if cu_seqlens.dim() != 1 or cu_seqlens.shape[0] < 2:
+        raise ValueError("cu_seqlens must be a 1-D tensor of batch + 1 >= 2 entries")
+    return cu_seqlens.shape[0] - 1, q.shape[0], q.shape[1], v.shape[1]
+
+
+def _expected_shapes(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, d_k: int,
+                     d_v: int) -> dict:
+    """Shapes of every tensor of a call (FlashKDA README, sections 参数说明 and 返回值说明)."""
+    if layout == "BNSD":
+        qs, vs, bs = (batch, n_qk, seq_len, d_k), (batch, n_v, seq_len, d_v), (batch, n_v, seq_len)
+    elif layout == "BSND":
+        qs, vs, bs = (batch, seq_len, n_qk, d_k), (batch, seq_len, n_v, d_v), (batch, seq_len, n_v)
+    else:
+        qs, vs, bs = (seq_len, n_qk, d_k), (seq_len, n_v, d_v), (seq_len, n_v)
+    gs = tuple(vs[:-1]) + (d_k,)
+    return dict(q=qs, k=qs, v=vs, g=gs, g_scalar=bs, beta=bs, out=vs,
+                state=(batch, n_v, d_v, d_k), cu=(batch + 1,))
+
+
+def check_tensors(tensors: dict, layout: str):
+    """Dtype, shape and contiguity of every tensor of a call, then that all of them live on one
+    GPU.  `tensors` maps q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
+    workspace to tensors or None.  Returns (batch, seq_len, n_qk, n_v, scalar_gate).  Raises
+    ValueError / TypeError, so that no wrong-sized or host buffer reaches the kernels."""
+    q, v, g, beta = tensors["q"], tensors["v"], tensors["g"], tensors["beta"]
+    cu = tensors.get("cu_seqlens")
+    batch, seq_len, n_qk, n_v = infer_shape(q, v, layout, cu)
+    exp = _expected_shapes(layout, batch, seq_len, n_qk, n_v, q.shape[-1], v.shape[-1])
+    dtypes = dict(q=torch.bfloat16, k=torch.bfloat16, v=torch.bfloat16, g=torch.float32,
+                  beta=torch.bfloat16, initial_state=torch.float32, cu_seqlens=torch.int32,
+                  out=torch.bfloat16, final_state=torch.float32)
+    scalar_gate = tuple(g.shape) == exp["g_scalar"]
+    shapes = dict(q=exp["q"], k=exp["k"], v=exp["v"], g=exp["g_scalar"] if scalar_gate else exp["g"],
+                  beta=exp["beta"], initial_state=exp["state"], cu_seqlens=exp["cu"],
+                  out=exp["out"], final_state=exp["state"])
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if name in dtypes and t.dtype != dtypes[name]:
+            raise TypeError(f"{name} must be {dtypes[name]}, got {t.dtype}")
+        if name in shapes and tuple(t.shape) != tuple(shapes[name]):
+            what = " (or beta's shape for one gate per token and head)" if name == "g" else ""
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shapes[name])}{what}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    devices = {(t.device.type, t.device.index) for t in tensors.values() if t is not None}
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if len(devices) != 1:
+        raise ValueError(f"all tensors must be on one GPU, got {sorted(devices)}")
+    return batch, seq_len, n_qk, n_v, scalar_gate
 
 
 def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -97,36 +166,15 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     q, k: bf16; v: bf16; g: fp32 natural-log decay, either v's shape (one gate per key
     channel) or beta's shape (one gate per token and value head, shared by every key channel:
     the library's scalar-gate option); beta: bf16 (logits when beta_sigmoid); initial_state:
-    fp32 [batch, n_v, 128, 128] or None; cu_seqlens: int32 [batch+1] (required for TND).  All
-    tensors must be contiguous and on one GPU.
+    fp32 [batch, n_v, d_v, d_k] or None; cu_seqlens: int32 [batch+1] (required for TND).  All
+    tensors, including caller-supplied out, final_state and workspace, must be contiguous and
+    on one GPU; every shape and dtype is checked before anything is launched.
     """
-    batch, seq_len, n_qk, n_v = infer_shape(q, v, layout, cu_seqlens)
+    tensors = dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state,
+                   cu_seqlens=cu_seqlens, out=out, final_state=final_state, workspace=workspace)
+    batch, seq_len, n_qk, n_v, scalar_gate = check_tensors(tensors, layout)
     if scale is None:
         scale = q.shape[-1] ** -0.5
-    for name, t, dt in (("q", q, torch.bfloat16), ("k", k, torch.bfloat16),
-                        ("v", v, torch.bfloat16), ("g", g, torch.float32),
-                        ("beta", beta, torch.bfloat16)):
-        if t.dtype != dt:
-            raise TypeError(f"{name} must be {dt}, got {t.dtype}")
-        if not t.is_cuda:
-            raise ValueError(f"{name} must be a GPU tensor")
-        if not t.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if k.shape != q.shape:
-        raise ValueError("k must match q")
-    if g.shape == v.shape:
-        scalar_gate = False
-    elif g.shape == beta.shape:
-        scalar_gate = True
-    else:
-        raise ValueError("g must have v's shape (per channel) or beta's shape (scalar gate)")
-    if initial_state is not None and (initial_state.dtype != torch.float32
-                                      or not initial_state.is_contiguous()
-                                      or tuple(initial_state.shape) != (batch, n_v, v.shape[-1],
-                                                                         q.shape[-1])):
-        raise ValueError("initial_state must be contiguous fp32 [batch, n_v, d_v, d_k]")
-    if cu_seqlens is not None and (cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_cuda):
-        raise ValueError("cu_seqlens must be an int32 GPU tensor")
     shape = make_shape(layout, batch, seq_len, n_qk, n_v, scale, qk_l2norm, beta_sigmoid,
                        q.shape[-1], v.shape[-1], scalar_gate)
     lib = _lib.load()
@@ -136,8 +184,11 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
         final_state = torch.empty((batch, n_v, v.shape[-1], q.shape[-1]), dtype=torch.float32,
                                   device=v.device)
     nbytes = kda_chunk_fwd_workspace(shape)
-    if workspace is None or workspace.numel() * workspace.element_size() < nbytes:
+    if workspace is None:
         workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=v.device)
+    elif workspace.numel() * workspace.element_size() < nbytes:
+        raise ValueError(f"workspace holds {workspace.numel() * workspace.element_size()} bytes, "
+                         f"the call needs {nbytes}")
     stream = ctypes.c_void_p(torch.cuda.current_stream(v.device).cuda_stream)
     args = [ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
             _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),

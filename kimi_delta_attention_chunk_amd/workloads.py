@@ -167,14 +167,30 @@ def make_inputs(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, *,
     return Inputs(layout, batch, stored, n_qk, n_v, q, k, v, g, beta, st, cu)
 
 
+def _tnd_lengths(w: Workload, s: int) -> list:
+    gen = torch.Generator().manual_seed(s + 7919)
+    return torch.randint(1, w.tnd_max_len + 1, (w.batch,), generator=gen).tolist()
+
+
+def workload_shape(w) -> dict:
+    """make_inputs keyword arguments of a named workload's shape (sequence lengths drawn as
+    workload_inputs draws them; no tensors)."""
+    if isinstance(w, str):
+        w = BY_NAME[w]
+    kw = dict(layout=w.layout, batch=w.batch, seq_len=w.seq_len, n_qk=w.n_qk, n_v=w.n_v,
+              d=w.d, scalar_gate=w.scalar_gate)
+    if w.layout == "TND":
+        kw.update(seq_len=0, lengths=_tnd_lengths(w, w.seed))
+    return kw
+
+
 def workload_inputs(w, seed: Optional[int] = None) -> Inputs:
     """Inputs of one named workload (seed defaults to the workload's own)."""
     if isinstance(w, str):
         w = BY_NAME[w]
     s = w.seed if seed is None else seed
     if w.layout == "TND":
-        gen = torch.Generator().manual_seed(s + 7919)
-        lengths = torch.randint(1, w.tnd_max_len + 1, (w.batch,), generator=gen).tolist()
+        lengths = _tnd_lengths(w, s)
         inp = make_inputs("TND", w.batch, 0, w.n_qk, w.n_v, g_kind=w.g_kind, init=w.init,
                           seed=s, lengths=lengths, scalar_gate=w.scalar_gate, d=w.d)
     else:

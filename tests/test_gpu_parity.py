@@ -1,10 +1,11 @@
 """GPU parity: the gfx950 library against the fp64 oracle, through the C ABI.
 
 Small cases (several chunks, ragged tails, every layout, GQA, both fused-option settings) are
-compared in full, for the per-channel gate and the scalar (GDN) gate.  The named workloads run
-at their full sizes in the launch configuration the benchmark times; the oracle checks every
-output of the tiny and both 8K workloads and one full 16-row Dv tile (all tokens, all heads) of
-the three large ones, since state rows evolve independently in the recurrence.  Further tests check invariants that hold at any size.
+compared in full, for the per-channel gate and the scalar (GDN) gate, with cases that make the
+plan select every kernel variant the library holds.  The named workloads run at their full
+sizes in the launch configuration the benchmark times, and every output and final-state element
+is compared with the oracle (head by head, to bound host memory).  Further tests check
+invariants that hold at any size.
 """
 import json
 import math
@@ -19,6 +20,9 @@ from parity import assert_parity
 from kimi_delta_attention_chunk_amd import kda_chunk_fwd, chunk_fwd
 from kimi_delta_attention_chunk_amd.workloads import (Inputs, make_inputs, workload_inputs,
                                                       WORKLOADS)
+from gpu_cases import (SMALL, SCALAR_GATE_CASES, D64_CASES, TWO_LEVEL, VARIANT_CASES,
+                       case_shape)
+from kimi_delta_attention_chunk_amd.ops import kda_chunk_fwd_plan_kernels
 
 pytestmark = pytest.mark.gpu
 
@@ -80,68 +84,6 @@ def test_hand_example_zero_padded():
     assert_parity(fin[0, 0], exp_fin, "hand example final_state")
 
 
-SMALL = [
-    ("bnsd_b2_n2_s200_strong_init", dict(layout="BNSD", batch=2, seq_len=200, n_qk=2, n_v=2,
-                                         g_kind="strong", init=True, seed=5)),
-    ("bsnd_gqa_b2_s150", dict(layout="BSND", batch=2, seq_len=150, n_qk=1, n_v=4,
-                              g_kind="unit", init=False, seed=6)),
-    ("tnd_ragged", dict(layout="TND", batch=6, seq_len=0, n_qk=2, n_v=2, g_kind="strong",
-                        init=True, seed=7, lengths=[1, 63, 64, 65, 130, 17])),
-    ("bnsd_valid_lengths", dict(layout="BNSD", batch=3, seq_len=140, n_qk=1, n_v=1,
-                                g_kind="small", init=True, seed=8, valid_lengths=[140, 65, 3])),
-    ("bnsd_floor_decay", dict(layout="BNSD", batch=1, seq_len=256, n_qk=1, n_v=2,
-                              g_kind="floor", init=True, seed=9)),
-    ("bnsd_no_decay", dict(layout="BNSD", batch=1, seq_len=192, n_qk=1, n_v=1,
-                           g_kind="zero", init=True, seed=10)),
-    # no decay over 64 chunks: the state never forgets, so rounding accumulates longest here
-    ("bnsd_no_decay_s4096", dict(layout="BNSD", batch=1, seq_len=4096, n_qk=1, n_v=1,
-                                 g_kind="zero", init=True, seed=11)),
-    # the scan walks sequences longest first: equal lengths (ties broken by index) and more
-    # sequences than it ranks (index order)
-    ("tnd_equal_lengths", dict(layout="TND", batch=6, seq_len=0, n_qk=1, n_v=2,
-                               g_kind="strong", init=True, seed=12,
-                               lengths=[100, 3, 100, 100, 64, 100])),
-    ("tnd_300_short_seqs", dict(layout="TND", batch=300, seq_len=0, n_qk=1, n_v=1,
-                                g_kind="strong", init=True, seed=13,
-                                lengths=[1 + (37 * i) % 90 for i in range(300)])),
-]
-
-# One gate per (token, value head) (KDA_SCALAR_GATE, the GDN form): every layout, GQA, ragged
-# tails, valid lengths, and a sequence long enough for the two-level scan.
-SCALAR_GATE_CASES = [
-    ("gdn_bnsd_gqa_tail", dict(layout="BNSD", batch=2, seq_len=300, n_qk=1, n_v=2,
-                               g_kind="strong", init=True, seed=41, scalar_gate=True)),
-    ("gdn_bsnd_valid_lengths", dict(layout="BSND", batch=2, seq_len=200, n_qk=2, n_v=2,
-                                    g_kind="unit", init=False, seed=42, valid_lengths=[200, 77],
-                                    scalar_gate=True)),
-    ("gdn_tnd_ragged", dict(layout="TND", batch=4, seq_len=0, n_qk=2, n_v=4, g_kind="strong",
-                            init=True, seed=43, lengths=[150, 64, 1, 90], scalar_gate=True)),
-    ("gdn_bnsd_two_level", dict(layout="BNSD", batch=1, seq_len=64 * 40 + 5, n_qk=1, n_v=1,
-                                g_kind="small", init=True, seed=44, scalar_gate=True)),
-]
-
-
-# Head dim 64 (d_k = d_v = 64): every layout, GQA, ragged tails, valid lengths, no decay, the
-# scalar gate, and a sequence long enough for the two-level scan.
-D64_CASES = [
-    ("d64_bnsd_b2_s200", dict(layout="BNSD", batch=2, seq_len=200, n_qk=2, n_v=2,
-                              g_kind="strong", init=True, seed=51, d=64)),
-    ("d64_bsnd_gqa_tail", dict(layout="BSND", batch=2, seq_len=150, n_qk=1, n_v=4,
-                               g_kind="unit", init=False, seed=52, d=64)),
-    ("d64_tnd_ragged", dict(layout="TND", batch=5, seq_len=0, n_qk=2, n_v=2, g_kind="strong",
-                            init=True, seed=53, lengths=[1, 63, 65, 130, 17], d=64)),
-    ("d64_bnsd_valid_lengths", dict(layout="BNSD", batch=3, seq_len=140, n_qk=1, n_v=1,
-                                    g_kind="small", init=True, seed=54,
-                                    valid_lengths=[140, 65, 3], d=64)),
-    ("d64_bnsd_no_decay", dict(layout="BNSD", batch=1, seq_len=1024, n_qk=1, n_v=1,
-                               g_kind="zero", init=True, seed=55, d=64)),
-    ("d64_two_level", dict(layout="BNSD", batch=1, seq_len=64 * 40 + 17, n_qk=1, n_v=1,
-                           g_kind="strong", init=True, seed=56, d=64)),
-    ("d64_gdn_tnd", dict(layout="TND", batch=3, seq_len=0, n_qk=1, n_v=2, g_kind="strong",
-                         init=True, seed=57, lengths=[100, 64, 33], scalar_gate=True, d=64)),
-]
-
-
 @pytest.mark.parametrize("name,kw", D64_CASES, ids=[s[0] for s in D64_CASES])
 def test_head_dim_64(name, kw):
     inp = make_inputs(**kw)
@@ -154,29 +96,6 @@ def test_scalar_gate(name, kw):
     inp = make_inputs(**kw)
     assert inp.scalar_gate
     compare(inp, name)
-
-
-# Few (sequence, head) chains and long enough sequences: the library runs the two-level scan
-# (segments from zero and from the identity, then an affine combine); see kda_plan.cpp.
-TWO_LEVEL = [
-    ("bnsd_1head_41chunks_tail", dict(layout="BNSD", batch=1, seq_len=64 * 40 + 17, n_qk=1,
-                                      n_v=1, g_kind="strong", init=True, seed=31)),
-    ("bnsd_valid_lengths", dict(layout="BNSD", batch=2, seq_len=3000, n_qk=1, n_v=1,
-                                g_kind="unit", init=True, seed=32, valid_lengths=[3000, 1300])),
-    ("tnd_two_seqs", dict(layout="TND", batch=2, seq_len=0, n_qk=1, n_v=1, g_kind="small",
-                          init=True, seed=33, lengths=[2100, 700])),
-    ("bsnd_gqa", dict(layout="BSND", batch=1, seq_len=1600, n_qk=1, n_v=2, g_kind="mixed",
-                      init=False, seed=34)),
-    # the most segments (16: one head, 128 chunks) and two heads (8 segments)
-    ("bnsd_1head_16seg", dict(layout="BNSD", batch=1, seq_len=8192, n_qk=1, n_v=1,
-                              g_kind="strong", init=True, seed=35)),
-    ("bnsd_2head_8seg", dict(layout="BNSD", batch=1, seq_len=4096 + 30, n_qk=2, n_v=2,
-                             g_kind="small", init=True, seed=36)),
-    # packed sequences of very different lengths: the short ones leave later segments empty
-    # (their walks return at once, the combine meets identity transfers and zero end states)
-    ("tnd_length_mix", dict(layout="TND", batch=5, seq_len=0, n_qk=1, n_v=1, g_kind="strong",
-                            init=True, seed=37, lengths=[1, 5000, 64, 65, 700])),
-]
 
 
 @pytest.mark.parametrize("name,kw", TWO_LEVEL, ids=[s[0] for s in TWO_LEVEL])
@@ -203,15 +122,58 @@ def test_flags_off_prenormalised_inputs():
     compare(inp, "flags off")
 
 
-WL_ROWS = {"tiny_s256": None, "prefill_s8k_n3": None, "gqa_tail_s4100": (16, 32),
-           "varlen_tnd_32seq": (48, 64), "long_s128k_n32": (112, 128),
-           "gdn_prefill_s8k_n3": None, "prefill_s8k_n6_d64": None}
+@pytest.mark.parametrize("name,kw", VARIANT_CASES, ids=[s[0] for s in VARIANT_CASES])
+def test_kernel_variants(name, kw):
+    kernels = kda_chunk_fwd_plan_kernels(case_shape(kw))
+    compare(make_inputs(**kw), f"{name} {kernels}")
+
+
+HEAD_AXIS = {"BNSD": 1, "BSND": 2, "TND": 1}
 
 
 @pytest.mark.parametrize("name", [w.name for w in WORKLOADS])
 def test_workload(name):
+    """Full size, every element: outputs compared one value head at a time (each head's slice
+    meets the bar on its own, which implies it for the whole tensor)."""
     inp = workload_inputs(name)
-    compare(inp, f"workload {name}", WL_ROWS[name])
+    print(f"[case] workload {name}", flush=True)
+    out, fin = run_gpu(inp)
+    out = out.cpu()
+    ro, rf = oracle_of(inp)
+    ax = HEAD_AXIS[inp.layout]
+    for h in range(inp.n_v):
+        assert_parity(out.select(ax, h), np.take(ro, h, axis=ax), f"workload {name} out head {h}")
+    assert_parity(fin, rf, f"workload {name} final_state")
+
+
+# Range of the fp16 intermediates (U, the innovation v - S k, the combine's state operand):
+# v and the initial state scaled by c.  The recurrence is linear in (v, S_0), so out and
+# final_state scale by c as well; both sides are divided by c (a power of two, exact) and held
+# to the same bar as unscaled inputs.  One-level and two-level forms, both head dims.
+RANGE_CASES = [
+    (c, kw) for c in (64.0, 512.0, 2048.0) for kw in (
+        dict(layout="BNSD", batch=1, seq_len=300, n_qk=1, n_v=2, g_kind="unit", init=True,
+             seed=71),
+        dict(layout="BNSD", batch=1, seq_len=64 * 40 + 17, n_qk=1, n_v=1, g_kind="small",
+             init=True, seed=72),
+        dict(layout="BSND", batch=1, seq_len=64 * 24 + 3, n_qk=1, n_v=1, g_kind="zero",
+             init=True, seed=73, d=64),
+    )
+]
+
+
+@pytest.mark.parametrize("c,kw", RANGE_CASES,
+                         ids=[f"v_x{int(c)}_{kw['layout']}_s{kw['seq_len']}_d{kw.get('d', 128)}"
+                              for c, kw in RANGE_CASES])
+def test_value_range(c, kw):
+    inp = make_inputs(**kw)
+    inp.v = (inp.v.float() * c).bfloat16()
+    inp.initial_state = inp.initial_state * c
+    print(f"[case] v and initial state x{c} {kw}", flush=True)
+    out, fin = run_gpu(inp)
+    ro, rf = oracle_of(inp)
+    assert_parity(out.double() / c, ro / c, f"x{c} out / {c}")
+    assert_parity(fin.double() / c, rf / c, f"x{c} final_state / {c}")
 
 
 def test_layout_invariance_bitwise():
