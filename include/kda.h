@@ -121,6 +121,25 @@ kda_status kda_chunk_fwd(const kda_shape* shape,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/* Allocation-free variant of kda_chunk_fwd, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * computation and kernels, with the workspace taken from a device array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on, until the process
+ * ends, instead of a caller buffer.  The caller still passes every input and output.
+ * Limit: shapes whose kda_chunk_fwd_workspace() exceeds KDA_NOALLOC_SCRATCH_BYTES return
+ * KDA_ERR_WORKSPACE and launch nothing (64 MiB holds, e.g., the 8K-token prefill with three
+ * 128-dim heads).  The first call on a device looks up the array's device address
+ * (hipGetSymbolAddress; a failure is KDA_ERR_HIP); no call allocates or frees device memory.
+ * Every call on one GPU uses the same array: calls that overlap in time on one GPU (two
+ * streams, two host threads) race and must be serialised by the caller.  Nothing in the array
+ * needs to be cleared between calls. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_chunk_fwd_noalloc(const kda_shape* shape,
+                                 const void* q, const void* k, const void* v,
+                                 const float* g, const void* beta,
+                                 const float* initial_state, const int32_t* cu_seqlens,
+                                 void* out, float* final_state, hipStream_t stream);
+
 /* Number of stages of one kda_chunk_fwd call and the name of each, one kernel per stage: the
  * intra-chunk kernel; then, when few (sequence, head) chains would leave the GPU idle through a
  * long sequential scan, the two-level scan's segment pass (every segment walked at once from a

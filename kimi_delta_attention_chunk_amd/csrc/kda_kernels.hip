@@ -36,6 +36,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_plan.h"
@@ -2010,6 +2011,36 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     return KDA_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Allocation-free entry point
+// ---------------------------------------------------------------------------------------------
+//
+// For callers that cannot allocate device memory (HIP graph capture, tight serving loops):
+// the workspace lives in a file-scope device array, one copy per GPU the library runs on, held
+// until the process ends.  Host code never passes the array's name to a kernel (on the host it
+// is only a stand-in for the symbol): its device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and that address is what the kernels get.
+// Every call on one GPU shares the array; nothing in it has to start at zero (every workspace
+// element a kernel reads was written by an earlier kernel of the same call), but calls that
+// overlap in time on one GPU (two streams, two threads) race on it.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+kda_status scratch_of_current_device(void** ptr) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return KDA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return KDA_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return KDA_OK;
+}
+
 }  // namespace kda
 
 extern "C" {
@@ -2029,6 +2060,20 @@ kda_status kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, c
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
     return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
                        workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+kda_status kda_chunk_fwd_noalloc(const kda_shape* shape, const void* q, const void* k,
+                                 const void* v, const float* g, const void* beta,
+                                 const float* initial_state, const int32_t* cu_seqlens, void* out,
+                                 float* final_state, hipStream_t stream) {
+    kda::Plan plan;
+    const kda_status st = kda::make_plan(shape, &plan);
+    if (st != KDA_OK) return st;
+    if (plan.total > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (kda::scratch_of_current_device(&ws) != KDA_OK) return KDA_ERR_HIP;
+    return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, ws,
+                       KDA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 kda_status kda_chunk_fwd_timed(const kda_shape* shape, const void* q, const void* k,

@@ -204,6 +204,31 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
     return out, final_state
 
 
+def kda_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, scale: Optional[float], initial_state,
+                          cu_seqlens, layout: str, out: torch.Tensor,
+                          final_state: Optional[torch.Tensor] = None, qk_l2norm: bool = True,
+                          beta_sigmoid: bool = True) -> None:
+    """kda_chunk_fwd_noalloc: the chunked forward with the library's own device scratch as the
+    workspace; allocates nothing (the caller passes out and, optionally, final_state).  Calls
+    that overlap in time on one GPU race on that scratch."""
+    if out is None:
+        raise ValueError("kda_chunk_fwd_noalloc writes into a caller-supplied out")
+    tensors = dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state,
+                   cu_seqlens=cu_seqlens, out=out, final_state=final_state)
+    batch, seq_len, n_qk, n_v, scalar_gate = check_tensors(tensors, layout)
+    if scale is None:
+        scale = q.shape[-1] ** -0.5
+    shape = make_shape(layout, batch, seq_len, n_qk, n_v, scale, qk_l2norm, beta_sigmoid,
+                       q.shape[-1], v.shape[-1], scalar_gate)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(v.device).cuda_stream)
+    st = _lib.load().kda_chunk_fwd_noalloc(
+        ctypes.byref(shape), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(initial_state),
+        _ptr(cu_seqlens), _ptr(out), _ptr(final_state), stream)
+    if st != KDA_OK:
+        raise KdaError(st, "kda_chunk_fwd_noalloc")
+
+
 def chunk_fwd(inp, **kw):
     """Convenience: run on a workloads.Inputs bundle already on the GPU."""
     return kda_chunk_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
