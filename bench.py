@@ -36,7 +36,10 @@ def head_dim(inp) -> int:
 
 
 def gate_bytes(inp) -> int:
-    """Bytes of g per token-head: D fp32 per-channel gates, or one fp32 with the scalar gate."""
+    """Bytes of g per token-head: D fp32 per-channel gates, one fp32 with the scalar gate, or
+    D bf16 raw gates (activated in the kernel)."""
+    if inp.raw_gate:
+        return head_dim(inp) * 2
     return 4 if inp.scalar_gate else head_dim(inp) * 4
 
 
@@ -46,14 +49,16 @@ def path_bytes(inp) -> int:
     t, d = inp.tokens, head_dim(inp)
     b = t * inp.n_qk * d * 2 * 2 + t * inp.n_v * (d * 2 + gate_bytes(inp) + 2 + d * 2)
     states = inp.batch * inp.n_v * d * d * 4
-    return b + states * ((inp.initial_state is not None) + 1)
+    gate_params = inp.n_v * (d + 1) * 4 if inp.raw_gate else 0   # dt_bias and A_log
+    return b + states * ((inp.initial_state is not None) + 1) + gate_params
 
 
 def shape_of(inp):
     from kimi_delta_attention_chunk_amd import make_shape
     d = head_dim(inp)
     return make_shape(inp.layout, inp.batch, inp.seq_len, inp.n_qk, inp.n_v, inp.scale,
-                      inp.qk_l2norm, inp.beta_sigmoid, d, d, inp.scalar_gate)
+                      inp.qk_l2norm, inp.beta_sigmoid, d, d, inp.scalar_gate,
+                      raw_gate=inp.raw_gate)
 
 
 def seg_p_of(inp) -> int:
@@ -206,7 +211,7 @@ def cpu_baseline(inp, min_seconds: float = 10.0) -> dict:
     while len(times) < 3 or time.perf_counter() - t_start < min_seconds:
         t0 = time.perf_counter()
         kda_oracle(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
-                   inp.cu_seqlens, inp.layout, flags)
+                   inp.cu_seqlens, inp.layout, flags, raw_gate=inp.gate_args)
         times.append(time.perf_counter() - t0)
         if len(times) >= 200:
             break
@@ -282,16 +287,15 @@ def main() -> int:
 
     wl = BY_NAME[args.workload]
     host = workload_inputs(wl)
-    in_bytes = (host.q.numel() * 4 + host.v.numel() * 2 + host.g.numel() * 4 +
-                host.beta.numel() * 2)
+    in_bytes = (host.q.numel() * 4 + host.v.numel() * 2 +
+                host.g.numel() * host.g.element_size() + host.beta.numel() * 2)
     copies = args.copies or max(1, min(16, math.ceil(2 * MALL_BYTES / max(in_bytes, 1))))
     dev = torch.device("cuda", 0)
     sets = [host.to(dev) for _ in range(copies)]
     out = torch.empty_like(sets[0].v)
     d = head_dim(host)
     fin = torch.empty((host.batch, host.n_v, d, d), dtype=torch.float32, device=dev)
-    shape = make_shape(host.layout, host.batch, host.seq_len, host.n_qk, host.n_v, host.scale,
-                       host.qk_l2norm, host.beta_sigmoid, d, d, host.scalar_gate)
+    shape = shape_of(host)
     ws = torch.empty(kda_chunk_fwd_workspace(shape), dtype=torch.uint8, device=dev)
     nst = kda_num_stages()
 
@@ -358,6 +362,7 @@ def main() -> int:
         "config": {"workload": wl.name, "layout": host.layout, "batch": host.batch,
                    "seq_len": host.seq_len, "tokens": host.tokens, "n_qk": host.n_qk,
                    "n_v": host.n_v, "head_dim": d, "scalar_gate": host.scalar_gate,
+                   "raw_gate": host.raw_gate,
                    "input_copies": copies,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "kernel": kda_stage_name(dom), "achieved": achieved / 1e9,

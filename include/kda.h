@@ -65,8 +65,23 @@ typedef enum {
 enum {
     KDA_QK_L2NORM = 1u << 0,
     KDA_BETA_SIGMOID = 1u << 1,
-    KDA_SCALAR_GATE = 1u << 2
+    KDA_SCALAR_GATE = 1u << 2,
+    KDA_RAW_GATE = 1u << 3     /* kda_chunk_fwd_raw_gate only: g is the raw bf16 gate */
 };
+
+/* Raw-gate activation (FlashKDA README, sections 参数说明 and 快速开始: a raw bf16 gate shaped
+ * like v with A_log [n_v] fp32, "the log time scale of each value head", dt_bias [n_v, d_k] fp32,
+ * "the gate bias", and lower_bound in [-5, 0], "the gate's lower bound"; section 约束说明 bounds
+ * lower_bound).  The README prints no formula; this library reads it as
+ *     g[t, j] = lower_bound * sigmoid(exp(A_log[h]) * (g_raw[t, j] + dt_bias[h, j]))
+ * for value head h and key channel j, so every activated gate lies in [lower_bound, 0] (the
+ * form -5 * sigmoid(x) of the 8K-prefill workload's own gate), and then runs the recurrence
+ * above on it. */
+typedef struct {
+    const float* a_log;     /* device pointer, fp32 [n_v], 4-byte aligned                   */
+    const float* dt_bias;   /* device pointer, fp32 [n_v, d_k], 16-byte aligned             */
+    float lower_bound;      /* in [-5, 0]; KDA_ERR_INVALID_ARG otherwise (NaN included)      */
+} kda_raw_gate;
 
 typedef enum {
     KDA_OK = 0,
@@ -87,7 +102,7 @@ typedef struct {
     int32_t d_k;       /* head dim of q/k: 128 (FlashKDA README, 约束说明) or 64; equal to d_v  */
     int32_t d_v;       /* head dim of v and out: equal to d_k                                 */
     float scale;       /* output scale, typically d_k ** -0.5; must be finite                 */
-    uint32_t flags;    /* KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE                  */
+    uint32_t flags;    /* KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE | KDA_RAW_GATE   */
 } kda_shape;
 
 /* Bytes of device workspace kda_chunk_fwd needs for `shape` (FlashKDA README, section 功能说明:
@@ -120,6 +135,21 @@ kda_status kda_chunk_fwd(const kda_shape* shape,
                          void* out, float* final_state,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
+
+/* kda_chunk_fwd with the gate activation fused (FlashKDA README, sections 功能说明 and 参数说明:
+ * the operator activates the raw gate itself).  shape->flags must include KDA_RAW_GATE (and
+ * not KDA_SCALAR_GATE: KDA_ERR_UNSUPPORTED); g_raw is bf16 with v's shape and layout; gate holds
+ * A_log, dt_bias (device pointers, read only, not overlapping anything the call writes) and
+ * lower_bound (see kda_raw_gate).  Every other argument, the workspace size and the errors are
+ * those of kda_chunk_fwd; KDA_ERR_INVALID_ARG also for a NULL gate or parameter pointer, a
+ * lower_bound outside [-5, 0], or the KDA_RAW_GATE flag missing (kda_chunk_fwd rejects the flag). */
+kda_status kda_chunk_fwd_raw_gate(const kda_shape* shape,
+                                  const void* q, const void* k, const void* v,
+                                  const void* g_raw, const void* beta, const kda_raw_gate* gate,
+                                  const float* initial_state, const int32_t* cu_seqlens,
+                                  void* out, float* final_state,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
 
 /* Allocation-free variant of kda_chunk_fwd, for callers that cannot allocate device memory
  * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
@@ -187,6 +217,17 @@ kda_status kda_chunk_fwd_plan_kernels(const kda_shape* shape, char* names, size_
  * launch shape. */
 int32_t kda_num_kernel_variants(void);
 const char* kda_kernel_variant(int32_t i);
+
+/* Profiling variant of kda_chunk_fwd_raw_gate, with the stage events of kda_chunk_fwd_timed. */
+kda_status kda_chunk_fwd_raw_gate_timed(const kda_shape* shape,
+                                        const void* q, const void* k, const void* v,
+                                        const void* g_raw, const void* beta,
+                                        const kda_raw_gate* gate,
+                                        const float* initial_state, const int32_t* cu_seqlens,
+                                        void* out, float* final_state,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream,
+                                        hipEvent_t* stage_events, int32_t n_stage_events);
 
 /* Static string naming a status code ("KDA_OK", ...); "unknown kda_status" otherwise.  The codes
  * report the argument checks of the FlashKDA README, section 约束说明 (supported head dims,

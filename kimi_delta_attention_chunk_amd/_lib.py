@@ -14,13 +14,15 @@ KDA_LAYOUT = {"BNSD": 0, "BSND": 1, "TND": 2}
 KDA_QK_L2NORM = 1
 KDA_BETA_SIGMOID = 2
 KDA_SCALAR_GATE = 4
+KDA_RAW_GATE = 8
 NOALLOC_SCRATCH_BYTES = 64 << 20   # KDA_NOALLOC_SCRATCH_BYTES in include/kda.h
 KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
 
 EXPORTED = ["kda_chunk_fwd_workspace", "kda_chunk_fwd", "kda_chunk_fwd_timed",
             "kda_num_stages", "kda_stage_name", "kda_chunk_fwd_plan", "kda_status_str",
             "kda_version", "kda_chunk_fwd_plan_kernels", "kda_num_kernel_variants",
-            "kda_kernel_variant", "kda_chunk_fwd_noalloc"]
+            "kda_kernel_variant", "kda_chunk_fwd_noalloc", "kda_chunk_fwd_raw_gate",
+            "kda_chunk_fwd_raw_gate_timed"]
 
 
 class KdaShape(ctypes.Structure):
@@ -29,6 +31,12 @@ class KdaShape(ctypes.Structure):
                 ("seq_len", ctypes.c_int32), ("n_qk", ctypes.c_int32),
                 ("n_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("flags", ctypes.c_uint32)]
+
+
+class KdaRawGate(ctypes.Structure):
+    """Mirror of ``kda_raw_gate`` in include/kda.h."""
+    _fields_ = [("a_log", ctypes.c_void_p), ("dt_bias", ctypes.c_void_p),
+                ("lower_bound", ctypes.c_float)]
 
 
 _lib = None
@@ -51,6 +59,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     args = [S, P, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.kda_chunk_fwd.argtypes = args
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    G = ctypes.POINTER(KdaRawGate)
+    raw = [S, P, P, P, P, P, G, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.kda_chunk_fwd_raw_gate.argtypes = raw
+    lib.kda_chunk_fwd_raw_gate.restype = ctypes.c_int
+    lib.kda_chunk_fwd_raw_gate_timed.argtypes = raw + [ctypes.POINTER(ctypes.c_void_p),
+                                                       ctypes.c_int32]
+    lib.kda_chunk_fwd_raw_gate_timed.restype = ctypes.c_int
     lib.kda_chunk_fwd_noalloc.argtypes = [S, P, P, P, P, P, P, P, P, P, P]
     lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_chunk_fwd_timed.argtypes = args + [ctypes.POINTER(ctypes.c_void_p), ctypes.c_int32]

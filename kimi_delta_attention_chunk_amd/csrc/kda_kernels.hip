@@ -58,6 +58,10 @@ struct Params {
     const __bf16* k;
     const __bf16* v;
     const float* g;
+    const __bf16* graw;      // raw bf16 gate (gate mode 2), v's layout
+    const float* a_log;      // [n_v]     gate mode 2
+    const float* dt_bias;    // [n_v, D]  gate mode 2
+    float lower_bound;       //           gate mode 2
     const __bf16* beta;
     const float* init;
     const int32_t* cu;
@@ -342,7 +346,9 @@ __device__ __forceinline__ void blk_row8(const float* m, int I, int s, int q4, i
 }
 
 // GM: gate mode.  0: one fp32 natural-log decay per (token, key channel); 1: one per (token,
-// value head) (KDA_SCALAR_GATE), broadcast over the key channels.
+// value head) (KDA_SCALAR_GATE), broadcast over the key channels; 2: the raw bf16 gate per
+// (token, key channel), activated at load as lower_bound * sigmoid(exp(A_log[h]) * (g_raw +
+// dt_bias[h, c])) (KDA_RAW_GATE).
 // D: head dim (d_k = d_v), 128 or 64.
 // HV: waves per 16-token block.  With HV = 2 (eight waves) wave w owns token block I = w >> 1
 // and channel half hc = w & 1: its loads, gate sums, decayed operands and transposes cover
@@ -428,11 +434,24 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     // tail are read clamped and masked where they are consumed, so that no register written
     // here is rewritten before its load returns (which would make the wave wait for it).
     bf16x8 xq[KBW], xk[KBW], xv[KBW];
-    f32x4 xg[2 * KBW];
+    f32x4 xg[2 * KBW];   // the fp32 gate, or (gate mode 2) dt_bias of the lane's channels
+    bf16x8 xgr[KBW];     // gate mode 2: the raw gate
     float gsv;   // the one gate of this token with KDA_SCALAR_GATE (beta's layout)
+    float alog = 0.f;
     float braw;
     if constexpr (SG) {
         gsv = p.g[bb + size_t(tc) * bs];
+    } else if constexpr (GM == 2) {
+        const __bf16* gr = p.graw + vb + size_t(tc) * vs;
+        const float* db = p.dt_bias + size_t(h) * D;
+#pragma unroll
+        for (int i = 0; i < KBW; ++i) {
+            const int c = 32 * (kb0 + i) + 8 * q4;
+            xgr[i] = *reinterpret_cast<const bf16x8*>(gr + c);
+            xg[2 * i] = *reinterpret_cast<const f32x4*>(db + c);
+            xg[2 * i + 1] = *reinterpret_cast<const f32x4*>(db + c + 4);
+        }
+        alog = p.a_log[h];
     } else {
         const float* gr = p.g + vb + size_t(tc) * vs;
 #pragma unroll
@@ -474,8 +493,17 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
             d[i] = ds;
         }
     } else {
+        if constexpr (GM == 2) {   // g = lower_bound * sigmoid(exp(A_log) (g_raw + dt_bias))
+            const float ts = exp2_fast(alog * kLog2e);
 #pragma unroll
-        for (int i = 0; i < 8 * KBW; ++i) gv[i] = xg[i >> 2][i & 3];
+            for (int i = 0; i < 8 * KBW; ++i) {
+                const float x = ts * ((float)xgr[i >> 3][i & 7] + xg[i >> 2][i & 3]);
+                gv[i] = p.lower_bound / (1.0f + exp2_fast(-x * kLog2e));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8 * KBW; ++i) gv[i] = xg[i >> 2][i & 3];
+        }
         if (n < kChunk) {   // a tail chunk: rows past it add nothing
 #pragma unroll
             for (int i = 0; i < 8 * KBW; ++i) gv[i] = tv ? gv[i] : 0.f;
@@ -1899,6 +1927,10 @@ const Variant kVariants[] = {
     KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 0,64,2),
     KDA_VARIANT(kda_intra_kernel, kThreads, 1,64,1),
     KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 1,64,2),
+    KDA_VARIANT(kda_intra_kernel, kThreads, 2,128,1),
+    KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 2,128,2),
+    KDA_VARIANT(kda_intra_kernel, kThreads, 2,64,1),
+    KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 2,64,2),
     KDA_VARIANT(kda_seg_kernel, kThreads, 128),
     KDA_VARIANT(kda_seg_kernel, kThreads, 64),
     KDA_VARIANT(kda_combine_kernel, kThreads, 128),
@@ -1923,7 +1955,7 @@ constexpr int kNameCap = 64;
 // Name of the kernel each stage of `plan` launches; an empty name for a stage the plan skips.
 void stage_kernels(const Plan& plan, uint32_t flags, char (&names)[kStages][kNameCap]) {
     for (auto& n : names) n[0] = '\0';
-    const int gm = (flags & KDA_SCALAR_GATE) ? 1 : 0;
+    const int gm = (flags & KDA_RAW_GATE) ? 2 : (flags & KDA_SCALAR_GATE) ? 1 : 0;
     std::snprintf(names[ST_INTRA], kNameCap, "kda_intra_kernel<%d,%d,%d>", gm, plan.d,
                   plan.intra_hv);
     if (plan.seg_p > 1) {
@@ -1942,15 +1974,19 @@ const Variant* find_variant(const char* name) {
     return nullptr;
 }
 
+// `gate` is the raw-gate activation (kda_chunk_fwd_raw_gate; g then points at the raw bf16
+// gate) or NULL (g is the fp32 activated gate).  The shape's KDA_RAW_GATE flag must agree.
 kda_status launch(const kda_shape* shape, const void* q, const void* k, const void* v,
-                  const float* g, const void* beta, const float* initial_state,
-                  const int32_t* cu_seqlens, void* out, float* final_state, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream, hipEvent_t* ev, int n_ev) {
+                  const void* g, const kda_raw_gate* gate, const void* beta,
+                  const float* initial_state, const int32_t* cu_seqlens, void* out,
+                  float* final_state, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream, hipEvent_t* ev, int n_ev) {
     Plan plan;
     kda_status st = make_plan(shape, &plan);
     if (st != KDA_OK) return st;
-    st = check_call(shape, plan, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
-                    workspace, workspace_bytes);
+    if (((shape->flags & KDA_RAW_GATE) != 0) != (gate != nullptr)) return KDA_ERR_INVALID_ARG;
+    st = check_call(shape, plan, q, k, v, g, gate, beta, initial_state, cu_seqlens, out,
+                    final_state, workspace, workspace_bytes);
     if (st != KDA_OK) return st;
     if (ev && n_ev < 2 * kStages) return KDA_ERR_INVALID_ARG;
 
@@ -1958,7 +1994,11 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.q = static_cast<const __bf16*>(q);
     p.k = static_cast<const __bf16*>(k);
     p.v = static_cast<const __bf16*>(v);
-    p.g = g;
+    p.g = gate ? nullptr : static_cast<const float*>(g);
+    p.graw = gate ? static_cast<const __bf16*>(g) : nullptr;
+    p.a_log = gate ? gate->a_log : nullptr;
+    p.dt_bias = gate ? gate->dt_bias : nullptr;
+    p.lower_bound = gate ? gate->lower_bound : 0.f;
     p.beta = static_cast<const __bf16*>(beta);
     p.init = initial_state;
     p.cu = cu_seqlens;
@@ -2058,8 +2098,31 @@ kda_status kda_chunk_fwd(const kda_shape* shape, const void* q, const void* k, c
                          const float* g, const void* beta, const float* initial_state,
                          const int32_t* cu_seqlens, void* out, float* final_state,
                          void* workspace, size_t workspace_bytes, hipStream_t stream) {
-    return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
-                       workspace, workspace_bytes, stream, nullptr, 0);
+    return kda::launch(shape, q, k, v, g, nullptr, beta, initial_state, cu_seqlens, out,
+                       final_state, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+kda_status kda_chunk_fwd_raw_gate(const kda_shape* shape, const void* q, const void* k,
+                                  const void* v, const void* g_raw, const void* beta,
+                                  const kda_raw_gate* gate, const float* initial_state,
+                                  const int32_t* cu_seqlens, void* out, float* final_state,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    if (!gate) return KDA_ERR_INVALID_ARG;
+    return kda::launch(shape, q, k, v, g_raw, gate, beta, initial_state, cu_seqlens, out,
+                       final_state, workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+kda_status kda_chunk_fwd_raw_gate_timed(const kda_shape* shape, const void* q, const void* k,
+                                        const void* v, const void* g_raw, const void* beta,
+                                        const kda_raw_gate* gate, const float* initial_state,
+                                        const int32_t* cu_seqlens, void* out, float* final_state,
+                                        void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream, hipEvent_t* stage_events,
+                                        int32_t n_stage_events) {
+    if (!gate || !stage_events || n_stage_events < 2 * kda::kStages) return KDA_ERR_INVALID_ARG;
+    return kda::launch(shape, q, k, v, g_raw, gate, beta, initial_state, cu_seqlens, out,
+                       final_state, workspace, workspace_bytes, stream, stage_events,
+                       n_stage_events);
 }
 
 kda_status kda_chunk_fwd_noalloc(const kda_shape* shape, const void* q, const void* k,
@@ -2072,8 +2135,8 @@ kda_status kda_chunk_fwd_noalloc(const kda_shape* shape, const void* q, const vo
     if (plan.total > KDA_NOALLOC_SCRATCH_BYTES) return KDA_ERR_WORKSPACE;
     void* ws = nullptr;
     if (kda::scratch_of_current_device(&ws) != KDA_OK) return KDA_ERR_HIP;
-    return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state, ws,
-                       KDA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
+    return kda::launch(shape, q, k, v, g, nullptr, beta, initial_state, cu_seqlens, out,
+                       final_state, ws, KDA_NOALLOC_SCRATCH_BYTES, stream, nullptr, 0);
 }
 
 kda_status kda_chunk_fwd_timed(const kda_shape* shape, const void* q, const void* k,
@@ -2083,8 +2146,9 @@ kda_status kda_chunk_fwd_timed(const kda_shape* shape, const void* q, const void
                                hipStream_t stream, hipEvent_t* stage_events,
                                int32_t n_stage_events) {
     if (!stage_events || n_stage_events < 2 * kda::kStages) return KDA_ERR_INVALID_ARG;
-    return kda::launch(shape, q, k, v, g, beta, initial_state, cu_seqlens, out, final_state,
-                       workspace, workspace_bytes, stream, stage_events, n_stage_events);
+    return kda::launch(shape, q, k, v, g, nullptr, beta, initial_state, cu_seqlens, out,
+                       final_state, workspace, workspace_bytes, stream, stage_events,
+                       n_stage_events);
 }
 
 int32_t kda_num_stages(void) { return kda::kStages; }

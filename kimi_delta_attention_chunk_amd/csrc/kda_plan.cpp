@@ -33,8 +33,10 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     if (s->d_k < 1 || s->d_v < 1) return KDA_ERR_INVALID_ARG;
     if (s->d_k != s->d_v || !head_dim_ok(s->d_k)) return KDA_ERR_UNSUPPORTED;
     if (!std::isfinite(s->scale)) return KDA_ERR_INVALID_ARG;
-    if (s->flags & ~uint32_t(KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE))
+    if (s->flags & ~uint32_t(KDA_QK_L2NORM | KDA_BETA_SIGMOID | KDA_SCALAR_GATE | KDA_RAW_GATE))
         return KDA_ERR_INVALID_ARG;
+    // the raw gate (FlashKDA README, 参数说明) has one value per key channel
+    if ((s->flags & KDA_RAW_GATE) && (s->flags & KDA_SCALAR_GATE)) return KDA_ERR_UNSUPPORTED;
     if (s->layout == KDA_LAYOUT_TND && s->seq_len < s->batch) return KDA_ERR_INVALID_ARG;
 
     Plan p;
@@ -157,11 +159,16 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
 }
 
 kda_status check_call(const kda_shape* s, const Plan& p, const void* q, const void* k,
-                      const void* v, const float* g, const void* beta,
+                      const void* v, const void* g, const kda_raw_gate* gate, const void* beta,
                       const float* initial_state, const int32_t* cu_seqlens, const void* out,
                       const float* final_state, const void* workspace,
                       size_t workspace_bytes) {
     if (!q || !k || !v || !g || !beta || !out) return KDA_ERR_INVALID_ARG;
+    if (gate) {   // raw-gate activation parameters (FlashKDA README, 约束说明: lower_bound in [-5, 0])
+        if (!gate->a_log || !gate->dt_bias) return KDA_ERR_INVALID_ARG;
+        if (!aligned(gate->a_log, 4) || !aligned(gate->dt_bias, 16)) return KDA_ERR_INVALID_ARG;
+        if (!(gate->lower_bound >= -5.0f && gate->lower_bound <= 0.0f)) return KDA_ERR_INVALID_ARG;
+    }
     if (s->layout == KDA_LAYOUT_TND && !cu_seqlens) return KDA_ERR_INVALID_ARG;
     const void* ptrs16[] = {q, k, v, g, out};
     for (const void* ptr : ptrs16)
@@ -192,7 +199,9 @@ kda_status check_call(const kda_shape* s, const Plan& p, const void* q, const vo
         {q, tokens * p.n_qk * p.d * 2, false},
         {k, tokens * p.n_qk * p.d * 2, false},
         {v, per_v * p.d * 2, false},
-        {g, per_v * (sg ? 1 : p.d) * sizeof(float), false},
+        {g, per_v * (sg ? 1 : p.d) * (gate ? 2 : sizeof(float)), false},
+        {gate ? gate->a_log : nullptr, gate ? size_t(p.n_v) * sizeof(float) : 0, false},
+        {gate ? gate->dt_bias : nullptr, gate ? size_t(p.n_v) * p.d * sizeof(float) : 0, false},
         {beta, per_v * 2, false},
         {initial_state, initial_state ? state_bytes : 0, false},
         {cu_seqlens, cu_seqlens ? (size_t(s->batch) + 1) * sizeof(int32_t) : 0, false},

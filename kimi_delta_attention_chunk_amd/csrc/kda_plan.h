@@ -65,9 +65,10 @@ struct Plan {
 // Validates the shape alone; fills `plan` when it is valid.
 kda_status make_plan(const kda_shape* shape, Plan* plan);
 
-// Validates pointers and sizes of a call against a valid plan.
+// Validates pointers and sizes of a call against a valid plan.  `gate` is the raw-gate
+// activation (g then points at the raw bf16 gate) or NULL (g is the fp32 activated gate).
 kda_status check_call(const kda_shape* shape, const Plan& plan, const void* q, const void* k,
-                      const void* v, const float* g, const void* beta,
+                      const void* v, const void* g, const kda_raw_gate* gate, const void* beta,
                       const float* initial_state, const int32_t* cu_seqlens, const void* out,
                       const float* final_state, const void* workspace,
                       size_t workspace_bytes);

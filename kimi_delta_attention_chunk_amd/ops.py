@@ -12,7 +12,8 @@ from typing import Optional, Sequence
 import torch
 
 from . import _lib
-from ._lib import KdaShape, KDA_LAYOUT, KDA_QK_L2NORM, KDA_BETA_SIGMOID, KDA_SCALAR_GATE, KDA_OK
+from ._lib import (KdaShape, KdaRawGate, KDA_LAYOUT, KDA_QK_L2NORM, KDA_BETA_SIGMOID,
+                   KDA_SCALAR_GATE, KDA_RAW_GATE, KDA_OK)
 
 D = 128
 
@@ -37,11 +38,11 @@ def kda_stage_name(i: int) -> str:
 
 def make_shape(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, scale: float,
                qk_l2norm: bool = True, beta_sigmoid: bool = True, d_k: int = D,
-               d_v: int = D, scalar_gate: bool = False) -> KdaShape:
+               d_v: int = D, scalar_gate: bool = False, raw_gate: bool = False) -> KdaShape:
     if layout not in KDA_LAYOUT:
         raise ValueError(f"unknown layout {layout!r}")
     flags = ((KDA_QK_L2NORM if qk_l2norm else 0) | (KDA_BETA_SIGMOID if beta_sigmoid else 0)
-             | (KDA_SCALAR_GATE if scalar_gate else 0))
+             | (KDA_SCALAR_GATE if scalar_gate else 0) | (KDA_RAW_GATE if raw_gate else 0))
     return KdaShape(KDA_LAYOUT[layout], int(batch), int(seq_len), int(n_qk), int(n_v),
                     int(d_k), int(d_v), float(scale), flags)
 
@@ -126,13 +127,19 @@ def check_tensors(tensors: dict, layout: str):
     cu = tensors.get("cu_seqlens")
     batch, seq_len, n_qk, n_v = infer_shape(q, v, layout, cu)
     exp = _expected_shapes(layout, batch, seq_len, n_qk, n_v, q.shape[-1], v.shape[-1])
-    dtypes = dict(q=torch.bfloat16, k=torch.bfloat16, v=torch.bfloat16, g=torch.float32,
+    raw = tensors.get("a_log") is not None or tensors.get("dt_bias") is not None
+    dtypes = dict(q=torch.bfloat16, k=torch.bfloat16, v=torch.bfloat16,
+                  g=torch.bfloat16 if raw else torch.float32,
                   beta=torch.bfloat16, initial_state=torch.float32, cu_seqlens=torch.int32,
-                  out=torch.bfloat16, final_state=torch.float32)
-    scalar_gate = tuple(g.shape) == exp["g_scalar"]
+                  out=torch.bfloat16, final_state=torch.float32, a_log=torch.float32,
+                  dt_bias=torch.float32)
+    scalar_gate = not raw and tuple(g.shape) == exp["g_scalar"]
     shapes = dict(q=exp["q"], k=exp["k"], v=exp["v"], g=exp["g_scalar"] if scalar_gate else exp["g"],
                   beta=exp["beta"], initial_state=exp["state"], cu_seqlens=exp["cu"],
-                  out=exp["out"], final_state=exp["state"])
+                  out=exp["out"], final_state=exp["state"], a_log=(n_v,),
+                  dt_bias=(n_v, q.shape[-1]))
+    if raw and (tensors.get("a_log") is None or tensors.get("dt_bias") is None):
+        raise ValueError("the raw-gate form needs both A_log and dt_bias")
     for name, t in tensors.items():
         if t is None:
             continue
@@ -160,23 +167,30 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
                   output_final_state: bool = True, out: Optional[torch.Tensor] = None,
                   final_state: Optional[torch.Tensor] = None,
                   workspace: Optional[torch.Tensor] = None,
-                  stage_events: Optional[Sequence] = None):
+                  stage_events: Optional[Sequence] = None,
+                  gate: Optional[tuple] = None):
     """KDA chunked forward on the current HIP device and stream.  Returns (out, final_state).
 
     q, k: bf16; v: bf16; g: fp32 natural-log decay, either v's shape (one gate per key
     channel) or beta's shape (one gate per token and value head, shared by every key channel:
     the library's scalar-gate option); beta: bf16 (logits when beta_sigmoid); initial_state:
-    fp32 [batch, n_v, d_v, d_k] or None; cu_seqlens: int32 [batch+1] (required for TND).  All
-    tensors, including caller-supplied out, final_state and workspace, must be contiguous and
-    on one GPU; every shape and dtype is checked before anything is launched.
+    fp32 [batch, n_v, d_v, d_k] or None; cu_seqlens: int32 [batch+1] (required for TND).
+    gate = (A_log fp32 [n_v], dt_bias fp32 [n_v, d_k], lower_bound): g is then the raw bf16
+    gate (v's shape), activated in the kernel (kda_chunk_fwd_raw_gate).  All tensors, including
+    caller-supplied out, final_state and workspace, must be contiguous and on one GPU; every
+    shape and dtype is checked before anything is launched.
     """
+    a_log, dt_bias, lower_bound = gate if gate is not None else (None, None, None)
     tensors = dict(q=q, k=k, v=v, g=g, beta=beta, initial_state=initial_state,
-                   cu_seqlens=cu_seqlens, out=out, final_state=final_state, workspace=workspace)
+                   cu_seqlens=cu_seqlens, out=out, final_state=final_state, workspace=workspace,
+                   a_log=a_log, dt_bias=dt_bias)
+    if gate is not None and (a_log is None or dt_bias is None):
+        raise ValueError("gate needs A_log and dt_bias tensors")
     batch, seq_len, n_qk, n_v, scalar_gate = check_tensors(tensors, layout)
     if scale is None:
         scale = q.shape[-1] ** -0.5
     shape = make_shape(layout, batch, seq_len, n_qk, n_v, scale, qk_l2norm, beta_sigmoid,
-                       q.shape[-1], v.shape[-1], scalar_gate)
+                       q.shape[-1], v.shape[-1], scalar_gate, raw_gate=gate is not None)
     lib = _lib.load()
     if out is None:
         out = torch.empty_like(v)
@@ -194,11 +208,17 @@ def kda_chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Te
             _ptr(initial_state), _ptr(cu_seqlens), _ptr(out), _ptr(final_state),
             _ptr(workspace), ctypes.c_size_t(workspace.numel() * workspace.element_size()),
             stream]
+    if gate is not None:
+        rg = KdaRawGate(a_log.data_ptr(), dt_bias.data_ptr(), float(lower_bound))
+        args[6:6] = [ctypes.byref(rg)]     # after beta
+        fn, fn_timed = lib.kda_chunk_fwd_raw_gate, lib.kda_chunk_fwd_raw_gate_timed
+    else:
+        fn, fn_timed = lib.kda_chunk_fwd, lib.kda_chunk_fwd_timed
     if stage_events is None:
-        st = lib.kda_chunk_fwd(*args)
+        st = fn(*args)
     else:
         evs = (ctypes.c_void_p * len(stage_events))(*[ctypes.c_void_p(e) for e in stage_events])
-        st = lib.kda_chunk_fwd_timed(*args, evs, len(stage_events))
+        st = fn_timed(*args, evs, len(stage_events))
     if st != KDA_OK:
         raise KdaError(st, "kda_chunk_fwd")
     return out, final_state
@@ -232,4 +252,5 @@ def kda_chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: 
 def chunk_fwd(inp, **kw):
     """Convenience: run on a workloads.Inputs bundle already on the GPU."""
     return kda_chunk_fwd(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
-                         inp.cu_seqlens, inp.layout, inp.qk_l2norm, inp.beta_sigmoid, **kw)
+                         inp.cu_seqlens, inp.layout, inp.qk_l2norm, inp.beta_sigmoid,
+                         gate=inp.gate_args, **kw)

@@ -36,6 +36,7 @@ class Workload:
     note: str = ""
     scalar_gate: bool = False   # one gate per (token, value head), shaped like beta
     d: int = D                  # head dim d_k = d_v (128 or 64)
+    raw_gate: bool = False      # raw bf16 gate with A_log, dt_bias, lower_bound = -5
 
 
 WORKLOADS = [
@@ -52,6 +53,10 @@ WORKLOADS = [
     Workload("gdn_prefill_s8k_n3", "BNSD", 1, 8192, 3, 3, "strong", True, 1005,
              note="the 8K prefill with one gate per (token, head) (the GDN form); "
                   "g = -5*sigmoid(N(0,1))", scalar_gate=True),
+    Workload("prefill_s8k_n3_raw_gate", "BNSD", 1, 8192, 3, 3, "raw", True, 1007,
+             note="the 8K prefill with the raw bf16 gate activated in the kernel, as in the "
+                  "FlashKDA README's quick start: g, A_log, dt_bias ~ N(0,1), lower_bound = -5",
+             raw_gate=True),
     Workload("prefill_s8k_n6_d64", "BNSD", 1, 8192, 6, 6, "strong", True, 1006,
              note="the 8K prefill at head dim 64 with six heads (the same q/k/v bytes as three "
                   "128-dim heads); g = -5*sigmoid(N(0,1)); state N(0,0.1^2)", d=64),
@@ -77,6 +82,20 @@ class Inputs:
     qk_l2norm: bool = True
     beta_sigmoid: bool = True
     meta: dict = field(default_factory=dict)
+    # raw-gate form: g is the raw bf16 gate (v's shape) and these activate it
+    a_log: Optional[torch.Tensor] = None      # fp32 [n_v]
+    dt_bias: Optional[torch.Tensor] = None    # fp32 [n_v, d_k]
+    lower_bound: float = -5.0
+
+    @property
+    def raw_gate(self) -> bool:
+        """g is the raw bf16 gate, activated with a_log, dt_bias and lower_bound."""
+        return self.a_log is not None
+
+    @property
+    def gate_args(self):
+        """(A_log, dt_bias, lower_bound) of the raw-gate form, or None."""
+        return (self.a_log, self.dt_bias, self.lower_bound) if self.raw_gate else None
 
     @property
     def scalar_gate(self) -> bool:
@@ -100,7 +119,8 @@ class Inputs:
         return Inputs(self.layout, self.batch, self.seq_len, self.n_qk, self.n_v,
                       mv(self.q), mv(self.k), mv(self.v), mv(self.g), mv(self.beta),
                       mv(self.initial_state), mv(self.cu_seqlens), self.scale,
-                      self.qk_l2norm, self.beta_sigmoid, dict(self.meta))
+                      self.qk_l2norm, self.beta_sigmoid, dict(self.meta), mv(self.a_log),
+                      mv(self.dt_bias), self.lower_bound)
 
 
 def _gate(kind: str, shape, gen: torch.Generator) -> torch.Tensor:
@@ -127,12 +147,15 @@ def _gate(kind: str, shape, gen: torch.Generator) -> torch.Tensor:
 def make_inputs(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, *,
                 g_kind: str = "strong", init: bool = False, seed: int = 0,
                 lengths: Optional[list] = None, valid_lengths: Optional[list] = None,
-                d: int = D, scalar_gate: bool = False) -> Inputs:
+                d: int = D, scalar_gate: bool = False, raw_gate: bool = False,
+                lower_bound: float = -5.0) -> Inputs:
     """Draw one seeded input set.
 
     layout "TND" packs ``lengths`` (a list of sequence lengths) into T tokens; for BNSD/BSND
     ``valid_lengths`` (optional) becomes a cu_seqlens prefix sum of per-row valid lengths.
     ``scalar_gate`` draws g with beta's shape (one gate per token and value head).
+    ``raw_gate`` draws, as the FlashKDA README's quick start does, a raw bf16 gate g ~ N(0,1)
+    (v's shape), A_log ~ N(0,1) [n_v] and dt_bias ~ N(0,1) [n_v, d] in fp32 (g_kind unused).
     """
     gen = torch.Generator().manual_seed(int(seed))
     if layout == "TND":
@@ -159,12 +182,22 @@ def make_inputs(layout: str, batch: int, seq_len: int, n_qk: int, n_v: int, *,
     q = torch.randn(qs, generator=gen).to(torch.bfloat16)
     k = torch.randn(qs, generator=gen).to(torch.bfloat16)
     v = torch.randn(vs, generator=gen).to(torch.bfloat16)
-    g = _gate(g_kind, bs if scalar_gate else vs, gen).to(torch.float32).contiguous()
+    if raw_gate:
+        if scalar_gate:
+            raise ValueError("the raw-gate form has one gate per key channel")
+        g = torch.randn(vs, generator=gen).to(torch.bfloat16)
+    else:
+        g = _gate(g_kind, bs if scalar_gate else vs, gen).to(torch.float32).contiguous()
     beta = torch.randn(bs, generator=gen).to(torch.bfloat16)
     st = None
     if init:
         st = (0.1 * torch.randn((batch, n_v, d, d), generator=gen)).to(torch.float32)
-    return Inputs(layout, batch, stored, n_qk, n_v, q, k, v, g, beta, st, cu)
+    inp = Inputs(layout, batch, stored, n_qk, n_v, q, k, v, g, beta, st, cu)
+    if raw_gate:
+        inp.a_log = torch.randn((n_v,), generator=gen).to(torch.float32)
+        inp.dt_bias = torch.randn((n_v, d), generator=gen).to(torch.float32)
+        inp.lower_bound = float(lower_bound)
+    return inp
 
 
 def _tnd_lengths(w: Workload, s: int) -> list:
@@ -178,7 +211,7 @@ def workload_shape(w) -> dict:
     if isinstance(w, str):
         w = BY_NAME[w]
     kw = dict(layout=w.layout, batch=w.batch, seq_len=w.seq_len, n_qk=w.n_qk, n_v=w.n_v,
-              d=w.d, scalar_gate=w.scalar_gate)
+              d=w.d, scalar_gate=w.scalar_gate, raw_gate=w.raw_gate)
     if w.layout == "TND":
         kw.update(seq_len=0, lengths=_tnd_lengths(w, w.seed))
     return kw
@@ -192,9 +225,11 @@ def workload_inputs(w, seed: Optional[int] = None) -> Inputs:
     if w.layout == "TND":
         lengths = _tnd_lengths(w, s)
         inp = make_inputs("TND", w.batch, 0, w.n_qk, w.n_v, g_kind=w.g_kind, init=w.init,
-                          seed=s, lengths=lengths, scalar_gate=w.scalar_gate, d=w.d)
+                          seed=s, lengths=lengths, scalar_gate=w.scalar_gate, d=w.d,
+                          raw_gate=w.raw_gate)
     else:
         inp = make_inputs(w.layout, w.batch, w.seq_len, w.n_qk, w.n_v, g_kind=w.g_kind,
-                          init=w.init, seed=s, scalar_gate=w.scalar_gate, d=w.d)
+                          init=w.init, seed=s, scalar_gate=w.scalar_gate, d=w.d,
+                          raw_gate=w.raw_gate)
     inp.meta["workload"] = w.name
     return inp

@@ -18,6 +18,10 @@
  *   the logistic sigmoid of the stored value.
  *   With ORACLE_SCALAR_GATE, g holds one value per (token, value head), laid out like beta,
  *   and exp(g_t) decays every key column alike: the scalar-gate (GDN) form of the same rule.
+ *   oracle_kda_fwd_raw_gate takes the raw bf16 gate instead and activates it per (token, key
+ *   channel j) of value head h as
+ *       g = lower_bound * sigmoid(exp(A_log[h]) * (g_raw + dt_bias[h, j]))
+ *   (a reading, see below), then runs the same recurrence.
  *
  * Sources (the pages this follows):
  *   - vLLM PR #43195 summary "KDA chunk prefill decay uses exp2", section 功能与动机: the
@@ -42,6 +46,15 @@
  *   - Scalar gate: one fp32 value per (token, value head), the natural-log decay of every key
  *     channel of that token (the GDN pages show the gate applied after the key product, which
  *     only a channel-independent gate permits).
+ *   - Raw-gate activation.  The FlashKDA README (sections 参数说明, 快速开始, 约束说明) takes
+ *     a raw bf16 gate shaped like v, A_log [Nv] (a per-value-head log time scale), dt_bias
+ *     [Nv, D] (a gate bias) and lower_bound in [-5, 0] (the gate's lower bound), and prints no
+ *     formula.  Read here as: bias the raw gate, scale it by the head's time scale
+ *     exp(A_log), squash it with the logistic sigmoid and scale by lower_bound, so every
+ *     activated gate lies in [lower_bound, 0] -- the form of the 8K-prefill workload's own
+ *     gate, -5 * sigmoid(N(0,1)).  The pins check this function's arithmetic (sigmoid(0) = 1/2,
+ *     saturation at lower_bound, the exp(A_log) scale per value head, the dt_bias index, the
+ *     range); whether it is FlashKDA's own formula cannot be checked from the pages.
  *
  * Parity pins for this function live in the CPU test suite: a hand-worked two-token example,
  * an independent brute-force evaluation of the chunk equations, and closed-form invariants.
@@ -110,17 +123,44 @@ int oracle_mutant_id(void) { return KDA_ORACLE_MUTANT; }
  * Work is split over (sequence, value head, block of 16 state rows), the independent chains
  * of the recurrence: every state row evolves on its own given q, k, g and beta.
  */
-int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_k, int d_v,
-                   double scale, unsigned flags,
-                   const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
-                   const uint16_t *beta, const float *initial_state, const int32_t *cu_seqlens,
-                   int dv_lo, int dv_hi, double *out, double *final_state) {
+/* The raw gate and its activation parameters (oracle_kda_fwd_raw_gate). */
+typedef struct {
+    const uint16_t *raw;      /* bf16 bits, v's shape and layout */
+    const float *a_log;       /* [n_v] */
+    const float *dt_bias;     /* [n_v, d_k] */
+    double lower_bound;
+} raw_gate;
+
+/* Activated gate of key channel j of value head h: lower_bound * sigmoid(exp(A_log[h]) *
+ * (g_raw + dt_bias[h, j])), in fp64. */
+static double activate_gate(const raw_gate *rg, size_t og, int h, int j, int d_k) {
+    const double x0 = bf16_bits_to_double(rg->raw[og + (size_t)j]) +
+                      (double)rg->dt_bias[(size_t)h * d_k + j];
+#if KDA_ORACLE_MUTANT == 14
+    const double x = (double)rg->a_log[h] * x0;        /* planted: time scale not exponentiated */
+#else
+    const double x = exp((double)rg->a_log[h]) * x0;
+#endif
+#if KDA_ORACLE_MUTANT == 15
+    return rg->lower_bound / (1.0 + exp(x));           /* planted: sigmoid of -x */
+#else
+    return rg->lower_bound / (1.0 + exp(-x));
+#endif
+}
+
+static int kda_fwd_core(int layout, int batch, int seq_len, int n_qk, int n_v, int d_k, int d_v,
+                        double scale, unsigned flags,
+                        const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                        const raw_gate *rg,
+                        const uint16_t *beta, const float *initial_state, const int32_t *cu_seqlens,
+                        int dv_lo, int dv_hi, double *out, double *final_state) {
     if (layout < ORACLE_BNSD || layout > ORACLE_TND) return -1;
     if (batch < 1 || n_qk < 1 || n_v < n_qk || n_v % n_qk != 0 || d_k < 1 || d_v < 1) return -2;
     if (layout == ORACLE_TND && cu_seqlens == NULL) return -3;
     if (layout != ORACLE_TND && seq_len < 1) return -4;
     if (dv_lo < 0 || dv_hi > d_v || dv_lo >= dv_hi) return -5;
-    if (!q || !k || !v || !g || !beta || !out) return -6;
+    if (!q || !k || !v || (!g && !rg) || !beta || !out) return -6;
+    if (rg && (!rg->raw || !rg->a_log || !rg->dt_bias || (flags & ORACLE_SCALAR_GATE))) return -7;
 
     const int group = n_v / n_qk;
     const int scalar_gate = (flags & ORACLE_SCALAR_GATE) != 0;
@@ -202,6 +242,10 @@ int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_
 #else
                     const size_t gi = scalar_gate ? ob : og + (size_t)j;
 #endif
+                    if (rg) {   /* raw gate: activated here */
+                        dec[j] = exp(activate_gate(rg, og, h, j, d_k));
+                        continue;
+                    }
 #if KDA_ORACLE_MUTANT == 11
                     /* planted: gate taken from the previous token */
                     size_t gip = gi;
@@ -222,7 +266,9 @@ int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_
                     const int dv = r0 + i;
 #if KDA_ORACLE_MUTANT == 3
                     /* planted: decay the value rows instead of the key columns */
-                    const double drow = (dv < d_k) ? exp((double)g[scalar_gate ? ob : og + dv]) : 1.0;
+                    const double drow = (dv >= d_k) ? 1.0
+                                        : rg ? exp(activate_gate(rg, og, h, dv, d_k))
+                                             : exp((double)g[scalar_gate ? ob : og + dv]);
                     for (int j = 0; j < d_k; ++j) Si[j] *= drow;
 #elif KDA_ORACLE_MUTANT == 1
                     /* planted: decay applied after the write (below) */
@@ -273,4 +319,27 @@ int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_
         free(dec);
     }
     return 0;
+}
+
+int oracle_kda_fwd(int layout, int batch, int seq_len, int n_qk, int n_v, int d_k, int d_v,
+                   double scale, unsigned flags,
+                   const uint16_t *q, const uint16_t *k, const uint16_t *v, const float *g,
+                   const uint16_t *beta, const float *initial_state, const int32_t *cu_seqlens,
+                   int dv_lo, int dv_hi, double *out, double *final_state) {
+    return kda_fwd_core(layout, batch, seq_len, n_qk, n_v, d_k, d_v, scale, flags, q, k, v, g,
+                        NULL, beta, initial_state, cu_seqlens, dv_lo, dv_hi, out, final_state);
+}
+
+/* The same with the raw bf16 gate g_raw (v's shape) activated per token and key channel (see
+ * the top of this file); scalar gate not allowed (returns -7). */
+int oracle_kda_fwd_raw_gate(int layout, int batch, int seq_len, int n_qk, int n_v, int d_k,
+                            int d_v, double scale, unsigned flags,
+                            const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            const uint16_t *g_raw, const float *a_log, const float *dt_bias,
+                            double lower_bound, const uint16_t *beta, const float *initial_state,
+                            const int32_t *cu_seqlens, int dv_lo, int dv_hi, double *out,
+                            double *final_state) {
+    const raw_gate rg = {g_raw, a_log, dt_bias, lower_bound};
+    return kda_fwd_core(layout, batch, seq_len, n_qk, n_v, d_k, d_v, scale, flags, q, k, v, NULL,
+                        &rg, beta, initial_state, cu_seqlens, dv_lo, dv_hi, out, final_state);
 }

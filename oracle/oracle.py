@@ -49,6 +49,10 @@ def load_oracle(path: str = LIB) -> ctypes.CDLL:
     lib.oracle_kda_fwd.argtypes = [I, I, I, I, I, I, I, ctypes.c_double, ctypes.c_uint,
                                    P, P, P, P, P, P, P, I, I, P, P]
     lib.oracle_kda_fwd.restype = I
+    lib.oracle_kda_fwd_raw_gate.argtypes = [I, I, I, I, I, I, I, ctypes.c_double, ctypes.c_uint,
+                                            P, P, P, P, P, P, ctypes.c_double, P, P, P, I, I,
+                                            P, P]
+    lib.oracle_kda_fwd_raw_gate.restype = I
     lib.oracle_num_threads.restype = I
     lib.oracle_mutant_id.restype = I
     _loaded[path] = lib
@@ -92,16 +96,18 @@ def _arr(x, dtype) -> np.ndarray:
 def kda_oracle(q, k, v, g, beta, scale: float, initial_state=None, cu_seqlens=None,
                layout: str = "BNSD", flags: int = QK_L2NORM | BETA_SIGMOID,
                dv_range: Optional[tuple] = None, want_final: bool = True,
-               lib_path: str = LIB):
+               lib_path: str = LIB, raw_gate: Optional[tuple] = None):
     """Run the oracle.  Returns (out, final_state) as float64 arrays.
 
     out has v's shape; entries that the recurrence does not define (rows past a sequence's
     valid length, value channels outside dv_range) are NaN.  final_state is
     [batch, n_v, d_v, d_k] (rows outside dv_range are NaN) or None when want_final is False.
+    raw_gate = (A_log [n_v] fp32, dt_bias [n_v, d_k] fp32, lower_bound): g is then the raw bf16
+    gate (v's shape), activated by the oracle.
     """
     lib = load_oracle(lib_path)
     qb, kb, vb, bb = _bits16(q), _bits16(k), _bits16(v), _bits16(beta)
-    ga = _arr(g, np.float32)
+    ga = _bits16(g) if raw_gate is not None else _arr(g, np.float32)
     lay = LAYOUTS[layout]
     if layout == "BNSD":
         batch, n_qk, seq_len, d_k = qb.shape
@@ -127,9 +133,20 @@ def kda_oracle(q, k, v, g, beta, scale: float, initial_state=None, cu_seqlens=No
     def ptr(a):
         return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
 
-    rc = lib.oracle_kda_fwd(lay, batch, seq_len, n_qk, n_v, d_k, d_v, float(scale),
-                            int(flags), ptr(qb), ptr(kb), ptr(vb), ptr(ga), ptr(bb),
-                            ptr(init), ptr(cu), lo, hi, ptr(out), ptr(fin))
+    if raw_gate is not None:
+        a_log = _arr(raw_gate[0], np.float32)
+        dt_bias = _arr(raw_gate[1], np.float32)
+        if a_log.shape != (n_v,) or dt_bias.shape != (n_v, d_k):
+            raise ValueError(f"A_log {a_log.shape} / dt_bias {dt_bias.shape}: expected "
+                             f"({n_v},) / ({n_v}, {d_k})")
+        rc = lib.oracle_kda_fwd_raw_gate(lay, batch, seq_len, n_qk, n_v, d_k, d_v, float(scale),
+                                         int(flags), ptr(qb), ptr(kb), ptr(vb), ptr(ga),
+                                         ptr(a_log), ptr(dt_bias), float(raw_gate[2]), ptr(bb),
+                                         ptr(init), ptr(cu), lo, hi, ptr(out), ptr(fin))
+    else:
+        rc = lib.oracle_kda_fwd(lay, batch, seq_len, n_qk, n_v, d_k, d_v, float(scale),
+                                int(flags), ptr(qb), ptr(kb), ptr(vb), ptr(ga), ptr(bb),
+                                ptr(init), ptr(cu), lo, hi, ptr(out), ptr(fin))
     if rc != 0:
         raise ValueError(f"oracle_kda_fwd rejected its arguments (code {rc})")
     return out, fin

@@ -120,20 +120,43 @@ VARIANT_CASES = [
 ]
 
 
+# The raw bf16 gate activated in the kernel (KDA_RAW_GATE; g, A_log, dt_bias ~ N(0,1) as in the
+# FlashKDA README's quick start): every layout, GQA, ragged tails, valid lengths, head dim 64,
+# the two-level scan, a lower bound other than -5, and the four-wave intra kernel (more than 512
+# chunk records) at both head dims.
+RAW_GATE_CASES = [
+    ("raw_bnsd_b2_tail", dict(layout="BNSD", batch=2, seq_len=200, n_qk=2, n_v=2, init=True,
+                              seed=91, raw_gate=True)),
+    ("raw_bsnd_gqa_valid", dict(layout="BSND", batch=2, seq_len=150, n_qk=1, n_v=4, init=False,
+                                seed=92, valid_lengths=[150, 61], raw_gate=True)),
+    ("raw_tnd_ragged", dict(layout="TND", batch=4, seq_len=0, n_qk=2, n_v=2, init=True, seed=93,
+                            lengths=[1, 64, 130, 17], raw_gate=True, lower_bound=-1.5)),
+    ("raw_two_level", dict(layout="BNSD", batch=1, seq_len=64 * 40 + 5, n_qk=1, n_v=1,
+                           init=True, seed=94, raw_gate=True)),
+    ("raw_d64_bsnd", dict(layout="BSND", batch=2, seq_len=100, n_qk=2, n_v=4, init=True,
+                          seed=95, raw_gate=True, d=64)),
+    ("raw_intra4w_d128", dict(layout="BNSD", batch=1, seq_len=4160, n_qk=8, n_v=8, init=True,
+                              seed=96, raw_gate=True)),
+    ("raw_intra4w_d64", dict(layout="TND", batch=2, seq_len=0, n_qk=4, n_v=8, init=False,
+                             seed=97, lengths=[2100, 2060], raw_gate=True, d=64)),
+]
+
+
 def case_shape(kw: dict, flags_on: bool = True):
     """The library shape of a make_inputs case (no tensors drawn)."""
     layout = kw["layout"]
     seq_len = sum(kw["lengths"]) if layout == "TND" else kw["seq_len"]
     d = kw.get("d", 128)
     return make_shape(layout, kw["batch"], seq_len, kw["n_qk"], kw["n_v"], d ** -0.5,
-                      flags_on, flags_on, d, d, kw.get("scalar_gate", False))
+                      flags_on, flags_on, d, d, kw.get("scalar_gate", False),
+                      raw_gate=kw.get("raw_gate", False))
 
 
 def all_case_shapes() -> list:
     """(name, shape) of every fixed GPU parity case, the named workloads and the sweep."""
     from test_gpu_sweep import CASES as SWEEP
     out = []
-    for group in (SMALL, SCALAR_GATE_CASES, D64_CASES, TWO_LEVEL, VARIANT_CASES):
+    for group in (SMALL, SCALAR_GATE_CASES, D64_CASES, TWO_LEVEL, VARIANT_CASES, RAW_GATE_CASES):
         out += [(name, case_shape(kw)) for name, kw in group]
     out += [(name, case_shape(kw, flags_on)) for name, kw, flags_on in SWEEP]
     for w in WORKLOADS:

@@ -19,6 +19,11 @@ when that library disagrees with the pages or with mathematics:
   scalar gate       one gate per (token, head): the gated delta rule in the form
                     S_t = a_t S_{t-1} (I - b_t k_t k_t^T) + b_t v_t k_t^T, and the per-channel
                     form with the gate repeated over the channels, in every layout
+  raw gate          the activation g = lower_bound * sigmoid(exp(A_log[h]) (g_raw + dt_bias[h]))
+                    at closed-form points: a raw gate cancelling dt_bias gives lower_bound / 2,
+                    a large one lower_bound, exp(A_log) = 3 or 1/2 per value head gives
+                    lower_bound * sigmoid(3) or sigmoid(1/2), lower_bound = 0 gives no decay;
+                    with beta = 0 every activated gate lies in [lower_bound, 0]
 
 The same functions run against compile-time planted mistakes in the oracle
 (tests/test_oracle_mutants.py) to show that each mistake is caught by at least one pin.
@@ -43,7 +48,8 @@ def _run(lib, inp: Inputs, **kw):
     flags = ((QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
              | (SCALAR_GATE if inp.scalar_gate else 0))
     return kda_oracle(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
-                      inp.cu_seqlens, inp.layout, flags, lib_path=lib, **kw)
+                      inp.cu_seqlens, inp.layout, flags, lib_path=lib, raw_gate=inp.gate_args,
+                      **kw)
 
 
 def _close(a, b, atol, what):
@@ -336,7 +342,81 @@ def pin_scalar_gate(lib):
         _close(sf, pf, 0.0, f"scalar vs repeated gate final_state ({layout})")
 
 
+def _raw_and_fp32(layout, seed, d=16, n=37, n_qk=1, n_v=2):
+    """A raw-gate input set and a copy with an fp32 gate in its place (same other tensors)."""
+    raw = make_inputs(layout, 1, n, n_qk, n_v, init=True, seed=seed, d=d, raw_gate=True)
+    f32 = make_inputs(layout, 1, n, n_qk, n_v, g_kind="zero", init=True, seed=seed, d=d)
+    f32.q, f32.k, f32.v, f32.beta, f32.initial_state = raw.q, raw.k, raw.v, raw.beta, \
+        raw.initial_state
+    return raw, f32
+
+
+def _per_head(x, layout, vals):
+    """A tensor shaped like v whose value head h holds vals[h] (broadcast over tokens and channels)."""
+    ax = 1 if layout == "BNSD" else 2
+    shape = [1] * x.dim()
+    shape[ax] = len(vals)
+    return torch.as_tensor(vals, dtype=torch.float32).reshape(shape).expand(x.shape)
+
+
+def pin_raw_gate(lib):
+    """The raw-gate activation at points where it has a closed form."""
+    lb = -5.0
+    for layout in ("BNSD", "BSND"):
+        # (a) g_raw = -dt_bias (dt_bias rounded to bf16 so that -dt_bias is a bf16 value):
+        #     sigmoid(0) = 1/2 for any A_log, so g = lb / 2 everywhere
+        raw, f32 = _raw_and_fp32(layout, 141)
+        raw.dt_bias = raw.dt_bias.to(torch.bfloat16).float()
+        db = raw.dt_bias[None, :, None, :] if layout == "BNSD" else raw.dt_bias[None, None]
+        raw.g = (-db).expand(raw.v.shape).contiguous().to(torch.bfloat16)
+        f32.g = torch.full(raw.v.shape, lb / 2, dtype=torch.float32)
+        for (o1, f1), (o2, f2) in [(_run(lib, raw), _run(lib, f32))]:
+            _close(o1, o2, 0.0, f"raw gate at -dt_bias out ({layout})")
+            _close(f1, f2, 0.0, f"raw gate at -dt_bias final_state ({layout})")
+        # (b) g_raw = 64, |dt_bias| < 6, A_log = 0: sigmoid(58..70) is 1 in fp64, so g = lb
+        raw, f32 = _raw_and_fp32(layout, 142)
+        raw.g = torch.full(raw.v.shape, 64.0).to(torch.bfloat16)
+        raw.dt_bias = raw.dt_bias.clamp(-5.9, 5.9)
+        raw.a_log = torch.zeros_like(raw.a_log)
+        f32.g = torch.full(raw.v.shape, lb, dtype=torch.float32)
+        (o1, f1), (o2, f2) = _run(lib, raw), _run(lib, f32)
+        _close(o1, o2, 0.0, f"saturated raw gate out ({layout})")
+        _close(f1, f2, 0.0, f"saturated raw gate final_state ({layout})")
+        # (c) g_raw = 1, dt_bias = 0, exp(A_log) = 3 for value head 0 and 1/2 for head 1 (both
+        #     read the one q/k head): g = lb sigmoid(3) and lb sigmoid(1/2); the fp32 copy holds
+        #     those constants rounded to fp32, and A_log is itself an fp32 value
+        raw, f32 = _raw_and_fp32(layout, 143)
+        raw.g = torch.ones(raw.v.shape).to(torch.bfloat16)
+        raw.dt_bias = torch.zeros_like(raw.dt_bias)
+        raw.a_log = torch.tensor([math.log(3.0), math.log(0.5)], dtype=torch.float32)
+        s3, sh = 1.0 / (1.0 + math.exp(-3.0)), 1.0 / (1.0 + math.exp(-0.5))
+        f32.g = _per_head(raw.v, layout, [lb * s3, lb * sh]).contiguous()
+        (o1, f1), (o2, f2) = _run(lib, raw), _run(lib, f32)
+        _close(o1, o2, 1e-5, f"time scale exp(A_log) out ({layout})")
+        _close(f1, f2, 1e-5, f"time scale exp(A_log) final_state ({layout})")
+    # (d) lower_bound = 0: no decay at all, whatever the raw gate
+    raw, f32 = _raw_and_fp32("BNSD", 144)
+    raw.lower_bound = 0.0
+    (o1, f1), (o2, f2) = _run(lib, raw), _run(lib, f32)
+    _close(o1, o2, 0.0, "lower_bound 0 out")
+    _close(f1, f2, 0.0, "lower_bound 0 final_state")
+    # (e) beta = 0: S_T = S_0 Diag(exp(sum_t g_t)), so log(S_T / S_0) per key channel is the sum
+    #     of the activated gates over the T tokens, which must lie in [T lb, 0] (and strictly
+    #     inside for finite raw gates)
+    raw, _ = _raw_and_fp32("BNSD", 145, n=23)
+    raw.g = (3.0 * raw.g.float()).to(torch.bfloat16)
+    raw.beta = torch.zeros_like(raw.beta)
+    raw.beta_sigmoid = False
+    raw.qk_l2norm = False
+    _, fin = _run(lib, raw)
+    s0 = raw.initial_state.double().numpy()
+    with np.errstate(invalid="ignore", divide="ignore"):
+        tot = np.log(fin / s0)   # [1, h, dv, dk], equal along dv
+    assert np.all(tot < 0) and np.all(tot > 23 * lb), "activated gates outside (lb, 0)"
+    assert np.allclose(tot, tot[:, :, :1, :], atol=1e-9), "decay must depend on the key channel only"
+
+
 ALL_PINS = [pin_hand_example, pin_bruteforce_chunked, pin_beta_zero, pin_plain_delta_rule,
             pin_perfect_retrieval, pin_linearity, pin_resume_split, pin_layout_invariance,
             pin_packing_invariance, pin_gqa, pin_fused_options, pin_valid_lengths,
-            pin_row_subset, pin_scalar_gate]
+            pin_row_subset, pin_scalar_gate, pin_raw_gate]

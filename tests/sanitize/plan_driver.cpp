@@ -23,6 +23,7 @@ void expect(bool ok, const char* what) {
 // Fake device addresses: every region of a call in its own 2^59-byte window, so none overlap
 // (shapes whose tensors could exceed a window skip the checks that need disjoint regions).
 const void* addr(int region) { return reinterpret_cast<const void*>(uintptr_t(region + 1) << 59); }
+static_assert(sizeof(uintptr_t) == 8, "12 windows of 2^59 bytes need 64-bit addresses");
 
 }  // namespace
 
@@ -36,7 +37,7 @@ int main() {
     const int dims[][2] = {{128, 128}, {64, 64}, {64, 128}, {32, 32}, {256, 256}, {0, 0}};
     const float scales[] = {0.088f, std::numeric_limits<float>::quiet_NaN(),
                             std::numeric_limits<float>::infinity()};
-    const uint32_t flag_sets[] = {0u, 1u, 3u, 7u, 8u, 0x80000000u};
+    const uint32_t flag_sets[] = {0u, 1u, 3u, 7u, 8u, 11u, 12u, 16u, 0x80000000u};
     long n_ok = 0, n_bad = 0, n_calls = 0;
     for (int lay : layouts)
         for (int b : batches)
@@ -60,10 +61,13 @@ int main() {
                                 const void* ptr[10];
                                 for (int i = 0; i < 10; ++i) ptr[i] = addr(i);
                                 const int32_t* cu = static_cast<const int32_t*>(ptr[6]);
+                                const kda_raw_gate gate{static_cast<const float*>(addr(10)),
+                                                        static_cast<const float*>(addr(11)), -5.f};
                                 auto call = [&](const void* const* x, size_t ws_bytes) {
                                     ++n_calls;
                                     return kda::check_call(
-                                        &sh, p, x[0], x[1], x[2], static_cast<const float*>(x[3]),
+                                        &sh, p, x[0], x[1], x[2], x[3],
+                                        (fl & KDA_RAW_GATE) ? &gate : nullptr,
                                         x[4], static_cast<const float*>(x[5]),
                                         static_cast<const int32_t*>(x[6]), x[7],
                                         static_cast<const float*>(x[8]), x[9], ws_bytes);

@@ -86,3 +86,18 @@ def test_tnd_cu_seqlens_checks():
 def test_unknown_layout():
     with pytest.raises(ValueError, match="layout"):
         check_tensors(tensors("BNSD"), "NSD")
+
+
+def test_raw_gate_tensor_checks():
+    base = tensors("BNSD", g=torch.zeros(B, NV, S, D, dtype=torch.bfloat16))
+    ok = dict(base, a_log=torch.zeros(NV), dt_bias=torch.zeros(NV, D))
+    with pytest.raises(ValueError, match="GPU"):
+        check_tensors(ok, "BNSD")
+    with pytest.raises(TypeError):   # the raw gate is bf16
+        check_tensors(dict(ok, g=torch.zeros(B, NV, S, D)), "BNSD")
+    with pytest.raises(ValueError, match="shape"):
+        check_tensors(dict(ok, dt_bias=torch.zeros(NV, D - 1)), "BNSD")
+    with pytest.raises(ValueError, match="shape"):
+        check_tensors(dict(ok, a_log=torch.zeros(NV + 1)), "BNSD")
+    with pytest.raises(ValueError, match="both"):
+        check_tensors(dict(base, a_log=torch.zeros(NV)), "BNSD")

@@ -118,7 +118,7 @@ def test_plan_query(lib):
     (dict(layout=7), 1), (dict(batch=0), 1), (dict(seq_len=0), 1), (dict(n_qk=0), 1),
     (dict(n_qk=4, n_v=2), 1), (dict(n_qk=3, n_v=4), 1), (dict(d_k=64), 2), (dict(d_v=256), 2),
     (dict(d_k=64, d_v=64), 0), (dict(d_k=32, d_v=32), 2), (dict(d_k=256, d_v=256), 2),
-    (dict(scale=float("nan")), 1), (dict(flags=8), 1), (dict(flags=16), 1),
+    (dict(scale=float("nan")), 1), (dict(flags=8), 0), (dict(flags=12), 2), (dict(flags=16), 1),
     (dict(flags=7), 0), (dict(flags=4), 0),
     (dict(layout=1, n_v=1 << 17), 2), (dict(layout=1, n_v=(1 << 17) - 2), 0),
 ])
@@ -192,3 +192,52 @@ def test_bench_record_model_matches_workspace(lib):
         assert st == 0
         body = 300 * nv * bench.record_bytes(d)
         assert body <= n < body + 8 * 256, (d, n, body)
+
+
+def call_raw(lib, shape, gate, timed_events=None, **ptrs):
+    base = dict(q=0x10000, k=0x20000, v=0x30000, g=0x40000, beta=0x50000, init=None, cu=None,
+                out=0x60000, fin=0x70000, ws=0x100000, ws_bytes=1 << 40)
+    base.update(ptrs)
+    P = ctypes.c_void_p
+    args = [ctypes.byref(shape), P(base["q"]), P(base["k"]), P(base["v"]), P(base["g"]),
+            P(base["beta"]), None if gate is None else ctypes.byref(gate), P(base["init"]),
+            P(base["cu"]), P(base["out"]), P(base["fin"]), P(base["ws"]),
+            ctypes.c_size_t(base["ws_bytes"]), P(None)]
+    if timed_events is not None:
+        return lib.kda_chunk_fwd_raw_gate_timed(*args, timed_events, 10)
+    return lib.kda_chunk_fwd_raw_gate(*args)
+
+
+@pytest.mark.parametrize("what, gate_kw, flags, ptrs, code", [
+    ("no KDA_RAW_GATE flag", {}, 3, {}, 1),
+    ("NULL gate", None, 11, {}, 1),
+    ("NULL A_log", dict(a_log=None), 11, {}, 1),
+    ("NULL dt_bias", dict(dt_bias=None), 11, {}, 1),
+    ("misaligned dt_bias", dict(dt_bias=0x90004), 11, {}, 1),
+    ("lower_bound below -5", dict(lower_bound=-5.5), 11, {}, 1),
+    ("lower_bound above 0", dict(lower_bound=0.25), 11, {}, 1),
+    ("lower_bound NaN", dict(lower_bound=float("nan")), 11, {}, 1),
+    ("with the scalar gate", {}, 15, {}, 2),
+    ("out over dt_bias", {}, 11, dict(out=0x90000 - 256), 1),
+])
+def test_raw_gate_rejections(lib, what, gate_kw, flags, ptrs, code):
+    """The raw-gate entry point checks its activation parameters on the host, before any launch
+    (so the fake pointers are never dereferenced)."""
+    shape = make_shape("BNSD", 1, 100, 1, 2, 0.1)
+    shape.flags = flags
+    gate = None
+    if gate_kw is not None:
+        kw = dict(a_log=0x80000, dt_bias=0x90000, lower_bound=-5.0)
+        kw.update(gate_kw)
+        gate = _lib.KdaRawGate(kw["a_log"], kw["dt_bias"], kw["lower_bound"])
+    assert call_raw(lib, shape, gate, **ptrs) == code, what
+    if gate is not None:
+        evs = (ctypes.c_void_p * 10)()
+        assert call_raw(lib, shape, gate, timed_events=evs, **ptrs) == code, what
+
+
+def test_raw_gate_flag_refused_by_plain_entry(lib):
+    shape = make_shape("BNSD", 1, 100, 1, 2, 0.1, raw_gate=True)
+    assert call(lib, shape) == 1
+    assert ws(lib, shape)[0] == 0   # the workspace query accepts it (same size)
+    assert ws(lib, shape)[1] == ws(lib, make_shape("BNSD", 1, 100, 1, 2, 0.1))[1]

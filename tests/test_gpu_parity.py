@@ -21,7 +21,7 @@ from kimi_delta_attention_chunk_amd import kda_chunk_fwd, chunk_fwd
 from kimi_delta_attention_chunk_amd.workloads import (Inputs, make_inputs, workload_inputs,
                                                       WORKLOADS)
 from gpu_cases import (SMALL, SCALAR_GATE_CASES, D64_CASES, TWO_LEVEL, VARIANT_CASES,
-                       case_shape)
+                       RAW_GATE_CASES, case_shape)
 from kimi_delta_attention_chunk_amd.ops import kda_chunk_fwd_plan_kernels
 
 pytestmark = pytest.mark.gpu
@@ -41,7 +41,8 @@ def oracle_of(inp: Inputs, dv_range=None):
     flags = ((QK_L2NORM if inp.qk_l2norm else 0) | (BETA_SIGMOID if inp.beta_sigmoid else 0)
              | (SCALAR_GATE if inp.scalar_gate else 0))
     return kda_oracle(inp.q, inp.k, inp.v, inp.g, inp.beta, inp.scale, inp.initial_state,
-                      inp.cu_seqlens, inp.layout, flags, dv_range=dv_range)
+                      inp.cu_seqlens, inp.layout, flags, dv_range=dv_range,
+                      raw_gate=inp.gate_args)
 
 
 def run_gpu(inp: Inputs, **kw):
@@ -126,6 +127,13 @@ def test_flags_off_prenormalised_inputs():
 def test_kernel_variants(name, kw):
     kernels = kda_chunk_fwd_plan_kernels(case_shape(kw))
     compare(make_inputs(**kw), f"{name} {kernels}")
+
+
+@pytest.mark.parametrize("name,kw", RAW_GATE_CASES, ids=[s[0] for s in RAW_GATE_CASES])
+def test_raw_gate(name, kw):
+    inp = make_inputs(**kw)
+    assert inp.raw_gate and inp.g.dtype == torch.bfloat16
+    compare(inp, f"{name} {kda_chunk_fwd_plan_kernels(case_shape(kw))}")
 
 
 HEAD_AXIS = {"BNSD": 1, "BSND": 2, "TND": 1}

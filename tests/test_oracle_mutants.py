@@ -1,6 +1,6 @@
 """Every planted mistake in the oracle must be caught by at least one pin.
 
-The oracle source carries compile-time mutants (KDA_ORACLE_MUTANT=1..13): decay after the
+The oracle source carries compile-time mutants (KDA_ORACLE_MUTANT=1..15): decay after the
 write, read before the write, decay of the value rows, a flipped delta sign, a wrong GQA head
 map, a dropped scale, a skipped sigmoid, a skipped L2 norm, a transposed initial state, beta on
 v only, the gate of the previous token, base-2 instead of natural exp, and a scalar gate read
@@ -14,7 +14,7 @@ import pytest
 from oracle import build_oracle
 import oracle_pins
 
-MUTANTS = list(range(1, 14))
+MUTANTS = list(range(1, 16))
 
 
 @pytest.mark.parametrize("mutant", MUTANTS)
