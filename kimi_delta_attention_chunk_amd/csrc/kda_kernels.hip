@@ -722,37 +722,72 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         for (int i = 0; i < 16; ++i) ab[i * BLK_LD + lane] = x[i];
     }
     __syncthreads();
-    // Below the diagonal, wave w < 4 fills block column w, top to bottom:
-    //     Ainv[I2][w] = -Ainv[I2][I2] * sum_{K=w}^{I2-1} T[I2][K] Ainv[K][w]
-    // (block forward substitution of (I + T) X = I); every block it reads in column w is its
-    // own earlier result.  Products on fp32 MFMA.
-    if (w < 4) {
-        float* sP = sTmp + w * BLK_SZ;
+    // Below the diagonal.  With D' the block diagonal of I + T (inverses Dinv_I above) and L its
+    // blocks below the diagonal, I + T = D' (I + N) with N = D'^-1 L, and N^4 = 0 (four block
+    // rows), so  (I + T)^-1 = (I - N + N^2 - N^3) D'^-1.  Evaluated in four levels of
+    // independent 16 x 16 products on the fp32 MFMA, each level spread over the waves:
+    //   1: N_IJ = Dinv_I T_IJ (in place of T_IJ, which only its own wave reads);
+    //   2: Ainv_{J+1,J} = -N_{J+1,J} Dinv_J;  M_20 = N_21 N_10 - N_20;  M_31 = N_32 N_21 - N_31;
+    //      Z_30 = N_31 N_10 - N_30;
+    //   3: Ainv_20 = M_20 Dinv_0;  Ainv_31 = M_31 Dinv_1;  M_30 = Z_30 - N_32 M_20;
+    //   4: Ainv_30 = M_30 Dinv_0.
+    // (Block forward substitution down a block column is a chain of nine such products.)
+    {
+        constexpr int NW = 4 * HV;   // waves of the workgroup
         const int lr = lane & 15, lk = lane >> 4;
-        for (int I2 = w + 1; I2 < 4; ++I2) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int K = w; K < I2; ++K) {
-                const float* tb = sT + blk(I2, K) * BLK_SZ;
-                const float* ab = sAi + blk(K, w) * BLK_SZ;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(tb[lr * BLK_LD + 4 * ks + lk],
-                                                               ab[(4 * ks + lk) * BLK_LD + lr],
-                                                               acc, 0, 0, 0);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sP[(4 * lk + i) * BLK_LD + lr] = acc[i];
-            const float* dg = sAi + blk(I2, I2) * BLK_SZ;
-            f32x4 acc2 = {0.f, 0.f, 0.f, 0.f};
+        float* const sM20 = sTmp;
+        float* const sM31 = sTmp + BLK_SZ;
+        float* const sZ30 = sTmp + 2 * BLK_SZ;   // Z_30, then M_30
+        auto tb = [&](int I2, int J2) { return sT + blk(I2, J2) * BLK_SZ; };
+        auto ab = [&](int I2, int J2) { return sAi + blk(I2, J2) * BLK_SZ; };
+        // acc + X Y for 16 x 16 blocks of row stride BLK_LD; lane (lk, lr) holds rows 4 lk + i,
+        // column lr of the result
+        auto mm = [&](const float* X, const float* Y, f32x4 acc) {
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks)
-                acc2 = __builtin_amdgcn_mfma_f32_16x16x4f32(dg[lr * BLK_LD + 4 * ks + lk],
-                                                            sP[(4 * ks + lk) * BLK_LD + lr],
-                                                            acc2, 0, 0, 0);
-            float* ob = sAi + blk(I2, w) * BLK_SZ;
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[lr * BLK_LD + 4 * ks + lk],
+                                                           Y[(4 * ks + lk) * BLK_LD + lr], acc,
+                                                           0, 0, 0);
+            return acc;
+        };
+        auto put = [&](float* dst, f32x4 v) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) ob[(4 * lk + i) * BLK_LD + lr] = -acc2[i];
+            for (int i = 0; i < 4; ++i) dst[(4 * lk + i) * BLK_LD + lr] = v[i];
+        };
+        auto get = [&](const float* src) {
+            f32x4 v;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] = src[(4 * lk + i) * BLK_LD + lr];
+            return v;
+        };
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        for (int t = w; t < 6; t += NW) {   // level 1, blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+            const int I2 = t < 1 ? 1 : (t < 3 ? 2 : 3);
+            const int J2 = t - (I2 * (I2 - 1)) / 2;
+            put(tb(I2, J2), mm(ab(I2, I2), tb(I2, J2), zero));
         }
+        __syncthreads();
+        for (int t = w; t < 6; t += NW) {   // level 2
+            if (t < 3)
+                put(ab(t + 1, t), -mm(tb(t + 1, t), ab(t, t), zero));
+            else if (t == 3)
+                put(sM20, mm(tb(2, 1), tb(1, 0), -get(tb(2, 0))));
+            else if (t == 4)
+                put(sM31, mm(tb(3, 2), tb(2, 1), -get(tb(3, 1))));
+            else
+                put(sZ30, mm(tb(3, 1), tb(1, 0), -get(tb(3, 0))));
+        }
+        __syncthreads();
+        for (int t = w; t < 3; t += NW) {   // level 3
+            if (t == 0)
+                put(ab(2, 0), mm(sM20, ab(0, 0), zero));
+            else if (t == 1)
+                put(ab(3, 1), mm(sM31, ab(1, 1), zero));
+            else
+                put(sZ30, get(sZ30) - mm(tb(3, 2), sM20, zero));   // read before write, one wave
+        }
+        __syncthreads();
+        if (w == 0) put(ab(3, 0), mm(sZ30, ab(0, 0), zero));   // level 4
     }
     __syncthreads();   // Ainv ready; T and the staging tiles dead
 
@@ -1450,8 +1485,11 @@ __device__ __forceinline__ void zero_rows_past_len(const Params& p, int len, siz
 // of the sequence from the initial state.  The one-tile form keeps under 256 registers so that
 // two workgroups share a compute unit.  PFW: at most one workgroup per compute unit, with the
 // record prefetch wave.
+// The register budget of two workgroups per compute unit (at most 256 VGPRs a lane) for every
+// form: with one, the compiler spreads the two- and four-tile forms over VGPRs and AGPRs and
+// copies the accumulators back and forth inside the chunk loop.
 template <int NT, int D, bool PFW>
-__global__ __launch_bounds__(PFW ? kPfThreads : kThreads, (NT == 1 && !PFW) ? 2 : 1)
+__global__ __launch_bounds__(PFW ? kPfThreads : kThreads, 2)
 void kda_scan_kernel(Params p) {
     constexpr int BV = 16 * NT;
     constexpr int MW = HD<D>::MW;
@@ -1665,9 +1703,9 @@ __device__ __forceinline__ void complete_record(const Params& p, int64_t rec, in
 // S_in(seg_p-1) P_last + N_last, runs in the completion pass beside the outputs, so that the
 // outputs do not wait for it.  No step's operands depend on an earlier step, so they load two
 // steps ahead, in three register sets (a load past the end rereads the last step's matrices,
-// never used).  Few workgroups: the register budget of one per compute unit.
+// never used).  The register budget of two workgroups per compute unit (no AGPR copies).
 template <int D>
-__global__ __launch_bounds__(kThreads, 1) void kda_combine_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 2) void kda_combine_kernel(Params p) {
     constexpr int MW = HD<D>::MW, KB = HD<D>::KB, TILES = HD<D>::TILES;
     __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
