@@ -10,8 +10,18 @@ Timing: W untimed warm-up steps, then K steps bracketed by torch.cuda.synchroniz
 region: `value`, `ms_per_step`); the input set rotates over enough copies that the step's
 inputs exceed the 256 MB last-level cache, so the bytes really come from HBM.  The same K steps
 then run again through kda_chunk_fwd_timed, whose kernels' own dispatches record HIP events at
-each kernel's start and end on the launch stream: those give the per-kernel durations of the
-roofline (they agree with rocprofv3's kernel trace).  The CPU baseline times the fp64 oracle on the host cores on the full workload.
+each kernel's start and end on the launch stream: those give the per-kernel durations
+(`stages_ms`; they agree with rocprofv3's kernel trace).  A third pass puts an event pair
+around every call: `per_call_ms` (median, min, mean).
+
+Roofline: `roofline` is the dominant kernel's: the call's algorithmic bytes (1,538 B per
+token-head at Nqk = Nv plus the states; `path_bytes`) over that kernel's average duration,
+against the 8 TB/s HBM peak; `traffic` is that kernel's HBM bytes per launch from the committed
+rocprofv3 counter summary (profiles/), null when the kernel sources changed since; and
+`traffic_ratio` the counter bytes of all launched kernels over the algorithmic bytes.
+`path_roofline` uses the whole step time.  `copy_ceiling` times a plain device copy of the
+algorithmic bytes (the practical bandwidth of a transfer that size).  The CPU baseline times the
+fp64 oracle on the host cores on the full workload.
 """
 from __future__ import annotations
 

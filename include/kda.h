@@ -13,15 +13,17 @@
  * with 16-token sub-blocks, log2-space gates and bf16 MFMA, exactly up to rounding.
  *
  * Interface model: the FlashKDA README (sections 参数说明, 返回值说明, 约束说明) -- q, k, v,
- * g, beta, scale, initial_state, layout, cu_seqlens in; out and a new final_state back.  The
- * raw-gate activation (A_log, dt_bias, lower_bound) and the Ascend scheduling metadata of that
- * interface are not part of this library: g is the already activated natural-log decay.
+ * g, beta, scale, initial_state, layout, cu_seqlens in; out and a new final_state back.  g is
+ * the activated natural-log decay for kda_chunk_fwd; kda_chunk_fwd_raw_gate takes the raw gate
+ * with A_log, dt_bias and lower_bound and activates it in the kernel.  The Ascend scheduling
+ * metadata of that interface has no counterpart here (the plan follows from the shape).
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer on the current HIP device, 16-byte aligned and
  *     contiguous in the stated layout.  The caller owns all buffers and the stream; the library
  *     allocates no device memory and keeps no state between calls (it is reentrant; concurrent
- *     calls need distinct workspaces).
+ *     calls need distinct workspaces).  The one exception is kda_chunk_fwd_noalloc, whose
+ *     workspace is a device array the library holds per GPU (see there).
  *   - Work is enqueued on `stream`; the call returns right after enqueueing.  The host never
  *     reads device data.
  *   - Arguments are validated on the host, from shapes and pointers only, before any launch.
@@ -29,9 +31,12 @@
  *   - Not checked (preconditions, as in the FlashKDA README, section 约束说明): cu_seqlens
  *     starts at 0, is strictly increasing and ends at seq_len (TND); with BNSD/BSND each valid
  *     length lies in [1, seq_len]; -5 <= g <= 0; all tensors live on one device.  The decayed
- *     keys (at most |k|), the values transformed inside a chunk (about |v|) and the innovation
- *     v - S k of the state update are held in fp16: they stay far below the fp16 limit of 65504
- *     with L2-normalised keys and values of ordinary size (larger magnitudes overflow to inf).
+ *     keys (at most |k|), the values transformed inside a chunk (about |v|), the innovation
+ *     v - S k of the state update and, in the two-level scan, the segment entry state are held
+ *     in fp16 (limit 65504; larger magnitudes overflow to inf).  Tested range: L2-normalised
+ *     keys with v and the initial state scaled by up to 2048 (|v| up to about 1e4), every output
+ *     and final state within the tolerance in units of that scale, one- and two-level scans,
+ *     head dims 128 and 64.
  */
 #ifndef KDA_H_
 #define KDA_H_
