@@ -324,3 +324,23 @@ def test_null_states(seq_len, init):
     assert fin is None
     ro, _ = oracle_of(inp)
     assert_parity(out, ro, "no final_state out")
+
+
+@pytest.mark.parametrize("raw", [False, True], ids=["activated_gate", "raw_gate"])
+def test_timed_entry_points_bitwise(raw):
+    """kda_chunk_fwd_timed and kda_chunk_fwd_raw_gate_timed run the same kernels as the untimed
+    calls (their dispatches only record HIP events): bitwise equal outputs, and every event of a
+    launched stage completes with a non-negative duration."""
+    from kimi_delta_attention_chunk_amd import kda_num_stages
+    inp = make_inputs("BNSD", 1, 64 * 40 + 9, 1, 2, g_kind="strong", init=True, seed=29,
+                      raw_gate=raw).to("cuda")
+    o1, f1 = chunk_fwd(inp)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * kda_num_stages())]
+    for e in evs:
+        e.record()
+    torch.cuda.synchronize()
+    o2, f2 = chunk_fwd(inp, stage_events=[e.cuda_event for e in evs])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    for s in range(kda_num_stages()):
+        assert evs[2 * s].elapsed_time(evs[2 * s + 1]) >= 0.0
