@@ -1241,6 +1241,170 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     }
 }
 
+// Eight-wave chunk step (the segment pass at head dim 128, one 16-row Dv tile).  With four
+// waves every SIMD holds one wave of the walk, and nothing covers its LDS and memory waits.
+// Here waves 0..3 take token tile w & 3 of X = W S^T and its V_new, waves 4..7 the same token
+// tile of Y^T = S Q'^T and its outputs, and in the state update each wave takes one 16-row Dk
+// tile: the workgroup loads exactly what the four-wave step loads (each operand once), with two
+// waves on every SIMD.  Measured at the 8K prefill: segment pass 24.5-24.9 -> 23.3-24.0 us.
+template <int D>
+struct Frags8 {
+    bf16x8 a[HD<D>::KB];   // W (X waves) or Q' (Y waves), token tile w & 3
+    f16x8 kh[2];           // K_dec^T of Dk tile w, token steps 0 and 1
+    f32x4 gm;              // gamma_last of the lane's rows of Dk tile w
+    f16x4 u;               // U (X waves), token tile w & 3, the Dv tile
+    bf16x4 o;              // O_intra (Y waves), the same
+};
+
+// Every operand of one chunk for a wave of the eight-wave walk: W (X waves) or Q' (Y waves) of
+// its token tile, U (X) or O_intra (Y) of that tile and the Dv tile, and the K_dec and gamma
+// of its Dk tile.
+template <int ROLE, bool WITH_U, int OUT, int D>
+__device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w, int lane,
+                                            int dv_tile, Frags8<D>& f) {
+    constexpr int KB = HD<D>::KB;
+    const int tt = w & 3;
+    const size_t rb = size_t(rec) * (64 * D);
+    const int uo = ((dv_tile * 4 + tt) * 64 + lane) * 4;
+    const __bf16* src = (ROLE == 0 ? p.Wf : p.Qf) + rb;
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+        f.a[kb] = *reinterpret_cast<const bf16x8*>(src + ((tt * KB + kb) * 64 + lane) * 8);
+    if constexpr (ROLE == 0 && WITH_U) f.u = *reinterpret_cast<const f16x4*>(p.Uf + rb + uo);
+    if constexpr (ROLE == 1 && (OUT == OUT_FINAL || OUT == OUT_O0))
+        f.o = *reinterpret_cast<const bf16x4*>(p.Of + rb + uo);
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        f.kh[s] = *reinterpret_cast<const f16x8*>(p.Kf + rb + ((w * 2 + s) * 64 + lane) * 8);
+    f.gm = *reinterpret_cast<const f32x4*>(p.Gf + size_t(rec) * D + 16 * w + 4 * (lane >> 4));
+}
+
+// One chunk for the workgroup's Dv tile with eight waves (see Frags8); ROLE 0 is an X wave
+// (waves 0..3), ROLE 1 a Y wave (4..7), each running its own branch-free copy of the walk.
+// Outputs are stored at device scope (the segment pass).
+template <int ROLE, bool WITH_U, int OUT, int D>
+__device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur, f32x4& S,
+                                           const ScanLds& L, int w, int jc, int len, size_t ob,
+                                           size_t os, int dv_tile, int64_t rec) {
+    constexpr int KB = HD<D>::KB, SLD = HD<D>::SLD;
+    static_assert(D / 16 == 8, "one 16-row Dk tile per wave");
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const int n16 = lane & 15;
+    const int tt = w & 3;
+
+    // X = W (S_hi + S_lo)^T, or Y^T = S_hi Q'^T (with S_lo too for R), token tile tt
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+        const int off = n16 * SLD + 32 * kb + 8 * q4;
+        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
+        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
+        if constexpr (ROLE == 0) {
+            acc = mfma(cur.a[kb], sh, acc);
+            acc = mfma(cur.a[kb], sl, acc);
+        } else {
+            acc = mfma(sh, cur.a[kb], acc);
+            if constexpr (OUT == OUT_R) acc = mfma(sl, cur.a[kb], acc);
+        }
+    }
+    if constexpr (ROLE == 0) {   // V_new as an fp16 pair, the operand of the fp16 update product
+        f16x4 vh, vl;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float x = (WITH_U ? (float)cur.u[r] : 0.f) - acc[r];
+            vh[r] = (_Float16)x;
+            vl[r] = (_Float16)(x - (float)vh[r]);
+        }
+        const int off = n16 * VN_LD + 16 * tt + 4 * q4;
+        *reinterpret_cast<f16x4*>(L.vh + off) = vh;
+        *reinterpret_cast<f16x4*>(L.vl + off) = vl;
+    } else {
+        const int tok = jc * kChunk + 16 * tt + n16;   // output token of this lane
+        bf16x4 yb;
+        if constexpr (OUT == OUT_FINAL) {
+            if (tok < len) {
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(acc[r] + (float)cur.o[r]);
+                const DevStore dst(p.out + ob + size_t(jc) * kChunk * os, unsigned(kChunk * os * 2));
+                dst.put(unsigned((tok - jc * kChunk) * os + 16 * dv_tile + 4 * q4) * 2, yb);
+            }
+        } else if constexpr (OUT == OUT_O0) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(acc[r] + (float)cur.o[r]);
+            DevStore(p.O0 + size_t(rec) * (64 * D), 64 * D * 2)
+                .put(unsigned((dv_tile * 4 + tt) * 64 + lane) * 8, yb);
+        } else if constexpr (OUT == OUT_R) {   // R in the completion pass's B-operand order
+#pragma unroll
+            for (int r = 0; r < 4; ++r) yb[r] = (__bf16)acc[r];
+            const int lb = (2 * (dv_tile & 1) + (q4 >> 1)) * 16 + n16;
+            DevStore(p.Rf + size_t(rec) * (64 * D), 64 * D * 2)
+                .put(unsigned(((tt * KB + (dv_tile >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1)) * 2, yb);
+        }
+    }
+    lds_barrier();
+
+    // S^T <- gamma * S^T + K_dec^T V_new for Dk tile w, on the fp16 MFMA
+    {
+        f16x8 vh[2], vl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int off = n16 * VN_LD + 32 * s + 8 * q4;
+            vh[s] = *reinterpret_cast<const f16x8*>(L.vh + off);
+            vl[s] = *reinterpret_cast<const f16x8*>(L.vl + off);
+        }
+        f32x4 a = S * cur.gm;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            a = mfma(cur.kh[s], vh[s], a);
+            a = mfma(cur.kh[s], vl[s], a);
+        }
+        S = a;
+        put_state<D>(L.sh, L.sl, n16, 16 * w + 4 * q4, a);
+    }
+    lds_barrier();
+}
+
+// Chunks [cb, ce) with the eight-wave step (as run_chunks, state in S and in LDS on entry);
+// waves 0..3 run the X copy and waves 4..7 the Y copy of the walk, with the same barriers.
+template <int ROLE, bool WITH_U, int OUT, int D>
+__device__ __forceinline__ void run_walk8(const Params& p, f32x4& S, const ScanLds& L, int w,
+                                          int64_t rec0, int cb, int ce, int len, size_t ob,
+                                          size_t os, int dv_tile) {
+    const int lane = threadIdx.x & 63;
+    const int last = ce - 1;
+    // every load of the next chunk is issued at the start of the step before it (the step's
+    // own operands arrived during the previous step).  Measured: as fast as issuing them two
+    // chunks ahead from a third operand set, and faster than loads split around the products
+    // (with which the compiler folded the two-step loop into one and drained every load,
+    // K_dec's included, at the top of each step)
+    Frags8<D> fa, fb;
+    load_chunk8<ROLE, WITH_U, OUT, D>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile, fa);
+    for (int jc = cb; jc < ce; jc += 2) {
+        const int c1 = jc + 1 < last ? jc + 1 : last;
+        load_chunk8<ROLE, WITH_U, OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile, fb);
+        scan_step8<ROLE, WITH_U, OUT, D>(p, fa, S, L, w, jc, len, ob, os, dv_tile,
+                                         rec0 + int64_t(jc) * p.n_v);
+        if (jc + 1 >= ce) break;
+        const int c2 = jc + 2 < last ? jc + 2 : last;
+        load_chunk8<ROLE, WITH_U, OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile, fa);
+        scan_step8<ROLE, WITH_U, OUT, D>(p, fb, S, L, w, jc + 1, len, ob, os, dv_tile,
+                                         rec0 + int64_t(jc + 1) * p.n_v);
+    }
+}
+
+template <bool WITH_U, int OUT, int D>
+__device__ __forceinline__ void run_chunks8(const Params& p, f32x4& S, const ScanLds& L,
+                                            int64_t rec0, int cb, int ce, int len, size_t ob,
+                                            size_t os, int dv_tile) {
+    if (cb >= ce) return;
+    const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
+    if (w < 4)
+        run_walk8<0, WITH_U, OUT, D>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
+    else
+        run_walk8<1, WITH_U, OUT, D>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
+}
+
 // Sequences of different lengths (cu_seqlens given) are walked longest first: workgroup rank r
 // takes the sequence of rank r in the order of decreasing valid length (ties by index), so the
 // long walks start first and the short ones fill the end of the grid (longest processing time
@@ -1574,10 +1738,15 @@ void kda_scan_kernel(Params p) {
 // from S = 0 (from the initial state for s = 0) with U: the outputs of segment 0 are final,
 // those of later segments go to O0, and the end state is N_s.  The identity walk (D/16
 // workgroups from 16 identity rows each, without U) writes the columns of R = Q' P^T as its
-// outputs and ends with the rows of P_s.
+// outputs and ends with the rows of P_s.  At head dim 128 the walk runs on eight waves (the
+// eight-wave step, scan_step8: two waves on every SIMD, one 16-row Dk tile of the state each).
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
-    constexpr int MW = HD<D>::MW, TILES = HD<D>::TILES;
+constexpr int seg_waves() { return D == 128 ? 8 : 4; }
+
+template <int D>
+__global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params p) {
+    constexpr int NW = seg_waves<D>();
+    constexpr int MW = D / (16 * NW), TILES = HD<D>::TILES;   // Dk tiles per wave
     constexpr bool SEG_SPLIT = D == 128;   // split loads: faster at D = 128, slower at 64 (measured)
     __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
@@ -1652,8 +1821,11 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
 
     const size_t m = (size_t(bh) * p.seg_p + seg) * D * D;
     if (is_p) {
-        run_chunks<1, false, OUT_R, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len, ob, os,
-                                                              tile);
+        if constexpr (NW == 8)
+            run_chunks8<false, OUT_R, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
+        else
+            run_chunks<1, false, OUT_R, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len, ob,
+                                                                  os, tile);
         // rows 16 tile .. of P_s, in fp16, into the combine's A fragments of P_s^T: element
         // P_s[16 tile + n16][16 M + 4 q4 + i] is lane (2 (tile & 1) + (n16 >> 3), 4 q4 + i),
         // entry n16 & 7, of fragment (M, tile >> 1)
@@ -1668,12 +1840,19 @@ __global__ __launch_bounds__(kThreads, 2) void kda_seg_kernel(Params p) {
                 pt[at] = (_Float16)S[mt][0][i];
             }
     } else {
-        if (seg == 0)
-            run_chunks<1, true, OUT_FINAL, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len,
-                                                                     ob, os, tile);
-        else
-            run_chunks<1, true, OUT_O0, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len, ob,
-                                                                  os, tile);
+        if constexpr (NW == 8) {
+            if (seg == 0)
+                run_chunks8<true, OUT_FINAL, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
+            else
+                run_chunks8<true, OUT_O0, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
+        } else {
+            if (seg == 0)
+                run_chunks<1, true, OUT_FINAL, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce,
+                                                                         len, ob, os, tile);
+            else
+                run_chunks<1, true, OUT_O0, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len,
+                                                                      ob, os, tile);
+        }
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
             *reinterpret_cast<f32x4*>(p.Nst + m + ((tile * TILES + MW * w + mt) * 64 + lane) * 4) =
@@ -1969,7 +2148,7 @@ const Variant kVariants[] = {
     KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 2,128,2),
     KDA_VARIANT(kda_intra_kernel, kThreads, 2,64,1),
     KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 2,64,2),
-    KDA_VARIANT(kda_seg_kernel, kThreads, 128),
+    KDA_VARIANT(kda_seg_kernel, 64 * seg_waves<128>(), 128),
     KDA_VARIANT(kda_seg_kernel, kThreads, 64),
     KDA_VARIANT(kda_combine_kernel, kThreads, 128),
     KDA_VARIANT(kda_combine_kernel, kThreads, 64),
