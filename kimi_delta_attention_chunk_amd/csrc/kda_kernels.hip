@@ -649,6 +649,9 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
             Lkb[i][e] = (__bf16)Lk[8 * i + e];
             Lqb[i][e] = (__bf16)Lq[8 * i + e];
         }
+    // The key side is the A operand, so the accumulators hold the transposed blocks: lane
+    // (q4, n16) has row i = 16I + n16 and the four consecutive columns 16J + 4q4 .. +3, one
+    // 16-byte store per block into the row-major block below.
     f32x4 aT[4], aQ[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
@@ -659,8 +662,8 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         for (int i = 0; i < KBW; ++i) {
             const int kb = kb0 + i;
             const bf16x8 bf = (J == I) ? KFb[i] : sR[(pair_index(I, J) * KB + kb) * 64 + lane];
-            aT[J] = mfma(Lkb[i], bf, aT[J]);
-            aQ[J] = mfma(Lqb[i], bf, aQ[J]);
+            aT[J] = mfma(bf, Lkb[i], aT[J]);
+            aQ[J] = mfma(bf, Lqb[i], aQ[J]);
         }
     }
     if constexpr (HV == 2) {
@@ -675,22 +678,26 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         __syncthreads();   // the second halves' sums
     }
     if (hc == 0) {
+        const int i = 16 * I + n16;   // this lane's row
+        const float bi = sBeta[i];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (J > I) continue;
             float* tb = sT + blk(I, J) * BLK_SZ;
             float* qb2 = sAqk + blk(I, J) * BLK_SZ;
-            if constexpr (HV == 2) {
+            if constexpr (HV == 2) {   // (the second half's sums, read before this wave writes)
                 aT[J] += *reinterpret_cast<const f32x4*>(sTp + blk(I, J) * 256 + 4 * lane);
                 aQ[J] += *reinterpret_cast<const f32x4*>(qb2 + 4 * lane);
             }
+            f32x4 t4, q4v;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * q4 + r;
-                const int jj = 16 * J + n16;
-                tb[(4 * q4 + r) * BLK_LD + n16] = (i > jj) ? sBeta[i] * aT[J][r] : 0.f;
-                qb2[(4 * q4 + r) * BLK_LD + n16] = (i >= jj) ? p.scale * aQ[J][r] : 0.f;
+                const int jj = 16 * J + 4 * q4 + r;
+                t4[r] = (i > jj) ? bi * aT[J][r] : 0.f;
+                q4v[r] = (i >= jj) ? p.scale * aQ[J][r] : 0.f;
             }
+            *reinterpret_cast<f32x4*>(tb + n16 * BLK_LD + 4 * q4) = t4;
+            *reinterpret_cast<f32x4*>(qb2 + n16 * BLK_LD + 4 * q4) = q4v;
         }
     }
     // operands kept for later phases: Q~ = scale * q * exp(G) and K~ hi/lo
