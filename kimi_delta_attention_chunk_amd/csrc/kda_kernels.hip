@@ -719,10 +719,10 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         float x[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            float s = (i == lane) ? 1.f : 0.f;
+            float s[4] = {(i == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < i; ++m) s -= tb[i * BLK_LD + m] * x[m];
-            x[i] = s;
+            for (int m = 0; m < i; ++m) s[(i - 1 - m) & 3] -= tb[i * BLK_LD + m] * x[m];
+            x[i] = (s[0] + s[1]) + (s[2] + s[3]);
         }
         float* ab = sAi + blk(w, w) * BLK_SZ;
 #pragma unroll
@@ -979,7 +979,8 @@ struct ChunkFrags {
     bf16x8 w[HD<D>::KB];                          // W, token tile w, 32-channel block kb
     bf16x8 qp[HD<D>::KB];                         // Q', token tile w
     f16x8 kh[HD<D>::MW][2];                       // K_dec^T (fp16), Dk tile MW*w+mt, token step s
-    f32x4 gm[HD<D>::MW];                          // gamma_last for the lane's Dk rows, or
+    float gm[HD<D>::MW];                          // gamma_last, Dk row 4 q4 + (lane & 3) of
+                                                  // tile MW*w+mt (quad-broadcast at use), or
     float g[D / 64];                              // gamma_last[lane D/64 ..] (wave 0, GLDS)
     f16x4 u[NT];                                  // U (fp16), token tile w, Dv tile
     bf16x4 o[NT];                                 // O_intra (bf16), token tile w, Dv tile
@@ -1035,13 +1036,23 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
                 }
             }
         } else {
-            const float* gsrc = p.Gf + size_t(rec) * D;
+            const float* gsrc = p.Gf + size_t(rec) * D + 4 * (lane >> 4) + (lane & 3);
 #pragma unroll
-            for (int mt = 0; mt < MW; ++mt)
-                f.gm[mt] = *reinterpret_cast<const f32x4*>(gsrc + 16 * (MW * w + mt) +
-                                                           4 * (lane >> 4));
+            for (int mt = 0; mt < MW; ++mt) f.gm[mt] = gsrc[16 * (MW * w + mt)];
         }
     }
+}
+
+// The four values of a lane quad, each broadcast to every lane of the quad (DPP quad_perm
+// [r,r,r,r]): with lane 4k + r holding row 4 q4 + r of a 16-row tile, every lane gets the four
+// rows 4 q4 .. 4 q4 + 3 of its accumulator fragment.  Each lane then loads one dword of
+// gamma_last per Dk tile instead of a 16-byte vector that all 16 lanes of its row share.
+__device__ __forceinline__ f32x4 quad_bcast(float x) {
+    const int v = __builtin_bit_cast(int, x);
+#define KDA_QUAD(c) __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, c, 0xf, 0xf, false))
+    const f32x4 r = {KDA_QUAD(0x00), KDA_QUAD(0x55), KDA_QUAD(0xaa), KDA_QUAD(0xff)};
+#undef KDA_QUAD
+    return r;
 }
 
 // Writes one fp32 state fragment (4 consecutive Dk values of one Dv row) as hi/lo bf16.
@@ -1194,7 +1205,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
         for (int mt = 0; mt < MW; ++mt) {
             f32x4 acc = S[mt][nt] * (GLDS ? *reinterpret_cast<const f32x4*>(
                                                 L.g + 16 * (MW * w + mt) + 4 * q4)
-                                          : cur.gm[mt]);
+                                          : quad_bcast(cur.gm[mt]));
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 acc = mfma(cur.kh[mt][s], vh[s], acc);
@@ -1258,7 +1269,7 @@ template <int D>
 struct Frags8 {
     bf16x8 a[HD<D>::KB];   // W (X waves) or Q' (Y waves), token tile w & 3
     f16x8 kh[2];           // K_dec^T of Dk tile w, token steps 0 and 1
-    f32x4 gm;              // gamma_last of the lane's rows of Dk tile w
+    float gm;              // gamma_last of row 4 q4 + (lane & 3) of Dk tile w (quad-broadcast)
     f16x4 u;               // U (X waves), token tile w & 3, the Dv tile
     bf16x4 o;              // O_intra (Y waves), the same
 };
@@ -1283,7 +1294,7 @@ __device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w,
 #pragma unroll
     for (int s = 0; s < 2; ++s)
         f.kh[s] = *reinterpret_cast<const f16x8*>(p.Kf + rb + ((w * 2 + s) * 64 + lane) * 8);
-    f.gm = *reinterpret_cast<const f32x4*>(p.Gf + size_t(rec) * D + 16 * w + 4 * (lane >> 4));
+    f.gm = p.Gf[size_t(rec) * D + 16 * w + 4 * (lane >> 4) + (lane & 3)];
 }
 
 // One chunk for the workgroup's Dv tile with eight waves (see Frags8); ROLE 0 is an X wave
@@ -1360,7 +1371,7 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
             vh[s] = *reinterpret_cast<const f16x8*>(L.vh + off);
             vl[s] = *reinterpret_cast<const f16x8*>(L.vl + off);
         }
-        f32x4 a = S * cur.gm;
+        f32x4 a = S * quad_bcast(cur.gm);
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
             a = mfma(cur.kh[s], vh[s], a);
