@@ -122,6 +122,29 @@ struct DevStore {
     }
 };
 
+// Buffer load from a wave-uniform base (scalar resource) at a per-lane byte offset: no 64-bit
+// per-lane address is formed per chunk, so a loop of chunk loads keeps no address registers
+// that alias the loaded data.
+template <typename T>
+__device__ __forceinline__ T buf_load(const void* base, unsigned bytes, unsigned byte_off) {
+    const __amdgpu_buffer_rsrc_t r =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), 0x00020000);
+    if constexpr (sizeof(T) == 16)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b128(r, int(byte_off), 0, 0));
+    else if constexpr (sizeof(T) == 8)
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b64(r, int(byte_off), 0, 0));
+    else
+        return __builtin_bit_cast(T, __builtin_amdgcn_raw_buffer_load_b32(r, int(byte_off), 0, 0));
+}
+
+// Chunk operand load: a buffer load (scalar base, no per-chunk 64-bit lane address) for the
+// one-tile prefetched scan, where it was measured faster; a plain load elsewhere.
+template <bool BUF, typename T>
+__device__ __forceinline__ T ld_op(const void* base, unsigned bytes, unsigned byte_off) {
+    if constexpr (BUF) return buf_load<T>(base, bytes, byte_off);
+    else return *reinterpret_cast<const T*>(static_cast<const char*>(base) + byte_off);
+}
+
 #define SPLIT_BF16(x, hi, lo)          \
     do {                               \
         const float x_ = (x);          \
@@ -990,19 +1013,23 @@ struct ChunkFrags {
 // state update (K_dec, gamma); PART 0: all.
 // GLDS: wave 0 loads gamma for the workgroup (one load instead of one per wave and Dk tile) and
 // the step passes it on through LDS.  Taken by the one-tile scan with the record prefetch wave
-// (128K scan 2.54 -> 2.31 ms); slower for the segment pass.
+// (128K scan 2.54 -> 2.31 ms); slower for the segment pass.  With GLDS every operand is also a
+// buffer load (ld_op): the compiler then keeps no per-chunk address registers that alias loaded
+// data, and the chunk loop loses the full drain of outstanding loads it had at its top (128K
+// scan 2.24 -> 1.98 ms; no faster for the other scans, slower for the segment pass).
 template <int NT, bool WITH_U, int OUT, int D, int PART = 0, bool GLDS = false>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
                                            int dv_tile0, ChunkFrags<NT, D>& f) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
     if constexpr (PART != 2) {
+        constexpr unsigned RB = 64 * D * 2;   // bytes of one record array
         const __bf16* wsrc = p.Wf + size_t(rec) * (64 * D);
         const __bf16* qsrc = p.Qf + size_t(rec) * (64 * D);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            f.w[kb] = *reinterpret_cast<const bf16x8*>(wsrc + ((w * KB + kb) * 64 + lane) * 8);
+            f.w[kb] = ld_op<GLDS, bf16x8>(wsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
             if constexpr (OUT != OUT_NONE)
-                f.qp[kb] = *reinterpret_cast<const bf16x8*>(qsrc + ((w * KB + kb) * 64 + lane) * 8);
+                f.qp[kb] = ld_op<GLDS, bf16x8>(qsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
         }
         const _Float16* usrc = p.Uf + size_t(rec) * (64 * D);
         const __bf16* osrc = p.Of + size_t(rec) * (64 * D);
@@ -1010,9 +1037,9 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
         for (int nt = 0; nt < NT; ++nt) {
             const int dt = dv_tile0 + nt;
             if constexpr (WITH_U)
-                f.u[nt] = *reinterpret_cast<const f16x4*>(usrc + ((dt * 4 + w) * 64 + lane) * 4);
+                f.u[nt] = ld_op<GLDS, f16x4>(usrc, RB, unsigned((dt * 4 + w) * 64 + lane) * 8);
             if constexpr (OUT == OUT_FINAL || OUT == OUT_O0)
-                f.o[nt] = *reinterpret_cast<const bf16x4*>(osrc + ((dt * 4 + w) * 64 + lane) * 4);
+                f.o[nt] = ld_op<GLDS, bf16x4>(osrc, RB, unsigned((dt * 4 + w) * 64 + lane) * 8);
         }
     }
     if constexpr (PART != 1) {
@@ -1022,23 +1049,25 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int off = (((MW * w + mt) * 2 + s) * 64 + lane) * 8;
-                f.kh[mt][s] = *reinterpret_cast<const f16x8*>(ksrc + off);
+                f.kh[mt][s] = ld_op<GLDS, f16x8>(ksrc, 64 * D * 2, unsigned(off) * 2);
             }
         if constexpr (GLDS) {
             if (w == 0) {
-                const float* gsrc = p.Gf + size_t(rec) * D + lane * (D / 64);
+                const float* gsrc = p.Gf + size_t(rec) * D;
                 if constexpr (D == 128) {
-                    const float2 x = *reinterpret_cast<const float2*>(gsrc);
+                    const float2 x = ld_op<GLDS, float2>(gsrc, D * 4, unsigned(lane) * 8);
                     f.g[0] = x.x;
                     f.g[D / 64 - 1] = x.y;
                 } else {
-                    f.g[0] = *gsrc;
+                    f.g[0] = ld_op<GLDS, float>(gsrc, D * 4, unsigned(lane) * 4);
                 }
             }
         } else {
-            const float* gsrc = p.Gf + size_t(rec) * D + 4 * (lane >> 4) + (lane & 3);
+            const float* gsrc = p.Gf + size_t(rec) * D;
 #pragma unroll
-            for (int mt = 0; mt < MW; ++mt) f.gm[mt] = gsrc[16 * (MW * w + mt)];
+            for (int mt = 0; mt < MW; ++mt)
+                f.gm[mt] = ld_op<GLDS, float>(
+                    gsrc, D * 4, unsigned(16 * (MW * w + mt) + 4 * (lane >> 4) + (lane & 3)) * 4);
         }
     }
 }
