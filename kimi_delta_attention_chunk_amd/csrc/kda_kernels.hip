@@ -1306,30 +1306,32 @@ struct Frags8 {
 // Every operand of one chunk for a wave of the eight-wave walk: W (X waves) or Q' (Y waves) of
 // its token tile, U (X) or O_intra (Y) of that tile and the Dv tile, and the K_dec and gamma
 // of its Dk tile.
-template <int ROLE, bool WITH_U, int OUT, int D>
+template <int ROLE, bool WITH_U, int OUT, int D, bool BUF>
 __device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w, int lane,
                                             int dv_tile, Frags8<D>& f) {
     constexpr int KB = HD<D>::KB;
     const int tt = w & 3;
     const size_t rb = size_t(rec) * (64 * D);
     const int uo = ((dv_tile * 4 + tt) * 64 + lane) * 4;
+    constexpr unsigned RB = 64 * D * 2;
     const __bf16* src = (ROLE == 0 ? p.Wf : p.Qf) + rb;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-        f.a[kb] = *reinterpret_cast<const bf16x8*>(src + ((tt * KB + kb) * 64 + lane) * 8);
-    if constexpr (ROLE == 0 && WITH_U) f.u = *reinterpret_cast<const f16x4*>(p.Uf + rb + uo);
+        f.a[kb] = ld_op<BUF, bf16x8>(src, RB, unsigned((tt * KB + kb) * 64 + lane) * 16);
+    if constexpr (ROLE == 0 && WITH_U) f.u = ld_op<BUF, f16x4>(p.Uf + rb, RB, unsigned(uo) * 2);
     if constexpr (ROLE == 1 && (OUT == OUT_FINAL || OUT == OUT_O0))
-        f.o = *reinterpret_cast<const bf16x4*>(p.Of + rb + uo);
+        f.o = ld_op<BUF, bf16x4>(p.Of + rb, RB, unsigned(uo) * 2);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        f.kh[s] = *reinterpret_cast<const f16x8*>(p.Kf + rb + ((w * 2 + s) * 64 + lane) * 8);
-    f.gm = p.Gf[size_t(rec) * D + 16 * w + 4 * (lane >> 4) + (lane & 3)];
+        f.kh[s] = ld_op<BUF, f16x8>(p.Kf + rb, RB, unsigned((w * 2 + s) * 64 + lane) * 16);
+    f.gm = ld_op<BUF, float>(p.Gf + size_t(rec) * D, D * 4,
+                             unsigned(16 * w + 4 * (lane >> 4) + (lane & 3)) * 4);
 }
 
 // One chunk for the workgroup's Dv tile with eight waves (see Frags8); ROLE 0 is an X wave
 // (waves 0..3), ROLE 1 a Y wave (4..7), each running its own branch-free copy of the walk.
 // Outputs are stored at device scope (the segment pass).
-template <int ROLE, bool WITH_U, int OUT, int D>
+template <int ROLE, bool WITH_U, int OUT, int D, bool ONE_LEVEL = false>
 __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur, f32x4& S,
                                            const ScanLds& L, int w, int jc, int len, size_t ob,
                                            size_t os, int dv_tile, int64_t rec) {
@@ -1373,8 +1375,14 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
             if (tok < len) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(acc[r] + (float)cur.o[r]);
-                const DevStore dst(p.out + ob + size_t(jc) * kChunk * os, unsigned(kChunk * os * 2));
-                dst.put(unsigned((tok - jc * kChunk) * os + 16 * dv_tile + 4 * q4) * 2, yb);
+                if constexpr (!ONE_LEVEL) {
+                    const DevStore dst(p.out + ob + size_t(jc) * kChunk * os,
+                                       unsigned(kChunk * os * 2));
+                    dst.put(unsigned((tok - jc * kChunk) * os + 16 * dv_tile + 4 * q4) * 2, yb);
+                } else {
+                    *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * dv_tile +
+                                               4 * q4) = yb;
+                }
             }
         } else if constexpr (OUT == OUT_O0) {
 #pragma unroll
@@ -1414,7 +1422,9 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
 
 // Chunks [cb, ce) with the eight-wave step (as run_chunks, state in S and in LDS on entry);
 // waves 0..3 run the X copy and waves 4..7 the Y copy of the walk, with the same barriers.
-template <int ROLE, bool WITH_U, int OUT, int D>
+// ONE_LEVEL: the one-level scan (outputs stored plainly, operands as buffer loads); otherwise
+// the segment pass (outputs at device scope, plain operand loads): each measured faster there.
+template <int ROLE, bool WITH_U, int OUT, int D, bool ONE_LEVEL = false>
 __device__ __forceinline__ void run_walk8(const Params& p, f32x4& S, const ScanLds& L, int w,
                                           int64_t rec0, int cb, int ce, int len, size_t ob,
                                           size_t os, int dv_tile) {
@@ -1428,30 +1438,30 @@ __device__ __forceinline__ void run_walk8(const Params& p, f32x4& S, const ScanL
     // split around the products (with which the compiler folded the two-step loop into one and
     // drained every load, K_dec's included, at the top of each step)
     Frags8<D> fa, fb;
-    load_chunk8<ROLE, WITH_U, OUT, D>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile, fa);
+    load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile, fa);
     for (int jc = cb; jc < ce; jc += 2) {
         const int c1 = jc + 1 < last ? jc + 1 : last;
-        load_chunk8<ROLE, WITH_U, OUT, D>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile, fb);
-        scan_step8<ROLE, WITH_U, OUT, D>(p, fa, S, L, w, jc, len, ob, os, dv_tile,
+        load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile, fb);
+        scan_step8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, fa, S, L, w, jc, len, ob, os, dv_tile,
                                          rec0 + int64_t(jc) * p.n_v);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
-        load_chunk8<ROLE, WITH_U, OUT, D>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile, fa);
-        scan_step8<ROLE, WITH_U, OUT, D>(p, fb, S, L, w, jc + 1, len, ob, os, dv_tile,
+        load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile, fa);
+        scan_step8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, fb, S, L, w, jc + 1, len, ob, os, dv_tile,
                                          rec0 + int64_t(jc + 1) * p.n_v);
     }
 }
 
-template <bool WITH_U, int OUT, int D>
+template <bool WITH_U, int OUT, int D, bool ONE_LEVEL = false>
 __device__ __forceinline__ void run_chunks8(const Params& p, f32x4& S, const ScanLds& L,
                                             int64_t rec0, int cb, int ce, int len, size_t ob,
                                             size_t os, int dv_tile) {
     if (cb >= ce) return;
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     if (w < 4)
-        run_walk8<0, WITH_U, OUT, D>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
+        run_walk8<0, WITH_U, OUT, D, ONE_LEVEL>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
     else
-        run_walk8<1, WITH_U, OUT, D>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
+        run_walk8<1, WITH_U, OUT, D, ONE_LEVEL>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
 }
 
 // Sequences of different lengths (cu_seqlens given) are walked longest first: workgroup rank r
@@ -1701,8 +1711,17 @@ __device__ __forceinline__ void zero_rows_past_len(const Params& p, int len, siz
 // The register budget of two workgroups per compute unit (at most 256 VGPRs a lane) for every
 // form: with one, the compiler spreads the two- and four-tile forms over VGPRs and AGPRs and
 // copies the accumulators back and forth inside the chunk loop.
+// The one-tile prefetched scan at head dim 128 walks on eight waves (the eight-wave step) with
+// the prefetch wave as a ninth, one workgroup per compute unit (its budget: 9 waves, at most
+// three on a SIMD).  128K scan 1.96 -> 1.92 ms against the four-wave walk with buffer loads;
+// with plain loads the eight-wave walk was slower (2.03 ms).
 template <int NT, int D, bool PFW>
-__global__ __launch_bounds__(PFW ? kPfThreads : kThreads, 2)
+constexpr bool scan_w8() { return PFW && NT == 1 && D == 128; }
+template <int NT, int D, bool PFW>
+constexpr int scan_threads() { return scan_w8<NT, D, PFW>() ? 9 * 64 : (PFW ? kPfThreads : kThreads); }
+
+template <int NT, int D, bool PFW>
+__global__ __launch_bounds__((scan_threads<NT, D, PFW>()), (scan_w8<NT, D, PFW>() ? 1 : 2))
 void kda_scan_kernel(Params p) {
     constexpr int BV = 16 * NT;
     constexpr int MW = HD<D>::MW;
@@ -1736,8 +1755,9 @@ void kda_scan_kernel(Params p) {
     size_t ob, os;
     row_geom(p, b, h, p.n_v, D, c0, ob, os);
     const int64_t rec0 = int64_t(slot0) * p.n_v + h;
+    constexpr bool W8 = scan_w8<NT, D, PFW>();
     if constexpr (PFW) {
-        if (w == 4) {   // the prefetch wave: the setup barrier, then the walk's barriers
+        if (w == (W8 ? 8 : 4)) {   // the prefetch wave: the setup barrier, then the walk's barriers
             RecPrefetch<D> pf;
             pf.init(p, tile, p.scan_tiles, dv_tile0, NT);
             if (nchunks > 1) pf.template touch<3>(rec0 + p.n_v);
@@ -1748,9 +1768,21 @@ void kda_scan_kernel(Params p) {
         }
     }
 
+    const size_t st_base = (size_t(b) * p.n_v + h) * D * D;
+    if constexpr (W8) {   // wave w holds Dk tile w of the workgroup's 16 state rows
+        const int dv = 16 * dv_tile0 + n16;
+        const int dk = 16 * w + 4 * q4;
+        f32x4 S8 = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+        put_state<D>(sSh, sSl, n16, dk, S8);
+        lds_barrier();
+        run_chunks8<true, OUT_FINAL, D, true>(p, S8, L, rec0, 0, nchunks, len, ob, os, dv_tile0);
+        if (p.fin) *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * D + dk) = S8;
+        if (tid < kThreads) zero_rows_past_len(p, len, ob, os, 16 * dv_tile0, 16);
+        return;
+    }
     // state tile: S[mt][nt][i] = S[dv = 16(dv_tile0+nt) + n16][dk = 16(MW w+mt) + 4q4 + i]
     f32x4 S[MW][NT];
-    const size_t st_base = (size_t(b) * p.n_v + h) * D * D;
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt)
 #pragma unroll
@@ -2203,7 +2235,7 @@ const Variant kVariants[] = {
     KDA_VARIANT(kda_combine_kernel, kThreads, 64),
     KDA_VARIANT(kda_out_kernel, kThreads, 128),
     KDA_VARIANT(kda_out_kernel, kThreads, 64),
-    KDA_VARIANT(kda_scan_kernel, kPfThreads, 1,128,true),
+    KDA_VARIANT(kda_scan_kernel, (scan_threads<1, 128, true>()), 1,128,true),
     KDA_VARIANT(kda_scan_kernel, kPfThreads, 2,128,true),
     KDA_VARIANT(kda_scan_kernel, kThreads, 1,128,false),
     KDA_VARIANT(kda_scan_kernel, kThreads, 2,128,false),
