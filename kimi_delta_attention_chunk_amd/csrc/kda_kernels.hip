@@ -182,7 +182,7 @@ __device__ __forceinline__ void seq_info(const Params& p, int b, int& c0, int& l
 
 // Sequence of a chunk slot: the last b whose first slot is <= slot (TND), or slot / nc_max.
 __device__ __forceinline__ int slot_batch(const Params& p, int slot) {
-    if (p.layout != KDA_LAYOUT_TND) return slot / p.nc_max;
+    if (p.layout != KDA_LAYOUT_TND) return int(unsigned(slot) / unsigned(p.nc_max));
     int lo = 0, hi = p.batch - 1;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
@@ -421,15 +421,21 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     // group value heads of a unit (one chunk of one q/k head) run on one XCD, dispatched one
     // after another, so its L2 fetches that q/k chunk once: workgroup 8 r + x takes unit
     // (r / group) 8 + x, member r mod group (the identity without GQA).
+    // (unsigned 32-bit arithmetic throughout: records and slots stay below 2^31, the plan
+    // rejects larger grids, and a 64-bit or signed division costs the prologue that delays
+    // every load of the workgroup)
     const unsigned pid = blockIdx.x;
     const unsigned gr = unsigned(p.group);
     const unsigned rr = pid >> 3;
-    const unsigned unit = (rr / gr) * 8u + (pid & 7u);
+    const unsigned rq = rr / gr;
+    const unsigned unit = rq * 8u + (pid & 7u);
     if (unit >= unsigned(p.intra_units)) return;   // grid padding
-    const int64_t rec = int64_t(unit) * gr + rr % gr;
-    const int slot = int(rec / p.n_v);   // grids stay below 2^31
-    const int h = int(rec - int64_t(slot) * p.n_v);
-    const int hq = h / p.group;
+    const unsigned rec32 = unit * gr + (rr - rq * gr);
+    const unsigned slot_u = rec32 / unsigned(p.n_v);
+    const int64_t rec = rec32;
+    const int slot = int(slot_u);
+    const int h = int(rec32 - slot_u * unsigned(p.n_v));
+    const int hq = int(unsigned(h) / gr);
 
     // chunk slot -> (sequence b, chunk j)
     const int b = slot_batch(p, slot);
@@ -2109,15 +2115,16 @@ __device__ __forceinline__ void complete_record(const Params& p, int64_t rec, in
     const int lane = tid & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
-    const int slot = int(rec / p.n_v);
-    const int h = int(rec - int64_t(slot) * p.n_v);
+    const unsigned slot_u = unsigned(rec) / unsigned(p.n_v);   // records stay below 2^31
+    const int slot = int(slot_u);
+    const int h = int(unsigned(rec) - slot_u * unsigned(p.n_v));
     const int b = slot_batch(p, slot);
     int c0, len, slot0;
     seq_info(p, b, c0, len, slot0);
     const int j = slot - slot0;
     if (j < 0 || j * kChunk >= len) return;   // an unused slot
     const int nchunks = (len + kChunk - 1) / kChunk;
-    const int seg = j / ((nchunks + p.seg_p - 1) / p.seg_p);
+    const int seg = int(unsigned(j) / ((unsigned(nchunks) + p.seg_p - 1) / unsigned(p.seg_p)));
     if (seg < seg_lo || seg > seg_hi) return;
     size_t ob, os;
     row_geom(p, b, h, p.n_v, D, c0, ob, os);
