@@ -1715,8 +1715,8 @@ __device__ __forceinline__ void zero_rows_past_len(const Params& p, int len, siz
 // two workgroups share a compute unit.  PFW: at most one workgroup per compute unit, with the
 // record prefetch wave.
 // The register budget of two workgroups per compute unit (at most 256 VGPRs a lane) for every
-// form: with one, the compiler spreads the two- and four-tile forms over VGPRs and AGPRs and
-// copies the accumulators back and forth inside the chunk loop.
+// four-wave form: with one, the compiler spreads the two- and four-tile forms over VGPRs and
+// AGPRs and copies the accumulators back and forth inside the chunk loop.
 // The one-tile prefetched scan at head dim 128 walks on eight waves (the eight-wave step) with
 // the prefetch wave as a ninth, one workgroup per compute unit (its budget: 9 waves, at most
 // three on a SIMD).  128K scan 1.96 -> 1.92 ms against the four-wave walk with buffer loads;
