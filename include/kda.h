@@ -91,7 +91,7 @@ typedef struct {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,  /* a NULL or misaligned pointer, bad enum, negative size, alias */
-    KDA_ERR_UNSUPPORTED = 2,  /* a valid request this build does not implement: head dim, or
+    KDA_ERR_UNSUPPORTED = 2,  /* a valid request the library does not implement: head dim, or
                                  sizes past its limits (n_v * d_k >= 2^24; more than 2^31 - 1
                                  workgroups in a kernel; tensors of 2^60 elements or more) */
     KDA_ERR_WORKSPACE = 3,    /* workspace pointer NULL or workspace_bytes too small */
