@@ -1258,8 +1258,8 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
 }
 
 // Chunks [cb, ce) of one sequence (records rec0 + c * n_v), state in S and in LDS on entry.
-// DEVST: the step's outputs are stored at device scope (the segment pass; measured slower for
-// the one-level scan's output stream).
+// DEVST: the step's outputs are stored at device scope (as the segment pass stores them, on the
+// eight-wave walk; measured slower for the one-level scan's output stream).
 // The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
 // record, never used): with the same number of loads in flight on every path, the compiler's
 // wait counts let each step wait only for its own operands, not for the next chunk's.
@@ -1294,12 +1294,14 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     }
 }
 
-// Eight-wave chunk step (the segment pass at head dim 128, one 16-row Dv tile).  With four
-// waves every SIMD holds one wave of the walk, and nothing covers its LDS and memory waits.
-// Here waves 0..3 take token tile w & 3 of X = W S^T and its V_new, waves 4..7 the same token
-// tile of Y^T = S Q'^T and its outputs, and in the state update each wave takes one 16-row Dk
-// tile: the workgroup loads exactly what the four-wave step loads (each operand once), with two
-// waves on every SIMD.  Measured at the 8K prefill: segment pass 24.5-24.9 -> 23.3-24.0 us.
+// Eight-wave chunk step (the segment pass, and at head dim 128 the one-level one-tile scan with
+// the prefetch wave; one 16-row Dv tile).  With four waves every SIMD holds one wave of the
+// walk, and nothing covers its LDS and memory waits.  Here waves 0..3 take token tile w & 3 of
+// X = W S^T and its V_new, waves 4..7 the same token tile of Y^T = S Q'^T and its outputs, and
+// in the state update each wave takes one 16-row Dk tile (at head dim 64, whose state has four,
+// the X waves alone): the workgroup loads exactly what the four-wave step loads (each operand
+// once), with two waves on every SIMD.  Measured at the 8K prefill: segment pass 24.5-24.9 ->
+// 23.3-24.0 us.
 template <int D>
 struct Frags8 {
     bf16x8 a[HD<D>::KB];   // W (X waves) or Q' (Y waves), token tile w & 3
@@ -1327,11 +1329,13 @@ __device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w,
     if constexpr (ROLE == 0 && WITH_U) f.u = ld_op<BUF, f16x4>(p.Uf + rb, RB, unsigned(uo) * 2);
     if constexpr (ROLE == 1 && (OUT == OUT_FINAL || OUT == OUT_O0))
         f.o = ld_op<BUF, bf16x4>(p.Of + rb, RB, unsigned(uo) * 2);
+    if constexpr (D == 128 || ROLE == 0) {   // the waves that update a Dk tile of the state
 #pragma unroll
-    for (int s = 0; s < 2; ++s)
-        f.kh[s] = ld_op<BUF, f16x8>(p.Kf + rb, RB, unsigned((w * 2 + s) * 64 + lane) * 16);
-    f.gm = ld_op<BUF, float>(p.Gf + size_t(rec) * D, D * 4,
-                             unsigned(16 * w + 4 * (lane >> 4) + (lane & 3)) * 4);
+        for (int s = 0; s < 2; ++s)
+            f.kh[s] = ld_op<BUF, f16x8>(p.Kf + rb, RB, unsigned((w * 2 + s) * 64 + lane) * 16);
+        f.gm = ld_op<BUF, float>(p.Gf + size_t(rec) * D, D * 4,
+                                 unsigned(16 * w + 4 * (lane >> 4) + (lane & 3)) * 4);
+    }
 }
 
 // One chunk for the workgroup's Dv tile with eight waves (see Frags8); ROLE 0 is an X wave
@@ -1342,7 +1346,7 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
                                            const ScanLds& L, int w, int jc, int len, size_t ob,
                                            size_t os, int dv_tile, int64_t rec) {
     constexpr int KB = HD<D>::KB, SLD = HD<D>::SLD;
-    static_assert(D / 16 == 8, "one 16-row Dk tile per wave");
+    static_assert(D / 16 == 8 || D / 16 == 4, "one 16-row Dk tile per wave or per X wave");
     const int lane = threadIdx.x & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
@@ -1405,8 +1409,9 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
     }
     lds_barrier();
 
-    // S^T <- gamma * S^T + K_dec^T V_new for Dk tile w, on the fp16 MFMA
-    {
+    // S^T <- gamma * S^T + K_dec^T V_new for Dk tile w, on the fp16 MFMA (at head dim 64, four
+    // Dk tiles: the X waves only)
+    if constexpr (D == 128 || ROLE == 0) {
         f16x8 vh[2], vl[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -1825,16 +1830,19 @@ void kda_scan_kernel(Params p) {
 // from S = 0 (from the initial state for s = 0) with U: the outputs of segment 0 are final,
 // those of later segments go to O0, and the end state is N_s.  The identity walk (D/16
 // workgroups from 16 identity rows each, without U) writes the columns of R = Q' P^T as its
-// outputs and ends with the rows of P_s.  At head dim 128 the walk runs on eight waves (the
-// eight-wave step, scan_step8: two waves on every SIMD, one 16-row Dk tile of the state each).
+// outputs and ends with the rows of P_s.  The walk runs on eight waves (the eight-wave step,
+// scan_step8: two waves on every SIMD; one 16-row Dk tile of the state per wave at head dim
+// 128, per X wave at 64).  Head dim 64: segment pass at 8K 17.9-18.2 -> 17.0-17.4 us against
+// the four-wave walk.
 template <int D>
-constexpr int seg_waves() { return D == 128 ? 8 : 4; }
+constexpr int seg_waves() { return 8; }
 
 template <int D>
 __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params p) {
     constexpr int NW = seg_waves<D>();
-    constexpr int MW = D / (16 * NW), TILES = HD<D>::TILES;   // Dk tiles per wave
-    constexpr bool SEG_SPLIT = D == 128;   // split loads: faster at D = 128, slower at 64 (measured)
+    constexpr int NDK = D / 16;                               // Dk tiles of the state
+    constexpr int MW = NDK >= NW ? NDK / NW : 1, TILES = HD<D>::TILES;   // Dk tiles per wave
+    const bool holds = int(threadIdx.x >> 6) < NDK;           // this wave holds a Dk tile
     __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) __bf16 sVh[16 * VN_LD];
@@ -1893,6 +1901,7 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
     const int row = 16 * tile + n16;   // state row (value channel, or identity row)
 #pragma unroll
     for (int mt = 0; mt < MW; ++mt) {
+        if (!holds) { S[mt][0] = f32x4{0.f, 0.f, 0.f, 0.f}; continue; }
         const int dk = 16 * (MW * w + mt) + 4 * q4;
         f32x4 x = {0.f, 0.f, 0.f, 0.f};
         if (is_p) {
@@ -1908,11 +1917,7 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
 
     const size_t m = (size_t(bh) * p.seg_p + seg) * D * D;
     if (is_p) {
-        if constexpr (NW == 8)
-            run_chunks8<false, OUT_R, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
-        else
-            run_chunks<1, false, OUT_R, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len, ob,
-                                                                  os, tile);
+        run_chunks8<false, OUT_R, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
         // rows 16 tile .. of P_s, in fp16, into the combine's A fragments of P_s^T: element
         // P_s[16 tile + n16][16 M + 4 q4 + i] is lane (2 (tile & 1) + (n16 >> 3), 4 q4 + i),
         // entry n16 & 7, of fragment (M, tile >> 1)
@@ -1920,6 +1925,7 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
         constexpr int KB = HD<D>::KB;
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
+            if (holds)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int lp = (2 * (tile & 1) + (n16 >> 3)) * 16 + 4 * q4 + i;
@@ -1927,28 +1933,21 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
                 pt[at] = (_Float16)S[mt][0][i];
             }
     } else {
-        if constexpr (NW == 8) {
-            if (seg == 0)
-                run_chunks8<true, OUT_FINAL, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
-            else
-                run_chunks8<true, OUT_O0, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
-        } else {
-            if (seg == 0)
-                run_chunks<1, true, OUT_FINAL, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce,
-                                                                         len, ob, os, tile);
-            else
-                run_chunks<1, true, OUT_O0, D, SEG_SPLIT, false, true>(p, S, L, rec0, cb, ce, len,
-                                                                      ob, os, tile);
-        }
+        if (seg == 0)
+            run_chunks8<true, OUT_FINAL, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
+        else
+            run_chunks8<true, OUT_O0, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
-            *reinterpret_cast<f32x4*>(p.Nst + m + ((tile * TILES + MW * w + mt) * 64 + lane) * 4) =
-                S[mt][0];
+            if (holds)
+                *reinterpret_cast<f32x4*>(p.Nst + m + ((tile * TILES + MW * w + mt) * 64 + lane) * 4) =
+                    S[mt][0];
         if (seg == 0) {   // S_in(1) = N_0 for the completion of segment 1 (combine pass layout)
             constexpr int KB = HD<D>::KB;
             __bf16* dst = p.Sin + (size_t(bh) * p.seg_p + 1) * D * D;
 #pragma unroll
             for (int mt = 0; mt < MW; ++mt) {
+                if (!holds) continue;
                 const int M = MW * w + mt;
                 const int lb = (2 * (M & 1) + (q4 >> 1)) * 16 + n16;
                 *reinterpret_cast<bf16x4*>(dst + ((tile * KB + (M >> 1)) * 64 + lb) * 8 +
@@ -2237,7 +2236,7 @@ const Variant kVariants[] = {
     KDA_VARIANT(kda_intra_kernel, kThreads, 2,64,1),
     KDA_VARIANT(kda_intra_kernel, 2 * kThreads, 2,64,2),
     KDA_VARIANT(kda_seg_kernel, 64 * seg_waves<128>(), 128),
-    KDA_VARIANT(kda_seg_kernel, kThreads, 64),
+    KDA_VARIANT(kda_seg_kernel, 64 * seg_waves<64>(), 64),
     KDA_VARIANT(kda_combine_kernel, kThreads, 128),
     KDA_VARIANT(kda_combine_kernel, kThreads, 64),
     KDA_VARIANT(kda_out_kernel, kThreads, 128),
