@@ -997,7 +997,6 @@ constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = va
 
 // What a chunk step writes besides the state update.
 enum OutMode {
-    OUT_NONE = 0,    // nothing (segment end state and transfer matrix only)
     OUT_FINAL = 1,   // out = Q' S^T + O_intra in bf16, valid tokens only
     OUT_O0 = 2,      // O0 = Q' S^T + O_intra in bf16, workspace (state from a zero start)
     OUT_R = 3,       // R = Q' S^T in bf16, workspace (state rows of the transfer matrix)
@@ -1018,12 +1017,13 @@ struct ChunkFrags {
 // PART 1: the operands of a step's first products (W, Q', U, O_intra); PART 2: those of its
 // state update (K_dec, gamma); PART 0: all.
 // GLDS: wave 0 loads gamma for the workgroup (one load instead of one per wave and Dk tile) and
-// the step passes it on through LDS.  Taken by the one-tile scan with the record prefetch wave
-// (128K scan 2.54 -> 2.31 ms); slower for the segment pass.  With GLDS every operand is also a
-// buffer load (ld_op): the compiler then keeps no per-chunk address registers that alias loaded
-// data, and the chunk loop loses the full drain of outstanding loads it had at its top (128K
-// scan 2.24 -> 1.98 ms; no faster for the other scans, slower for the segment pass).
-template <int NT, bool WITH_U, int OUT, int D, int PART = 0, bool GLDS = false>
+// the step passes it on through LDS.  Taken by the four-wave one-tile scan with the record
+// prefetch wave (at head dim 64; at 128 that scan now runs the eight-wave walk), measured on the
+// 128K workload when it ran this walk: 2.54 -> 2.31 ms; slower for the segment pass.  With GLDS
+// every operand is also a buffer load (ld_op): the compiler then keeps no per-chunk address
+// registers that alias loaded data, and the chunk loop loses the full drain of outstanding
+// loads it had at its top (128K scan 2.24 -> 1.98 ms; no faster for the other scans).
+template <int NT, int D, int PART = 0, bool GLDS = false>
 __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, int lane,
                                            int dv_tile0, ChunkFrags<NT, D>& f) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
@@ -1034,18 +1034,15 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             f.w[kb] = ld_op<GLDS, bf16x8>(wsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
-            if constexpr (OUT != OUT_NONE)
-                f.qp[kb] = ld_op<GLDS, bf16x8>(qsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
+            f.qp[kb] = ld_op<GLDS, bf16x8>(qsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
         }
         const _Float16* usrc = p.Uf + size_t(rec) * (64 * D);
         const __bf16* osrc = p.Of + size_t(rec) * (64 * D);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
             const int dt = dv_tile0 + nt;
-            if constexpr (WITH_U)
-                f.u[nt] = ld_op<GLDS, f16x4>(usrc, RB, unsigned((dt * 4 + w) * 64 + lane) * 8);
-            if constexpr (OUT == OUT_FINAL || OUT == OUT_O0)
-                f.o[nt] = ld_op<GLDS, bf16x4>(osrc, RB, unsigned((dt * 4 + w) * 64 + lane) * 8);
+            f.u[nt] = ld_op<GLDS, f16x4>(usrc, RB, unsigned((dt * 4 + w) * 64 + lane) * 8);
+            f.o[nt] = ld_op<GLDS, bf16x4>(osrc, RB, unsigned((dt * 4 + w) * 64 + lane) * 8);
         }
     }
     if constexpr (PART != 1) {
@@ -1130,12 +1127,11 @@ struct ScanLds {
 //   each issued after the products it must not delay (a wave that issues a burst of loads
 //   waits at issue while the compute unit's address unit takes them); without it the caller
 //   has issued them all before the step.  Which is faster depends on the kernel (measured).
-template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS, bool DEVST>
+template <int NT, int D, bool SPLIT, bool GLDS>
 __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, D>& cur,
                                           ChunkFrags<NT, D>& nxt, int64_t rec_nxt,
                                           f32x4 (&S)[HD<D>::MW][NT], const ScanLds& L, int jc,
-                                          int len, size_t ob, size_t os, int dv_tile0,
-                                          int64_t rec) {
+                                          int len, size_t ob, size_t os, int dv_tile0) {
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW, SLD = HD<D>::SLD;
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1143,8 +1139,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
-    // X = W (S_hi + S_lo)^T (tokens of tile w x Dv); Y^T = S_hi Q'^T (Dv x tokens), with S_lo
-    // too for R (the transfer matrix rows are not rounded again by a state of their own)
+    // X = W (S_hi + S_lo)^T (tokens of tile w x Dv); Y^T = S_hi Q'^T (Dv x tokens)
     f32x4 accX[NT], accY[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1157,13 +1152,12 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
             const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
             accX[nt] = mfma(cur.w[kb], sh, accX[nt]);
             accX[nt] = mfma(cur.w[kb], sl, accX[nt]);
-            if constexpr (OUT != OUT_NONE) accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
-            if constexpr (OUT == OUT_R) accY[nt] = mfma(sl, cur.qp[kb], accY[nt]);
+            accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
         }
     }
     if constexpr (SPLIT) {
         __builtin_amdgcn_sched_barrier(0);
-        load_chunk<NT, WITH_U, OUT, D, 1>(p, rec_nxt, w, lane, dv_tile0, nxt);
+        load_chunk<NT, D, 1>(p, rec_nxt, w, lane, dv_tile0, nxt);
         __builtin_amdgcn_sched_barrier(0);
     }
     const int tok = jc * kChunk + 16 * w + n16;  // output token of this lane
@@ -1172,48 +1166,19 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
         f16x4 vh, vl;   // V_new as an fp16 pair, the operand of the fp16 update product
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float x = (WITH_U ? (float)cur.u[nt][r] : 0.f) - accX[nt][r];
+            const float x = (float)cur.u[nt][r] - accX[nt][r];
             vh[r] = (_Float16)x;
             vl[r] = (_Float16)(x - (float)vh[r]);
         }
         const int off = (16 * nt + n16) * VN_LD + 16 * w + 4 * q4;
         *reinterpret_cast<f16x4*>(L.vh + off) = vh;
         *reinterpret_cast<f16x4*>(L.vl + off) = vl;
-        if constexpr (OUT == OUT_FINAL) {
-            if (tok < len) {
-                bf16x4 o;
+        if (tok < len) {
+            bf16x4 o;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)cur.o[nt][r]);
-                if constexpr (DEVST) {   // the chunk's 64 output rows as one store region
-                    const DevStore dst(p.out + ob + size_t(jc) * kChunk * os,
-                                       unsigned(kChunk * os * 2));
-                    dst.put(unsigned((tok - jc * kChunk) * os + 16 * (dv_tile0 + nt) + 4 * q4) * 2,
-                            o);
-                } else {
-                    *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os +
-                                               16 * (dv_tile0 + nt) + 4 * q4) = o;
-                }
-            }
-        } else if constexpr (OUT == OUT_O0 || OUT == OUT_R) {
-            // every row, so the completion pass reads no unwritten memory (rows past the
-            // tail are zero: their q and every Aqk entry are)
-            const int t = dv_tile0 + nt;
-            f32x4 y = accY[nt];
-            // both in bf16: each adds one bf16 rounding to an output that is itself rounded
-            // to bf16, against the fp32 sums of the completion pass
-            bf16x4 yb;
-            if constexpr (OUT == OUT_O0) {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(y[r] + (float)cur.o[nt][r]);
-                DevStore(p.O0 + size_t(rec) * (64 * D), 64 * D * 2)
-                    .put(unsigned((t * 4 + w) * 64 + lane) * 8, yb);
-            } else {   // R in the completion pass's B-operand order
-#pragma unroll
-                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)y[r];
-                const int lb = (2 * (t & 1) + (q4 >> 1)) * 16 + n16;
-                DevStore(p.Rf + size_t(rec) * (64 * D), 64 * D * 2)
-                    .put(unsigned(((w * KB + (t >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1)) * 2, yb);
-            }
+            for (int r = 0; r < 4; ++r) o[r] = (__bf16)(accY[nt][r] + (float)cur.o[nt][r]);
+            *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * (dv_tile0 + nt) +
+                                       4 * q4) = o;
         }
     }
     static_assert(!(GLDS && SPLIT), "gamma through LDS comes with unsplit loads");
@@ -1252,18 +1217,18 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
     }
     if constexpr (SPLIT) {
         __builtin_amdgcn_sched_barrier(0);
-        load_chunk<NT, WITH_U, OUT, D, 2>(p, rec_nxt, w, lane, dv_tile0, nxt);
+        load_chunk<NT, D, 2>(p, rec_nxt, w, lane, dv_tile0, nxt);
     }
     lds_barrier();
 }
 
-// Chunks [cb, ce) of one sequence (records rec0 + c * n_v), state in S and in LDS on entry.
-// DEVST: the step's outputs are stored at device scope (as the segment pass stores them, on the
-// eight-wave walk; measured slower for the one-level scan's output stream).
+// Chunks [cb, ce) of one sequence (records rec0 + c * n_v), state in S and in LDS on entry:
+// the one-level scan's four-wave walk (its outputs stored plainly; at device scope, as the
+// segment pass stores them, the one-level scan's output stream measured slower).
 // The prefetch is issued on every step, past the end as a reload of the last chunk (a valid
 // record, never used): with the same number of loads in flight on every path, the compiler's
 // wait counts let each step wait only for its own operands, not for the next chunk's.
-template <int NT, bool WITH_U, int OUT, int D, bool SPLIT, bool GLDS = false, bool DEVST = false>
+template <int NT, int D, bool SPLIT, bool GLDS = false>
 __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW][NT],
                                            const ScanLds& L,
                                            int64_t rec0, int cb, int ce, int len, size_t ob,
@@ -1273,24 +1238,19 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     const int lane = threadIdx.x & 63;
     const int last = ce - 1;
     ChunkFrags<NT, D> fa, fb;
-    load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0,
-                                            fa);
+    load_chunk<NT, D, 0, GLDS>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile0, fa);
     for (int jc = cb; jc < ce; jc += 2) {
         const int c1 = jc + 1 < last ? jc + 1 : last;
         if constexpr (!SPLIT)
-            load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(c1) * p.n_v, w, lane,
-                                                    dv_tile0, fb);
-        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS, DEVST>(
-            p, fa, fb, rec0 + int64_t(c1) * p.n_v, S, L, jc, len, ob, os, dv_tile0,
-            rec0 + int64_t(jc) * p.n_v);
+            load_chunk<NT, D, 0, GLDS>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile0, fb);
+        scan_step<NT, D, SPLIT, GLDS>(p, fa, fb, rec0 + int64_t(c1) * p.n_v, S, L, jc, len, ob,
+                                      os, dv_tile0);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
         if constexpr (!SPLIT)
-            load_chunk<NT, WITH_U, OUT, D, 0, GLDS>(p, rec0 + int64_t(c2) * p.n_v, w, lane,
-                                                    dv_tile0, fa);
-        scan_step<NT, WITH_U, OUT, D, SPLIT, GLDS, DEVST>(
-            p, fb, fa, rec0 + int64_t(c2) * p.n_v, S, L, jc + 1, len, ob, os, dv_tile0,
-            rec0 + int64_t(jc + 1) * p.n_v);
+            load_chunk<NT, D, 0, GLDS>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile0, fa);
+        scan_step<NT, D, SPLIT, GLDS>(p, fb, fa, rec0 + int64_t(c2) * p.n_v, S, L, jc + 1, len,
+                                      ob, os, dv_tile0);
     }
 }
 
@@ -1809,8 +1769,7 @@ void kda_scan_kernel(Params p) {
     // split loads measured faster for the wider tiles, slower for the one-tile prefetched form,
     // which takes gamma through LDS instead
     constexpr bool SPLIT = NT > 1, GLDS = PFW && NT == 1;
-    run_chunks<NT, true, OUT_FINAL, D, SPLIT, GLDS>(p, S, L, rec0, 0, nchunks, len, ob, os,
-                                                   dv_tile0);
+    run_chunks<NT, D, SPLIT, GLDS>(p, S, L, rec0, 0, nchunks, len, ob, os, dv_tile0);
 
     if (p.fin) {
 #pragma unroll
