@@ -527,7 +527,9 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
 #pragma unroll
             for (int i = 0; i < 8 * KBW; ++i) {
                 const float x = ts * ((float)xgr[i >> 3][i & 7] + xg[i >> 2][i & 3]);
-                gv[i] = p.lower_bound / (1.0f + exp2_fast(-x * kLog2e));
+                // the hardware reciprocal (1 ulp) instead of a correctly rounded division:
+                // raw-gate intra at 8K 23.0-23.5 -> 21.6-22.2 us
+                gv[i] = p.lower_bound * __builtin_amdgcn_rcpf(1.0f + exp2_fast(-x * kLog2e));
             }
         } else {
 #pragma unroll
@@ -607,10 +609,15 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     {
         const bool l2 = (p.flags & KDA_QK_L2NORM) != 0;
         // a zero factor removes the clamped rows past the tail from every q/k product
-        qn = !tv ? 0.f : (l2 ? 1.0f / sqrtf(sq + 1e-6f) : 1.0f);
-        kn = !tv ? 0.f : (l2 ? 1.0f / sqrtf(sk + 1e-6f) : 1.0f);
+        // (the hardware reciprocal square root and reciprocal, 1 ulp, for the correctly
+        // rounded quotients: no measurable difference in any parity margin)
+        qn = !tv ? 0.f : (l2 ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f);
+        kn = !tv ? 0.f : (l2 ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.0f);
         bt = 0.f;
-        if (tv) bt = (p.flags & KDA_BETA_SIGMOID) ? 1.0f / (1.0f + expf(-braw)) : braw;
+        if (tv)
+            bt = (p.flags & KDA_BETA_SIGMOID)
+                     ? __builtin_amdgcn_rcpf(1.0f + exp2_fast(-braw * kLog2e))
+                     : braw;
     }
     if (q4 == 0 && hc == 0) sBeta[tok] = bt;
 
