@@ -157,6 +157,11 @@ __device__ __forceinline__ T ld_op(const void* base, unsigned bytes, unsigned by
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
+// Orders this wave's LDS accesses (a wave's LDS operations complete in issue order; the
+// compiler must not move accesses across this point).
+__device__ __forceinline__ void wave_lds_fence() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
 
 // Sequence geometry: valid length and the chunk-slot base, identical in both kernels.
 __device__ __forceinline__ void seq_info(const Params& p, int b, int& c0, int& len,
@@ -236,9 +241,11 @@ constexpr int N_BLK = 10;               // lower-triangular 16 x 16 blocks of a 
 constexpr int TILE = 8 * 16 * 8 * 2;    // one token-grouped tile [group 8][n16][8] bf16: 2 KB
 
 // LDS of the intra kernel for head dim D:
-//   Aqk blocks (12800) | Ainv blocks (12800) | beta[64] (256) | region X
-// The Ainv region holds, until the inverse is formed, the per-channel factor rows:
-//   vec: BV[6][128], C[4][128] fp32 (5120) at Ainv + 0;  vecA[4][128] fp32 (2048) at + 5120.
+//   Aqk blocks (12800) | Ainv blocks (12800) | beta[64] (256) | region X | vecA[4][128] fp32
+// The Ainv region holds, until the inverse is formed, the per-channel factor rows
+//   vec: BV[6][128], C[4][128] fp32 (5120) at Ainv + 0;
+// vecA, the factor rows of Q~ and K~, has its own 2048 bytes, so that the operands made from it
+// can be formed while the inverse writes its blocks.
 // Region X, by phase:
 //   gate sums      first[4][128], dlast[4][128] fp32 (4096)                  at X + 0
 //   T/Aqk          sR [pair 6][kb D/32][lane 64] bf16x8 (6 D/32 KB)           at X + 0
@@ -246,7 +253,7 @@ constexpr int TILE = 8 * 16 * 8 * 2;    // one token-grouped tile [group 8][n16]
 //   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                      at X + 0
 //   W, U           sKt hi/lo tiles (2 D/16 tiles), sVt (D/16 tiles)           at X + 0
 //   O_intra, Q'    sW (-W, D/16 tiles), sU (D/16 tiles)                       at X + 0
-// D = 128: 75,008 B (two workgroups per compute unit); D = 64: 50,944 B (three).  The eight-wave
+// D = 128: 77,056 B (two workgroups per compute unit); D = 64: 52,992 B (three).  The eight-wave
 // form (HV = 2) also keeps, through phases 1 and 2, the half sums of squares [2][64][2] fp32 and
 // the second channel half's T products [block 10][lane 64][4] fp32 after the T blocks.
 template <int D, int HV = 1>
@@ -256,7 +263,6 @@ struct IntraLds {
     static constexpr int OFF_BETA = OFF_AI + N_BLK * BLK_SZ * 4;
     static constexpr int OFF_X = OFF_BETA + 256;
     static constexpr int AI_VEC = 0;
-    static constexpr int AI_VECA = 5120;
     static constexpr int TILES = D / 16;
     static constexpr int X_R = 0;
     static constexpr int X_T = 6 * (D / 32) * 64 * 16;
@@ -270,9 +276,12 @@ struct IntraLds {
     static constexpr int X_TP = X_NRM + 1024;                  // eight waves: T half products
     static constexpr int X_P2 = HV == 2 ? X_TP + N_BLK * 1024 : X_NRM;   // end of phase 1-2 use
     static constexpr int X_BYTES = X_P2 > 3 * TILES * TILE ? X_P2 : 3 * TILES * TILE;
-    static constexpr int BYTES = OFF_X + X_BYTES;
-    static constexpr int PER_CU = HV == 2 ? 1 : (D == 64 ? 3 : 2);   // workgroups per compute unit
-    static_assert(AI_VECA + 2048 <= N_BLK * BLK_SZ * 4, "factor rows fit the Ainv region");
+    static constexpr int OFF_VECA = OFF_X + X_BYTES;   // factor rows vecA[4][128] fp32
+    static constexpr int BYTES = OFF_VECA + 2048;
+    // workgroups per compute unit; as the launch bound it caps the registers: the eight-wave form
+    // must fit 128 so that two of its workgroups share a compute unit
+    static constexpr int PER_CU = (D == 64 && HV == 1) ? 3 : 2;
+    static_assert(5120 <= N_BLK * BLK_SZ * 4, "factor rows fit the Ainv region");
     static_assert(X_BYTES >= 4096 && X_BYTES >= 4 * BLK_SZ * 4, "gate sums and staging fit X");
     static_assert(X_TMP + 4 * BLK_SZ * 4 <= X_T, "inverse staging ends before the T blocks");
     static_assert(PER_CU * BYTES <= 160 * 1024, "the workgroups of one compute unit fit its LDS");
@@ -392,7 +401,7 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     float* sAi = reinterpret_cast<float*>(smem + LY::OFF_AI);
     float* sBeta = reinterpret_cast<float*>(smem + LY::OFF_BETA);
     float* sVec = reinterpret_cast<float*>(smem + LY::OFF_AI + LY::AI_VEC);
-    float* sVecA = reinterpret_cast<float*>(smem + LY::OFF_AI + LY::AI_VECA);
+    float* sVecA = reinterpret_cast<float*>(smem + LY::OFF_VECA);
     unsigned char* X = smem + LY::OFF_X;
     float* sFirst = reinterpret_cast<float*>(X);               // [4][128]
     float* sDlast = sFirst + 512;                              // [4][128]
@@ -713,13 +722,52 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         }
         __syncthreads();   // the second halves' sums
     }
-    if (hc == 0) {
+    // ---- phase 3: Ainv = (I + T)^-1 in fp32 -------------------------------------------------------
+    // With D' the block diagonal of I + T (inverses Dinv_I) and L its blocks below the diagonal,
+    // I + T = D' (I + N) with N = D'^-1 L, and N^4 = 0 (four block rows), so
+    // (I + T)^-1 = (I - N + N^2 - N^3) D'^-1.  The diagonal blocks are inverted by forward
+    // substitution (one column per lane, each row's dot product in four partial sums), the rest
+    // on the fp32 MFMA as 16 x 16 products:
+    //   N_IJ = Dinv_I T_IJ;  Ainv_{J+1,J} = -N_{J+1,J} Dinv_J;
+    //   Ainv_20 = M_20 Dinv_0, M_20 = N_21 N_10 - N_20;  Ainv_31 = M_31 Dinv_1, M_31 = N_32 N_21 - N_31;
+    //   Ainv_30 = M_30 Dinv_0, M_30 = Z_30 - N_32 M_20, Z_30 = N_31 N_10 - N_30.
+    // (Block forward substitution down a block column is a chain of nine such products.)
+    // Four waves: the wave that forms row block I of T inverts its diagonal block and forms N_IJ
+    // (J < I) in place in the T blocks with no workgroup barrier (its own LDS accesses stay in
+    // order); after one barrier every block below the diagonal comes out of one phase, the
+    // M_20, M_30 chain (three products deep) in one wave.  Eight waves: the same products in four
+    // barrier-separated levels spread over the waves (measured faster there).
+    const int lr = lane & 15, lk = lane >> 4;
+    auto tb = [&](int I2, int J2) { return sT + blk(I2, J2) * BLK_SZ; };
+    auto ab = [&](int I2, int J2) { return sAi + blk(I2, J2) * BLK_SZ; };
+    // acc + X Y for 16 x 16 blocks of row stride BLK_LD; lane (lk, lr) holds rows 4 lk + i,
+    // column lr of the result
+    auto mm = [&](const float* X, const float* Y, f32x4 acc) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[lr * BLK_LD + 4 * ks + lk],
+                                                       Y[(4 * ks + lk) * BLK_LD + lr], acc,
+                                                       0, 0, 0);
+        return acc;
+    };
+    auto put = [&](float* dst, f32x4 v) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(4 * lk + i) * BLK_LD + lr] = v[i];
+    };
+    auto get = [&](const float* src) {
+        f32x4 v;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = src[(4 * lk + i) * BLK_LD + lr];
+        return v;
+    };
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    if (hc == 0) {   // T and Aqk blocks of row block I
         const int i = 16 * I + n16;   // this lane's row
         const float bi = sBeta[i];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             if (J > I) continue;
-            float* tb = sT + blk(I, J) * BLK_SZ;
+            float* tbl = tb(I, J);
             float* qb2 = sAqk + blk(I, J) * BLK_SZ;
             if constexpr (HV == 2) {   // (the second half's sums, read before this wave writes)
                 aT[J] += *reinterpret_cast<const f32x4*>(sTp + blk(I, J) * 256 + 4 * lane);
@@ -732,78 +780,104 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
                 t4[r] = (i > jj) ? bi * aT[J][r] : 0.f;
                 q4v[r] = (i >= jj) ? p.scale * aQ[J][r] : 0.f;
             }
-            *reinterpret_cast<f32x4*>(tb + n16 * BLK_LD + 4 * q4) = t4;
+            *reinterpret_cast<f32x4*>(tbl + n16 * BLK_LD + 4 * q4) = t4;
             *reinterpret_cast<f32x4*>(qb2 + n16 * BLK_LD + 4 * q4) = q4v;
+        }
+        if constexpr (HV == 1) {
+            wave_lds_fence();
+            if (lane < 16) {   // Dinv_I, column `lane`, over T's diagonal block (row i's
+                               // elements are all read before its result is stored)
+                float* const db = tb(I, I);
+                float x[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    float s4[4] = {(r == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int m = 0; m < r; ++m) s4[(r - 1 - m) & 3] -= db[r * BLK_LD + m] * x[m];
+                    x[r] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) db[r * BLK_LD + lane] = x[r];
+            }
+            wave_lds_fence();
+            f32x4 nb[3];   // N_IJ, J < I, in place of T_IJ (only this wave reads it until the barrier)
+#pragma unroll
+            for (int J = 0; J < 3; ++J)
+                if (J < I) nb[J] = mm(tb(I, I), tb(I, J), zero);
+#pragma unroll
+            for (int J = 0; J < 3; ++J)
+                if (J < I) put(tb(I, J), nb[J]);
         }
     }
     // operands kept for later phases: Q~ = scale * q * exp(G) and K~ hi/lo
     float Qt[8 * KBW];
     bf16x8 bkh[KBW], bkl[KBW];
+    auto keep_operands = [&]() {
 #pragma unroll
-    for (int i = 0; i < KBW; ++i)
+        for (int i = 0; i < KBW; ++i)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float a = sVecA[I * 128 + 32 * (kb0 + i) + 8 * q4 + e];
-            Qt[8 * i + e] = p.scale * Lq[8 * i + e] * a;
-            SPLIT_BF16(Lk[8 * i + e] * a, bkh[i][e], bkl[i][e]);   // K~ (beta goes with Ainv)
+            for (int e = 0; e < 8; ++e) {
+                const float a = sVecA[I * 128 + 32 * (kb0 + i) + 8 * q4 + e];
+                Qt[8 * i + e] = p.scale * Lq[8 * i + e] * a;
+                SPLIT_BF16(Lk[8 * i + e] * a, bkh[i][e], bkl[i][e]);   // K~ (beta goes with Ainv)
+            }
+    };
+    if constexpr (HV == 2) keep_operands();
+    __syncthreads();   // T and Aqk ready (four waves: N below the diagonal, Dinv on it)
+    if constexpr (HV == 1) {
+        keep_operands();   // independent work beside the product chains
+        float* const sM20 = sTmp;
+        float* const sM31 = sTmp + BLK_SZ;
+        float* const sM30 = sTmp + 2 * BLK_SZ;
+        if (w == 0) {   // the M_20, M_30 chain
+            const f32x4 m20 = mm(tb(2, 1), tb(1, 0), -get(tb(2, 0)));
+            const f32x4 z30 = mm(tb(3, 1), tb(1, 0), -get(tb(3, 0)));
+            put(sM20, m20);
+            wave_lds_fence();
+            put(sM30, -mm(tb(3, 2), sM20, -z30));
+            const f32x4 a20 = mm(sM20, tb(0, 0), zero);
+            wave_lds_fence();
+            const f32x4 a30 = mm(sM30, tb(0, 0), zero);
+            put(ab(2, 0), a20);
+            put(ab(3, 0), a30);
+        } else if (w == 1) {   // the M_31 chain; Dinv_0, Dinv_1 into Ainv
+            put(sM31, mm(tb(3, 2), tb(2, 1), -get(tb(3, 1))));
+            put(ab(0, 0), get(tb(0, 0)));
+            put(ab(1, 1), get(tb(1, 1)));
+            wave_lds_fence();
+            put(ab(3, 1), mm(sM31, tb(1, 1), zero));
+        } else if (w == 2) {   // Ainv_10, Ainv_21; Dinv_2 into Ainv
+            const f32x4 a10 = -mm(tb(1, 0), tb(0, 0), zero);
+            const f32x4 a21 = -mm(tb(2, 1), tb(1, 1), zero);
+            put(ab(1, 0), a10);
+            put(ab(2, 1), a21);
+            put(ab(2, 2), get(tb(2, 2)));
+        } else {   // Ainv_32; Dinv_3 into Ainv
+            put(ab(3, 2), -mm(tb(3, 2), tb(2, 2), zero));
+            put(ab(3, 3), get(tb(3, 3)));
         }
-    __syncthreads();   // T, Aqk ready
-
-    // ---- phase 3: Ainv = (I + T)^-1 in fp32 (waves 0..3) ----------------------------------------
-    if (w < 4 && lane < 16) {  // diagonal block w by forward substitution, column `lane`
-        const float* tb = sT + blk(w, w) * BLK_SZ;
-        float x[16];
+    } else {
+        if (w < 4 && lane < 16) {   // Dinv_w, column `lane` (the same substitution; written
+                                    // out at each site: as a shared helper the compiler's
+                                    // register use grew past the eight-wave form's 128)
+            const float* const tw = tb(w, w);
+            float* const aw = ab(w, w);
+            float x[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float s[4] = {(i == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+            for (int r = 0; r < 16; ++r) {
+                float s4[4] = {(r == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int m = 0; m < i; ++m) s[(i - 1 - m) & 3] -= tb[i * BLK_LD + m] * x[m];
-            x[i] = (s[0] + s[1]) + (s[2] + s[3]);
+                for (int m = 0; m < r; ++m) s4[(r - 1 - m) & 3] -= tw[r * BLK_LD + m] * x[m];
+                x[r] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
+            }
+#pragma unroll
+            for (int r = 0; r < 16; ++r) aw[r * BLK_LD + lane] = x[r];
         }
-        float* ab = sAi + blk(w, w) * BLK_SZ;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) ab[i * BLK_LD + lane] = x[i];
-    }
-    __syncthreads();
-    // Below the diagonal.  With D' the block diagonal of I + T (inverses Dinv_I above) and L its
-    // blocks below the diagonal, I + T = D' (I + N) with N = D'^-1 L, and N^4 = 0 (four block
-    // rows), so  (I + T)^-1 = (I - N + N^2 - N^3) D'^-1.  Evaluated in four levels of
-    // independent 16 x 16 products on the fp32 MFMA, each level spread over the waves:
-    //   1: N_IJ = Dinv_I T_IJ (in place of T_IJ, which only its own wave reads);
-    //   2: Ainv_{J+1,J} = -N_{J+1,J} Dinv_J;  M_20 = N_21 N_10 - N_20;  M_31 = N_32 N_21 - N_31;
-    //      Z_30 = N_31 N_10 - N_30;
-    //   3: Ainv_20 = M_20 Dinv_0;  Ainv_31 = M_31 Dinv_1;  M_30 = Z_30 - N_32 M_20;
-    //   4: Ainv_30 = M_30 Dinv_0.
-    // (Block forward substitution down a block column is a chain of nine such products.)
-    {
+        __syncthreads();
         constexpr int NW = 4 * HV;   // waves of the workgroup
-        const int lr = lane & 15, lk = lane >> 4;
         float* const sM20 = sTmp;
         float* const sM31 = sTmp + BLK_SZ;
         float* const sZ30 = sTmp + 2 * BLK_SZ;   // Z_30, then M_30
-        auto tb = [&](int I2, int J2) { return sT + blk(I2, J2) * BLK_SZ; };
-        auto ab = [&](int I2, int J2) { return sAi + blk(I2, J2) * BLK_SZ; };
-        // acc + X Y for 16 x 16 blocks of row stride BLK_LD; lane (lk, lr) holds rows 4 lk + i,
-        // column lr of the result
-        auto mm = [&](const float* X, const float* Y, f32x4 acc) {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(X[lr * BLK_LD + 4 * ks + lk],
-                                                           Y[(4 * ks + lk) * BLK_LD + lr], acc,
-                                                           0, 0, 0);
-            return acc;
-        };
-        auto put = [&](float* dst, f32x4 v) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) dst[(4 * lk + i) * BLK_LD + lr] = v[i];
-        };
-        auto get = [&](const float* src) {
-            f32x4 v;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) v[i] = src[(4 * lk + i) * BLK_LD + lr];
-            return v;
-        };
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         for (int t = w; t < 6; t += NW) {   // level 1, blocks (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
             const int I2 = t < 1 ? 1 : (t < 3 ? 2 : 3);
             const int J2 = t - (I2 * (I2 - 1)) / 2;
