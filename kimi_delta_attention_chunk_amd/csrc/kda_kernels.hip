@@ -315,24 +315,28 @@ __device__ __forceinline__ float row_scan16(float x) {
 //   sel_phi(h): C[token][n] = X[token][32kb + 8(n>>2) + 4h + (n&3)]       (tile 2kb+h, phi order)
 // The phi order makes the accumulator rows 4q4 + r of tile (kb, h) the lane's own channels
 // 32kb + 8q4 + 4h + r, so an accumulator initialised from row-layout registers lines up.
+// Eight 16-bit elements, element t holding `bits` and the others zero (all zero when t lies
+// outside [0, 8)): four selects instead of eight compares, eight selects and four packs.
+__device__ __forceinline__ bf16x8 onehot8(int t, unsigned bits) {
+    typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+    const unsigned v = bits << ((unsigned(t) & 1u) * 16u);
+    const unsigned d = unsigned(t) >> 1;
+    u32x4 r;
+    r.x = d == 0u ? v : 0u;
+    r.y = d == 1u ? v : 0u;
+    r.z = d == 2u ? v : 0u;
+    r.w = d == 3u ? v : 0u;
+    return __builtin_bit_cast(bf16x8, r);
+}
 __device__ __forceinline__ bf16x8 sel_nat(int h, int q4, int n16) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (8 * q4 + j == 16 * h + n16) ? (__bf16)1.f : (__bf16)0.f;
-    return r;
+    return onehot8(16 * h + n16 - 8 * q4, 0x3F80u);   // bf16 1
 }
 __device__ __forceinline__ f16x8 sel_nat16(int h, int q4, int n16) {
-    f16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) r[j] = (8 * q4 + j == 16 * h + n16) ? (_Float16)1.f : (_Float16)0.f;
-    return r;
+    return __builtin_bit_cast(f16x8, onehot8(16 * h + n16 - 8 * q4, 0x3C00u));   // fp16 1
 }
-__device__ __forceinline__ bf16x8 sel_phi(int h, int q4, int n16, float one = 1.f) {
-    bf16x8 r;
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        r[j] = (q4 == (n16 >> 2) && j == 4 * h + (n16 & 3)) ? (__bf16)one : (__bf16)0.f;
-    return r;
+// negative: -1 in place of 1
+__device__ __forceinline__ bf16x8 sel_phi(int h, int q4, int n16, bool negative = false) {
+    return onehot8(q4 == (n16 >> 2) ? 4 * h + (n16 & 3) : -1, negative ? 0xBF80u : 0x3F80u);
 }
 
 __device__ __forceinline__ bf16x4 to_bf16x4(f32x4 x) {
@@ -417,7 +421,7 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     __bf16* sU = reinterpret_cast<__bf16*>(X + LY::X_U);
 
     const int tid = threadIdx.x;
-    const int w = tid >> 6;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar block indices
     const int lane = tid & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
@@ -980,8 +984,8 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
             }
             wdst.put(unsigned((I * KB + kb0 + i) * 64 + lane) * 16, oh);
             // token-major -W (phi channel order) for Q' = Q~ + Aqk (-W): a selection with -1
-            wT[2 * i] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, -1.f), zero));
-            wT[2 * i + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, -1.f), zero));
+            wT[2 * i] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, true), zero));
+            wT[2 * i + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, true), zero));
         }
         // U accumulator: lane (q4, n16) holds U[16I + 4q4 + r][16nt + n16]
         const DevStore udst(p.Uf + size_t(rec) * (64 * D), 64 * D * 2);
