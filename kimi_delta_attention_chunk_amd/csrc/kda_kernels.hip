@@ -624,7 +624,8 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         // a zero factor removes the clamped rows past the tail from every q/k product
         // (the hardware reciprocal square root and reciprocal, 1 ulp, for the correctly
         // rounded quotients: no measurable difference in any parity margin)
-        qn = !tv ? 0.f : (l2 ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f);
+        // (the query factor carries the output scale, so Aqk and Q~ need no product with it)
+        qn = !tv ? 0.f : (l2 ? __builtin_amdgcn_rsqf(sq + 1e-6f) : 1.0f) * p.scale;
         kn = !tv ? 0.f : (l2 ? __builtin_amdgcn_rsqf(sk + 1e-6f) : 1.0f);
         bt = 0.f;
         if (tv)
@@ -782,7 +783,7 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
             for (int r = 0; r < 4; ++r) {
                 const int jj = 16 * J + 4 * q4 + r;
                 t4[r] = (i > jj) ? bi * aT[J][r] : 0.f;
-                q4v[r] = (i >= jj) ? p.scale * aQ[J][r] : 0.f;
+                q4v[r] = (i >= jj) ? aQ[J][r] : 0.f;
             }
             *reinterpret_cast<f32x4*>(tbl + n16 * BLK_LD + 4 * q4) = t4;
             *reinterpret_cast<f32x4*>(qb2 + n16 * BLK_LD + 4 * q4) = q4v;
@@ -822,7 +823,7 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const float a = sVecA[I * 128 + 32 * (kb0 + i) + 8 * q4 + e];
-                Qt[8 * i + e] = p.scale * Lq[8 * i + e] * a;
+                Qt[8 * i + e] = Lq[8 * i + e] * a;
                 SPLIT_BF16(Lk[8 * i + e] * a, bkh[i][e], bkl[i][e]);   // K~ (beta goes with Ainv)
             }
     };
