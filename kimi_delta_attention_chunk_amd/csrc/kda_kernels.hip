@@ -779,11 +779,19 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
                 aQ[J] += *reinterpret_cast<const f32x4*>(qb2 + 4 * lane);
             }
             f32x4 t4, q4v;
+            if (J < I) {   // below the diagonal block every entry is kept
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int jj = 16 * J + 4 * q4 + r;
-                t4[r] = (i > jj) ? bi * aT[J][r] : 0.f;
-                q4v[r] = (i >= jj) ? aQ[J][r] : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    t4[r] = bi * aT[J][r];
+                    q4v[r] = aQ[J][r];
+                }
+            } else {       // the diagonal block: T strictly lower, Aqk lower with the diagonal
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int jj = 16 * J + 4 * q4 + r;
+                    t4[r] = (i > jj) ? bi * aT[J][r] : 0.f;
+                    q4v[r] = (i >= jj) ? aQ[J][r] : 0.f;
+                }
             }
             *reinterpret_cast<f32x4*>(tbl + n16 * BLK_LD + 4 * q4) = t4;
             *reinterpret_cast<f32x4*>(qb2 + n16 * BLK_LD + 4 * q4) = q4v;
@@ -862,21 +870,22 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
             put(ab(3, 3), get(tb(3, 3)));
         }
     } else {
-        if (w < 4 && lane < 16) {   // Dinv_w, column `lane` (the same substitution; written
-                                    // out at each site: as a shared helper the compiler's
-                                    // register use grew past the eight-wave form's 128)
-            const float* const tw = tb(w, w);
-            float* const aw = ab(w, w);
+        if (w == 0) {   // all four Dinv in one wave: block lane >> 4, column lane & 15 (the
+                        // same substitution, written out at each site: as a shared helper the
+                        // compiler's register use grew past the eight-wave form's 128)
+            const int g = lane >> 4, col = lane & 15;
+            const float* const tw = sT + blk(g, g) * BLK_SZ;
+            float* const aw = sAi + blk(g, g) * BLK_SZ;
             float x[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float s4[4] = {(r == lane) ? 1.f : 0.f, 0.f, 0.f, 0.f};
+                float s4[4] = {(r == col) ? 1.f : 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int m = 0; m < r; ++m) s4[(r - 1 - m) & 3] -= tw[r * BLK_LD + m] * x[m];
                 x[r] = (s4[0] + s4[1]) + (s4[2] + s4[3]);
             }
 #pragma unroll
-            for (int r = 0; r < 16; ++r) aw[r * BLK_LD + lane] = x[r];
+            for (int r = 0; r < 16; ++r) aw[r * BLK_LD + col] = x[r];
         }
         __syncthreads();
         constexpr int NW = 4 * HV;   // waves of the workgroup
