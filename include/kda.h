@@ -31,9 +31,10 @@
  *   - Not checked (preconditions, as in the FlashKDA README, section 约束说明): cu_seqlens
  *     starts at 0, is strictly increasing and ends at seq_len (TND); with BNSD/BSND each valid
  *     length lies in [1, seq_len]; -5 <= g <= 0; all tensors live on one device.  The decayed
- *     keys (at most |k|), the values transformed inside a chunk (about |v|), the innovation
- *     v - S k of the state update and, in the two-level scan, the segment entry state are held
- *     in fp16 (limit 65504; larger magnitudes overflow to inf).  Tested range: L2-normalised
+ *     keys (at most |k|), the decayed queries times scale (at most |q| scale), the values
+ *     transformed inside a chunk (about |v|), the innovation v - S k of the state update and,
+ *     in the two-level scan, the segment entry state are held in fp16 (limit 65504; larger
+ *     magnitudes overflow to inf).  Tested range: L2-normalised
  *     keys with v and the initial state scaled by up to 2048 (|v| up to about 1e4), every output
  *     and final state within the tolerance in units of that scale, one- and two-level scans,
  *     head dims 128 and 64.

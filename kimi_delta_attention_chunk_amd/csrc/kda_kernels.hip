@@ -409,7 +409,7 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     unsigned char* X = smem + LY::OFF_X;
     float* sFirst = reinterpret_cast<float*>(X);               // [4][128]
     float* sDlast = sFirst + 512;                              // [4][128]
-    bf16x8* sR = reinterpret_cast<bf16x8*>(X + LY::X_R);       // [pair 6][kb KB][lane 64]
+    f16x8* sR = reinterpret_cast<f16x8*>(X + LY::X_R);         // [pair 6][kb KB][lane 64]
     float* sT = reinterpret_cast<float*>(X + LY::X_T);
     float* sNrm = reinterpret_cast<float*>(X + LY::X_NRM);     // [half 2][token 64][q, k]
     float* sTp = reinterpret_cast<float*>(X + LY::X_TP);       // [block 10][lane 64][4]
@@ -636,7 +636,13 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     if (q4 == 0 && hc == 0) sBeta[tok] = bt;
 
     float Lk[8 * KBW], Lq[8 * KBW];
-    bf16x8 KFb[KBW];
+    // the diagonal T and Aqk blocks of row block I (this wave's channels): both sides are this
+    // wave's own rows, so they are formed here, beside the operands, with no LDS exchange.  The
+    // key side KF = k_j exp(G[16I] - G_j) < 2^109 stays in bf16; masked entries may be huge and
+    // are removed by select.  T takes both sides as bf16 hi/lo pairs (three terms; with single
+    // bf16 operands the rounding of T was half of the error of a final state without decay),
+    // Aqk the hi parts.
+    f32x4 aTd = {0.f, 0.f, 0.f, 0.f}, aQd = {0.f, 0.f, 0.f, 0.f};
     {
         const DevStore kdst(p.Kf + size_t(rec) * (64 * D), 64 * D * 2);
         const int s_k = I >> 1;
@@ -659,16 +665,29 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
                 Lk[ii] = kv * ef;
                 Lq[ii] = (float)xq[i][e] * qn * ef;
                 kf[e] = kv * ff;
-                KFb[i][e] = (__bf16)kf[e];
                 kd[e] = (_Float16)(kf[e] * sVec[(VEC_C + I) * 128 + c]);   // K_dec <= |k|, one fp16 value
             }
-            // the key operand of every later row block I2 > I: k_j exp(G[16 I2] - G_j) <= 1
+            {
+                bf16x8 kh, kl, lh, ll, qh;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    SPLIT_BF16(kf[e], kh[e], kl[e]);
+                    SPLIT_BF16(Lk[8 * i + e], lh[e], ll[e]);
+                    qh[e] = (__bf16)Lq[8 * i + e];
+                }
+                aTd = mfma(kh, lh, aTd);
+                aTd = mfma(kh, ll, aTd);
+                aTd = mfma(kl, lh, aTd);
+                aQd = mfma(kh, qh, aQd);
+            }
+            // the key operand of every later row block I2 > I: k_j exp(G[16 I2] - G_j) <= 1, in
+            // fp16 (11 bits; terms below its range are under 2^-24 and dropped)
             for (int I2 = I + 1; I2 < 4; ++I2) {
                 const int pi = pair_index(I2, I);
                 const float* bv = sVec + (VEC_BV + pi) * 128 + 32 * kb + 8 * q4;
-                bf16x8 r;
+                f16x8 r;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) r[e] = (__bf16)(kf[e] * bv[e]);
+                for (int e = 0; e < 8; ++e) r[e] = (_Float16)(kf[e] * bv[e]);
                 sR[(pi * KB + kb) * 64 + lane] = r;
             }
             // K_dec^T fragments of Dk tiles 2kb, 2kb+1: [mt D/16][s 2][lane 64][8] fp16
@@ -683,37 +702,41 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
     }
     __syncthreads();   // scaled key blocks, sBeta ready
 
-    // ---- phase 2: T and Aqk blocks of row block I on MFMA -------------------------------------
+    // ---- phase 2: T and Aqk blocks of row block I below the diagonal, on MFMA ------------------
     // Both products use the row block's own operands relative to its first token 16I,
-    // k_i exp(G_i - G[16I]) <= 1 and q_i exp(G_i - G[16I]).  Diagonal: the key side is KF,
-    // exp(G[16I] - G_j) < 2^109; masked entries may be huge and are removed by select.
-    // Off-diagonal (I > J): the key side arrives scaled by its owner wave to k_j exp(G[16I] - G_j)
-    // <= 1.  With two waves per block each sums over its channel half; the second half's sums
-    // pass through LDS (T's after the T blocks, Aqk's in its own not yet written block slots) to
-    // the first half's wave, which adds them and stores T and Aqk.
-    bf16x8 Lkb[KBW], Lqb[KBW];
-#pragma unroll
-    for (int i = 0; i < KBW; ++i)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            Lkb[i][e] = (__bf16)Lk[8 * i + e];
-            Lqb[i][e] = (__bf16)Lq[8 * i + e];
-        }
+    // k_i exp(G_i - G[16I]) <= 1 and q_i exp(G_i - G[16I]); the key side arrives scaled by its
+    // owner wave to k_j exp(G[16I] - G_j) <= 1.  Both sides, at most 1 in magnitude, are fp16.
+    // With two waves per block each sums over its channel half; the second half's sums pass
+    // through LDS (T's after the T blocks, Aqk's in its own not yet written block slots) to the
+    // first half's wave, which adds them and stores T and Aqk.
     // The key side is the A operand, so the accumulators hold the transposed blocks: lane
     // (q4, n16) has row i = 16I + n16 and the four consecutive columns 16J + 4q4 .. +3, one
     // 16-byte store per block into the row-major block below.
     f32x4 aT[4], aQ[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
-        aT[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-        aQ[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (J > I) continue;
+        const bool dg = J == I;
+        aT[J] = dg ? aTd : f32x4{0.f, 0.f, 0.f, 0.f};
+        aQ[J] = dg ? aQd : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (I > 0) {
+        f16x8 Lkh16[KBW], Lqh16[KBW];
 #pragma unroll
-        for (int i = 0; i < KBW; ++i) {
-            const int kb = kb0 + i;
-            const bf16x8 bf = (J == I) ? KFb[i] : sR[(pair_index(I, J) * KB + kb) * 64 + lane];
-            aT[J] = mfma(bf, Lkb[i], aT[J]);
-            aQ[J] = mfma(bf, Lqb[i], aQ[J]);
+        for (int i = 0; i < KBW; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                Lkh16[i][e] = (_Float16)Lk[8 * i + e];
+                Lqh16[i][e] = (_Float16)Lq[8 * i + e];
+            }
+#pragma unroll
+        for (int J = 0; J < 3; ++J) {
+            if (J >= I) continue;
+#pragma unroll
+            for (int i = 0; i < KBW; ++i) {
+                const f16x8 bf = sR[(pair_index(I, J) * KB + kb0 + i) * 64 + lane];
+                aT[J] = mfma(bf, Lkh16[i], aT[J]);
+                aQ[J] = mfma(bf, Lqh16[i], aQ[J]);
+            }
         }
     }
     if constexpr (HV == 2) {
