@@ -49,6 +49,21 @@ SCALAR_GATE_CASES = [
 ]
 
 
+# No decay: the state never forgets, so the final state is the case nearest the bound.  These
+# are the worst of 150 seeded random no-decay draws (at up to 0.95 of the bound before the
+# T/Aqk operands of the intra kernel were made more precise, about 0.56-0.69 after), kept as
+# fixed cases so that a loss of precision shows here first.
+NO_DECAY_CASES = [
+    ("nd_d64_bsnd_b2_init", dict(layout="BSND", batch=2, seq_len=604, n_qk=4, n_v=4, d=64,
+                                 g_kind="zero", init=True, seed=9015)),
+    ("nd_d64_bsnd_gqa16", dict(layout="BSND", batch=1, seq_len=1102, n_qk=8, n_v=16, d=64,
+                               g_kind="zero", init=False, seed=9011)),
+    ("nd_d64_bnsd_scalar_gate", dict(layout="BNSD", batch=1, seq_len=712, n_qk=8, n_v=16, d=64,
+                                     g_kind="zero", init=True, seed=9107, scalar_gate=True)),
+    ("nd_d128_tnd_ragged", dict(layout="TND", batch=3, seq_len=0, n_qk=4, n_v=8, d=128,
+                                g_kind="zero", init=False, seed=9146, lengths=[23, 867, 1145])),
+]
+
 # Head dim 64 (d_k = d_v = 64): every layout, GQA, ragged tails, valid lengths, no decay, the
 # scalar gate, and a sequence long enough for the two-level scan.
 D64_CASES = [
@@ -156,7 +171,8 @@ def all_case_shapes() -> list:
     """(name, shape) of every fixed GPU parity case, the named workloads and the sweep."""
     from test_gpu_sweep import CASES as SWEEP
     out = []
-    for group in (SMALL, SCALAR_GATE_CASES, D64_CASES, TWO_LEVEL, VARIANT_CASES, RAW_GATE_CASES):
+    for group in (SMALL, SCALAR_GATE_CASES, D64_CASES, TWO_LEVEL, VARIANT_CASES, RAW_GATE_CASES,
+                  NO_DECAY_CASES):
         out += [(name, case_shape(kw)) for name, kw in group]
     out += [(name, case_shape(kw, flags_on)) for name, kw, flags_on in SWEEP]
     for w in WORKLOADS:

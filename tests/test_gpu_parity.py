@@ -21,7 +21,7 @@ from kimi_delta_attention_chunk_amd import kda_chunk_fwd, chunk_fwd
 from kimi_delta_attention_chunk_amd.workloads import (Inputs, make_inputs, workload_inputs,
                                                       WORKLOADS)
 from gpu_cases import (SMALL, SCALAR_GATE_CASES, D64_CASES, TWO_LEVEL, VARIANT_CASES,
-                       RAW_GATE_CASES, case_shape)
+                       RAW_GATE_CASES, NO_DECAY_CASES, case_shape)
 from kimi_delta_attention_chunk_amd.ops import kda_chunk_fwd_plan_kernels
 
 pytestmark = pytest.mark.gpu
@@ -109,6 +109,11 @@ def test_two_level_scan(name, kw):
 def test_small_cases(name, kw):
     inp = make_inputs(**kw)
     compare(inp, name)
+
+
+@pytest.mark.parametrize("name,kw", NO_DECAY_CASES, ids=[s[0] for s in NO_DECAY_CASES])
+def test_no_decay_final_state(name, kw):
+    compare(make_inputs(**kw), name)
 
 
 def test_flags_off_prenormalised_inputs():
