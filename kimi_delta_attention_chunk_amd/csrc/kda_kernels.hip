@@ -12,8 +12,9 @@
 //     S <- S diag(exp(G_last)) + V_new^T (K * exp(G_last - G)).
 // Kernels:
 //   kda_intra_kernel  one workgroup per (64-token chunk, value head), fully parallel.  Computes
-//                     the log2-space running gate sum, the decayed operands, T and Aqk on bf16
-//                     MFMA, the fp32 blocked inverse, W and U, and folds the chunk-local terms:
+//                     the log2-space running gate sum, the decayed operands, T and Aqk on MFMA
+//                     (diagonal blocks bf16, T's as hi/lo pairs; blocks below the diagonal
+//                     fp16), the fp32 blocked inverse, W and U, and folds the chunk-local terms:
 //                     Q' = Qt - Aqk W and O_intra = Aqk U, so that O = Q' S^T + O_intra.
 //                     Writes W, Q', K_dec, U, O_intra and gamma_last in MFMA fragment order.
 //   kda_scan_kernel   one workgroup per (sequence, value head, Dv tiles) walks the chunks in
@@ -29,7 +30,8 @@
 // exp(-G) is never formed.  For sub-blocks I > J the decay between rows i (block I) and j
 // (block J) is split at the first row r_I of block I into two factors <= 1; inside a diagonal
 // block the read key carries 2^(G_r - G_j) <= 2^(15 * 5 * log2 e) < 2^109 for g >= -5, finite
-// in fp32/bf16, and masked entries are removed by select, never by multiplication.
+// in fp32/bf16 (so the diagonal blocks stay in bf16; the factors <= 1 of the other blocks fit
+// fp16), and masked entries are removed by select, never by multiplication.
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
@@ -248,7 +250,7 @@ constexpr int TILE = 8 * 16 * 8 * 2;    // one token-grouped tile [group 8][n16]
 // can be formed while the inverse writes its blocks.
 // Region X, by phase:
 //   gate sums      first[4][128], dlast[4][128] fp32 (4096)                  at X + 0
-//   T/Aqk          sR [pair 6][kb D/32][lane 64] bf16x8 (6 D/32 KB)           at X + 0
+//   T/Aqk          sR [pair 6][kb D/32][lane 64] f16x8 (6 D/32 KB)            at X + 0
 //                  sT blocks (12800)                                          at X + X_T
 //   inverse        sTmp [wave 4][16][BLK_LD] fp32 (5120)                      at X + 0
 //   W, U           sKt hi/lo tiles (2 D/16 tiles), sVt (D/16 tiles)           at X + 0
