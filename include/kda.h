@@ -32,8 +32,9 @@
  *     starts at 0, is strictly increasing and ends at seq_len (TND); with BNSD/BSND each valid
  *     length lies in [1, seq_len]; -5 <= g <= 0; all tensors live on one device.  The decayed
  *     keys (at most |k|), the decayed queries times scale (at most |q| scale), the values
- *     transformed inside a chunk (about |v|), the innovation v - S k of the state update and,
- *     in the two-level scan, the segment entry state are held in fp16 (limit 65504; larger
+ *     transformed inside a chunk (about |v|), the innovation v - S k of the state update and
+ *     the state itself (initial, carried from chunk to chunk and, in the two-level scan, the
+ *     segment entry state) are held in fp16 or as fp16 hi/lo pairs (limit 65504; larger
  *     magnitudes overflow to inf).  Tested range: L2-normalised
  *     keys with v and the initial state scaled by up to 2048 (|v| up to about 1e4), every output
  *     and final state within the tolerance in units of that scale, one- and two-level scans,

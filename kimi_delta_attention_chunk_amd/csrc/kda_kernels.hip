@@ -69,8 +69,8 @@ struct Params {
     const int32_t* cu;
     __bf16* out;
     float* fin;
-    __bf16* Wf;   // [record][tt 4][kb 4][lane 64][8]         W[16tt+m][32kb+8q+j]
-    __bf16* Qf;   // [record][tt 4][kb 4][lane 64][8]         Q'[16tt+m][32kb+8q+j]
+    _Float16* Wf; // [record][tt 4][kb 4][lane 64][8]         W[16tt+m][32kb+8q+j] (fp16)
+    _Float16* Qf; // [record][tt 4][kb 4][lane 64][8]         Q'[16tt+m][32kb+8q+j] (fp16)
     _Float16* Kf; // [record][mt 8][s 2][lane 64][8]          K_dec[32s+8q+j][16mt+m] (fp16)
     _Float16* Uf; // [record][nt 8][tt 4][lane 64][4]         U[16tt+4q+i][16nt+n] (fp16)
     __bf16* Of;   // [record][nt 8][tt 4][lane 64][4]         O_intra[16tt+n][16nt+4q+i]
@@ -1011,13 +1011,16 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < KBW; ++i) {
-            bf16x8 oh;
+            bf16x8 oh;   // (bf16 for the transpose below; the record takes fp16)
+            f16x8 wh;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 oh[r] = (__bf16)accW[2 * i][r];
                 oh[4 + r] = (__bf16)accW[2 * i + 1][r];
+                wh[r] = (_Float16)accW[2 * i][r];
+                wh[4 + r] = (_Float16)accW[2 * i + 1][r];
             }
-            wdst.put(unsigned((I * KB + kb0 + i) * 64 + lane) * 16, oh);
+            wdst.put(unsigned((I * KB + kb0 + i) * 64 + lane) * 16, wh);
             // token-major -W (phi channel order) for Q' = Q~ + Aqk (-W): a selection with -1
             wT[2 * i] = to_bf16x4(mfma(oh, sel_phi(0, q4, n16, true), zero));
             wT[2 * i + 1] = to_bf16x4(mfma(oh, sel_phi(1, q4, n16, true), zero));
@@ -1074,11 +1077,11 @@ __global__ __launch_bounds__(kThreads * HV, (IntraLds<D, HV>::PER_CU * HV)) void
         const DevStore qdst(p.Qf + size_t(rec) * (64 * D), 64 * D * 2);
 #pragma unroll
         for (int i = 0; i < KBW; ++i) {
-            bf16x8 o;
+            f16x8 o;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                o[r] = (__bf16)accQ[2 * i][r];
-                o[4 + r] = (__bf16)accQ[2 * i + 1][r];
+                o[r] = (_Float16)accQ[2 * i][r];
+                o[4 + r] = (_Float16)accQ[2 * i + 1][r];
             }
             qdst.put(unsigned((I * KB + kb0 + i) * 64 + lane) * 16, o);
         }
@@ -1111,9 +1114,9 @@ struct HD {
     static constexpr int KB = D / 32;    // 32-channel K steps of a product over Dk
     static constexpr int MW = D / 64;    // 16-row Dk tiles per wave
     static constexpr int TILES = D / 16; // 16-row Dv tiles per head
-    static constexpr int SLD = D + 8;    // bf16 row stride of the LDS state tile (hi or lo)
+    static constexpr int SLD = D + 8;    // fp16 row stride of the LDS state tile (hi or lo)
 };
-constexpr int VN_LD = 72;   // bf16 [BV][72]   V_new^T tile (hi or lo), row = value channel
+constexpr int VN_LD = 72;   // fp16 [BV][72]   V_new^T tile (hi or lo), row = value channel
 
 // What a chunk step writes besides the state update.
 enum OutMode {
@@ -1124,8 +1127,8 @@ enum OutMode {
 
 template <int NT, int D>
 struct ChunkFrags {
-    bf16x8 w[HD<D>::KB];                          // W, token tile w, 32-channel block kb
-    bf16x8 qp[HD<D>::KB];                         // Q', token tile w
+    f16x8 w[HD<D>::KB];                           // W (fp16), token tile w, 32-channel block kb
+    f16x8 qp[HD<D>::KB];                          // Q' (fp16), token tile w
     f16x8 kh[HD<D>::MW][2];                       // K_dec^T (fp16), Dk tile MW*w+mt, token step s
     float gm[HD<D>::MW];                          // gamma_last, Dk row 4 q4 + (lane & 3) of
                                                   // tile MW*w+mt (quad-broadcast at use), or
@@ -1149,12 +1152,12 @@ __device__ __forceinline__ void load_chunk(const Params& p, int64_t rec, int w, 
     constexpr int KB = HD<D>::KB, MW = HD<D>::MW;
     if constexpr (PART != 2) {
         constexpr unsigned RB = 64 * D * 2;   // bytes of one record array
-        const __bf16* wsrc = p.Wf + size_t(rec) * (64 * D);
-        const __bf16* qsrc = p.Qf + size_t(rec) * (64 * D);
+        const _Float16* wsrc = p.Wf + size_t(rec) * (64 * D);
+        const _Float16* qsrc = p.Qf + size_t(rec) * (64 * D);
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
-            f.w[kb] = ld_op<GLDS, bf16x8>(wsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
-            f.qp[kb] = ld_op<GLDS, bf16x8>(qsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
+            f.w[kb] = ld_op<GLDS, f16x8>(wsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
+            f.qp[kb] = ld_op<GLDS, f16x8>(qsrc, RB, unsigned((w * KB + kb) * 64 + lane) * 16);
         }
         const _Float16* usrc = p.Uf + size_t(rec) * (64 * D);
         const __bf16* osrc = p.Of + size_t(rec) * (64 * D);
@@ -1207,20 +1210,11 @@ __device__ __forceinline__ f32x4 quad_bcast(float x) {
     return r;
 }
 
-// Writes one fp32 state fragment (4 consecutive Dk values of one Dv row) as hi/lo bf16.
+// Writes one fp32 state fragment (4 consecutive Dk values of one Dv row) as an fp16 hi/lo pair,
+// the operands of the fp16 state products (about 22 significant bits; the state's magnitude is
+// bounded by fp16's 65504).
 template <int D>
-__device__ __forceinline__ void put_state(__bf16* sSh, __bf16* sSl, int row, int col,
-                                          f32x4 x) {
-    bf16x4 h, l;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) SPLIT_BF16(x[i], h[i], l[i]);
-    *reinterpret_cast<bf16x4*>(sSh + row * HD<D>::SLD + col) = h;
-    *reinterpret_cast<bf16x4*>(sSl + row * HD<D>::SLD + col) = l;
-}
-
-// The same fragment as an fp16 hi/lo pair (the combine's fp16 products), in the same LDS tiles.
-template <int D>
-__device__ __forceinline__ void put_state16(__bf16* sSh, __bf16* sSl, int row, int col, f32x4 x) {
+__device__ __forceinline__ void put_state16(_Float16* sSh, _Float16* sSl, int row, int col, f32x4 x) {
     f16x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1232,10 +1226,10 @@ __device__ __forceinline__ void put_state16(__bf16* sSh, __bf16* sSl, int row, i
 }
 
 struct ScanLds {
-    __bf16* sh;
-    __bf16* sl;
-    __bf16* vh;
-    __bf16* vl;
+    _Float16* sh;   // the state, fp16 hi/lo
+    _Float16* sl;
+    _Float16* vh;   // V_new, fp16 hi/lo
+    _Float16* vl;
     float* g;   // gamma_last of the current chunk [D]
 };
 
@@ -1268,8 +1262,8 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
             const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
-            const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
-            const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
+            const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
+            const f16x8 sl = *reinterpret_cast<const f16x8*>(L.sl + off);
             accX[nt] = mfma(cur.w[kb], sh, accX[nt]);
             accX[nt] = mfma(cur.w[kb], sl, accX[nt]);
             accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
@@ -1332,7 +1326,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
                 acc = mfma(cur.kh[mt][s], vl[s], acc);
             }
             S[mt][nt] = acc;
-            put_state<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, acc);
+            put_state16<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, acc);
         }
     }
     if constexpr (SPLIT) {
@@ -1384,7 +1378,7 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
 // 23.3-24.0 us.
 template <int D>
 struct Frags8 {
-    bf16x8 a[HD<D>::KB];   // W (X waves) or Q' (Y waves), token tile w & 3
+    f16x8 a[HD<D>::KB];    // W (X waves) or Q' (Y waves), fp16, token tile w & 3
     f16x8 kh[2];           // K_dec^T of Dk tile w, token steps 0 and 1
     float gm;              // gamma_last of row 4 q4 + (lane & 3) of Dk tile w (quad-broadcast)
     f16x4 u;               // U (X waves), token tile w & 3, the Dv tile
@@ -1402,10 +1396,10 @@ __device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w,
     const size_t rb = size_t(rec) * (64 * D);
     const int uo = ((dv_tile * 4 + tt) * 64 + lane) * 4;
     constexpr unsigned RB = 64 * D * 2;
-    const __bf16* src = (ROLE == 0 ? p.Wf : p.Qf) + rb;
+    const _Float16* src = (ROLE == 0 ? p.Wf : p.Qf) + rb;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
-        f.a[kb] = ld_op<BUF, bf16x8>(src, RB, unsigned((tt * KB + kb) * 64 + lane) * 16);
+        f.a[kb] = ld_op<BUF, f16x8>(src, RB, unsigned((tt * KB + kb) * 64 + lane) * 16);
     if constexpr (ROLE == 0 && WITH_U) f.u = ld_op<BUF, f16x4>(p.Uf + rb, RB, unsigned(uo) * 2);
     if constexpr (ROLE == 1 && (OUT == OUT_FINAL || OUT == OUT_O0))
         f.o = ld_op<BUF, bf16x4>(p.Of + rb, RB, unsigned(uo) * 2);
@@ -1437,8 +1431,8 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         const int off = n16 * SLD + 32 * kb + 8 * q4;
-        const bf16x8 sh = *reinterpret_cast<const bf16x8*>(L.sh + off);
-        const bf16x8 sl = *reinterpret_cast<const bf16x8*>(L.sl + off);
+        const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
+        const f16x8 sl = *reinterpret_cast<const f16x8*>(L.sl + off);
         if constexpr (ROLE == 0) {
             acc = mfma(cur.a[kb], sh, acc);
             acc = mfma(cur.a[kb], sl, acc);
@@ -1506,7 +1500,7 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
             a = mfma(cur.kh[s], vl[s], a);
         }
         S = a;
-        put_state<D>(L.sh, L.sl, n16, 16 * w + 4 * q4, a);
+        put_state16<D>(L.sh, L.sl, n16, 16 * w + 4 * q4, a);
     }
     lds_barrier();
 }
@@ -1816,10 +1810,10 @@ __global__ __launch_bounds__((scan_threads<NT, D, PFW>()), (scan_w8<NT, D, PFW>(
 void kda_scan_kernel(Params p) {
     constexpr int BV = 16 * NT;
     constexpr int MW = HD<D>::MW;
-    __shared__ __attribute__((aligned(16))) __bf16 sSh[BV * HD<D>::SLD];
-    __shared__ __attribute__((aligned(16))) __bf16 sSl[BV * HD<D>::SLD];
-    __shared__ __attribute__((aligned(16))) __bf16 sVh[BV * VN_LD];
-    __shared__ __attribute__((aligned(16))) __bf16 sVl[BV * VN_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 sSh[BV * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) _Float16 sSl[BV * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) _Float16 sVh[BV * VN_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 sVl[BV * VN_LD];
     __shared__ __attribute__((aligned(16))) float sG[D];
     const ScanLds L{sSh, sSl, sVh, sVl, sG};
 
@@ -1865,7 +1859,7 @@ void kda_scan_kernel(Params p) {
         const int dk = 16 * w + 4 * q4;
         f32x4 S8 = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
                           : f32x4{0.f, 0.f, 0.f, 0.f};
-        put_state<D>(sSh, sSl, n16, dk, S8);
+        put_state16<D>(sSh, sSl, n16, dk, S8);
         lds_barrier();
         run_chunks8<true, OUT_FINAL, D, true>(p, S8, L, rec0, 0, nchunks, len, ob, os, dv_tile0);
         if (p.fin) *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * D + dk) = S8;
@@ -1882,7 +1876,7 @@ void kda_scan_kernel(Params p) {
             const int dk = 16 * (MW * w + mt) + 4 * q4;
             S[mt][nt] = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
                                : f32x4{0.f, 0.f, 0.f, 0.f};
-            put_state<D>(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
+            put_state16<D>(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
         }
     lds_barrier();
 
@@ -1922,10 +1916,10 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
     constexpr int NDK = D / 16;                               // Dk tiles of the state
     constexpr int MW = NDK >= NW ? NDK / NW : 1, TILES = HD<D>::TILES;   // Dk tiles per wave
     const bool holds = int(threadIdx.x >> 6) < NDK;           // this wave holds a Dk tile
-    __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
-    __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
-    __shared__ __attribute__((aligned(16))) __bf16 sVh[16 * VN_LD];
-    __shared__ __attribute__((aligned(16))) __bf16 sVl[16 * VN_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 sSh[16 * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) _Float16 sSl[16 * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) _Float16 sVh[16 * VN_LD];
+    __shared__ __attribute__((aligned(16))) _Float16 sVl[16 * VN_LD];
     __shared__ __attribute__((aligned(16))) float sG[D];
     const ScanLds L{sSh, sSl, sVh, sVl, sG};
 
@@ -1990,7 +1984,7 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
             x = *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(row) * D + dk);
         }
         S[mt][0] = x;
-        put_state<D>(sSh, sSl, n16, dk, x);
+        put_state16<D>(sSh, sSl, n16, dk, x);
     }
     lds_barrier();
 
@@ -2051,8 +2045,8 @@ __device__ __forceinline__ void complete_record(const Params& p, int64_t rec, in
 template <int D>
 __global__ __launch_bounds__(kThreads, 2) void kda_combine_kernel(Params p) {
     constexpr int MW = HD<D>::MW, KB = HD<D>::KB, TILES = HD<D>::TILES;
-    __shared__ __attribute__((aligned(16))) __bf16 sSh[16 * HD<D>::SLD];
-    __shared__ __attribute__((aligned(16))) __bf16 sSl[16 * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) _Float16 sSh[16 * HD<D>::SLD];
+    __shared__ __attribute__((aligned(16))) _Float16 sSl[16 * HD<D>::SLD];
     const ScanLds L{sSh, sSl, nullptr, nullptr, nullptr};
 
     const int tid = threadIdx.x;
@@ -2145,7 +2139,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_combine_kernel(Params p) {
 // Final state of one 16-row Dv tile of a (sequence, head): S_in(seg_p-1) P_last + N_last, with
 // S_in(seg_p-1) in fp32 where the combine pass left it (the place of N_0).
 template <int D>
-__device__ __forceinline__ void final_state_step(const Params& p, int f, __bf16* lds) {
+__device__ __forceinline__ void final_state_step(const Params& p, int f, _Float16* lds) {
     constexpr int MW = HD<D>::MW, TILES = HD<D>::TILES;
     const int bh = f / TILES, tile = f % TILES;
     if (bh >= p.batch * p.n_v) return;
@@ -2269,7 +2263,7 @@ __global__ __launch_bounds__(kThreads, 2) void kda_out_kernel(Params p) {
     const int64_t rec = blockIdx.x;
     const int64_t n_rec = int64_t(p.intra_units) * p.group;
     if (rec >= n_rec) {
-        if (p.fin) final_state_step<D>(p, int(rec - n_rec), reinterpret_cast<__bf16*>(sR));
+        if (p.fin) final_state_step<D>(p, int(rec - n_rec), reinterpret_cast<_Float16*>(sR));
         return;
     }
     complete_record<D>(p, rec, 2, p.seg_p - 1, sR);   // segment 1 runs in the combine pass
@@ -2388,8 +2382,8 @@ kda_status launch(const kda_shape* shape, const void* q, const void* k, const vo
     p.out = static_cast<__bf16*>(out);
     p.fin = final_state;
     unsigned char* ws = static_cast<unsigned char*>(workspace);
-    p.Wf = reinterpret_cast<__bf16*>(ws + plan.off_w);
-    p.Qf = reinterpret_cast<__bf16*>(ws + plan.off_q);
+    p.Wf = reinterpret_cast<_Float16*>(ws + plan.off_w);
+    p.Qf = reinterpret_cast<_Float16*>(ws + plan.off_q);
     p.Kf = reinterpret_cast<_Float16*>(ws + plan.off_k);
     p.Uf = reinterpret_cast<_Float16*>(ws + plan.off_u);
     p.Of = reinterpret_cast<__bf16*>(ws + plan.off_o);
