@@ -1211,8 +1211,8 @@ __device__ __forceinline__ f32x4 quad_bcast(float x) {
 }
 
 // Writes one fp32 state fragment (4 consecutive Dk values of one Dv row) as an fp16 hi/lo pair,
-// the operands of the fp16 state products (about 22 significant bits; the state's magnitude is
-// bounded by fp16's 65504).
+// the operands of the combine's fp16 products (about 22 significant bits; the state's magnitude
+// is bounded by fp16's 65504).
 template <int D>
 __device__ __forceinline__ void put_state16(_Float16* sSh, _Float16* sSl, int row, int col, f32x4 x) {
     f16x4 h, l;
@@ -1225,8 +1225,18 @@ __device__ __forceinline__ void put_state16(_Float16* sSh, _Float16* sSl, int ro
     *reinterpret_cast<f16x4*>(sSl + row * HD<D>::SLD + col) = l;
 }
 
+// The walks' copy of the state fragment: fp16 (11 significant bits) as the operand of their
+// products with W and Q' (fp16 themselves); the state stays fp32 in registers.
+template <int D>
+__device__ __forceinline__ void put_state_hi(_Float16* sSh, int row, int col, f32x4 x) {
+    f16x4 h;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = (_Float16)x[i];
+    *reinterpret_cast<f16x4*>(sSh + row * HD<D>::SLD + col) = h;
+}
+
 struct ScanLds {
-    _Float16* sh;   // the state, fp16 hi/lo
+    _Float16* sh;   // the state, fp16 (the combine: hi/lo)
     _Float16* sl;
     _Float16* vh;   // V_new, fp16 hi/lo
     _Float16* vl;
@@ -1253,7 +1263,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
 
-    // X = W (S_hi + S_lo)^T (tokens of tile w x Dv); Y^T = S_hi Q'^T (Dv x tokens)
+    // X = W S^T (tokens of tile w x Dv); Y^T = S Q'^T (Dv x tokens), S as its fp16 copy
     f32x4 accX[NT], accY[NT];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
@@ -1263,9 +1273,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
         for (int kb = 0; kb < KB; ++kb) {
             const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
             const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
-            const f16x8 sl = *reinterpret_cast<const f16x8*>(L.sl + off);
             accX[nt] = mfma(cur.w[kb], sh, accX[nt]);
-            accX[nt] = mfma(cur.w[kb], sl, accX[nt]);
             accY[nt] = mfma(sh, cur.qp[kb], accY[nt]);
         }
     }
@@ -1326,7 +1334,7 @@ __device__ __forceinline__ void scan_step(const Params& p, const ChunkFrags<NT, 
                 acc = mfma(cur.kh[mt][s], vl[s], acc);
             }
             S[mt][nt] = acc;
-            put_state16<D>(L.sh, L.sl, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, acc);
+            put_state_hi<D>(L.sh, 16 * nt + n16, 16 * (MW * w + mt) + 4 * q4, acc);
         }
     }
     if constexpr (SPLIT) {
@@ -1426,20 +1434,16 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
     const int n16 = lane & 15;
     const int tt = w & 3;
 
-    // X = W (S_hi + S_lo)^T, or Y^T = S_hi Q'^T (with S_lo too for R), token tile tt
+    // X = W S^T, or Y^T = S Q'^T, token tile tt (S as its fp16 copy)
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
         const int off = n16 * SLD + 32 * kb + 8 * q4;
         const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
-        const f16x8 sl = *reinterpret_cast<const f16x8*>(L.sl + off);
-        if constexpr (ROLE == 0) {
+        if constexpr (ROLE == 0)
             acc = mfma(cur.a[kb], sh, acc);
-            acc = mfma(cur.a[kb], sl, acc);
-        } else {
+        else
             acc = mfma(sh, cur.a[kb], acc);
-            if constexpr (OUT == OUT_R) acc = mfma(sl, cur.a[kb], acc);
-        }
     }
     if constexpr (ROLE == 0) {   // V_new as an fp16 pair, the operand of the fp16 update product
         f16x4 vh, vl;
@@ -1500,7 +1504,7 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
             a = mfma(cur.kh[s], vl[s], a);
         }
         S = a;
-        put_state16<D>(L.sh, L.sl, n16, 16 * w + 4 * q4, a);
+        put_state_hi<D>(L.sh, n16, 16 * w + 4 * q4, a);
     }
     lds_barrier();
 }
@@ -1811,11 +1815,10 @@ void kda_scan_kernel(Params p) {
     constexpr int BV = 16 * NT;
     constexpr int MW = HD<D>::MW;
     __shared__ __attribute__((aligned(16))) _Float16 sSh[BV * HD<D>::SLD];
-    __shared__ __attribute__((aligned(16))) _Float16 sSl[BV * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) _Float16 sVh[BV * VN_LD];
     __shared__ __attribute__((aligned(16))) _Float16 sVl[BV * VN_LD];
     __shared__ __attribute__((aligned(16))) float sG[D];
-    const ScanLds L{sSh, sSl, sVh, sVl, sG};
+    const ScanLds L{sSh, nullptr, sVh, sVl, sG};
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1859,7 +1862,7 @@ void kda_scan_kernel(Params p) {
         const int dk = 16 * w + 4 * q4;
         f32x4 S8 = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
                           : f32x4{0.f, 0.f, 0.f, 0.f};
-        put_state16<D>(sSh, sSl, n16, dk, S8);
+        put_state_hi<D>(sSh, n16, dk, S8);
         lds_barrier();
         run_chunks8<true, OUT_FINAL, D, true>(p, S8, L, rec0, 0, nchunks, len, ob, os, dv_tile0);
         if (p.fin) *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * D + dk) = S8;
@@ -1876,7 +1879,7 @@ void kda_scan_kernel(Params p) {
             const int dk = 16 * (MW * w + mt) + 4 * q4;
             S[mt][nt] = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
                                : f32x4{0.f, 0.f, 0.f, 0.f};
-            put_state16<D>(sSh, sSl, 16 * nt + n16, dk, S[mt][nt]);
+            put_state_hi<D>(sSh, 16 * nt + n16, dk, S[mt][nt]);
         }
     lds_barrier();
 
@@ -1917,11 +1920,10 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
     constexpr int MW = NDK >= NW ? NDK / NW : 1, TILES = HD<D>::TILES;   // Dk tiles per wave
     const bool holds = int(threadIdx.x >> 6) < NDK;           // this wave holds a Dk tile
     __shared__ __attribute__((aligned(16))) _Float16 sSh[16 * HD<D>::SLD];
-    __shared__ __attribute__((aligned(16))) _Float16 sSl[16 * HD<D>::SLD];
     __shared__ __attribute__((aligned(16))) _Float16 sVh[16 * VN_LD];
     __shared__ __attribute__((aligned(16))) _Float16 sVl[16 * VN_LD];
     __shared__ __attribute__((aligned(16))) float sG[D];
-    const ScanLds L{sSh, sSl, sVh, sVl, sG};
+    const ScanLds L{sSh, nullptr, sVh, sVl, sG};
 
     const int tid = threadIdx.x;
     const int w = tid >> 6;
@@ -1984,7 +1986,7 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
             x = *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(row) * D + dk);
         }
         S[mt][0] = x;
-        put_state16<D>(sSh, sSl, n16, dk, x);
+        put_state_hi<D>(sSh, n16, dk, x);
     }
     lds_barrier();
 
