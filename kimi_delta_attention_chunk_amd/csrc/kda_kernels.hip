@@ -1376,41 +1376,45 @@ __device__ __forceinline__ void run_chunks(const Params& p, f32x4 (&S)[HD<D>::MW
     }
 }
 
-// Eight-wave chunk step (the segment pass, and at head dim 128 the one-level one-tile scan with
-// the prefetch wave; one 16-row Dv tile).  With four waves every SIMD holds one wave of the
-// walk, and nothing covers its LDS and memory waits.  Here waves 0..3 take token tile w & 3 of
-// X = W S^T and its V_new, waves 4..7 the same token tile of Y^T = S Q'^T and its outputs, and
-// in the state update each wave takes one 16-row Dk tile (at head dim 64, whose state has four,
-// the X waves alone): the workgroup loads exactly what the four-wave step loads (each operand
-// once), with two waves on every SIMD.  Measured at the 8K prefill: segment pass 24.5-24.9 ->
-// 23.3-24.0 us.
-template <int D>
+// Eight-wave chunk step (the segment pass, one 16-row Dv tile; and at head dim 128 the one-level
+// scans with the prefetch wave, NT = 1 or 2 Dv tiles).  With four waves every SIMD holds one
+// wave of the walk, and nothing covers its LDS and memory waits.  Here waves 0..3 take token
+// tile w & 3 of X = W S^T and its V_new, waves 4..7 the same token tile of Y^T = S Q'^T and its
+// outputs, for each of the NT Dv tiles, and in the state update each wave takes one 16-row Dk
+// tile of every Dv tile (at head dim 64, whose state has four, the X waves alone): the
+// workgroup loads exactly what the four-wave step loads (each operand once; W, Q', K_dec and
+// gamma once for all NT tiles), with two waves on every SIMD.  Measured at the 8K prefill:
+// segment pass 24.5-24.9 -> 23.3-24.0 us.
+template <int D, int NT = 1>
 struct Frags8 {
     f16x8 a[HD<D>::KB];    // W (X waves) or Q' (Y waves), fp16, token tile w & 3
     f16x8 kh[2];           // K_dec^T of Dk tile w, token steps 0 and 1
     float gm;              // gamma_last of row 4 q4 + (lane & 3) of Dk tile w (quad-broadcast)
-    f16x4 u;               // U (X waves), token tile w & 3, the Dv tile
-    bf16x4 o;              // O_intra (Y waves), the same
+    f16x4 u[NT];           // U (X waves), token tile w & 3, Dv tile nt
+    bf16x4 o[NT];          // O_intra (Y waves), the same
 };
 
 // Every operand of one chunk for a wave of the eight-wave walk: W (X waves) or Q' (Y waves) of
-// its token tile, U (X) or O_intra (Y) of that tile and the Dv tile, and the K_dec and gamma
+// its token tile, U (X) or O_intra (Y) of that tile and each Dv tile, and the K_dec and gamma
 // of its Dk tile.
-template <int ROLE, bool WITH_U, int OUT, int D, bool BUF>
+template <int ROLE, bool WITH_U, int OUT, int D, bool BUF, int NT = 1>
 __device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w, int lane,
-                                            int dv_tile, Frags8<D>& f) {
+                                            int dv_tile, Frags8<D, NT>& f) {
     constexpr int KB = HD<D>::KB;
     const int tt = w & 3;
     const size_t rb = size_t(rec) * (64 * D);
-    const int uo = ((dv_tile * 4 + tt) * 64 + lane) * 4;
     constexpr unsigned RB = 64 * D * 2;
     const _Float16* src = (ROLE == 0 ? p.Wf : p.Qf) + rb;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb)
         f.a[kb] = ld_op<BUF, f16x8>(src, RB, unsigned((tt * KB + kb) * 64 + lane) * 16);
-    if constexpr (ROLE == 0 && WITH_U) f.u = ld_op<BUF, f16x4>(p.Uf + rb, RB, unsigned(uo) * 2);
-    if constexpr (ROLE == 1 && (OUT == OUT_FINAL || OUT == OUT_O0))
-        f.o = ld_op<BUF, bf16x4>(p.Of + rb, RB, unsigned(uo) * 2);
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+        const int uo = (((dv_tile + nt) * 4 + tt) * 64 + lane) * 4;
+        if constexpr (ROLE == 0 && WITH_U) f.u[nt] = ld_op<BUF, f16x4>(p.Uf + rb, RB, unsigned(uo) * 2);
+        if constexpr (ROLE == 1 && (OUT == OUT_FINAL || OUT == OUT_O0))
+            f.o[nt] = ld_op<BUF, bf16x4>(p.Of + rb, RB, unsigned(uo) * 2);
+    }
     if constexpr (D == 128 || ROLE == 0) {   // the waves that update a Dk tile of the state
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -1420,91 +1424,97 @@ __device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w,
     }
 }
 
-// One chunk for the workgroup's Dv tile with eight waves (see Frags8); ROLE 0 is an X wave
+// One chunk for the workgroup's NT Dv tiles with eight waves (see Frags8); ROLE 0 is an X wave
 // (waves 0..3), ROLE 1 a Y wave (4..7), each running its own branch-free copy of the walk.
-// Outputs are stored at device scope (the segment pass).
-template <int ROLE, bool WITH_U, int OUT, int D, bool ONE_LEVEL = false>
-__device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur, f32x4& S,
-                                           const ScanLds& L, int w, int jc, int len, size_t ob,
-                                           size_t os, int dv_tile, int64_t rec) {
+// Outputs are stored at device scope (the segment pass) or plainly (ONE_LEVEL).
+template <int ROLE, bool WITH_U, int OUT, int D, bool ONE_LEVEL = false, int NT = 1>
+__device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D, NT>& cur,
+                                           f32x4 (&S)[NT], const ScanLds& L, int w, int jc,
+                                           int len, size_t ob, size_t os, int dv_tile,
+                                           int64_t rec) {
     constexpr int KB = HD<D>::KB, SLD = HD<D>::SLD;
-    static_assert(D / 16 == 8 || D / 16 == 4, "one 16-row Dk tile per wave or per X wave");
     const int lane = threadIdx.x & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
     const int tt = w & 3;
 
-    // X = W S^T, or Y^T = S Q'^T, token tile tt (S as its fp16 copy)
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-        const int off = n16 * SLD + 32 * kb + 8 * q4;
-        const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
-        if constexpr (ROLE == 0)
-            acc = mfma(cur.a[kb], sh, acc);
-        else
-            acc = mfma(sh, cur.a[kb], acc);
-    }
-    if constexpr (ROLE == 0) {   // V_new as an fp16 pair, the operand of the fp16 update product
-        f16x4 vh, vl;
+    for (int nt = 0; nt < NT; ++nt) {
+        // X = W S^T, or Y^T = S Q'^T, token tile tt, Dv tile nt (S as its fp16 copy)
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float x = (WITH_U ? (float)cur.u[r] : 0.f) - acc[r];
-            vh[r] = (_Float16)x;
-            vl[r] = (_Float16)(x - (float)vh[r]);
+        for (int kb = 0; kb < KB; ++kb) {
+            const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
+            const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
+            if constexpr (ROLE == 0) acc = mfma(cur.a[kb], sh, acc);
+            else acc = mfma(sh, cur.a[kb], acc);
         }
-        const int off = n16 * VN_LD + 16 * tt + 4 * q4;
-        *reinterpret_cast<f16x4*>(L.vh + off) = vh;
-        *reinterpret_cast<f16x4*>(L.vl + off) = vl;
-    } else {
-        const int tok = jc * kChunk + 16 * tt + n16;   // output token of this lane
-        bf16x4 yb;
-        if constexpr (OUT == OUT_FINAL) {
-            if (tok < len) {
+        const int dt = dv_tile + nt;
+        if constexpr (ROLE == 0) {   // V_new as an fp16 pair, the operand of the fp16 update
+            f16x4 vh, vl;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(acc[r] + (float)cur.o[r]);
-                if constexpr (!ONE_LEVEL) {
-                    const DevStore dst(p.out + ob + size_t(jc) * kChunk * os,
-                                       unsigned(kChunk * os * 2));
-                    dst.put(unsigned((tok - jc * kChunk) * os + 16 * dv_tile + 4 * q4) * 2, yb);
-                } else {
-                    *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * dv_tile +
-                                               4 * q4) = yb;
-                }
+            for (int r = 0; r < 4; ++r) {
+                const float x = (WITH_U ? (float)cur.u[nt][r] : 0.f) - acc[r];
+                vh[r] = (_Float16)x;
+                vl[r] = (_Float16)(x - (float)vh[r]);
             }
-        } else if constexpr (OUT == OUT_O0) {
+            const int off = (16 * nt + n16) * VN_LD + 16 * tt + 4 * q4;
+            *reinterpret_cast<f16x4*>(L.vh + off) = vh;
+            *reinterpret_cast<f16x4*>(L.vl + off) = vl;
+        } else {
+            const int tok = jc * kChunk + 16 * tt + n16;   // output token of this lane
+            bf16x4 yb;
+            if constexpr (OUT == OUT_FINAL) {
+                if (tok < len) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(acc[r] + (float)cur.o[r]);
-            DevStore(p.O0 + size_t(rec) * (64 * D), 64 * D * 2)
-                .put(unsigned((dv_tile * 4 + tt) * 64 + lane) * 8, yb);
-        } else if constexpr (OUT == OUT_R) {   // R in the completion pass's B-operand order
+                    for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(acc[r] + (float)cur.o[nt][r]);
+                    if constexpr (!ONE_LEVEL) {
+                        const DevStore dst(p.out + ob + size_t(jc) * kChunk * os,
+                                           unsigned(kChunk * os * 2));
+                        dst.put(unsigned((tok - jc * kChunk) * os + 16 * dt + 4 * q4) * 2, yb);
+                    } else {
+                        *reinterpret_cast<bf16x4*>(p.out + ob + size_t(tok) * os + 16 * dt +
+                                                   4 * q4) = yb;
+                    }
+                }
+            } else if constexpr (OUT == OUT_O0) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) yb[r] = (__bf16)acc[r];
-            const int lb = (2 * (dv_tile & 1) + (q4 >> 1)) * 16 + n16;
-            DevStore(p.Rf + size_t(rec) * (64 * D), 64 * D * 2)
-                .put(unsigned(((tt * KB + (dv_tile >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1)) * 2, yb);
+                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)(acc[r] + (float)cur.o[nt][r]);
+                DevStore(p.O0 + size_t(rec) * (64 * D), 64 * D * 2)
+                    .put(unsigned((dt * 4 + tt) * 64 + lane) * 8, yb);
+            } else if constexpr (OUT == OUT_R) {   // R in the completion pass's B-operand order
+#pragma unroll
+                for (int r = 0; r < 4; ++r) yb[r] = (__bf16)acc[r];
+                const int lb = (2 * (dt & 1) + (q4 >> 1)) * 16 + n16;
+                DevStore(p.Rf + size_t(rec) * (64 * D), 64 * D * 2)
+                    .put(unsigned(((tt * KB + (dt >> 1)) * 64 + lb) * 8 + 4 * (q4 & 1)) * 2, yb);
+            }
         }
     }
     lds_barrier();
 
-    // S^T <- gamma * S^T + K_dec^T V_new for Dk tile w, on the fp16 MFMA (at head dim 64, four
-    // Dk tiles: the X waves only)
+    // S^T <- gamma * S^T + K_dec^T V_new for Dk tile w of each Dv tile, on the fp16 MFMA (at head
+    // dim 64, four Dk tiles: the X waves only)
     if constexpr (D == 128 || ROLE == 0) {
-        f16x8 vh[2], vl[2];
+        const f32x4 gq = quad_bcast(cur.gm);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int off = n16 * VN_LD + 32 * s + 8 * q4;
-            vh[s] = *reinterpret_cast<const f16x8*>(L.vh + off);
-            vl[s] = *reinterpret_cast<const f16x8*>(L.vl + off);
-        }
-        f32x4 a = S * quad_bcast(cur.gm);
+        for (int nt = 0; nt < NT; ++nt) {
+            f16x8 vh[2], vl[2];
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            a = mfma(cur.kh[s], vh[s], a);
-            a = mfma(cur.kh[s], vl[s], a);
+            for (int s = 0; s < 2; ++s) {
+                const int off = (16 * nt + n16) * VN_LD + 32 * s + 8 * q4;
+                vh[s] = *reinterpret_cast<const f16x8*>(L.vh + off);
+                vl[s] = *reinterpret_cast<const f16x8*>(L.vl + off);
+            }
+            f32x4 a = S[nt] * gq;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                a = mfma(cur.kh[s], vh[s], a);
+                a = mfma(cur.kh[s], vl[s], a);
+            }
+            S[nt] = a;
+            put_state_hi<D>(L.sh + 16 * nt * SLD, n16, 16 * w + 4 * q4, a);
         }
-        S = a;
-        put_state_hi<D>(L.sh, n16, 16 * w + 4 * q4, a);
     }
     lds_barrier();
 }
@@ -1513,10 +1523,10 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D>& cur
 // waves 0..3 run the X copy and waves 4..7 the Y copy of the walk, with the same barriers.
 // ONE_LEVEL: the one-level scan (outputs stored plainly, operands as buffer loads); otherwise
 // the segment pass (outputs at device scope, plain operand loads): each measured faster there.
-template <int ROLE, bool WITH_U, int OUT, int D, bool ONE_LEVEL = false>
-__device__ __forceinline__ void run_walk8(const Params& p, f32x4& S, const ScanLds& L, int w,
-                                          int64_t rec0, int cb, int ce, int len, size_t ob,
-                                          size_t os, int dv_tile) {
+template <int ROLE, bool WITH_U, int OUT, int D, bool ONE_LEVEL = false, int NT = 1>
+__device__ __forceinline__ void run_walk8(const Params& p, f32x4 (&S)[NT], const ScanLds& L,
+                                          int w, int64_t rec0, int cb, int ce, int len,
+                                          size_t ob, size_t os, int dv_tile) {
     const int lane = threadIdx.x & 63;
     const int last = ce - 1;
     // the next chunk's loads are written ahead of the step; the compiler issues them after the
@@ -1526,31 +1536,36 @@ __device__ __forceinline__ void run_walk8(const Params& p, f32x4& S, const ScanL
     // fast as issuing them two chunks ahead from a third operand set, and faster than loads
     // split around the products (with which the compiler folded the two-step loop into one and
     // drained every load, K_dec's included, at the top of each step)
-    Frags8<D> fa, fb;
-    load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, rec0 + int64_t(cb) * p.n_v, w, lane, dv_tile, fa);
+    Frags8<D, NT> fa, fb;
+    load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL, NT>(p, rec0 + int64_t(cb) * p.n_v, w, lane,
+                                                     dv_tile, fa);
     for (int jc = cb; jc < ce; jc += 2) {
         const int c1 = jc + 1 < last ? jc + 1 : last;
-        load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, rec0 + int64_t(c1) * p.n_v, w, lane, dv_tile, fb);
-        scan_step8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, fa, S, L, w, jc, len, ob, os, dv_tile,
-                                         rec0 + int64_t(jc) * p.n_v);
+        load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL, NT>(p, rec0 + int64_t(c1) * p.n_v, w, lane,
+                                                         dv_tile, fb);
+        scan_step8<ROLE, WITH_U, OUT, D, ONE_LEVEL, NT>(p, fa, S, L, w, jc, len, ob, os,
+                                                        dv_tile, rec0 + int64_t(jc) * p.n_v);
         if (jc + 1 >= ce) break;
         const int c2 = jc + 2 < last ? jc + 2 : last;
-        load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, rec0 + int64_t(c2) * p.n_v, w, lane, dv_tile, fa);
-        scan_step8<ROLE, WITH_U, OUT, D, ONE_LEVEL>(p, fb, S, L, w, jc + 1, len, ob, os, dv_tile,
-                                         rec0 + int64_t(jc + 1) * p.n_v);
+        load_chunk8<ROLE, WITH_U, OUT, D, ONE_LEVEL, NT>(p, rec0 + int64_t(c2) * p.n_v, w, lane,
+                                                         dv_tile, fa);
+        scan_step8<ROLE, WITH_U, OUT, D, ONE_LEVEL, NT>(p, fb, S, L, w, jc + 1, len, ob, os,
+                                                        dv_tile, rec0 + int64_t(jc + 1) * p.n_v);
     }
 }
 
-template <bool WITH_U, int OUT, int D, bool ONE_LEVEL = false>
-__device__ __forceinline__ void run_chunks8(const Params& p, f32x4& S, const ScanLds& L,
+template <bool WITH_U, int OUT, int D, bool ONE_LEVEL = false, int NT = 1>
+__device__ __forceinline__ void run_chunks8(const Params& p, f32x4 (&S)[NT], const ScanLds& L,
                                             int64_t rec0, int cb, int ce, int len, size_t ob,
                                             size_t os, int dv_tile) {
     if (cb >= ce) return;
     const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x) >> 6);
     if (w < 4)
-        run_walk8<0, WITH_U, OUT, D, ONE_LEVEL>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
+        run_walk8<0, WITH_U, OUT, D, ONE_LEVEL, NT>(p, S, L, w, rec0, cb, ce, len, ob, os,
+                                                    dv_tile);
     else
-        run_walk8<1, WITH_U, OUT, D, ONE_LEVEL>(p, S, L, w, rec0, cb, ce, len, ob, os, dv_tile);
+        run_walk8<1, WITH_U, OUT, D, ONE_LEVEL, NT>(p, S, L, w, rec0, cb, ce, len, ob, os,
+                                                    dv_tile);
 }
 
 // Sequences of different lengths (cu_seqlens given) are walked longest first: workgroup rank r
@@ -1800,12 +1815,14 @@ __device__ __forceinline__ void zero_rows_past_len(const Params& p, int len, siz
 // The register budget of two workgroups per compute unit (at most 256 VGPRs a lane) for every
 // four-wave form: with one, the compiler spreads the two- and four-tile forms over VGPRs and
 // AGPRs and copies the accumulators back and forth inside the chunk loop.
-// The one-tile prefetched scan at head dim 128 walks on eight waves (the eight-wave step) with
-// the prefetch wave as a ninth, one workgroup per compute unit (its budget: 9 waves, at most
-// three on a SIMD).  128K scan 1.96 -> 1.92 ms against the four-wave walk with buffer loads;
-// with plain loads the eight-wave walk was slower (2.03 ms).
+// The one- and two-tile prefetched scans at head dim 128 walk on eight waves (the eight-wave
+// step) with the prefetch wave as a ninth, one workgroup per compute unit (its budget: 9 waves,
+// at most three on a SIMD).  One tile: 128K scan 1.96 -> 1.92 ms against the four-wave walk
+// with buffer loads; with plain loads the eight-wave walk was slower (2.03 ms).  Two tiles
+// (each chunk's W, Q', K_dec and gamma loaded once for 32 state rows): GQA scan (64 chains)
+// 110 -> 98 us against the four-wave two-tile walk.
 template <int NT, int D, bool PFW>
-constexpr bool scan_w8() { return PFW && NT == 1 && D == 128; }
+constexpr bool scan_w8() { return PFW && NT <= 2 && D == 128; }
 template <int NT, int D, bool PFW>
 constexpr int scan_threads() { return scan_w8<NT, D, PFW>() ? 9 * 64 : (PFW ? kPfThreads : kThreads); }
 
@@ -1857,16 +1874,27 @@ void kda_scan_kernel(Params p) {
     }
 
     const size_t st_base = (size_t(b) * p.n_v + h) * D * D;
-    if constexpr (W8) {   // wave w holds Dk tile w of the workgroup's 16 state rows
-        const int dv = 16 * dv_tile0 + n16;
+    if constexpr (W8) {   // wave w holds Dk tile w of each of the workgroup's NT Dv tiles
         const int dk = 16 * w + 4 * q4;
-        f32x4 S8 = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
-                          : f32x4{0.f, 0.f, 0.f, 0.f};
-        put_state_hi<D>(sSh, n16, dk, S8);
+        f32x4 S8[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+            const int dv = 16 * (dv_tile0 + nt) + n16;
+            S8[nt] = p.init ? *reinterpret_cast<const f32x4*>(p.init + st_base + size_t(dv) * D + dk)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+            put_state_hi<D>(sSh, 16 * nt + n16, dk, S8[nt]);
+        }
         lds_barrier();
-        run_chunks8<true, OUT_FINAL, D, true>(p, S8, L, rec0, 0, nchunks, len, ob, os, dv_tile0);
-        if (p.fin) *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * D + dk) = S8;
-        if (tid < kThreads) zero_rows_past_len(p, len, ob, os, 16 * dv_tile0, 16);
+        run_chunks8<true, OUT_FINAL, D, true, NT>(p, S8, L, rec0, 0, nchunks, len, ob, os,
+                                                  dv_tile0);
+        if (p.fin) {
+#pragma unroll
+            for (int nt = 0; nt < NT; ++nt) {
+                const int dv = 16 * (dv_tile0 + nt) + n16;
+                *reinterpret_cast<f32x4*>(p.fin + st_base + size_t(dv) * D + dk) = S8[nt];
+            }
+        }
+        if (tid < kThreads) zero_rows_past_len(p, len, ob, os, 16 * dv_tile0, 16 * NT);
         return;
     }
     // state tile: S[mt][nt][i] = S[dv = 16(dv_tile0+nt) + n16][dk = 16(MW w+mt) + 4q4 + i]
@@ -1992,7 +2020,7 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
 
     const size_t m = (size_t(bh) * p.seg_p + seg) * D * D;
     if (is_p) {
-        run_chunks8<false, OUT_R, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
+        run_chunks8<false, OUT_R, D>(p, S[0], L, rec0, cb, ce, len, ob, os, tile);
         // rows 16 tile .. of P_s, in fp16, into the combine's A fragments of P_s^T: element
         // P_s[16 tile + n16][16 M + 4 q4 + i] is lane (2 (tile & 1) + (n16 >> 3), 4 q4 + i),
         // entry n16 & 7, of fragment (M, tile >> 1)
@@ -2009,9 +2037,9 @@ __global__ __launch_bounds__(64 * seg_waves<D>(), 2) void kda_seg_kernel(Params 
             }
     } else {
         if (seg == 0)
-            run_chunks8<true, OUT_FINAL, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
+            run_chunks8<true, OUT_FINAL, D>(p, S[0], L, rec0, cb, ce, len, ob, os, tile);
         else
-            run_chunks8<true, OUT_O0, D>(p, S[0][0], L, rec0, cb, ce, len, ob, os, tile);
+            run_chunks8<true, OUT_O0, D>(p, S[0], L, rec0, cb, ce, len, ob, os, tile);
 #pragma unroll
         for (int mt = 0; mt < MW; ++mt)
             if (holds)
@@ -2317,12 +2345,11 @@ const Variant kVariants[] = {
     KDA_VARIANT(kda_out_kernel, kThreads, 128),
     KDA_VARIANT(kda_out_kernel, kThreads, 64),
     KDA_VARIANT(kda_scan_kernel, (scan_threads<1, 128, true>()), 1,128,true),
-    KDA_VARIANT(kda_scan_kernel, kPfThreads, 2,128,true),
-    KDA_VARIANT(kda_scan_kernel, kThreads, 1,128,false),
+    KDA_VARIANT(kda_scan_kernel, (scan_threads<2, 128, true>()), 2,128,true),
     KDA_VARIANT(kda_scan_kernel, kThreads, 2,128,false),
     KDA_VARIANT(kda_scan_kernel, kThreads, 4,128,false),
-    KDA_VARIANT(kda_scan_kernel, kPfThreads, 1,64,true),
-    KDA_VARIANT(kda_scan_kernel, kPfThreads, 2,64,true),
+    KDA_VARIANT(kda_scan_kernel, (scan_threads<1, 64, true>()), 1,64,true),
+    KDA_VARIANT(kda_scan_kernel, (scan_threads<2, 64, true>()), 2,64,true),
     KDA_VARIANT(kda_scan_kernel, kThreads, 1,64,false),
     KDA_VARIANT(kda_scan_kernel, kThreads, 2,64,false),
     KDA_VARIANT(kda_scan_kernel, kThreads, 4,64,false),

@@ -77,6 +77,11 @@ kda_status make_plan(const kda_shape* s, Plan* plan) {
     p.scan_nt = 1;
     for (int nt = 4; nt >= 2; nt /= 2)
         if (bh * (tiles / nt) >= 256) { p.scan_nt = nt; break; }
+    // At head dim 128, 33..63 chains would take 264..504 one-tile workgroups, two per compute
+    // unit; as 132..252 two-tile workgroups with the record prefetch wave they run one per unit
+    // on the eight-wave walk, which loads each chunk's shared operands once for both tiles
+    // (measured at 8K tokens: 48 heads scan 285 -> 171 us, 40 heads 276 -> 167 us).
+    if (p.scan_nt == 1 && p.d == 128 && bh * tiles > 256) p.scan_nt = 2;
     // Few (sequence, head) chains leave most compute units idle through a long sequential scan.
     // Then each sequence is cut into seg_p segments and every segment is walked at once: from
     // a zero state (from the initial state for segment 0), giving its end state N_s and the

@@ -111,12 +111,13 @@ TWO_LEVEL = [
 
 # Shapes that make the plan select each kernel variant no other case reaches (the selection
 # depends on the head dim, the number of (sequence, head) chains and of chunk records): the
-# one-level scan without the prefetch wave at one and two Dv tiles per workgroup (33-63 and
-# 65-127 chains at head dim 128; the FlashKDA README's performance shapes have 24-48 heads),
-# the head-dim-64 scans above 64 chains, and the scalar-gate intra kernel in its four-wave form
-# (more than 512 chunk records).  Each is compared in full.
+# one-level scan at head dim 128 with two Dv tiles per workgroup, on the eight-wave walk with
+# the prefetch wave (33-64 chains; the FlashKDA README's performance shapes have 24-48 heads)
+# and on four waves without it (65-127 chains), the head-dim-64 scans above 64 chains, and the
+# scalar-gate intra kernel in its four-wave form (more than 512 chunk records).  Each is
+# compared in full.
 VARIANT_CASES = [
-    ("scan_1x128_n48_gqa", dict(layout="BNSD", batch=1, seq_len=1100, n_qk=12, n_v=48,
+    ("scan_2x128_pf8w_n48_gqa", dict(layout="BNSD", batch=1, seq_len=1100, n_qk=12, n_v=48,
                                 g_kind="strong", init=True, seed=61)),
     ("scan_2x128_b2_n48", dict(layout="BSND", batch=2, seq_len=600, n_qk=48, n_v=48,
                                g_kind="unit", init=True, seed=62)),
