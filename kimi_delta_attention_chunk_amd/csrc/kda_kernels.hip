@@ -1411,7 +1411,8 @@ __device__ __forceinline__ void load_chunk8(const Params& p, int64_t rec, int w,
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
         const int uo = (((dv_tile + nt) * 4 + tt) * 64 + lane) * 4;
-        if constexpr (ROLE == 0 && WITH_U) f.u[nt] = ld_op<BUF, f16x4>(p.Uf + rb, RB, unsigned(uo) * 2);
+        if constexpr (ROLE == 0 && WITH_U)
+            f.u[nt] = ld_op<BUF, f16x4>(p.Uf + rb, RB, unsigned(uo) * 2);
         if constexpr (ROLE == 1 && (OUT == OUT_FINAL || OUT == OUT_O0))
             f.o[nt] = ld_op<BUF, bf16x4>(p.Of + rb, RB, unsigned(uo) * 2);
     }
@@ -1433,6 +1434,7 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D, NT>&
                                            int len, size_t ob, size_t os, int dv_tile,
                                            int64_t rec) {
     constexpr int KB = HD<D>::KB, SLD = HD<D>::SLD;
+    static_assert(D / 16 == 8 || D / 16 == 4, "one 16-row Dk tile per wave or per X wave");
     const int lane = threadIdx.x & 63;
     const int q4 = lane >> 4;
     const int n16 = lane & 15;
@@ -1446,8 +1448,10 @@ __device__ __forceinline__ void scan_step8(const Params& p, const Frags8<D, NT>&
         for (int kb = 0; kb < KB; ++kb) {
             const int off = (16 * nt + n16) * SLD + 32 * kb + 8 * q4;
             const f16x8 sh = *reinterpret_cast<const f16x8*>(L.sh + off);
-            if constexpr (ROLE == 0) acc = mfma(cur.a[kb], sh, acc);
-            else acc = mfma(sh, cur.a[kb], acc);
+            if constexpr (ROLE == 0)
+                acc = mfma(cur.a[kb], sh, acc);
+            else
+                acc = mfma(sh, cur.a[kb], acc);
         }
         const int dt = dv_tile + nt;
         if constexpr (ROLE == 0) {   // V_new as an fp16 pair, the operand of the fp16 update
