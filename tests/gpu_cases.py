@@ -119,6 +119,12 @@ TWO_LEVEL = [
 VARIANT_CASES = [
     ("scan_2x128_pf8w_n48_gqa", dict(layout="BNSD", batch=1, seq_len=1100, n_qk=12, n_v=48,
                                 g_kind="strong", init=True, seed=61)),
+    ("scan_2x128_pf8w_b2_valid", dict(layout="BSND", batch=2, seq_len=700, n_qk=10, n_v=20,
+                                      g_kind="strong", init=True, seed=69,
+                                      valid_lengths=[700, 333])),
+    ("scan_2x128_pf8w_tnd_40", dict(layout="TND", batch=4, seq_len=0, n_qk=5, n_v=10,
+                                    g_kind="mixed", init=True, seed=70,
+                                    lengths=[500, 64, 1, 300])),
     ("scan_2x128_b2_n48", dict(layout="BSND", batch=2, seq_len=600, n_qk=48, n_v=48,
                                g_kind="unit", init=True, seed=62)),
     ("scan_1x64_n96", dict(layout="BNSD", batch=1, seq_len=300, n_qk=96, n_v=96,
