@@ -331,13 +331,15 @@ def test_null_states(seq_len, init):
     assert_parity(out, ro, "no final_state out")
 
 
-@pytest.mark.parametrize("raw", [False, True], ids=["activated_gate", "raw_gate"])
-def test_timed_entry_points_bitwise(raw):
+@pytest.mark.parametrize("raw,n_v", [(False, 2), (True, 2), (False, 40)],
+                         ids=["activated_gate", "raw_gate", "one_level_2tile_8wave"])
+def test_timed_entry_points_bitwise(raw, n_v):
     """kda_chunk_fwd_timed and kda_chunk_fwd_raw_gate_timed run the same kernels as the untimed
     calls (their dispatches only record HIP events): bitwise equal outputs, and every event of a
-    launched stage completes with a non-negative duration."""
+    launched stage completes with a non-negative duration.  Two value heads take the two-level
+    scan; forty the one-level two-tile scan on eight waves with the prefetch wave."""
     from kimi_delta_attention_chunk_amd import kda_num_stages
-    inp = make_inputs("BNSD", 1, 64 * 40 + 9, 1, 2, g_kind="strong", init=True, seed=29,
+    inp = make_inputs("BNSD", 1, 64 * 40 + 9, 1, n_v, g_kind="strong", init=True, seed=29,
                       raw_gate=raw).to("cuda")
     o1, f1 = chunk_fwd(inp)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * kda_num_stages())]
