@@ -60,6 +60,9 @@ WORKLOADS = [
     Workload("prefill_s8k_n6_d64", "BNSD", 1, 8192, 6, 6, "strong", True, 1006,
              note="the 8K prefill at head dim 64 with six heads (the same q/k/v bytes as three "
                   "128-dim heads); g = -5*sigmoid(N(0,1)); state N(0,0.1^2)", d=64),
+    Workload("prefill_s8k_n48", "BNSD", 1, 8192, 48, 48, "strong", True, 1008,
+             note="B=1, Nqk=Nv=48, S=8192, BNSD (the largest head count of the FlashKDA README's "
+                  "performance shapes); g = -5*sigmoid(N(0,1)); state N(0,0.1^2)"),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS}
 
