@@ -114,6 +114,26 @@ def test_plan_query(lib):
                                   None, None) == 0
 
 
+@pytest.mark.parametrize("layout, batch, heads, d, scan", [
+    # 32 chains fill the compute units with one-tile workgroups and the prefetch wave
+    ("BNSD", 1, 32, 128, "kda_scan_kernel<1,128,true>"),
+    # 33..64 chains at head dim 128: two tiles a workgroup, eight waves and the prefetch wave
+    ("BNSD", 1, 33, 128, "kda_scan_kernel<2,128,true>"),
+    ("BNSD", 1, 48, 128, "kda_scan_kernel<2,128,true>"),
+    ("BSND", 4, 16, 128, "kda_scan_kernel<2,128,true>"),
+    # 65..127 chains: two tiles on four waves, two workgroups a compute unit
+    ("BNSD", 2, 48, 128, "kda_scan_kernel<2,128,false>"),
+    ("BNSD", 1, 128, 128, "kda_scan_kernel<4,128,false>"),
+    # head dim 64 keeps one tile up to 64 chains (with the prefetch wave up to 64)
+    ("BNSD", 1, 48, 64, "kda_scan_kernel<1,64,true>"),
+])
+def test_plan_scan_kernel(layout, batch, heads, d, scan):
+    """The one-level scan form the plan picks for a long sequence, by chains and head dim."""
+    from kimi_delta_attention_chunk_amd import kda_chunk_fwd_plan_kernels
+    shape = make_shape(layout, batch, 8192, heads, heads, 0.1, d_k=d, d_v=d)
+    assert kda_chunk_fwd_plan_kernels(shape)[-1] == scan
+
+
 @pytest.mark.parametrize("bad, code", [
     (dict(layout=7), 1), (dict(batch=0), 1), (dict(seq_len=0), 1), (dict(n_qk=0), 1),
     (dict(n_qk=4, n_v=2), 1), (dict(n_qk=3, n_v=4), 1), (dict(d_k=64), 2), (dict(d_v=256), 2),
