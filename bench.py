@@ -18,7 +18,9 @@ Roofline: `roofline` is the dominant kernel's: the call's algorithmic bytes (1,5
 token-head at Nqk = Nv plus the states; `path_bytes`) over that kernel's average duration,
 against the 8 TB/s HBM peak; `traffic` is that kernel's HBM bytes per launch from the committed
 rocprofv3 counter summary (profiles/), null when the kernel sources changed since; and
-`traffic_ratio` the counter bytes of all launched kernels over the algorithmic bytes.
+`traffic_ratio` the counter bytes of all launched kernels over the algorithmic bytes; `l2_read`
+each kernel's L1-to-L2 read bytes per launch (from the same summary) and their rate, the bound
+of the chunk walks (about 26 B per clock per compute unit).
 `path_roofline` uses the whole step time.  `copy_ceiling` times a plain device copy of the
 algorithmic bytes (the practical bandwidth of a transfer that size).  The CPU baseline times the
 fp64 oracle on the host cores on the full workload.
@@ -198,6 +200,14 @@ def measured_traffic(summary, kernel: str):
         return None
     k = summary["kernels"][kernel]
     return (k["fetch_kib"] * summary["fetch_scale"] + k["write_kib"] * summary["write_scale"]) * 1024
+
+
+def measured_l2_read(summary, kernel: str):
+    """Bytes the kernel's vector L1s read from L2 per launch (TCP_TCC_READ_REQ x 128 B) from a
+    counter summary, or None."""
+    if summary is None or kernel not in summary.get("kernels", {}):
+        return None
+    return summary["kernels"][kernel].get("l2_read_bytes")
 
 
 def cpu_model() -> str:
@@ -384,6 +394,13 @@ def main() -> int:
                           "frac": pbytes / (ms_step * 1e-3) / HBM_PEAK},
         "traffic_ratio": None if all_traffic is None else all_traffic / pbytes,
         "kernel_traffic": traffic,
+        # what bounds the chunk walks: the bytes each kernel's L1s pull from L2 per launch, and
+        # that rate per compute unit (256 units; the two-level segment pass runs on fewer)
+        "l2_read": {kda_stage_name(s): None if measured_l2_read(summary, kda_stage_name(s)) is None
+                    else {"bytes": measured_l2_read(summary, kda_stage_name(s)),
+                          "GB/s": measured_l2_read(summary, kda_stage_name(s))
+                          / (stage_ms[s] * 1e-3) / 1e9}
+                    for s in live},
         "per_call_ms": {"median": call_ms[len(call_ms) // 2], "min": call_ms[0],
                         "mean": sum(call_ms) / len(call_ms)},
         "copy_ceiling": copy_ceiling(pbytes),
